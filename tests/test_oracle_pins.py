@@ -1,0 +1,388 @@
+"""Pins for the fp64 oracle: each test checks the oracle against something
+other than itself -- an invariant the pages state, a closed form, a library
+routine, brute force on a tiny input, or a number the pages print.
+
+Pages: "L'attention hybride" (Qwen3.8-27B architecture chapter): section
+"La recurrence" (alpha fades the whole state; beta rewrites the association
+of k_t; identity I), "La dissymetrie 16 / 48" (3 value heads per key head),
+"L'etat, en memoire" (constant state size), table "Le decompte" (dimensions
+and parameter counts).  "Les briques d'un reseau de neurones": section 2
+(SiLU, sigmoid), section 4 (RMSNorm).  Course page "Chapitre 16", 16.2
+(blocks of 64).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.signal
+import torch
+
+import oracle
+from oracle.chunked import chunked_head, decode_single_pass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rand_problem(rng, B, T, Hk, Hv, Dk, Dv, unit_keys=True, state=True):
+    q = rng.standard_normal((B, T, Hk * Dk))
+    k = rng.standard_normal((B, T, Hk * Dk))
+    if unit_keys:
+        kk = k.reshape(B, T, Hk, Dk)
+        k = (kk / np.linalg.norm(kk, axis=-1, keepdims=True)).reshape(B, T, Hk * Dk)
+    v = rng.standard_normal((B, T, Hv * Dv))
+    la = -0.5 * rng.random((B, T, Hv))
+    be = rng.random((B, T, Hv))
+    M0 = rng.standard_normal((B, Hv, Dk, Dv)) * 0.1 if state else None
+    return q, k, v, la, be, M0
+
+
+def test_identity_gates_leave_state_unchanged():
+    # alpha = 1, beta = 0: nothing fades, nothing is written ("La recurrence" symbol table).
+    rng = np.random.default_rng(11)
+    B, T, Hk, Hv, Dk, Dv = 2, 9, 1, 2, 6, 4
+    q, k, v, _, _, M0 = _rand_problem(rng, B, T, Hk, Hv, Dk, Dv, unit_keys=False)
+    la = np.zeros((B, T, Hv))
+    be = np.zeros((B, T, Hv))
+    o, st = oracle.recurrence(q, k, v, la, be, Hk, Hv, M0)
+    np.testing.assert_array_equal(st.reshape(B, Hv, Dk, Dv), M0)
+    for b in range(B):
+        for h in range(Hv):
+            exp_o = q[b].reshape(T, Hk, Dk)[:, 0, :] @ M0[b, h]   # o_t = S_0 q_t
+            np.testing.assert_allclose(o[b * Hv + h], exp_o, rtol=1e-13, atol=1e-13)
+
+
+def test_pure_decay_when_nothing_is_written():
+    # beta = 0: S_T = (prod alpha_t) S_0 and o_t = (prod_{s<=t} alpha_s) S_0 q_t.
+    rng = np.random.default_rng(12)
+    B, T, Hk, Hv, Dk, Dv = 1, 17, 1, 1, 5, 7
+    q, k, v, la, _, M0 = _rand_problem(rng, B, T, Hk, Hv, Dk, Dv)
+    be = np.zeros((B, T, Hv))
+    o, st = oracle.recurrence(q, k, v, la, be, Hk, Hv, M0)
+    decay = np.exp(np.cumsum(la[0, :, 0]))
+    np.testing.assert_allclose(st[0], decay[-1] * M0[0, 0], rtol=1e-12)
+    np.testing.assert_allclose(o[0], decay[:, None] * (q[0] @ M0[0, 0]), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("Dk,Dv,n", [(8, 5, 8), (8, 5, 3), (16, 16, 11)])
+def test_orthonormal_keys_recall_exactly(Dk, Dv, n):
+    # alpha = beta = 1 with orthonormal keys from S_0 = 0: S_n k_j = v_j (exact recall),
+    # and reading with q_t = k_t right after writing returns v_t (read after the update).
+    rng = np.random.default_rng(13)
+    Qm, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+    keys = Qm[:, :n].T                                   # n orthonormal rows
+    vals = rng.standard_normal((n, Dv))
+    q = keys[None].copy()
+    k = keys[None].copy()
+    v = vals[None].copy()
+    la = np.zeros((1, n, 1))
+    be = np.ones((1, n, 1))
+    o, st = oracle.recurrence(q, k, v, la, be, 1, 1, None)
+    M = st[0]                                            # M = S^T, shape [Dk, Dv]
+    assert M.shape == (Dk, Dv)
+    np.testing.assert_allclose(keys @ M, vals, atol=1e-12)        # S k_j = M^T k_j = v_j
+    np.testing.assert_allclose(o[0], vals, atol=1e-12)
+    if n < Dk:
+        perp = Qm[:, n:].T
+        np.testing.assert_allclose(perp @ M, 0.0, atol=1e-12)   # nothing else was written
+
+
+def test_same_key_written_twice_keeps_latest():
+    # beta = 1 erases the line of k and rewrites it: S k = v_latest.
+    rng = np.random.default_rng(14)
+    Dk, Dv = 6, 4
+    kk = rng.standard_normal(Dk)
+    kk /= np.linalg.norm(kk)
+    other = rng.standard_normal(Dk)
+    other -= (other @ kk) * kk
+    other /= np.linalg.norm(other)
+    k = np.stack([kk, other, kk])[None]
+    v = rng.standard_normal((1, 3, Dv))
+    o, st = oracle.recurrence(k.copy(), k, v, np.zeros((1, 3, 1)), np.ones((1, 3, 1)), 1, 1)
+    np.testing.assert_allclose(kk @ st[0], v[0, 2], atol=1e-12)
+    np.testing.assert_allclose(other @ st[0], v[0, 1], atol=1e-12)
+
+
+def test_repeated_unit_key_is_first_order_iir():
+    # One repeated unit key k, constant alpha, beta: x_t = S_t k obeys
+    # x_t = alpha (1 - beta) x_{t-1} + beta v_t -- a first-order IIR filter (scipy lfilter);
+    # directions orthogonal to k only decay: S_T u = alpha^T S_0 u.
+    rng = np.random.default_rng(15)
+    Dk, Dv, T = 7, 5, 40
+    kk = rng.standard_normal(Dk)
+    kk /= np.linalg.norm(kk)
+    a, b = 0.93, 0.37
+    v = rng.standard_normal((1, T, Dv))
+    M0 = rng.standard_normal((1, 1, Dk, Dv))
+    k = np.tile(kk, (1, T, 1))
+    o, st = oracle.recurrence(k.copy(), k, v, np.full((1, T, 1), np.log(a)), np.full((1, T, 1), b), 1, 1, M0)
+    c = a * (1.0 - b)
+    x0 = kk @ M0[0, 0]
+    ref, _ = scipy.signal.lfilter([b], [1.0, -c], v[0], axis=0, zi=(c * x0)[None, :])
+    np.testing.assert_allclose(o[0], ref, rtol=1e-11, atol=1e-12)
+    u = rng.standard_normal(Dk)
+    u -= (u @ kk) * kk
+    np.testing.assert_allclose(u @ st[0], a ** T * (u @ M0[0, 0]), rtol=1e-11, atol=1e-13)
+
+
+def test_repeated_unit_key_time_varying_gates():
+    # Same closed form with per-token gates, as a two-line recursion.
+    rng = np.random.default_rng(16)
+    Dk, Dv, T = 4, 3, 25
+    kk = rng.standard_normal(Dk)
+    kk /= np.linalg.norm(kk)
+    la = -rng.random((1, T, 1))
+    be = rng.random((1, T, 1))
+    v = rng.standard_normal((1, T, Dv))
+    k = np.tile(kk, (1, T, 1))
+    o, _ = oracle.recurrence(k.copy(), k, v, la, be, 1, 1)
+    x = np.zeros(Dv)
+    for t in range(T):
+        x = np.exp(la[0, t, 0]) * (1 - be[0, t, 0]) * x + be[0, t, 0] * v[0, t]
+        np.testing.assert_allclose(o[0, t], x, rtol=1e-12, atol=1e-13)
+
+
+def test_contraction_bound_and_chaining():
+    # For unit k and beta in [0,1], (I - beta k k^T) has norm <= 1, so
+    # ||S_t||_F <= alpha_t ||S_{t-1}||_F + beta_t ||v_t||.  Also checks state chaining.
+    rng = np.random.default_rng(17)
+    B, T, Hk, Hv, Dk, Dv = 1, 30, 1, 1, 8, 8
+    q, k, v, la, be, M0 = _rand_problem(rng, B, T, Hk, Hv, Dk, Dv)
+    M = M0
+    for t in range(T):
+        _, st = oracle.recurrence(q[:, t:t + 1], k[:, t:t + 1], v[:, t:t + 1], la[:, t:t + 1],
+                                  be[:, t:t + 1], Hk, Hv, M)
+        lhs = np.linalg.norm(st[0])
+        rhs = np.exp(la[0, t, 0]) * np.linalg.norm(M[0, 0]) + be[0, t, 0] * np.linalg.norm(v[0, t])
+        assert lhs <= rhs * (1 + 1e-12)
+        M = st.reshape(1, 1, Dk, Dv)
+    _, st_all = oracle.recurrence(q, k, v, la, be, Hk, Hv, M0)
+    np.testing.assert_allclose(st_all[0], M[0, 0], rtol=1e-12, atol=1e-14)
+
+
+def test_two_halves_equal_one_pass():
+    rng = np.random.default_rng(18)
+    B, T, Hk, Hv, Dk, Dv = 2, 50, 2, 6, 8, 8
+    q, k, v, la, be, M0 = _rand_problem(rng, B, T, Hk, Hv, Dk, Dv)
+    o, st = oracle.recurrence(q, k, v, la, be, Hk, Hv, M0)
+    h = 23
+    c = np.ascontiguousarray
+    o1, st1 = oracle.recurrence(c(q[:, :h]), c(k[:, :h]), c(v[:, :h]), la[:, :h], be[:, :h], Hk, Hv, M0)
+    o2, st2 = oracle.recurrence(c(q[:, h:]), c(k[:, h:]), c(v[:, h:]), la[:, h:], be[:, h:], Hk, Hv,
+                                st1.reshape(B, Hv, Dk, Dv))
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=1), o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(st2, st, rtol=1e-12, atol=1e-13)
+
+
+def test_linear_in_state_and_values():
+    rng = np.random.default_rng(19)
+    B, T, Hk, Hv, Dk, Dv = 1, 20, 1, 3, 6, 5
+    q, k, v, la, be, M0 = _rand_problem(rng, B, T, Hk, Hv, Dk, Dv)
+    v2 = rng.standard_normal(v.shape)
+    M2 = rng.standard_normal(M0.shape)
+    oa, sa = oracle.recurrence(q, k, v, la, be, Hk, Hv, M0)
+    ob, sb = oracle.recurrence(q, k, v2, la, be, Hk, Hv, M2)
+    oc, sc = oracle.recurrence(q, k, v + 2.5 * v2, la, be, Hk, Hv, M0 + 2.5 * M2)
+    np.testing.assert_allclose(oc, oa + 2.5 * ob, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sc, sa + 2.5 * sb, rtol=1e-11, atol=1e-12)
+
+
+def test_value_columns_evolve_independently():
+    # Permuting the value coordinates of v (and of S_0) permutes o and S the same way.
+    rng = np.random.default_rng(20)
+    B, T, Hk, Hv, Dk, Dv = 1, 15, 1, 1, 5, 9
+    q, k, v, la, be, M0 = _rand_problem(rng, B, T, Hk, Hv, Dk, Dv)
+    perm = rng.permutation(Dv)
+    o, st = oracle.recurrence(q, k, v, la, be, Hk, Hv, M0)
+    op, stp = oracle.recurrence(q, k, np.ascontiguousarray(v[..., perm]), la, be, Hk, Hv,
+                                np.ascontiguousarray(M0[..., perm]))
+    np.testing.assert_allclose(op, o[..., perm], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(stp, st[..., perm], rtol=1e-13, atol=1e-14)
+
+
+def test_grouped_value_heads_use_key_head_h_div_G():
+    # "La dissymetrie 16 / 48": several value heads share one key head.  Value head h
+    # must equal a single-head run on key head h // G; value heads of one key head with
+    # identical v, alpha, beta give identical outputs.
+    rng = np.random.default_rng(21)
+    B, T, Hk, G, Dk, Dv = 1, 12, 2, 3, 6, 4
+    Hv = Hk * G
+    q, k, v, la, be, M0 = _rand_problem(rng, B, T, Hk, Hv, Dk, Dv)
+    o, st = oracle.recurrence(q, k, v, la, be, Hk, Hv, M0)
+    for h in range(Hv):
+        hk = h // G
+        sl = slice(hk * Dk, (hk + 1) * Dk)
+        o1, s1 = oracle.recurrence(np.ascontiguousarray(q[..., sl]), np.ascontiguousarray(k[..., sl]),
+                                   np.ascontiguousarray(v[..., h * Dv:(h + 1) * Dv]),
+                                   np.ascontiguousarray(la[..., h:h + 1]),
+                                   np.ascontiguousarray(be[..., h:h + 1]), 1, 1,
+                                   np.ascontiguousarray(M0[:, h:h + 1]))
+        np.testing.assert_allclose(o[h], o1[0], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(st[h], s1[0], rtol=1e-13, atol=1e-14)
+    v_same = v.copy().reshape(B, T, Hv, Dv)
+    v_same[:, :, 1] = v_same[:, :, 0]
+    v_same[:, :, 2] = v_same[:, :, 0]
+    la2, be2 = la.copy(), be.copy()
+    la2[..., 1:3] = la2[..., 0:1]
+    be2[..., 1:3] = be2[..., 0:1]
+    o2, _ = oracle.recurrence(q, k, v_same.reshape(B, T, Hv * Dv), la2, be2, Hk, Hv, None)
+    np.testing.assert_array_equal(o2[1], o2[0])
+    np.testing.assert_array_equal(o2[2], o2[0])
+
+
+def test_l2_flag_and_q_scale():
+    rng = np.random.default_rng(22)
+    B, T, Hk, Hv, Dk, Dv = 1, 10, 2, 4, 8, 8
+    q, k, v, la, be, M0 = _rand_problem(rng, B, T, Hk, Hv, Dk, Dv, unit_keys=False)
+    eps = 1e-6
+
+    def nrm(a):
+        h = a.reshape(B, T, Hk, Dk)
+        return (h / np.sqrt((h ** 2).sum(-1, keepdims=True) + eps)).reshape(a.shape)
+
+    o1, s1 = oracle.recurrence(q, k, v, la, be, Hk, Hv, M0, l2norm=True, l2_eps=eps)
+    o2, s2 = oracle.recurrence(nrm(q), nrm(k), v, la, be, Hk, Hv, M0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s1, s2, rtol=1e-12, atol=1e-13)
+    o3, s3 = oracle.recurrence(q, k, v, la, be, Hk, Hv, M0, l2norm=True, l2_eps=eps, q_scale=0.25)
+    np.testing.assert_allclose(o3, 0.25 * o1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(s3, s1)
+
+
+@pytest.mark.parametrize("C", [1, 3, 16, 64])
+@pytest.mark.parametrize("T", [37, 64, 100, 130])
+@pytest.mark.parametrize("form", ["fused", "wy"])
+def test_chunked_form_equals_sequential(C, T, form):
+    # The blocked algebra (intra-chunk triangular solve + state hand-off) reaches the
+    # definition's numbers; d_k != d_v pins the orientation, ragged tails are included.
+    rng = np.random.default_rng(100 + C + T)
+    Dk, Dv = 12, 7
+    q, k, v, _, be, M0 = _rand_problem(rng, 1, T, 1, 1, Dk, Dv)
+    la = -np.exp(rng.uniform(0, np.log(16), 1)) * np.logaddexp(0, rng.standard_normal((1, T, 1)))
+    o, st = oracle.recurrence(q, k, v, la, be, 1, 1, M0)
+    oc, Mc = chunked_head(q[0], k[0], v[0], la[0, :, 0], be[0, :, 0], M0[0, 0], C=C, form=form)
+    scale = np.abs(o).max()
+    np.testing.assert_allclose(oc, o[0], rtol=0, atol=1e-11 * scale)
+    np.testing.assert_allclose(Mc, st[0], rtol=0, atol=1e-11 * np.abs(st).max())
+
+
+def test_decode_single_pass_identity():
+    rng = np.random.default_rng(23)
+    Dk, Dv = 16, 16
+    q, k, v, la, be, M0 = _rand_problem(rng, 1, 1, 1, 1, Dk, Dv)
+    o, st = oracle.recurrence(q, k, v, la, be, 1, 1, M0)
+    od, Md = decode_single_pass(M0[0, 0], q[0, 0], k[0, 0], v[0, 0], la[0, 0, 0], be[0, 0, 0])
+    np.testing.assert_allclose(od, o[0, 0], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(Md, st[0], rtol=1e-13, atol=1e-15)
+
+
+def test_pages_dimensions_and_constant_state_size():
+    g = json.load(open(os.path.join(HERE, "golden", "qwen38_gdn_layer.json")))
+    cfg = g["config"]
+    Hv, Hk = cfg["linear_num_value_heads"], cfg["linear_num_key_heads"]
+    Dk, Dv, K = cfg["linear_key_head_dim"], cfg["linear_value_head_dim"], cfg["linear_conv_kernel_dim"]
+    dm, L = g["d_model"], g["n_gdn_layers"]
+    P = g["params"]
+    # Channel layout used by the conv / norm: conv over q|k|v, norm weight of width Dv.
+    conv_channels = 2 * Hk * Dk + Hv * Dv
+    assert dm * (2 * Hk * Dk + 2 * Hv * Dv) == P["in_proj_qkvz"]
+    assert dm * 2 * Hv == P["in_proj_ba"]
+    assert conv_channels * K == P["conv"]
+    assert Hv * Dv * dm == P["out_proj"]
+    assert Dv == P["norm"]
+    total = P["in_proj_qkvz"] + P["in_proj_ba"] + P["conv"] + P["out_proj"] + P["norm"]
+    assert total == P["total_per_layer"]
+    assert round(total * L / 1e9, 3) == P["total_all_layers_G"]
+    # The state is one fp32 [Dk, Dv] matrix per value head, whatever the length.
+    rng = np.random.default_rng(24)
+    sizes = []
+    for T in (3, 40):
+        q, k, v, la, be, _ = _rand_problem(rng, 1, T, Hk, Hv, Dk, Dv, state=False)
+        _, st = oracle.recurrence(q, k, v, la, be, Hk, Hv, None, want_o=False)
+        sizes.append(st.size * np.dtype(np.float32).itemsize)
+    assert sizes[0] == sizes[1] == Hv * Dk * Dv * 4 == 3_145_728
+    states = sizes[0] * L
+    assert states == 150_994_944 and states <= g["state_total_Mo"] * 1e6
+    conv_window = conv_channels * K * 4 * L        # reconstruction: a K-wide fp32 window per channel
+    assert round((states + conv_window) / 1e6) == g["state_total_Mo"]
+    # Course page 16.2: 256 prompt tokens in blocks of 64 make 4 blocks.
+    ex = g["chunk_example"]
+    assert -(-ex["prompt_tokens"] // ex["block"]) == ex["blocks"]
+
+
+def test_conv_impulse_response():
+    # A unit impulse at token t0 in channel c yields silu(w[c][K-1-m]) at token t0+m.
+    B, T, C, K = 1, 12, 3, 4
+    rng = np.random.default_rng(25)
+    w = rng.standard_normal((C, K))
+    x = np.zeros((B, T, C))
+    x[0, 5, 1] = 1.0
+    y, _ = oracle.conv1d_silu(x, w)
+    silu = lambda a: a / (1 + np.exp(-a))
+    exp = np.zeros((T, C))
+    for m in range(K):
+        exp[5 + m, 1] = silu(w[1, K - 1 - m])
+    np.testing.assert_allclose(y, exp, rtol=1e-14, atol=1e-15)
+
+
+def test_conv_matches_fir_filter_and_state_continuation():
+    B, T, C, K = 2, 37, 5, 4
+    rng = np.random.default_rng(26)
+    x = rng.standard_normal((B, T, C))
+    w = rng.standard_normal((C, K))
+    cs = rng.standard_normal((B, C, K - 1))
+    silu = lambda a: a / (1 + np.exp(-a))
+    for b in range(B):
+        y, st = oracle.conv1d_silu(x, w, cs, b=b, want_state=True)
+        for c in range(C):
+            full = np.concatenate([cs[b, c], x[b, :, c]])
+            ref = scipy.signal.lfilter(w[c, ::-1], [1.0], full)[K - 1:]
+            np.testing.assert_allclose(y[:, c], silu(ref), rtol=1e-12, atol=1e-14)
+        np.testing.assert_array_equal(st[b], x[b, T - (K - 1):, :].T)
+    # Two halves with the window handed over equal one pass.
+    h = 2
+    x1, x2 = np.ascontiguousarray(x[:, :h]), np.ascontiguousarray(x[:, h:])
+    _, s1 = oracle.conv1d_silu(x1, w, cs, want_state=True)
+    for b in range(B):
+        ya, _ = oracle.conv1d_silu(x, w, cs, b=b)
+        y2, _ = oracle.conv1d_silu(x2, w, s1, b=b)
+        np.testing.assert_allclose(y2, ya[h:], rtol=1e-13, atol=1e-15)
+
+
+def test_gated_rmsnorm_closed_forms():
+    D = 128
+    rng = np.random.default_rng(27)
+    w = rng.normal(1.0, 0.1, D)
+    eps = 1e-5
+    sig = lambda a: 1 / (1 + np.exp(-a))
+    # Constant row c*1: rms = |c|, so y = c / sqrt(c^2 + eps) * w * z sigmoid(z).
+    for c in (3.0, -0.01):
+        x = np.full((1, D), c)
+        z = rng.standard_normal((1, D))
+        y = oracle.gated_rmsnorm(x, z, w, eps)
+        np.testing.assert_allclose(y[0], c / np.sqrt(c * c + eps) * w * z[0] * sig(z[0]), rtol=1e-13)
+    # z = 0 closes the gate; with eps = 0 the norm is scale-free and odd, and the
+    # normalised part has unit RMS.
+    x = rng.standard_normal((4, D))
+    z = rng.standard_normal((4, D))
+    assert np.all(oracle.gated_rmsnorm(x, np.zeros_like(z), w, eps) == 0.0)
+    y0 = oracle.gated_rmsnorm(x, z, w, 0.0)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(7.5 * x, z, w, 0.0), y0, rtol=1e-13)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(-x, z, w, 0.0), -y0, rtol=1e-13)
+    n = y0 / (w * z * sig(z))
+    np.testing.assert_allclose(np.sqrt((n ** 2).mean(-1)), 1.0, rtol=1e-13)
+    # Row selection returns the same rows.
+    ys = oracle.gated_rmsnorm(x, z, w, eps, rows=[3, 1])
+    yall = oracle.gated_rmsnorm(x, z, w, eps)
+    np.testing.assert_array_equal(ys, yall[[3, 1]])
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(28)
+    a = np.concatenate([rng.standard_normal(20000).astype(np.float32),
+                        (rng.standard_normal(2000) * 1e-39).astype(np.float32),      # subnormals
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, -0.0], np.float32)])
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.round_bf16(a.astype(np.float64)), ref)
+    from gated_deltanet_recurrence_rule_amd.workloads import f32_to_bf16
+    np.testing.assert_array_equal(f32_to_bf16(a), ref)
