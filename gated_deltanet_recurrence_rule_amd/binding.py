@@ -1,0 +1,224 @@
+"""ctypes binding of libgdn (include/gdn.h): argument marshalling only.
+
+Each function takes torch tensors, checks their layout enough to build the C
+arguments (pointers, element strides, the current HIP stream) and calls the
+same-named C entry point.  Every step of the computation runs in the HIP
+kernels of libgdn.so; there is no Python or CPU fallback.  If the library
+has not been built, loading fails with an error that says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn.so")
+
+GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN, GDN_ERR_DEVICE = range(6)
+GDN_F32, GDN_BF16 = 0, 1
+GDN_FLAG_QK_L2NORM = 1
+
+# Every exported symbol, in the order include/gdn.h declares them.
+EXPORTS = ("gdn_prefill", "gdn_decode_step", "gdn_conv1d_silu", "gdn_gated_rmsnorm",
+           "gdn_last_error", "gdn_version")
+
+
+class GdnDims(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hk", ctypes.c_int32),
+        ("Hv", ctypes.c_int32), ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+        ("io", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("stride_q", ctypes.c_int64), ("stride_k", ctypes.c_int64),
+        ("stride_v", ctypes.c_int64), ("stride_o", ctypes.c_int64),
+        ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libgdn status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libgdn.so (built in-tree by build_lib.py); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(or python gated_deltanet_recurrence_rule_amd/build_lib.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.gdn_prefill.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p, p]
+        L.gdn_prefill.restype = ctypes.c_int
+        L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p]
+        L.gdn_decode_step.restype = ctypes.c_int
+        L.gdn_conv1d_silu.argtypes = [i32, i32, i32, i32, i32, p, i64, p, p, p, p, i64, p]
+        L.gdn_conv1d_silu.restype = ctypes.c_int
+        L.gdn_gated_rmsnorm.argtypes = [i64, i32, i32, i32, p, i64, p, i64, p, ctypes.c_float, p, i64, p]
+        L.gdn_gated_rmsnorm.restype = ctypes.c_int
+        L.gdn_last_error.argtypes = []
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_version.argtypes = []
+        L.gdn_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, lib().gdn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _io(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"io tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _token_stride(t, B: int, T: int, width: int, name: str) -> int:
+    """[B, T, >= width] tensor (or view) with contiguous last dim and batch
+    stride T * token stride; returns the token stride in elements."""
+    if t.dim() != 3 or t.shape[0] != B or t.shape[1] != T or t.shape[2] < width:
+        raise ValueError(f"{name}: expected [B={B}, T={T}, >={width}], got {tuple(t.shape)}")
+    s0, s1, s2 = t.stride()
+    if s2 != 1:
+        raise ValueError(f"{name}: last dim must be contiguous")
+    if T > 1:
+        if B > 1 and s0 != T * s1:
+            raise ValueError(f"{name}: batch stride must be T * token stride")
+        return s1
+    return s0 if B > 1 else max(width, s1)
+
+
+def make_dims(B, T, Hk, Hv, D, io, flags=0, sq=None, sk=None, sv=None, so=None,
+              q_scale=1.0, l2_eps=1e-6) -> GdnDims:
+    return GdnDims(B, T, Hk, Hv, D, D, io, flags,
+                   Hk * D if sq is None else sq, Hk * D if sk is None else sk,
+                   Hv * D if sv is None else sv, Hv * D if so is None else so,
+                   q_scale, l2_eps)
+
+
+def gdn_prefill(q, k, v, log_alpha, beta, state_in=None, state_out=None, o=None, *, Hk: int,
+                Hv: int, l2norm: bool = False, l2_eps: float = 1e-6, q_scale: float = 1.0,
+                stream=None):
+    """q, k: [B, T, Hk*D] views; v: [B, T, Hv*D]; log_alpha, beta: [B, T, Hv] fp32;
+    state_in / state_out: [B, Hv, D, D] fp32 or None; o: [B, T, >=Hv*D] or None
+    (allocated).  Returns o."""
+    import torch
+    B, T = int(q.shape[0]), int(q.shape[1])
+    if q.shape[2] % Hk or v.shape[2] % Hv or q.shape[2] // Hk != v.shape[2] // Hv:
+        raise ValueError("q must be [B, T, Hk*D] and v [B, T, Hv*D] (views of exactly that width)")
+    D = int(q.shape[2]) // Hk
+    io = _io(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or (o is not None and o.dtype != q.dtype):
+        raise ValueError("q, k, v and o must share one dtype")
+    if o is None:
+        o = torch.empty((B, T, Hv * D), dtype=q.dtype, device=q.device)
+    dims = make_dims(B, T, Hk, Hv, D, io, GDN_FLAG_QK_L2NORM if l2norm else 0,
+                     _token_stride(q, B, T, Hk * D, "q"), _token_stride(k, B, T, Hk * D, "k"),
+                     _token_stride(v, B, T, Hv * D, "v"), _token_stride(o, B, T, Hv * D, "o"),
+                     q_scale, l2_eps)
+    for name, g in (("log_alpha", log_alpha), ("beta", beta)):
+        if g.dtype != torch.float32 or not g.is_contiguous() or tuple(g.shape) != (B, T, Hv):
+            raise ValueError(f"{name} must be contiguous fp32 [B, T, Hv]")
+    for name, s in (("state_in", state_in), ("state_out", state_out)):
+        if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()
+                              or tuple(s.shape) != (B, Hv, D, D)):
+            raise ValueError(f"{name} must be contiguous fp32 [B, Hv, D, D]")
+    _check(lib().gdn_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                             _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o), _stream(stream)))
+    return o
+
+
+def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None, *, Hk: int, Hv: int,
+                    l2norm: bool = False, l2_eps: float = 1e-6, q_scale: float = 1.0, stream=None):
+    """q, k: [B, >=Hk*D]; v: [B, >=Hv*D]; log_alpha, beta: [B, Hv] fp32;
+    state: [B, Hv, D, D] fp32 (updated in place); o: [B, >=Hv*D] or None.  Returns o."""
+    import torch
+    B = int(state.shape[0])
+    D = int(state.shape[2])
+    io = _io(q)
+    if o is None:
+        o = torch.empty((B, Hv * D), dtype=q.dtype, device=q.device)
+    for name, t, w in (("q", q, Hk * D), ("k", k, Hk * D), ("v", v, Hv * D), ("o", o, Hv * D)):
+        if t.dim() != 2 or t.shape[0] != B or t.shape[1] < w or t.stride(1) != 1:
+            raise ValueError(f"{name}: expected [B, >={w}] with contiguous rows")
+    for name, g in (("log_alpha", log_alpha), ("beta", beta)):
+        if g.dtype != torch.float32 or not g.is_contiguous() or tuple(g.shape) != (B, Hv):
+            raise ValueError(f"{name} must be contiguous fp32 [B, Hv]")
+    if state.dtype != torch.float32 or not state.is_contiguous() or tuple(state.shape) != (B, Hv, D, D):
+        raise ValueError("state must be contiguous fp32 [B, Hv, D, D]")
+    dims = make_dims(B, 1, Hk, Hv, D, io, GDN_FLAG_QK_L2NORM if l2norm else 0,
+                     q.stride(0) if B > 1 else Hk * D, k.stride(0) if B > 1 else Hk * D,
+                     v.stride(0) if B > 1 else Hv * D, o.stride(0) if B > 1 else Hv * D,
+                     q_scale, l2_eps)
+    _check(lib().gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                 _ptr(beta), _ptr(state), _ptr(o), _stream(stream)))
+    return o
+
+
+def gdn_conv1d_silu(x, w, conv_state_in=None, conv_state_out=None, y=None, *, stream=None):
+    """x: [B, T, >=C] view (contiguous channels); w: [C, 4]; conv states [B, C, 3] or None;
+    y: [B, T, >=C] or None (allocated [B, T, C]).  Returns y."""
+    import torch
+    B, T = int(x.shape[0]), int(x.shape[1])
+    C, K = int(w.shape[0]), int(w.shape[1])
+    io = _io(x)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=x.dtype, device=x.device)
+    sx = _token_stride(x, B, T, C, "x") if T > 0 else C
+    sy = _token_stride(y, B, T, C, "y") if T > 0 else C
+    if w.dtype != x.dtype or not w.is_contiguous():
+        raise ValueError("w must be contiguous with x's dtype")
+    for name, s in (("conv_state_in", conv_state_in), ("conv_state_out", conv_state_out)):
+        if s is not None and (s.dtype != x.dtype or not s.is_contiguous() or tuple(s.shape) != (B, C, K - 1)):
+            raise ValueError(f"{name} must be contiguous [B, C, K-1] with x's dtype")
+    _check(lib().gdn_conv1d_silu(B, T, C, K, io, _ptr(x), sx, _ptr(w), _ptr(conv_state_in),
+                                 _ptr(conv_state_out), _ptr(y), sy, _stream(stream)))
+    return y
+
+
+def gdn_gated_rmsnorm(x, z, w, eps: float = 1e-5, y=None, *, H: int, stream=None):
+    """x, z: [n_tok, >=H*D] (contiguous channels); w: [D]; y: [n_tok, >=H*D] or None.
+    Rows are (token, head) D-vectors.  Returns y."""
+    import torch
+    D = int(w.shape[0])
+    n = int(x.shape[0])
+    io = _io(x)
+    if y is None:
+        y = torch.empty((n, H * D), dtype=x.dtype, device=x.device)
+    for name, t in (("x", x), ("z", z), ("y", y)):
+        if t.dim() != 2 or t.shape[0] != n or t.shape[1] < H * D or t.stride(1) != 1 or t.dtype != x.dtype:
+            raise ValueError(f"{name}: expected [n_tok, >={H * D}] with contiguous channels")
+    if w.dtype != x.dtype or not w.is_contiguous():
+        raise ValueError("w must be contiguous with x's dtype")
+    _check(lib().gdn_gated_rmsnorm(n, H, D, io, _ptr(x), x.stride(0) if n > 1 else H * D, _ptr(z),
+                                   z.stride(0) if n > 1 else H * D, _ptr(w), float(eps), _ptr(y),
+                                   y.stride(0) if n > 1 else H * D, _stream(stream)))
+    return y
+
+
+def gdn_version() -> int:
+    return int(lib().gdn_version())
+
+
+def gdn_last_error() -> str:
+    return lib().gdn_last_error().decode()

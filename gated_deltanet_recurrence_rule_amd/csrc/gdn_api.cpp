@@ -1,0 +1,211 @@
+// gdn_api.cpp -- the extern "C" entry points of libgdn (declared in
+// include/gdn.h): argument validation on the host, kernel dispatch, status
+// codes and the thread-local error message.  Validation happens before any
+// HIP call, so argument errors are reported even on a machine without a GPU.
+#include "../../include/gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdn_status fail(gdn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+gdn_status ok() {
+  g_err[0] = '\0';
+  return GDN_OK;
+}
+
+gdn_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(GDN_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Checks shared by prefill and decode.  `T1` demands T == 1.
+gdn_status check_dims(const gdn_dims* d, bool T1) {
+  if (!d) return fail(GDN_ERR_NULL, "dims is NULL");
+  if (d->B < 0 || d->T < 0) return fail(GDN_ERR_SHAPE, "B=%d T=%d must be >= 0", d->B, d->T);
+  if (T1 && d->T != 1) return fail(GDN_ERR_SHAPE, "decode step needs T == 1 (got %d)", d->T);
+  if (d->Hk < 1 || d->Hv < 1) return fail(GDN_ERR_SHAPE, "Hk=%d Hv=%d must be >= 1", d->Hk, d->Hv);
+  if (d->Hv % d->Hk != 0) return fail(GDN_ERR_SHAPE, "Hv=%d is not a multiple of Hk=%d", d->Hv, d->Hk);
+  if (d->Dk < 1 || d->Dv < 1) return fail(GDN_ERR_SHAPE, "Dk=%d Dv=%d must be >= 1", d->Dk, d->Dv);
+  if (d->io != GDN_F32 && d->io != GDN_BF16) return fail(GDN_ERR_SHAPE, "io dtype %d unknown", d->io);
+  if (d->Dk != d->Dv || !supported_d(d->Dk))
+    return fail(GDN_ERR_UNSUPPORTED, "head widths Dk=%d Dv=%d: kernels take Dk == Dv in {16,32,64,128}",
+                d->Dk, d->Dv);
+  if ((d->flags & ~GDN_FLAG_QK_L2NORM) != 0) return fail(GDN_ERR_SHAPE, "unknown flag bits 0x%x", d->flags);
+  const int64_t wq = static_cast<int64_t>(d->Hk) * d->Dk, wv = static_cast<int64_t>(d->Hv) * d->Dv;
+  if (d->stride_q < wq || d->stride_k < wq)
+    return fail(GDN_ERR_SHAPE, "stride_q=%lld / stride_k=%lld below Hk*Dk=%lld", (long long)d->stride_q,
+                (long long)d->stride_k, (long long)wq);
+  if (d->stride_v < wv || d->stride_o < wv)
+    return fail(GDN_ERR_SHAPE, "stride_v=%lld / stride_o=%lld below Hv*Dv=%lld", (long long)d->stride_v,
+                (long long)d->stride_o, (long long)wv);
+  if (d->flags & GDN_FLAG_QK_L2NORM) {
+    if (!(d->l2_eps >= 0.0f)) return fail(GDN_ERR_SHAPE, "l2_eps must be >= 0");
+  }
+  return GDN_OK;
+}
+
+bool use_chunk_kernel(const gdn_dims* d) { return d->io == GDN_BF16 && d->Dk == 128 && d->T > 0; }
+
+gdn::RecArgs rec_args(const gdn_dims* d, const void* q, const void* k, const void* v, const float* la,
+                      const float* beta, const float* sin, float* sout, void* o) {
+  gdn::RecArgs a;
+  a.B = d->B;
+  a.T = d->T;
+  a.Hk = d->Hk;
+  a.Hv = d->Hv;
+  a.G = d->Hv / d->Hk;
+  a.D = d->Dk;
+  a.flags = d->flags;
+  a.q_scale = d->q_scale;
+  a.l2_eps = d->l2_eps;
+  a.sq = d->stride_q;
+  a.sk = d->stride_k;
+  a.sv = d->stride_v;
+  a.so = d->stride_o;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.la = la;
+  a.beta = beta;
+  a.state_in = sin;
+  a.state_out = sout;
+  a.o = o;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const float* state_in,
+                       float* state_out, void* o, void* stream) {
+  gdn_status st = check_dims(d, false);
+  if (st != GDN_OK) return st;
+  if (d->B == 0) return ok();
+  if (d->T > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
+    return fail(GDN_ERR_NULL, "q, k, v, log_alpha, beta and o are required");
+  if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
+    return fail(GDN_ERR_ALIGN, "state pointers must be 16-byte aligned");
+  if (d->T == 0 && !state_out) return ok();
+  if (use_chunk_kernel(d)) {
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+      return fail(GDN_ERR_ALIGN, "bf16 q, k, v must be 16-byte aligned");
+    if ((d->stride_q % 8) || (d->stride_k % 8) || (d->stride_v % 8))
+      return fail(GDN_ERR_ALIGN, "bf16 strides of q, k, v must be multiples of 8 elements");
+    return from_hip(gdn::launch_chunk_prefill(
+                        rec_args(d, q, k, v, log_alpha, beta, state_in, state_out, o),
+                        static_cast<hipStream_t>(stream)),
+                    "gdn_prefill (chunk kernel)");
+  }
+  const size_t es = d->io == GDN_BF16 ? 2 : 4;
+  if (d->T > 0 && (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(o, es)))
+    return fail(GDN_ERR_ALIGN, "q, k, v, o must be aligned to their element size");
+  return from_hip(gdn::launch_recurrent(rec_args(d, q, k, v, log_alpha, beta, state_in, state_out, o),
+                                        d->io, static_cast<hipStream_t>(stream)),
+                  "gdn_prefill (token-serial kernel)");
+}
+
+gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, float* state, void* o,
+                           void* stream) {
+  gdn_status st = check_dims(d, true);
+  if (st != GDN_OK) return st;
+  if (d->B == 0) return ok();
+  if (!q || !k || !v || !log_alpha || !beta || !state || !o)
+    return fail(GDN_ERR_NULL, "q, k, v, log_alpha, beta, state and o are required");
+  if (!aligned(state, 16)) return fail(GDN_ERR_ALIGN, "state must be 16-byte aligned");
+  const size_t es = d->io == GDN_BF16 ? 2 : 4;
+  if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(o, es))
+    return fail(GDN_ERR_ALIGN, "q, k, v, o must be aligned to their element size");
+  return from_hip(gdn::launch_recurrent(rec_args(d, q, k, v, log_alpha, beta, state, state, o), d->io,
+                                        static_cast<hipStream_t>(stream)),
+                  "gdn_decode_step");
+}
+
+gdn_status gdn_conv1d_silu(int32_t B, int32_t T, int32_t C, int32_t K, int32_t dtype, const void* x,
+                           int64_t stride_x, const void* w, const void* conv_state_in,
+                           void* conv_state_out, void* y, int64_t stride_y, void* stream) {
+  if (B < 0 || T < 0 || C < 1) return fail(GDN_ERR_SHAPE, "B=%d T=%d C=%d", B, T, C);
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_SHAPE, "dtype %d unknown", dtype);
+  if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "conv kernel width K=%d: only K=4 is implemented", K);
+  if (C % 8) return fail(GDN_ERR_UNSUPPORTED, "C=%d must be a multiple of 8", C);
+  if (stride_x < C || stride_y < C) return fail(GDN_ERR_SHAPE, "strides must be >= C");
+  if (B == 0 || (T == 0 && !conv_state_out)) return ok();
+  if (!w || (T > 0 && (!x || !y))) return fail(GDN_ERR_NULL, "x, w and y are required");
+  if (conv_state_in && conv_state_in == conv_state_out)
+    return fail(GDN_ERR_SHAPE, "conv_state_out must not alias conv_state_in");
+  const size_t vec = 16;
+  if ((x && !aligned(x, vec)) || (y && !aligned(y, vec)))
+    return fail(GDN_ERR_ALIGN, "x and y must be 16-byte aligned");
+  if ((stride_x % 8) || (stride_y % 8)) return fail(GDN_ERR_ALIGN, "strides must be multiples of 8");
+  gdn::ConvArgs a;
+  a.B = B;
+  a.T = T;
+  a.C = C;
+  a.K = K;
+  a.sx = stride_x;
+  a.sy = stride_y;
+  a.x = x;
+  a.w = w;
+  a.cs_in = conv_state_in;
+  a.cs_out = conv_state_out;
+  a.y = y;
+  return from_hip(gdn::launch_conv1d_silu(a, dtype, static_cast<hipStream_t>(stream)), "gdn_conv1d_silu");
+}
+
+gdn_status gdn_gated_rmsnorm(int64_t n_tok, int32_t H, int32_t D, int32_t dtype, const void* x,
+                             int64_t stride_x, const void* z, int64_t stride_z, const void* w, float eps,
+                             void* y, int64_t stride_y, void* stream) {
+  if (n_tok < 0 || H < 1) return fail(GDN_ERR_SHAPE, "n_tok=%lld H=%d", (long long)n_tok, H);
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_SHAPE, "dtype %d unknown", dtype);
+  if (D != 64 && D != 128) return fail(GDN_ERR_UNSUPPORTED, "D=%d: only 64 and 128 are implemented", D);
+  const int64_t wd = static_cast<int64_t>(H) * D;
+  if (stride_x < wd || stride_z < wd || stride_y < wd) return fail(GDN_ERR_SHAPE, "strides must be >= H*D");
+  if (!(eps >= 0.0f)) return fail(GDN_ERR_SHAPE, "eps must be >= 0");
+  if (n_tok == 0) return ok();
+  if (!x || !z || !w || !y) return fail(GDN_ERR_NULL, "x, z, w and y are required");
+  if (!aligned(x, 16) || !aligned(z, 16) || !aligned(w, 16) || !aligned(y, 16))
+    return fail(GDN_ERR_ALIGN, "x, z, w, y must be 16-byte aligned");
+  if ((stride_x % 8) || (stride_z % 8) || (stride_y % 8))
+    return fail(GDN_ERR_ALIGN, "strides must be multiples of 8");
+  gdn::NormArgs a;
+  a.n_tok = n_tok;
+  a.H = H;
+  a.D = D;
+  a.sx = stride_x;
+  a.sz = stride_z;
+  a.sy = stride_y;
+  a.x = x;
+  a.z = z;
+  a.w = w;
+  a.eps = eps;
+  a.y = y;
+  return from_hip(gdn::launch_gated_rmsnorm(a, dtype, static_cast<hipStream_t>(stream)), "gdn_gated_rmsnorm");
+}
+
+const char* gdn_last_error(void) { return g_err; }
+
+int32_t gdn_version(void) { return 100; /* 0.1.0 */ }
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// gdn_device.h -- small device helpers for the gfx950 kernels: bf16 <-> fp32,
+// typed loads, wave reductions and the MFMA operand vector types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 h = static_cast<__bf16>(x);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <typename IO>
+struct IoTraits;
+
+template <>
+struct IoTraits<float> {
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float x) {
+    static_cast<float*>(p)[i] = x;
+  }
+};
+
+template <>
+struct IoTraits<uint16_t> {  // bf16 bit patterns
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float x) {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(x);
+  }
+};
+
+// Sum over the 64 lanes of a wave (result in every lane).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace gdn

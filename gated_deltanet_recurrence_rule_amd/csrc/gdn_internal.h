@@ -1,0 +1,54 @@
+// gdn_internal.h -- parameter blocks and kernel launchers shared between the
+// host API (gdn_api.cpp) and the HIP kernel translation units.  Host-visible
+// only; no device code here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Arguments of the recurrence kernels (prefill and decode share them).
+struct RecArgs {
+  int32_t B, T, Hk, Hv, G, D;
+  uint32_t flags;
+  float q_scale, l2_eps;
+  int64_t sq, sk, sv, so;  // token strides (elements)
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* la;
+  const float* beta;
+  const float* state_in;   // may be null (zero state)
+  float* state_out;        // may be null
+  void* o;
+};
+
+// io: 0 = fp32, 1 = bf16 (same codes as gdn_dtype).
+hipError_t launch_recurrent(const RecArgs& a, int io, hipStream_t s);
+hipError_t launch_chunk_prefill(const RecArgs& a, hipStream_t s);
+
+struct ConvArgs {
+  int32_t B, T, C, K;
+  int64_t sx, sy;
+  const void* x;
+  const void* w;
+  const void* cs_in;
+  void* cs_out;
+  void* y;
+};
+hipError_t launch_conv1d_silu(const ConvArgs& a, int io, hipStream_t s);
+
+struct NormArgs {
+  int64_t n_tok;
+  int32_t H, D;
+  int64_t sx, sz, sy;
+  const void* x;
+  const void* z;
+  const void* w;
+  float eps;
+  void* y;
+};
+hipError_t launch_gated_rmsnorm(const NormArgs& a, int io, hipStream_t s);
+
+}  // namespace gdn

@@ -1,0 +1,178 @@
+/*
+ * gdn.h -- C ABI of libgdn, the Gated DeltaNet sequence mixer on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *   "L'attention hybride" (Qwen3.8-27B architecture chapter, mkdocs.reaper.mx)
+ *     - config block "Les 48 couches Gated DeltaNet": 16 key heads, 48 value
+ *       heads, head width 128, conv kernel 4, swish output gate, float32
+ *       recurrent state;
+ *     - table "Le decompte": the q | k | v | z channel split of the input
+ *       projection, one beta and one alpha per value head, a depthwise causal
+ *       conv of kernel 4 over q, k, v without bias, a 128-weight output norm;
+ *     - section "La dissymetrie 16 / 48": one key head serves Hv/Hk value
+ *       heads (3 here, 8 in the larger variant); each value head keeps a
+ *       d_k x d_v state;
+ *     - section "La recurrence": alpha_t in (0,1) decays the whole state,
+ *       beta_t in (0,1) rewrites the association of k_t (the update formula
+ *       is missing from the page text; the gated delta rule
+ *       S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *       o_t = S_t q_t, read after the update, is what is computed);
+ *     - sections "L'etat, en memoire" and "Le float32 n'est pas un detail":
+ *       the state has a fixed size whatever the length and is kept in fp32.
+ *   "Chapitre 16 - Assembler un systeme de type Kimi K3" (course page,
+ *   cours.spawnkit.ai), sections 16.2 and 16.3: prefill processes a prompt
+ *   block by block and hands the state from block to block; decode reads the
+ *   fixed state, produces the token's output and updates the state.
+ *   "Les briques d'un reseau de neurones" (Kimi K3 foundations), section 2
+ *   (SiLU = x sigmoid(x)) and section 4 (RMSNorm with epsilon under the root
+ *   and a per-coordinate gain).
+ *
+ * Conventions common to every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously; the library never synchronises.
+ *   - Argument errors are detected on the host before any device work and
+ *     return a status; the thread-local message is in gdn_last_error().
+ *     A failed kernel launch returns GDN_ERR_DEVICE.  Nothing throws.
+ *   - Element strides are counted in elements of the tensor's own dtype.
+ *   - bf16 tensors hold IEEE bfloat16 bit patterns (uint16 storage).
+ *   - Gate values are data and are not checked: the domain is
+ *     log_alpha <= 0 and 0 <= beta <= 1 (the closed ends are allowed).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+  GDN_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes / strides */
+  GDN_ERR_UNSUPPORTED = 3, /* valid request that no kernel here implements */
+  GDN_ERR_ALIGN = 4,       /* pointer or stride not aligned as required */
+  GDN_ERR_DEVICE = 5       /* HIP runtime error (launch failure, no device) */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Flag: divide q and k of each (token, key head) by sqrt(sum of squares +
+ * l2_eps) before use (per-head L2 normalisation). */
+#define GDN_FLAG_QK_L2NORM 1u
+
+/*
+ * Shapes of one recurrence call.
+ *   B, T        batch and tokens per sequence (T >= 1)
+ *   Hk, Hv      key heads and value heads; Hv % Hk == 0; value head h uses
+ *               key head h / (Hv / Hk)  (consecutive groups)
+ *   Dk, Dv      head widths; the kernels implement Dk == Dv in {16,32,64,128}
+ *   io          gdn_dtype of q, k, v and o (gates and state are fp32)
+ *   flags       GDN_FLAG_* bits
+ *   stride_*    elements between consecutive tokens of q, k, v, o; heads are
+ *               packed inside a token (q: Hk*Dk, v and o: Hv*Dv) so each
+ *               stride is at least that width; the batch stride is
+ *               T * stride.  Strides larger than the width let q, k, v be
+ *               views into one [B, T, C] conv output.
+ *   q_scale     multiplies q after normalisation (1.0 reads S_t q_t as is)
+ *   l2_eps      epsilon of the L2 normalisation (used with the flag only)
+ */
+typedef struct {
+  int32_t B, T, Hk, Hv, Dk, Dv;
+  int32_t io;
+  uint32_t flags;
+  int64_t stride_q, stride_k, stride_v, stride_o;
+  float q_scale;
+  float l2_eps;
+} gdn_dims;
+
+/*
+ * gdn_prefill -- the gated delta rule over T tokens for every (b, value head),
+ * chunkwise ("Chapitre 16", 16.2; "L'attention hybride", "La recurrence").
+ *   q, k       [B, T, Hk, Dk]  io dtype, token strides stride_q / stride_k
+ *   v          [B, T, Hv, Dv]  io dtype, token stride stride_v
+ *   log_alpha  [B, T, Hv] fp32 contiguous (log of the decay, <= 0)
+ *   beta       [B, T, Hv] fp32 contiguous (write strength)
+ *   state_in   [B, Hv, Dk, Dv] fp32 contiguous, M = S^T (row i = key
+ *              coordinate, column j = value coordinate); NULL = zero state
+ *   state_out  [B, Hv, Dk, Dv] fp32, final state; NULL = not written; may be
+ *              the same pointer as state_in (updated in place)
+ *   o          [B, T, Hv, Dv]  io dtype, token stride stride_o;
+ *              o_t = S_t q_t with S_t after token t's update
+ * The bf16, Dk == Dv == 128 case runs the chunked MFMA kernel (chunks of
+ * 64 tokens); other supported shapes run the token-serial kernel.
+ * Alignment: bf16 with D == 128 needs q, k, v, o 16-byte aligned and strides
+ * multiples of 8; states need 16-byte alignment.
+ * o must not overlap q, k or v.
+ */
+gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const float* state_in,
+                       float* state_out, void* o, void* stream);
+
+/*
+ * gdn_decode_step -- one token per sequence from a resident state
+ * ("Chapitre 16", 16.3).  dims->T must be 1.
+ *   q, k [B, Hk, Dk]; v, o [B, Hv, Dv] (io dtype, per-sequence strides
+ *   stride_q/k/v/o); log_alpha, beta [B, Hv] fp32;
+ *   state [B, Hv, Dk, Dv] fp32, read once and overwritten in place.
+ * Computes u = M^T k, w = M^T q in one pass over M, then
+ * d = beta (v - alpha u), M <- alpha M + k d^T, o = alpha w + (k . q) d.
+ */
+gdn_status gdn_decode_step(const gdn_dims* dims, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, float* state, void* o,
+                           void* stream);
+
+/*
+ * gdn_conv1d_silu -- depthwise causal conv of K taps over C channels, then
+ * SiLU ("L'attention hybride", table "Le decompte": kernel 4 over the q|k|v
+ * channels, K weights per channel, no bias; "Les briques", section 2):
+ *     y[b,t,c] = silu( sum_{j<K} w[c][j] * x[b, t-(K-1)+j, c] )
+ *   x     [B, T, C] dtype, token stride stride_x (>= C), batch stride T*stride_x
+ *   w     [C, K] dtype, contiguous
+ *   conv_state_in  [B, C, K-1] dtype: the inputs at t = -(K-1) .. -1, oldest
+ *                  first; NULL = zeros
+ *   conv_state_out [B, C, K-1] dtype: the last K-1 inputs of this call
+ *                  (taken from conv_state_in when T < K-1); NULL = not written;
+ *                  must not alias conv_state_in
+ *   y     [B, T, C] dtype, token stride stride_y (>= C); must not overlap x
+ * Arithmetic is fp32; y is rounded once to the dtype.  K must be 4; C a
+ * multiple of 8 and, for bf16, pointers 16-byte aligned with strides
+ * multiples of 8.
+ */
+gdn_status gdn_conv1d_silu(int32_t B, int32_t T, int32_t C, int32_t K, int32_t dtype,
+                           const void* x, int64_t stride_x, const void* w,
+                           const void* conv_state_in, void* conv_state_out, void* y,
+                           int64_t stride_y, void* stream);
+
+/*
+ * gdn_gated_rmsnorm -- per-head RMSNorm with one shared D-weight, times
+ * swish(z) ("L'attention hybride", config block: swish output gate; table
+ * "Le decompte": 128 norm weights per layer; "Les briques", section 4):
+ *     y = x / sqrt(mean(x^2) + eps) * w * z * sigmoid(z)      per D-row
+ * Rows are (token, head) pairs: row (t, h) of x starts at x + t*stride_x +
+ * h*D (likewise z and y), so x can be the prefill output [n_tok, H*D] and z
+ * a view into the projection output.
+ *   n_tok >= 0, H >= 1, D in {64, 128}; x, z, w, y dtype; w is [D];
+ *   y may alias x (in place).  bf16 needs 16-byte aligned pointers and
+ *   strides multiples of 8.
+ */
+gdn_status gdn_gated_rmsnorm(int64_t n_tok, int32_t H, int32_t D, int32_t dtype, const void* x,
+                             int64_t stride_x, const void* z, int64_t stride_z, const void* w,
+                             float eps, void* y, int64_t stride_y, void* stream);
+
+/* Message of the last failed call on this thread ("" if none).  The string
+ * is owned by the library and valid until the next call on this thread. */
+const char* gdn_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

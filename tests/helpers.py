@@ -1,0 +1,80 @@
+"""Shared test helpers: host <-> device conversion and the parity criteria.
+
+Parity criteria (the oracle is fp64 and unrounded):
+  * state: relative Frobenius error ||M_gpu - M_ref||_F / ||M_ref||_F <= 1e-3;
+  * fp32 outputs: max |o_gpu - o_ref| <= 2e-2 * RMS(o_ref);
+  * bf16 outputs: the same bound after a one-ulp allowance for the rounding
+    that a bf16 output must undergo:
+        max_i max(0, |o_gpu,i - o_ref,i| - ulp_bf16(o_ref,i)) <= 2e-2 * RMS(o_ref),
+    with ulp_bf16(x) = 2^(floor(log2|x|) - 7).  Rounding the exact outputs to
+    bf16 alone already costs up to ~8e-2 RMS on these heavy-tailed outputs,
+    so the literal bound cannot hold for any bf16 result; the literal figure
+    is reported next to that floor.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+OUT_TOL = 2e-2
+STATE_TOL = 1e-3
+
+
+def to_dev(a: np.ndarray, device="cuda"):
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    """Device tensor -> float64 numpy (bf16 values widened exactly)."""
+    import torch
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    m, e = np.frexp(np.abs(x))          # |x| = m 2^e, m in [0.5, 1): floor(log2|x|) = e - 1
+    return np.where(x == 0, 0.0, np.ldexp(1.0, e - 8))
+
+
+def round_bf16_f64(x: np.ndarray) -> np.ndarray:
+    import oracle
+    b = oracle.round_bf16(x)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def out_metrics(o_gpu: np.ndarray, o_ref: np.ndarray, bf16: bool) -> dict:
+    rms = float(np.sqrt(np.mean(o_ref ** 2)))
+    err = np.abs(o_gpu - o_ref)
+    m = dict(rms=rms, max_err_rms=float(err.max() / rms), rms_err_rms=float(np.sqrt(np.mean(err ** 2)) / rms))
+    if bf16:
+        m["excess_rms"] = float(np.maximum(0.0, err - ulp_bf16(o_ref)).max() / rms)
+        m["floor_rms"] = float(np.abs(round_bf16_f64(o_ref) - o_ref).max() / rms)
+        m["metric"] = m["excess_rms"]
+    else:
+        m["metric"] = m["max_err_rms"]
+    return m
+
+
+def assert_out(o_gpu, o_ref, bf16: bool, tol: float = OUT_TOL, what: str = "o"):
+    m = out_metrics(np.asarray(o_gpu, np.float64), np.asarray(o_ref, np.float64), bf16)
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite values"
+    assert m["metric"] <= tol, f"{what}: {m}"
+    return m
+
+
+def state_err(m_gpu, m_ref) -> float:
+    m_gpu = np.asarray(m_gpu, np.float64)
+    m_ref = np.asarray(m_ref, np.float64)
+    return float(np.linalg.norm(m_gpu - m_ref) / np.linalg.norm(m_ref))
+
+
+def assert_state(m_gpu, m_ref, tol: float = STATE_TOL, what: str = "state"):
+    assert np.all(np.isfinite(m_gpu)), f"{what}: non-finite values"
+    e = state_err(m_gpu, m_ref)
+    assert e <= tol, f"{what}: relative Frobenius error {e:.3e} > {tol}"
+    return e

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: libgdn.so loads, exports every function that
+include/gdn.h declares, and rejects bad arguments on the host with the
+documented status before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_recurrence_rule_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p(0x10002)   # 2-byte aligned only
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(B.EXPORTS), names
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_struct_layout():
+    assert B.gdn_version() == 100
+    # gdn_dims: 8 x int32, 4 x int64, 2 x float -> 72 bytes with natural alignment
+    assert ctypes.sizeof(B.GdnDims) == 72
+    assert B.GdnDims.stride_q.offset == 32 and B.GdnDims.q_scale.offset == 64
+
+
+def call_prefill(d, q=FAKE, k=FAKE, v=FAKE, la=FAKE, be=FAKE, si=None, so=None, o=FAKE):
+    return B.lib().gdn_prefill(None if d is None else ctypes.byref(d), q, k, v, la, be, si, so, o, None)
+
+
+def dims(**kw):
+    base = dict(B=1, T=8, Hk=2, Hv=6, D=128, io=B.GDN_BF16)
+    base.update(kw)
+    return B.make_dims(base["B"], base["T"], base["Hk"], base["Hv"], base["D"], base["io"])
+
+
+def test_prefill_argument_errors():
+    assert call_prefill(None) == B.GDN_ERR_NULL
+    assert "NULL" in B.gdn_last_error()
+    assert call_prefill(dims(), q=None) == B.GDN_ERR_NULL
+    assert call_prefill(dims(Hv=5)) == B.GDN_ERR_SHAPE            # Hv % Hk != 0
+    assert call_prefill(dims(T=-1)) == B.GDN_ERR_SHAPE
+    assert call_prefill(dims(Hk=0)) == B.GDN_ERR_SHAPE
+    assert call_prefill(dims(D=96)) == B.GDN_ERR_UNSUPPORTED       # no kernel for D=96
+    d = dims()
+    d.Dv = 64
+    assert call_prefill(d) == B.GDN_ERR_UNSUPPORTED                 # Dk != Dv
+    d = dims()
+    d.stride_q = 2 * 128 - 1
+    assert call_prefill(d) == B.GDN_ERR_SHAPE                       # stride below Hk*Dk
+    d = dims()
+    d.stride_o = 6 * 128 - 8
+    assert call_prefill(d) == B.GDN_ERR_SHAPE
+    d = dims()
+    d.flags = 0x4
+    assert call_prefill(d) == B.GDN_ERR_SHAPE
+    d = dims()
+    d.io = 7
+    assert call_prefill(d) == B.GDN_ERR_SHAPE
+    assert call_prefill(dims(), q=FAKE_ODD) == B.GDN_ERR_ALIGN      # bf16 D=128 path wants 16 B
+    d = dims()
+    d.stride_v = 6 * 128 + 4
+    assert call_prefill(d) == B.GDN_ERR_ALIGN
+    assert call_prefill(dims(), si=ctypes.c_void_p(0x10004)) == B.GDN_ERR_ALIGN
+    # f32 path needs element alignment only
+    assert call_prefill(dims(io=B.GDN_F32, D=16), q=FAKE_ODD) == B.GDN_ERR_ALIGN
+    # empty batch / empty sequence without a state to write are no-ops
+    assert call_prefill(dims(B=0)) == B.GDN_OK
+    assert call_prefill(dims(T=0), q=None, k=None, v=None, la=None, be=None, o=None) == B.GDN_OK
+    assert B.gdn_last_error() == ""
+
+
+def test_decode_argument_errors():
+    L = B.lib()
+
+    def call(d, state=FAKE, q=FAKE):
+        return L.gdn_decode_step(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, state, FAKE, None)
+
+    assert call(dims(T=2)) == B.GDN_ERR_SHAPE          # a decode step is one token
+    assert call(dims(T=1), state=None) == B.GDN_ERR_NULL
+    assert call(dims(T=1), state=ctypes.c_void_p(0x10008)) == B.GDN_ERR_ALIGN
+    assert call(dims(T=1, Hv=7)) == B.GDN_ERR_SHAPE
+    assert call(dims(T=1, B=0)) == B.GDN_OK
+
+
+def test_conv_and_norm_argument_errors():
+    L = B.lib()
+    conv = lambda **kw: L.gdn_conv1d_silu(kw.get("B", 1), kw.get("T", 8), kw.get("C", 64), kw.get("K", 4),
+                                          kw.get("dt", B.GDN_BF16), kw.get("x", FAKE), kw.get("sx", 64),
+                                          kw.get("w", FAKE), kw.get("ci", None), kw.get("co", None),
+                                          kw.get("y", FAKE), kw.get("sy", 64), None)
+    assert conv(K=3) == B.GDN_ERR_UNSUPPORTED
+    assert conv(C=60, sx=60, sy=60) == B.GDN_ERR_UNSUPPORTED
+    assert conv(sx=32) == B.GDN_ERR_SHAPE
+    assert conv(w=None) == B.GDN_ERR_NULL
+    assert conv(x=FAKE_ODD) == B.GDN_ERR_ALIGN
+    assert conv(sx=68) == B.GDN_ERR_ALIGN
+    assert conv(ci=FAKE, co=FAKE) == B.GDN_ERR_SHAPE   # state out must not alias state in
+    assert conv(B=0) == B.GDN_OK
+    norm = lambda **kw: L.gdn_gated_rmsnorm(kw.get("n", 4), kw.get("H", 2), kw.get("D", 128),
+                                            kw.get("dt", B.GDN_BF16), kw.get("x", FAKE), kw.get("sx", 256),
+                                            kw.get("z", FAKE), kw.get("sz", 256), kw.get("w", FAKE),
+                                            ctypes.c_float(kw.get("eps", 1e-5)), kw.get("y", FAKE),
+                                            kw.get("sy", 256), None)
+    assert norm(D=96) == B.GDN_ERR_UNSUPPORTED
+    assert norm(sz=128) == B.GDN_ERR_SHAPE
+    assert norm(eps=-1.0) == B.GDN_ERR_SHAPE
+    assert norm(z=None) == B.GDN_ERR_NULL
+    assert norm(y=FAKE_ODD) == B.GDN_ERR_ALIGN
+    assert norm(n=0) == B.GDN_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()
