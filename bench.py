@@ -1,0 +1,343 @@
+"""Throughput of the Gated DeltaNet mixer on one MI355X.
+
+Headline (the JSON line's `value`): prefill tokens/s of one Qwen3.8-27B-like
+Gated DeltaNet layer -- batch 1, T = 4096, 16 key heads / 48 value heads of
+width 128, bf16 q/k/v, fp32 gates and state, chunks of 64 (the layer of the
+page "L'attention hybride").  A step is one gdn_prefill call over inputs
+already resident in HBM.  Extra fields of the same line report the decode
+step (64 sequences x 48 heads of resident fp32 state, HBM GB/s), the full
+block front end at batch 4, T = 32768, 16 key / 128 value heads (conv+SiLU,
+prefill with the L2 flag, gated RMSNorm), the 262144-token prefill, the
+roofline of the dominant kernel, and the fp64 oracle timed on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096 flop/clk)
+C = 64                          # chunk length
+
+
+def prefill_flops(B, T, Hk, Hv, D):
+    """Algorithmic flops of one prefill call: per token and value head
+    6 D^2 (state products) + (C+1)(D + 2D) (intra-chunk products) + C^2/3
+    (triangular solve), plus 2 C D per token and key head (the two Gram
+    matrices)."""
+    per_tok = Hv * (6 * D * D + (C + 1) * (D + 2 * D) + C * C / 3.0) + Hk * 2 * C * D
+    return per_tok * B * T
+
+
+def prefill_bytes(B, T, Hk, Hv, D, io_bytes=2, state_in=False):
+    """Algorithmic HBM bytes of one prefill call: q, k, v, o once at the I/O
+    dtype, fp32 log_alpha and beta, the fp32 final state (and initial state)."""
+    per_tok = 2 * Hk * D * io_bytes + 2 * Hv * D * io_bytes + 2 * Hv * 4
+    st = B * Hv * D * D * 4
+    return B * T * per_tok + st * (2 if state_in else 1)
+
+
+def decode_bytes(B, Hk, Hv, D, io_bytes=2):
+    """One decode step: state read + write (fp32), q, k, v, o and the gates."""
+    return B * (2 * Hv * D * D * 4 + 2 * Hk * D * io_bytes + 2 * Hv * D * io_bytes + 2 * Hv * 4)
+
+
+def bf16_dev(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def timed_launches(fn, steps, warmup, stream):
+    """Runs fn() warmup times, then `steps` times with a HIP event pair around
+    each launch on `stream`.  Returns (total ms of the timed region from the
+    first start event to the last end event, mean ms per launch, median ms)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    total = starts[0].elapsed_time(ends[-1])
+    return total, float(per.mean()), float(np.median(per))
+
+
+def bench_prefill4k(steps, warmup, dev):
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding as G
+    from gated_deltanet_recurrence_rule_amd import workloads as W
+    p = W.cfg_prefill4k()
+    B, T, Hk, Hv, D = p["B"], p["T"], p["Hk"], p["Hv"], p["D"]
+    q, k, v = bf16_dev(p["q"], dev), bf16_dev(p["k"], dev), bf16_dev(p["v"], dev)
+    la = torch.from_numpy(p["log_alpha"]).to(dev)
+    be = torch.from_numpy(p["beta"]).to(dev)
+    o = torch.empty((B, T, Hv * D), dtype=torch.bfloat16, device=dev)
+    so = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(G.gdn_prefill_workspace_size(G.make_dims(B, T, Hk, Hv, D, G.GDN_BF16)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        G.gdn_prefill(q, k, v, la, be, None, so, o, Hk=Hk, Hv=Hv, workspace=ws, stream=stream)
+
+    torch.cuda.synchronize()
+    total, mean_ms, med_ms = timed_launches(step, steps, warmup, stream)
+    return dict(B=B, T=T, Hk=Hk, Hv=Hv, D=D, total_ms=total, mean_ms=mean_ms, median_ms=med_ms,
+                flops=prefill_flops(B, T, Hk, Hv, D), bytes=prefill_bytes(B, T, Hk, Hv, D))
+
+
+def bench_decode(dev, n_steps=256, pools=1):
+    """256 successive decode steps on a resident [64, 48, 128, 128] fp32 pool
+    (`pools` independent pools rotated step by step to defeat the 256 MB
+    last-level cache); per-step inputs are staged in HBM beforehand."""
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding as G
+    from gated_deltanet_recurrence_rule_amd import workloads as W
+    B, Hk, Hv, D = 64, 16, 48, 128
+    pool_list = [torch.from_numpy(W.decode_pool(B, Hv, D, seed=3 + i)).to(dev) for i in range(pools)]
+    steps_in = []
+    for s in range(n_steps):
+        d = W.decode_step_inputs(s, B=B, Hk=Hk, Hv=Hv, D=D)
+        steps_in.append(tuple([bf16_dev(d[n][:, 0], dev) for n in ("q", "k", "v")] +
+                              [torch.from_numpy(np.ascontiguousarray(d[n][:, 0])).to(dev)
+                               for n in ("log_alpha", "beta")]))
+    o = torch.empty((B, Hv * D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    i = [0]
+
+    def step():
+        s = i[0] % n_steps
+        q, k, v, la, be = steps_in[s]
+        G.gdn_decode_step(q, k, v, la, be, pool_list[i[0] % pools], o, Hk=Hk, Hv=Hv, stream=stream)
+        i[0] += 1
+
+    torch.cuda.synchronize()
+    total, mean_ms, med_ms = timed_launches(step, n_steps, 8, stream)
+    per = decode_bytes(B, Hk, Hv, D)
+    return dict(steps=n_steps, pools=pools, total_ms=total, mean_ms=mean_ms, median_ms=med_ms,
+                bytes_per_step=per, GBs=per / (med_ms * 1e-3) / 1e9)
+
+
+def bench_block(dev, steps=5, warmup=2):
+    """Block front end at batch 4, T = 32768, 16 key / 128 value heads: conv+SiLU over
+    [q|k|v] (20480 channels), prefill on strided views with the L2 flag, gated
+    RMSNorm x swish(z).  Inputs are drawn on the GPU (seeded torch generator) with
+    the recipe's distributions; timing does not depend on the values."""
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding as G
+    B, T, Hk, Hv, D = 4, 32768, 16, 128, 128
+    Cc = (2 * Hk + Hv) * D
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    x = torch.randn((B, T, Cc), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    w = (0.5 * torch.randn((Cc, 4), generator=g, device=dev)).to(torch.bfloat16)
+    z = torch.randn((B * T, Hv * D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    nw = (1.0 + 0.1 * torch.randn((D,), generator=g, device=dev)).to(torch.bfloat16)
+    A = torch.rand((Hv,), generator=g, device=dev) * float(np.log(16.0))
+    dt = 0.5 * torch.randn((Hv,), generator=g, device=dev)
+    la = (-torch.exp(A) * torch.nn.functional.softplus(torch.randn((B, T, Hv), generator=g, device=dev) + dt)).contiguous()
+    be = torch.sigmoid(torch.randn((B, T, Hv), generator=g, device=dev)).contiguous()
+    y = torch.empty_like(x)
+    o = torch.empty((B, T, Hv * D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B * T, Hv * D), dtype=torch.bfloat16, device=dev)
+    so = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(G.gdn_prefill_workspace_size(G.make_dims(B, T, Hk, Hv, D, G.GDN_BF16)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    qv, kv, vv = y[:, :, :Hk * D], y[:, :, Hk * D:2 * Hk * D], y[:, :, 2 * Hk * D:]
+    conv = lambda: G.gdn_conv1d_silu(x, w, None, None, y, stream=stream)
+    pre = lambda: G.gdn_prefill(qv, kv, vv, la, be, None, so, o, Hk=Hk, Hv=Hv, l2norm=True, workspace=ws,
+                                stream=stream)
+    norm = lambda: G.gdn_gated_rmsnorm(o.view(B * T, Hv * D), z, nw, 1e-5, out, H=Hv, stream=stream)
+    res = {}
+    for name, fn in (("conv", conv), ("prefill", pre), ("norm", norm)):
+        _, mean_ms, med_ms = timed_launches(fn, steps, warmup, stream)
+        res[name + "_ms"] = med_ms
+
+    def block():
+        conv()
+        pre()
+        norm()
+
+    total, _, med = timed_launches(block, steps, 1, stream)
+    conv_bytes = B * T * Cc * 2 * 2 + Cc * 4 * 2
+    norm_bytes = B * T * Hv * D * 2 * 3 + D * 2
+    res.update(block_ms=med, tokens_per_s=B * T / (med * 1e-3),
+               conv_GBs=conv_bytes / (res["conv_ms"] * 1e-3) / 1e9,
+               norm_GBs=norm_bytes / (res["norm_ms"] * 1e-3) / 1e9,
+               prefill_tokens_per_s=B * T / (res["prefill_ms"] * 1e-3),
+               prefill_flops=prefill_flops(B, T, Hk, Hv, D),
+               prefill_bytes=prefill_bytes(B, T, Hk, Hv, D))
+    res["prefill_mfma_frac"] = res["prefill_flops"] / (res["prefill_ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+    del x, y, z, o, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_long(dev, steps=3, warmup=1):
+    """Prefill at T = 262144 (batch 1, 16/48 heads), inputs drawn on the GPU."""
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding as G
+    B, T, Hk, Hv, D = 1, 262144, 16, 48, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+
+    def unit(n, h):
+        a = torch.randn((B, T, h, D), generator=g, device=dev)
+        return (a / a.norm(dim=-1, keepdim=True)).reshape(B, T, h * D).to(torch.bfloat16)
+
+    q, k = unit(T, Hk), unit(T, Hk)
+    v = torch.randn((B, T, Hv * D), generator=g, device=dev).to(torch.bfloat16)
+    A = torch.rand((Hv,), generator=g, device=dev) * float(np.log(16.0))
+    dt = 0.5 * torch.randn((Hv,), generator=g, device=dev)
+    la = (-torch.exp(A) * torch.nn.functional.softplus(torch.randn((B, T, Hv), generator=g, device=dev) + dt)).contiguous()
+    be = torch.sigmoid(torch.randn((B, T, Hv), generator=g, device=dev)).contiguous()
+    o = torch.empty_like(v)
+    so = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(G.gdn_prefill_workspace_size(G.make_dims(B, T, Hk, Hv, D, G.GDN_BF16)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    fn = lambda: G.gdn_prefill(q, k, v, la, be, None, so, o, Hk=Hk, Hv=Hv, workspace=ws, stream=stream)
+    _, _, med = timed_launches(fn, steps, warmup, stream)
+    fl = prefill_flops(B, T, Hk, Hv, D)
+    by = prefill_bytes(B, T, Hk, Hv, D)
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return dict(T=T, ms=med, tokens_per_s=T / (med * 1e-3),
+                mfma_frac=fl / (med * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                hbm_frac=by / (med * 1e-3) / (HBM_PEAK_GBS * 1e9))
+
+
+def cpu_baseline(reps=2):
+    """The fp64 oracle (gdn_oracle.c, OpenMP) on the headline workload: all 48 value
+    heads over all 4096 tokens, timed on this host's cores."""
+    import oracle
+    from gated_deltanet_recurrence_rule_amd import workloads as W
+    p = W.cfg_prefill4k()
+    oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.recurrence(p["q"], p["k"], p["v"], p["log_alpha"], p["beta"], p["Hk"], p["Hv"], None,
+                          n_threads=threads)
+        times.append(time.perf_counter() - t0)
+    t = min(times)
+    return {"value": p["B"] * p["T"] / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole headline workload (B=1, T=4096, 48 value heads, fp64), best of {reps}: {t:.3f} s"}
+
+
+def traffic_from_profile(kernel_src_hash):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
+    scaled by a copy-kernel calibration; None when no matching measurement exists."""
+    path = os.path.join(ROOT, "profiles", "prefill4k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_src_sha256") != kernel_src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def kernel_src_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gdn_chunk.hip", "gdn_device.h"):
+        h.update(open(os.path.join(ROOT, "gated_deltanet_recurrence_rule_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true", help="headline only (no decode/block/long)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    h = bench_prefill4k(args.steps, args.warmup, dev)
+    ms = h["total_ms"] / args.steps
+    tokens_per_s = h["B"] * h["T"] / (ms * 1e-3)
+    kern_ms = h["mean_ms"]
+    achieved = h["bytes"] / (kern_ms * 1e-3) / 1e9
+    print(f"[bench] prefill4k: {ms * 1e3:.1f} us/step, kernel {kern_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    line = {
+        "metric": "GDN prefill tokens/s @T=4096, 16K/48V heads; decode-step HBM GB/s",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3.8-27B-like Gated DeltaNet layer prefill: batch 1, T=4096, "
+                               "16 key / 48 value heads, d_k=d_v=128, bf16 q/k/v, fp32 gates and state, "
+                               "chunk 64, S_0=0",
+                   "B": h["B"], "T": h["T"], "Hk": h["Hk"], "Hv": h["Hv"], "D": h["D"], "chunk": C},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic_from_profile(kernel_src_hash()),
+            "kernel": "gdn_prefill (chunk_prep_kernel + chunk_chain_kernel)",
+            "kernel_mean_us": kern_ms * 1e3,
+            "algorithmic_bytes": h["bytes"],
+            "algorithmic_flops": h["flops"],
+            "mfma_frac": h["flops"] / (kern_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        },
+    }
+    if not args.no_extras:
+        dec = bench_decode(dev)
+        print(f"[bench] decode: {dec['median_ms'] * 1e3:.1f} us/step, {dec['GBs']:.0f} GB/s", file=sys.stderr, flush=True)
+        dec2 = bench_decode(dev, pools=2)
+        line["decode"] = {"config": "64 sequences x 48 value heads x 128x128 fp32 state, 16 key heads, bf16 q/k/v, "
+                                    "256 steps",
+                          "median_us": dec["median_ms"] * 1e3, "mean_us": dec["mean_ms"] * 1e3,
+                          "GBs": dec["GBs"], "hbm_frac": dec["GBs"] / HBM_PEAK_GBS,
+                          "bytes_per_step": dec["bytes_per_step"],
+                          "two_pools_GBs": dec2["GBs"], "two_pools_median_us": dec2["median_ms"] * 1e3}
+        blk = bench_block(dev)
+        print(f"[bench] block: {blk['block_ms']:.2f} ms", file=sys.stderr, flush=True)
+        line["block"] = {"config": "batch 4, T=32768, 16 key / 128 value heads: conv+SiLU, prefill (L2 flag), "
+                                   "gated RMSNorm", **blk}
+        lg = bench_long(dev)
+        print(f"[bench] long: {lg['ms']:.2f} ms", file=sys.stderr, flush=True)
+        line["long"] = {"config": "batch 1, T=262144, 16 key / 48 value heads", **lg}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,8 +19,8 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_QK_L2NORM = 1
 
 # Every exported symbol, in the order include/gdn.h declares them.
-EXPORTS = ("gdn_prefill", "gdn_decode_step", "gdn_conv1d_silu", "gdn_gated_rmsnorm",
-           "gdn_last_error", "gdn_version")
+EXPORTS = ("gdn_prefill", "gdn_prefill_workspace_size", "gdn_decode_step", "gdn_conv1d_silu",
+           "gdn_gated_rmsnorm", "gdn_last_error", "gdn_version")
 
 
 class GdnDims(ctypes.Structure):
@@ -52,8 +52,10 @@ def lib() -> ctypes.CDLL:
                                "(or python gated_deltanet_recurrence_rule_amd/build_lib.py)")
         L = ctypes.CDLL(LIB_PATH)
         p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-        L.gdn_prefill.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p, p]
+        L.gdn_prefill.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p, p, ctypes.c_size_t, p]
         L.gdn_prefill.restype = ctypes.c_int
+        L.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnDims)]
+        L.gdn_prefill_workspace_size.restype = ctypes.c_size_t
         L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p]
         L.gdn_decode_step.restype = ctypes.c_int
         L.gdn_conv1d_silu.argtypes = [i32, i32, i32, i32, i32, p, i64, p, p, p, p, i64, p]
@@ -116,12 +118,17 @@ def make_dims(B, T, Hk, Hv, D, io, flags=0, sq=None, sk=None, sv=None, so=None,
                    q_scale, l2_eps)
 
 
+def gdn_prefill_workspace_size(dims: GdnDims) -> int:
+    return int(lib().gdn_prefill_workspace_size(ctypes.byref(dims)))
+
+
 def gdn_prefill(q, k, v, log_alpha, beta, state_in=None, state_out=None, o=None, *, Hk: int,
                 Hv: int, l2norm: bool = False, l2_eps: float = 1e-6, q_scale: float = 1.0,
-                stream=None):
+                workspace=None, stream=None):
     """q, k: [B, T, Hk*D] views; v: [B, T, Hv*D]; log_alpha, beta: [B, T, Hv] fp32;
     state_in / state_out: [B, Hv, D, D] fp32 or None; o: [B, T, >=Hv*D] or None
-    (allocated).  Returns o."""
+    (allocated); workspace: uint8 device tensor or None (allocated with the size
+    gdn_prefill_workspace_size asks for).  Returns o."""
     import torch
     B, T = int(q.shape[0]), int(q.shape[1])
     if q.shape[2] % Hk or v.shape[2] % Hv or q.shape[2] // Hk != v.shape[2] // Hv:
@@ -143,8 +150,13 @@ def gdn_prefill(q, k, v, log_alpha, beta, state_in=None, state_out=None, o=None,
         if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()
                               or tuple(s.shape) != (B, Hv, D, D)):
             raise ValueError(f"{name} must be contiguous fp32 [B, Hv, D, D]")
+    ws_bytes = gdn_prefill_workspace_size(dims)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().gdn_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                             _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o), _stream(stream)))
+                             _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o), _ptr(workspace),
+                             ws_len, _stream(stream)))
     return o
 
 

@@ -97,9 +97,21 @@ gdn::RecArgs rec_args(const gdn_dims* d, const void* q, const void* k, const voi
 
 extern "C" {
 
+size_t gdn_prefill_workspace_size(const gdn_dims* d) {
+  if (check_dims(d, false) != GDN_OK || d->B == 0 || !use_chunk_kernel(d)) return 0;
+  const gdn::RecArgs a = rec_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  const size_t per_chunk = gdn::chunk_ws_bytes_per_chunk(a);
+  const int64_t nchunks = (static_cast<int64_t>(d->T) + 63) / 64;
+  int64_t nwin = static_cast<int64_t>((size_t(128) << 20) / per_chunk);
+  if (nwin < 1) nwin = 1;
+  if (nwin >= nchunks) return static_cast<size_t>(nchunks) * per_chunk;
+  return static_cast<size_t>(nwin) * per_chunk + gdn::chunk_ws_carry_bytes(a);
+}
+
 gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const void* v,
                        const float* log_alpha, const float* beta, const float* state_in,
-                       float* state_out, void* o, void* stream) {
+                       float* state_out, void* o, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   gdn_status st = check_dims(d, false);
   if (st != GDN_OK) return st;
   if (d->B == 0) return ok();
@@ -113,10 +125,18 @@ gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const vo
       return fail(GDN_ERR_ALIGN, "bf16 q, k, v must be 16-byte aligned");
     if ((d->stride_q % 8) || (d->stride_k % 8) || (d->stride_v % 8))
       return fail(GDN_ERR_ALIGN, "bf16 strides of q, k, v must be multiples of 8 elements");
-    return from_hip(gdn::launch_chunk_prefill(
-                        rec_args(d, q, k, v, log_alpha, beta, state_in, state_out, o),
-                        static_cast<hipStream_t>(stream)),
-                    "gdn_prefill (chunk kernel)");
+    if (!aligned(o, 2)) return fail(GDN_ERR_ALIGN, "o must be 2-byte aligned");
+    const gdn::RecArgs a = rec_args(d, q, k, v, log_alpha, beta, state_in, state_out, o);
+    const size_t per_chunk = gdn::chunk_ws_bytes_per_chunk(a);
+    const int64_t nchunks = (static_cast<int64_t>(d->T) + 63) / 64;
+    const size_t need_min =
+        per_chunk + ((nchunks > 1 && !state_out) ? gdn::chunk_ws_carry_bytes(a) : 0);
+    if (!workspace) return fail(GDN_ERR_NULL, "the chunked prefill needs a workspace");
+    if (!aligned(workspace, 256)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need_min && workspace_bytes < static_cast<size_t>(nchunks) * per_chunk)
+      return fail(GDN_ERR_SHAPE, "workspace of %zu bytes is below the minimum %zu", workspace_bytes, need_min);
+    return from_hip(gdn::launch_chunk_prefill(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
+                    "gdn_prefill (chunk kernels)");
   }
   const size_t es = d->io == GDN_BF16 ? 2 : 4;
   if (d->T > 0 && (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(o, es)))

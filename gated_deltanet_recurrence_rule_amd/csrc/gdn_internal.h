@@ -26,7 +26,13 @@ struct RecArgs {
 
 // io: 0 = fp32, 1 = bf16 (same codes as gdn_dtype).
 hipError_t launch_recurrent(const RecArgs& a, int io, hipStream_t s);
-hipError_t launch_chunk_prefill(const RecArgs& a, hipStream_t s);
+// Chunked prefill: a prep kernel and a chain kernel per window of chunks.
+// The workspace holds, per (b, value head, chunk of the window), the
+// fragments and row scalings the prep kernel produces; when the sequence
+// needs several windows and there is no state_out, a state carry follows.
+size_t chunk_ws_bytes_per_chunk(const RecArgs& a);
+size_t chunk_ws_carry_bytes(const RecArgs& a);
+hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 
 struct ConvArgs {
   int32_t B, T, C, K;

@@ -30,7 +30,8 @@
  *
  * Conventions common to every call
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *     allocates nothing and keeps no state between calls.
+ *     allocates no device memory and keeps no state between calls; scratch
+ *     space comes from the caller (gdn_prefill_workspace_size).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously; the library never synchronises.
  *   - Argument errors are detected on the host before any device work and
@@ -44,6 +45,7 @@
 #ifndef GDN_H
 #define GDN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -103,7 +105,8 @@ typedef struct {
  *              the same pointer as state_in (updated in place)
  *   o          [B, T, Hv, Dv]  io dtype, token stride stride_o;
  *              o_t = S_t q_t with S_t after token t's update
- * The bf16, Dk == Dv == 128 case runs the chunked MFMA kernel (chunks of
+ *   workspace, workspace_bytes  device scratch, see gdn_prefill_workspace_size
+ * The bf16, Dk == Dv == 128 case runs the chunked MFMA kernels (chunks of
  * 64 tokens); other supported shapes run the token-serial kernel.
  * Alignment: bf16 with D == 128 needs q, k, v, o 16-byte aligned and strides
  * multiples of 8; states need 16-byte alignment.
@@ -111,7 +114,21 @@ typedef struct {
  */
 gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const void* v,
                        const float* log_alpha, const float* beta, const float* state_in,
-                       float* state_out, void* o, void* stream);
+                       float* state_out, void* o, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill wants
+ * for these dims (0 when the call needs none).  The chunked kernel keeps, per
+ * (sequence, value head, chunk of a window), the per-chunk matrices that do
+ * not depend on the state (about 25 KiB); windows are sized to about 128 MiB
+ * and the state is carried between windows through state_out, or through a
+ * carry area inside the workspace when state_out is NULL.  A smaller
+ * workspace is accepted down to one chunk per window (plus the carry when
+ * needed); GDN_ERR_SHAPE below that.  The workspace is caller-owned device
+ * memory, 256-byte aligned, used only during the call's kernels on `stream`.
+ */
+size_t gdn_prefill_workspace_size(const gdn_dims* dims);
 
 /*
  * gdn_decode_step -- one token per sequence from a resident state

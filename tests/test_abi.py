@@ -30,6 +30,18 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
+def test_workspace_size():
+    ws = B.gdn_prefill_workspace_size
+    per_chunk = 6 * 25600                               # B * Hv * (24 KiB fragments + 1 KiB scalars)
+    assert ws(dims(T=64)) == per_chunk
+    assert ws(dims(T=65)) == 2 * per_chunk
+    assert ws(dims(io=B.GDN_F32, D=16)) == 0            # token-serial path needs none
+    big = dims(B=4, T=32768, Hk=16, Hv=128)             # windows of ~128 MiB + a state carry
+    per = 4 * 128 * 25600
+    assert ws(big) == ((128 << 20) // per) * per + 4 * 128 * 128 * 128 * 4
+    assert ws(dims(Hv=5)) == 0                          # invalid dims
+
+
 def test_version_and_struct_layout():
     assert B.gdn_version() == 100
     # gdn_dims: 8 x int32, 4 x int64, 2 x float -> 72 bytes with natural alignment
@@ -37,8 +49,9 @@ def test_version_and_struct_layout():
     assert B.GdnDims.stride_q.offset == 32 and B.GdnDims.q_scale.offset == 64
 
 
-def call_prefill(d, q=FAKE, k=FAKE, v=FAKE, la=FAKE, be=FAKE, si=None, so=None, o=FAKE):
-    return B.lib().gdn_prefill(None if d is None else ctypes.byref(d), q, k, v, la, be, si, so, o, None)
+def call_prefill(d, q=FAKE, k=FAKE, v=FAKE, la=FAKE, be=FAKE, si=None, so=None, o=FAKE, ws=ctypes.c_void_p(0x100000),
+                 ws_bytes=1 << 30):
+    return B.lib().gdn_prefill(None if d is None else ctypes.byref(d), q, k, v, la, be, si, so, o, ws, ws_bytes, None)
 
 
 def dims(**kw):
@@ -77,6 +90,10 @@ def test_prefill_argument_errors():
     assert call_prefill(dims(), si=ctypes.c_void_p(0x10004)) == B.GDN_ERR_ALIGN
     # f32 path needs element alignment only
     assert call_prefill(dims(io=B.GDN_F32, D=16), q=FAKE_ODD) == B.GDN_ERR_ALIGN
+    # the chunked path needs an aligned workspace of at least one chunk
+    assert call_prefill(dims(), ws=None) == B.GDN_ERR_NULL
+    assert call_prefill(dims(), ws=ctypes.c_void_p(0x100010)) == B.GDN_ERR_ALIGN
+    assert call_prefill(dims(T=640), ws_bytes=1000) == B.GDN_ERR_SHAPE
     # empty batch / empty sequence without a state to write are no-ops
     assert call_prefill(dims(B=0)) == B.GDN_OK
     assert call_prefill(dims(T=0), q=None, k=None, v=None, la=None, be=None, o=None) == B.GDN_OK

@@ -126,6 +126,32 @@ def test_two_halves_equal_one_pass_and_oracle():
         assert_state(s2, s_full)
 
 
+@pytest.mark.parametrize("with_state_out", [True, False])
+def test_prefill_small_workspace_windows(with_state_out):
+    # A workspace of one or two chunks forces several prep/chain windows; the state is
+    # carried through state_out, or through the workspace's carry area without it.
+    torch = _torch()
+    B, T, Hk, Hv, D = 2, 300, 1, 3, 128
+    p = W.problem(4005, B, T, Hk, Hv, D, io="bf16", recipe="qwen", state="normal")
+    orf, srf = oracle_prefill(p, state_in=p["state_in"])
+    q, k, v = to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"])
+    la, be = to_dev(p["log_alpha"]), to_dev(p["beta"])
+    si = to_dev(p["state_in"].astype(np.float32))
+    dims = G.make_dims(B, T, Hk, Hv, D, G.GDN_BF16)
+    full = G.gdn_prefill_workspace_size(dims)
+    per_chunk = B * Hv * 25600
+    assert full == 5 * per_chunk
+    for nwin in (1, 2):
+        extra = 0 if with_state_out else B * Hv * D * D * 4
+        ws = torch.empty(nwin * per_chunk + extra, dtype=torch.uint8, device="cuda")
+        so = torch.empty((B, Hv, D, D), dtype=torch.float32, device="cuda") if with_state_out else None
+        o = G.gdn_prefill(q, k, v, la, be, si, so, Hk=Hk, Hv=Hv, workspace=ws)
+        torch.cuda.synchronize()
+        assert_out(to_host(o).reshape(B, T, Hv, D), orf, bf16=True)
+        if with_state_out:
+            assert_state(to_host(so), srf)
+
+
 def test_decode_steps_equal_prefill():
     torch = _torch()
     B, T, Hk, Hv, D = 2, 40, 1, 3, 128
