@@ -43,11 +43,14 @@ def _rng(seed: int, tag: str, slab: int = 0, sub: int = 0) -> np.random.Generato
 
 
 def normal_tokens(seed: int, tag: str, n_tok: int, width: int, loc: float = 0.0,
-                  scale: float = 1.0, sub: int = 0, tok0: int = 0, tok1: int | None = None) -> np.ndarray:
-    """float32 [tok1-tok0, width] slice of an N(loc, scale^2) stream laid out
-    as n_tok rows, drawn slab by slab (rows [tok0, tok1))."""
+                  scale: float = 1.0, sub: int = 0, tok0: int = 0, tok1: int | None = None,
+                  post=None, out_dtype=np.float32) -> np.ndarray:
+    """[tok1-tok0, width] slice of an N(loc, scale^2) float32 stream laid out
+    as n_tok rows, drawn slab by slab (rows [tok0, tok1)).  ``post`` maps each
+    float32 slab block to the stored values (e.g. normalise + round to bf16),
+    stored as ``out_dtype``."""
     tok1 = n_tok if tok1 is None else tok1
-    out = np.empty((tok1 - tok0, width), np.float32)
+    out = np.empty((tok1 - tok0, width), out_dtype)
     s_first, s_last = tok0 // SLAB, (max(tok1, 1) - 1) // SLAB
 
     def one(s):
@@ -58,7 +61,8 @@ def normal_tokens(seed: int, tag: str, n_tok: int, width: int, loc: float = 0.0,
         if loc != 0.0:
             blk += np.float32(loc)
         lo, hi = max(a0, tok0), min(a1, tok1)
-        out[lo - tok0:hi - tok0] = blk[lo - a0:hi - a0]
+        part = blk[lo - a0:hi - a0]
+        out[lo - tok0:hi - tok0] = part if post is None else post(part)
 
     if tok1 > tok0:
         with ThreadPoolExecutor(_threads()) as ex:
@@ -82,7 +86,7 @@ def l2_rows(a: np.ndarray, heads: int) -> np.ndarray:
     """Input recipe step: divide each head's D-vector by its L2 norm (float32)."""
     sh = a.shape
     h = a.reshape(sh[:-1] + (heads, sh[-1] // heads))
-    n = np.sqrt(np.sum(h.astype(np.float64) ** 2, axis=-1, keepdims=True)).astype(np.float32)
+    n = np.sqrt(np.einsum("...i,...i->...", h, h, dtype=np.float64))[..., None].astype(np.float32)
     return (h / n).reshape(sh)
 
 
@@ -120,17 +124,13 @@ def qkv(seed: int, B: int, T: int, Hk: int, Hv: int, D: int, io: str = "bf16", s
         normalise: bool = True):
     """q, k [B, T, Hk*D] (L2-normalised per head when ``normalise``), v [B, T, Hv*D] ~ N(0,1).
     io "bf16" -> uint16 bits; "f32" -> float32."""
-    q = normal_tokens(seed, "q", B * T, Hk * D, sub=sub)
-    k = normal_tokens(seed, "k", B * T, Hk * D, sub=sub)
-    v = normal_tokens(seed, "v", B * T, Hv * D, sub=sub)
-    if normalise:
-        q = l2_rows(q, Hk)
-        k = l2_rows(k, Hk)
-    out = []
-    for a, w in ((q, Hk * D), (k, Hk * D), (v, Hv * D)):
-        a = a.reshape(B, T, w)
-        out.append(f32_to_bf16(a) if io == "bf16" else np.ascontiguousarray(a, np.float32))
-    return tuple(out)
+    cast = f32_to_bf16 if io == "bf16" else (lambda a: a)
+    odt = np.uint16 if io == "bf16" else np.float32
+    qk_post = (lambda a: cast(l2_rows(a, Hk))) if normalise else cast
+    q = normal_tokens(seed, "q", B * T, Hk * D, sub=sub, post=qk_post, out_dtype=odt)
+    k = normal_tokens(seed, "k", B * T, Hk * D, sub=sub, post=qk_post, out_dtype=odt)
+    v = normal_tokens(seed, "v", B * T, Hv * D, sub=sub, post=cast, out_dtype=odt)
+    return q.reshape(B, T, Hk * D), k.reshape(B, T, Hk * D), v.reshape(B, T, Hv * D)
 
 
 def problem(seed: int, B: int, T: int, Hk: int, Hv: int, D: int, io: str = "bf16",
@@ -184,8 +184,8 @@ def block_inputs(B: int = 4, T: int = 32768, Hk: int = 16, Hv: int = 128, D: int
     C = (2 * Hk + Hv) * D
     n = B * T
     t1 = n if tok1 is None else tok1
-    x = f32_to_bf16(normal_tokens(seed, "x", n, C, tok0=tok0, tok1=t1))
-    z = f32_to_bf16(normal_tokens(seed, "z", n, Hv * D, tok0=tok0, tok1=t1))
+    x = normal_tokens(seed, "x", n, C, tok0=tok0, tok1=t1, post=f32_to_bf16, out_dtype=np.uint16)
+    z = normal_tokens(seed, "z", n, Hv * D, tok0=tok0, tok1=t1, post=f32_to_bf16, out_dtype=np.uint16)
     cw = f32_to_bf16(_rng(seed, "conv_w").normal(0.0, 0.5, size=(C, 4)).astype(np.float32))
     nw = f32_to_bf16(_rng(seed, "norm_w").normal(1.0, 0.1, size=(D,)).astype(np.float32))
     la, be = gates(seed, B, T, Hv, recipe)

@@ -47,12 +47,16 @@ def round_bf16_f64(x: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def out_metrics(o_gpu: np.ndarray, o_ref: np.ndarray, bf16: bool) -> dict:
+def out_metrics(o_gpu: np.ndarray, o_ref: np.ndarray, bf16: bool, upstream_rel: float = 0.0) -> dict:
+    """upstream_rel: extra allowance |o_ref| * upstream_rel for a bf16 rounding
+    that an earlier API boundary forced on this output's input (one bf16 ulp of
+    an input that enters the output linearly moves it by at most 2^-7 |o|)."""
     rms = float(np.sqrt(np.mean(o_ref ** 2)))
     err = np.abs(o_gpu - o_ref)
     m = dict(rms=rms, max_err_rms=float(err.max() / rms), rms_err_rms=float(np.sqrt(np.mean(err ** 2)) / rms))
     if bf16:
-        m["excess_rms"] = float(np.maximum(0.0, err - ulp_bf16(o_ref)).max() / rms)
+        allow = ulp_bf16(o_ref) + upstream_rel * np.abs(o_ref)
+        m["excess_rms"] = float(np.maximum(0.0, err - allow).max() / rms)
         m["floor_rms"] = float(np.abs(round_bf16_f64(o_ref) - o_ref).max() / rms)
         m["metric"] = m["excess_rms"]
     else:
@@ -60,8 +64,8 @@ def out_metrics(o_gpu: np.ndarray, o_ref: np.ndarray, bf16: bool) -> dict:
     return m
 
 
-def assert_out(o_gpu, o_ref, bf16: bool, tol: float = OUT_TOL, what: str = "o"):
-    m = out_metrics(np.asarray(o_gpu, np.float64), np.asarray(o_ref, np.float64), bf16)
+def assert_out(o_gpu, o_ref, bf16: bool, tol: float = OUT_TOL, what: str = "o", upstream_rel: float = 0.0):
+    m = out_metrics(np.asarray(o_gpu, np.float64), np.asarray(o_ref, np.float64), bf16, upstream_rel)
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite values"
     assert m["metric"] <= tol, f"{what}: {m}"
     return m
@@ -78,3 +82,23 @@ def assert_state(m_gpu, m_ref, tol: float = STATE_TOL, what: str = "state"):
     e = state_err(m_gpu, m_ref)
     assert e <= tol, f"{what}: relative Frobenius error {e:.3e} > {tol}"
     return e
+
+
+def conv_abs_sum(x_bits_or_f32, w, cs, b, c0, c1):
+    """S[t, c] = sum_j |w[c][j] x[b, t-3+j, c]| over the 4-tap causal window of
+    channels [c0, c1): the scale of the fp32 accumulation error of one output
+    (the error of a 4-term fp32 dot product is at most about 4 * 2^-24 * S)."""
+    from gated_deltanet_recurrence_rule_amd.workloads import bf16_to_f32
+    f = (lambda a: bf16_to_f32(a).astype(np.float64)) if x_bits_or_f32.dtype == np.uint16 else \
+        (lambda a: np.asarray(a, np.float64))
+    xs = f(x_bits_or_f32[b, :, c0:c1])
+    T = xs.shape[0]
+    pre = np.zeros((3, c1 - c0)) if cs is None else f(cs[b, c0:c1, :]).T
+    xw = np.concatenate([pre, xs], axis=0)
+    wf = np.abs(f(w[c0:c1]))
+    return sum(np.abs(xw[j:j + T]) * wf[:, j] for j in range(4))
+
+
+def conv_tol(yr, S):
+    """One bf16 ulp of the exact value plus the fp32 accumulation bound 2^-21 * S."""
+    return ulp_bf16(yr) + 2.0 ** -21 * S
