@@ -121,11 +121,10 @@ gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const vo
     return fail(GDN_ERR_ALIGN, "state pointers must be 16-byte aligned");
   if (d->T == 0 && !state_out) return ok();
   if (use_chunk_kernel(d)) {
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
-      return fail(GDN_ERR_ALIGN, "bf16 q, k, v must be 16-byte aligned");
-    if ((d->stride_q % 8) || (d->stride_k % 8) || (d->stride_v % 8))
-      return fail(GDN_ERR_ALIGN, "bf16 strides of q, k, v must be multiples of 8 elements");
-    if (!aligned(o, 2)) return fail(GDN_ERR_ALIGN, "o must be 2-byte aligned");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+      return fail(GDN_ERR_ALIGN, "bf16 q, k, v, o must be 16-byte aligned");
+    if ((d->stride_q % 8) || (d->stride_k % 8) || (d->stride_v % 8) || (d->stride_o % 8))
+      return fail(GDN_ERR_ALIGN, "bf16 strides of q, k, v, o must be multiples of 8 elements");
     const gdn::RecArgs a = rec_args(d, q, k, v, log_alpha, beta, state_in, state_out, o);
     const size_t per_chunk = gdn::chunk_ws_bytes_per_chunk(a);
     const int64_t nchunks = (static_cast<int64_t>(d->T) + 63) / 64;

@@ -30,14 +30,19 @@
 //    (fp32, blocked 16/32), T' and P -- written to the workspace as ready
 //    MFMA A-operand fragments (bf16 hi + lo pairs) plus three row-scaling
 //    vectors per (chunk, value head).
+//    The prep kernel also writes K, Q and K^T as fragments, so the chain
+//    kernel stages its inputs with plain 16-byte copies and reads every MFMA
+//    A operand with one conflict-free 16-byte LDS read per lane.
 //  * chain (one workgroup per sequence, value head and 64 value columns,
 //    looping over the chunks): only the state-dependent products.  Columns of
 //    M evolve independently; waves 0-1 ("state") each own a 32-column strip
-//    of M in MFMA accumulators for the whole window and compute
-//    K M, X, U = T'X and the update; waves 2-3 ("output") compute
-//    Q M and P U for the same strips from fragments the state waves publish
-//    in LDS, so the output work runs beside the critical path.  The next
-//    chunk's inputs are prefetched into registers while a chunk computes.
+//    of M in MFMA accumulators for the whole window and run the serial path
+//    K M, X, U = T'X and the update, with nothing else to do; waves 2-3
+//    ("output") compute Q M and P U for the same strips from fragments the
+//    state waves publish in LDS, and move the next chunk's inputs from HBM
+//    into LDS: loads are issued at the start of a chunk; inputs the update
+//    phase reads go to one of two alternating buffers at the chunk's end,
+//    the rest is restaged while the update runs.
 //
 // Precision.  MFMA operands are bf16 with fp32 accumulation.  Genuine bf16
 // inputs (K, Q, V) enter as they are.  fp32 operands whose rounding would
@@ -66,11 +71,12 @@ constexpr int CH = 64;    // chunk length
 constexpr int DK = 128;   // head width
 constexpr int KP = 136;   // LDS row pitch (bf16) of 64 x 128 K / Q tiles
 constexpr int RP = 72;    // LDS row pitch (bf16) of K^T and of the V slice
-constexpr int FP = 65;    // LDS row pitch (floats) of fp32 64 x 64 matrices
+constexpr int FP = 68;    // LDS row pitch (floats) of fp32 64 x 64 matrices (16-byte rows)
 constexpr int DVS = 64;   // value columns per chain workgroup
 constexpr int FT = 6;     // 32x16 fragment tiles covering a 64x64 lower triangle
 constexpr int WS_TP = 2 * FT * 2 * 1024;  // T' and P fragments, hi and lo
-constexpr int WS_CHUNK = WS_TP + 1024;    // + grk[64], grq[64], drk[64], gamma_63
+constexpr int WS_CHUNK = WS_TP + 2048;    // + grk[64], grq[64], drk[64], gamma_63 (2 KiB slot)
+constexpr int WS_KQ = 3 * 16 * 1024;      // per (b, key head, chunk): K, Q and K^T fragments
 
 // fragment tile f covers rows 32*kFtRt[f].., k step kFtKs[f] (16 columns)
 __device__ __forceinline__ int ft_rt(int f) { return f < 2 ? 0 : 1; }
@@ -125,12 +131,13 @@ struct PrepLds {
   static constexpr int kT = CH * FP * 4;
   static constexpr int kKK = 2 * CH * KP * 2;         // fp32 [64][FP]
   static constexpr int kQK = kKK + CH * FP * 4;
-  static constexpr int kY = kQK + CH * FP * 4;        // fp32 32 x 33 (or 2 x 16 x 17)
-  static constexpr int kVec = kY + 32 * 33 * 4;       // rk, rq, g, beta
+  static constexpr int kY = kQK + CH * FP * 4;        // fp32 32 x 36 (or 2 x 16 x 20)
+  static constexpr int kVec = kY + 32 * 36 * 4;       // rk, rq, g, beta
   static constexpr int kBytes = kVec + 4 * CH * 4;
 };
 
 __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, unsigned char* ws, int nwin) {
+  // workspace: region H = [B][Hv][nwin] x WS_CHUNK, then region K = [B][Hk][nwin] x WS_KQ
   using L = PrepLds;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sK = reinterpret_cast<uint16_t*>(smem + L::kKQ);
@@ -187,6 +194,30 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   }
   __syncthreads();
 
+  // ---- K, Q and K^T as the chain kernel's MFMA A fragments ------------------
+  // K, Q (A of K M / Q M): tile (rt, ks) holds rows 32rt + (lane&31), k = 16ks + kperm;
+  // K^T (A of K^T U): tile (dt, ks) holds key rows 32dt + (lane&31), k = chunk rows 16ks + kperm.
+  {
+    unsigned char* wsk = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WS_CHUNK +
+                         (static_cast<int64_t>(b * a.Hk + hk) * nwin + cl) * WS_KQ;
+    for (int slot = tid; slot < 3 * 16 * 64; slot += 256) {
+      const int mat = slot >> 10, tile = (slot >> 6) & 15, ln = slot & 63;
+      const int r32 = ln & 31, hh = ln >> 5;
+      u16x8 f;
+      if (mat < 2) {
+        const uint16_t* src = (mat == 0 ? sK : sQ) + (32 * (tile >> 3) + r32) * KP + 16 * (tile & 7);
+        const u16x4 lo = *reinterpret_cast<const u16x4*>(src + 4 * hh);
+        const u16x4 hi = *reinterpret_cast<const u16x4*>(src + 8 + 4 * hh);
+        f = u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const int d = 32 * (tile >> 2) + r32, k0 = 16 * (tile & 3);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = sK[(k0 + kperm(hh, e)) * KP + d];
+      }
+      *reinterpret_cast<u16x8*>(wsk + mat * 16384 + tile * 1024 + ln * 16) = f;
+    }
+  }
+
   // ---- Gram tiles (32x32): K K^T and Q K^T, lower blocks (0,0) (1,0) (1,1) --
   for (int job = wv; job < 6; job += 4) {
     const int m = job / 3, tI = job % 3;
@@ -232,22 +263,54 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       if (lane == 0) sc[192] = __expf(gl);
     }
     __syncthreads();
-    // ---- A (fp32, strictly lower) and the P fragments ----------------------
-    for (int e = tid; e < CH * CH; e += 256) {
-      const int r = e >> 6, i = e & 63;
-      float av = 0.f;
-      if (i < r) av = vBe[r] * __expf(vG[r] - vG[i]) * vRk[r] * vRk[i] * sKK[r * FP + i];
-      sA[r * FP + i] = av;
+    // ---- A (fp32, strictly lower), the P fragments, and zeros in the two ----
+    //      upper blocks of T that the block inverse reads
+    {
+      // A: thread -> row r, 16 consecutive columns; every load issued before use
+      const int r = tid >> 2, i0 = (tid & 3) * 16;
+      const float gr = vG[r], cr = vBe[r] * vRk[r];
+      floatx4 kk[4], gi[4], rki[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        kk[q] = *reinterpret_cast<const floatx4*>(sKK + r * FP + i0 + 4 * q);
+        gi[q] = *reinterpret_cast<const floatx4*>(vG + i0 + 4 * q);
+        rki[q] = *reinterpret_cast<const floatx4*>(vRk + i0 + 4 * q);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        floatx4 av;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + 4 * q + e;
+          const float x = cr * __expf(fminf(gr - gi[q][e], 0.f)) * rki[q][e] * kk[q][e];
+          av[e] = i < r ? x : 0.f;
+        }
+        *reinterpret_cast<floatx4*>(sA + r * FP + i0 + 4 * q) = av;
+      }
+      // T blocks (0,1) and (2,3) (above the diagonal, inside S0 and S1) are read as zeros
+      {
+        const int blk = tid >> 7, e2 = (tid & 127) * 2;
+        const int rr = 32 * blk + (e2 >> 4), cc = 32 * blk + 16 + (e2 & 15);
+        sT[rr * FP + cc] = 0.f;
+        sT[rr * FP + cc + 1] = 0.f;
+      }
     }
     for (int slot = tid; slot < FT * 64; slot += 256) {
       const int f = slot >> 6, ln = slot & 63;
       const int r = 32 * ft_rt(f) + (ln & 31), hh = ln >> 5;
-      u16x8 hi, lo;
+      const int ca = 16 * ft_ks(f) + 4 * hh, cb = ca + 8;   // the lane's two 4-column runs
       const float gr = vG[r], rq = vRq[r];
+      const floatx4 qa = *reinterpret_cast<const floatx4*>(sQK + r * FP + ca);
+      const floatx4 qb = *reinterpret_cast<const floatx4*>(sQK + r * FP + cb);
+      const floatx4 ga = *reinterpret_cast<const floatx4*>(vG + ca), gb = *reinterpret_cast<const floatx4*>(vG + cb);
+      const floatx4 ka = *reinterpret_cast<const floatx4*>(vRk + ca), kb = *reinterpret_cast<const floatx4*>(vRk + cb);
+      u16x8 hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int i = 16 * ft_ks(f) + kperm(hh, e);
-        const float pv = (i <= r) ? __expf(gr - vG[i]) * rq * vRk[i] * sQK[r * FP + i] : 0.f;
+        const int i = e < 4 ? ca + e : cb + e - 4;
+        const float qk = e < 4 ? qa[e] : qb[e - 4], g = e < 4 ? ga[e] : gb[e - 4], rk = e < 4 ? ka[e] : kb[e - 4];
+        const float x = __expf(fminf(gr - g, 0.f)) * rq * rk * qk;
+        const float pv = i <= r ? x : 0.f;
         const __bf16 hb = static_cast<__bf16>(pv);
         hi[e] = __builtin_bit_cast(uint16_t, hb);
         lo[e] = f32_to_bf16_bits(pv - static_cast<float>(hb));
@@ -278,25 +341,37 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       const int half = tid >> 7, idx = (tid & 127) * 2;
       const int yr = idx >> 4, yc = idx & 15;
       const int I = 2 * half + 1, J = 2 * half;
-      float y0 = 0.f, y1 = 0.f;
+      float arow[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 av = *reinterpret_cast<const floatx4*>(sA + (16 * I + yr) * FP + 16 * J + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) arow[4 * q + e] = av[e];
+      }
+      floatx2 y = {0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
-        const float av = sA[(16 * I + yr) * FP + 16 * J + m];
-        y0 = fmaf(av, sT[(16 * J + m) * FP + 16 * J + yc], y0);
-        y1 = fmaf(av, sT[(16 * J + m) * FP + 16 * J + yc + 1], y1);
+        const floatx2 tv = *reinterpret_cast<const floatx2*>(sT + (16 * J + m) * FP + 16 * J + yc);
+        y[0] = fmaf(arow[m], tv[0], y[0]);
+        y[1] = fmaf(arow[m], tv[1], y[1]);
       }
-      sY[half * 16 * 17 + yr * 17 + yc] = y0;
-      sY[half * 16 * 17 + yr * 17 + yc + 1] = y1;
+      *reinterpret_cast<floatx2*>(sY + half * 16 * 20 + yr * 20 + yc) = y;
       __syncthreads();
-      float t0v = 0.f, t1v = 0.f;
+      float trow[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 tv = *reinterpret_cast<const floatx4*>(sT + (16 * I + yr) * FP + 16 * I + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) trow[4 * q + e] = tv[e];
+      }
+      floatx2 t = {0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
-        const float tv = sT[(16 * I + yr) * FP + 16 * I + m];
-        t0v = fmaf(tv, sY[half * 16 * 17 + m * 17 + yc], t0v);
-        t1v = fmaf(tv, sY[half * 16 * 17 + m * 17 + yc + 1], t1v);
+        const floatx2 yv = *reinterpret_cast<const floatx2*>(sY + half * 16 * 20 + m * 20 + yc);
+        t[0] = fmaf(trow[m], yv[0], t[0]);
+        t[1] = fmaf(trow[m], yv[1], t[1]);
       }
-      sT[(16 * I + yr) * FP + 16 * J + yc] = -t0v;
-      sT[(16 * I + yr) * FP + 16 * J + yc + 1] = -t1v;
+      *reinterpret_cast<floatx2*>(sT + (16 * I + yr) * FP + 16 * J + yc) = floatx2{-t[0], -t[1]};
     }
     __syncthreads();
     // level 2: T[32:64, 0:32] = -S1 (A[32:64, 0:32] S0), S0/S1 the 32x32 diagonal inverses
@@ -304,33 +379,41 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       const int idx = tid * 4;
       const int yr = idx >> 5, yc = idx & 31;
       floatx4 y = {0.f, 0.f, 0.f, 0.f};
-      for (int m = yc; m < 32; ++m) {  // S0 is lower-triangular: rows m >= yc only
-        const float av = sA[(32 + yr) * FP + m];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = fmaf(av, sT[m * FP + yc + e], y[e]);
+      for (int q = 0; q < 8; ++q) {
+        const floatx4 av = *reinterpret_cast<const floatx4*>(sA + (32 + yr) * FP + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const floatx4 tv = *reinterpret_cast<const floatx4*>(sT + (4 * q + e) * FP + yc);
+          y += av[e] * tv;
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sY[yr * 33 + yc + e] = y[e];
+      *reinterpret_cast<floatx4*>(sY + yr * 36 + yc) = y;
       __syncthreads();
       floatx4 t = {0.f, 0.f, 0.f, 0.f};
-      for (int m = 0; m <= yr; ++m) {  // S1 is lower-triangular: columns m <= yr only
-        const float tv = sT[(32 + yr) * FP + 32 + m];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = fmaf(tv, sY[m * 33 + yc + e], t[e]);
+      for (int q = 0; q < 8; ++q) {
+        const floatx4 tv = *reinterpret_cast<const floatx4*>(sT + (32 + yr) * FP + 32 + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t += tv[e] * *reinterpret_cast<const floatx4*>(sY + (4 * q + e) * 36 + yc);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sT[(32 + yr) * FP + yc + e] = -t[e];
+      *reinterpret_cast<floatx4*>(sT + (32 + yr) * FP + yc) = -t;
     }
     __syncthreads();
     // ---- T' = T diag(beta) fragments ----------------------------------------
     for (int slot = tid; slot < FT * 64; slot += 256) {
       const int f = slot >> 6, ln = slot & 63;
       const int r = 32 * ft_rt(f) + (ln & 31), hh = ln >> 5;
+      const int ca = 16 * ft_ks(f) + 4 * hh, cb = ca + 8;
+      const floatx4 ta = *reinterpret_cast<const floatx4*>(sT + r * FP + ca);
+      const floatx4 tb = *reinterpret_cast<const floatx4*>(sT + r * FP + cb);
+      const floatx4 ba = *reinterpret_cast<const floatx4*>(vBe + ca), bb = *reinterpret_cast<const floatx4*>(vBe + cb);
       u16x8 hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int i = 16 * ft_ks(f) + kperm(hh, e);
-        const float tv = (i <= r) ? sT[r * FP + i] * vBe[i] : 0.f;
+        const int i = e < 4 ? ca + e : cb + e - 4;
+        const float x = e < 4 ? ta[e] * ba[e] : tb[e - 4] * bb[e - 4];
+        const float tv = i <= r ? x : 0.f;
         const __bf16 hb = static_cast<__bf16>(tv);
         hi[e] = __builtin_bit_cast(uint16_t, hb);
         lo[e] = f32_to_bf16_bits(tv - static_cast<float>(hb));
@@ -345,91 +428,92 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
 // =========================================================================
 // chain kernel: one workgroup (4 waves) per (64-column slice, value head, batch)
 // =========================================================================
+// LDS: a primary buffer (K, Q, T' fragments and the V slice) restaged once per
+// chunk after the state waves' first phase, and two alternating buffers
+// (K^T and P fragments, row scalings) staged a chunk ahead.
 struct ChainLds {
-  static constexpr int kK = 0;                        // bf16 [64][KP]
-  static constexpr int kQ = kK + CH * KP * 2;         // bf16 [64][KP]
-  static constexpr int kKt = kQ + CH * KP * 2;        // bf16 [128][RP]
-  static constexpr int kV = kKt + DK * RP * 2;        // bf16 [64][RP]
-  static constexpr int kTP = kV + CH * RP * 2;        // fragments, WS_TP bytes
-  static constexpr int kSc = kTP + WS_TP;             // 256 floats
-  static constexpr int kMf = kSc + 1024;              // M B-fragments: [2 strips][8 k steps][64 lanes] x 16 B
-  static constexpr int kUf = kMf + 2 * 8 * 1024;      // U B-fragments: [2 strips][4 k steps][hi/lo][64] x 16 B
-  static constexpr int kBytes = kUf + 2 * 4 * 2 * 1024;
+  static constexpr int kK = 0;                     // 16 fragment tiles
+  static constexpr int kQ = kK + 16 * 1024;        // 16 fragment tiles
+  static constexpr int kTp = kQ + 16 * 1024;       // T' 6 tiles x hi/lo
+  static constexpr int kV = kTp + 12 * 1024;       // bf16 [64][RP]
+  static constexpr int kAlt = kV + CH * RP * 2;    // 2 x {K^T 16 tiles | P 6 x hi/lo | scalings}
+  static constexpr int kAltKt = 0, kAltP = 16 * 1024, kAltSc = 28 * 1024;
+  static constexpr int kAltBytes = 30 * 1024;
+  static constexpr int kMf = kAlt + 2 * kAltBytes;  // M B-fragments [2 strips][8 k steps][64 lanes] x 16 B
+  static constexpr int kUf = kMf + 2 * 8 * 1024;    // U B-fragments [2 strips][4 k steps][hi/lo][64] x 16 B
+  static constexpr int kO = kUf + 2 * 4 * 2 * 1024; // O staging: [2 strips][64 rows][OP] bf16
+  static constexpr int OP = 40;
+  static constexpr int kBytes = kO + 2 * CH * OP * 2;
 };
 
-// Per-thread prefetch of one chunk's chain inputs (global -> registers).
-struct ChainPrefetch {
-  u16x8 kq[8];   // an 8x8 block of K (threads 0-127) or Q (threads 128-255)
-  u16x8 v[2];
-  u32x4 tp[6];
-  floatx4 sc;
+// Loader waves (2 and 3) move a chunk's chain inputs global -> registers -> LDS in two parts:
+// part A (K^T fragments, P fragments, row scalings; 30 KiB) into the alternating buffer, and
+// part B (K, Q, T' fragments; 44 KiB; plus the 8 KiB V slice) into the primary buffer.  Both
+// parts are whole multiples of 128 16-byte vectors and every source is a compile-time function of
+// the unrolled index, so the loads carry no per-lane branches and the compiler can wait for each
+// part on its own in issue order.
+constexpr int kRegA = 15;   // 8 x 128 K^T vectors, 6 x 128 P vectors, 1 x 128 scaling vectors
+constexpr int kRegB = 26;   // 16 x 128 K|Q vectors, 6 x 128 T' vectors, 4 x 128 V vectors
+
+struct ChainSrc {
+  const unsigned char* wsh;   // region H block of (b, hv, chunk)
+  const unsigned char* wsk;   // region K block of (b, hk, chunk)
+  const uint16_t* v;          // first V row of the chunk for this head and slice
+  int64_t sv;
+  int nval;
 };
 
-__device__ __forceinline__ void chain_prefetch(ChainPrefetch& pf, const RecArgs& a, const unsigned char* wsc,
-                                               int64_t tokbase, int nval, int hk, int h, int slice, int tid) {
-  const int which = tid >> 7, blk = tid & 127;
-  const int br = blk >> 4, bc = blk & 15;
-  const uint16_t* src = static_cast<const uint16_t*>(which == 0 ? a.k : a.q);
-  const int64_t st = which == 0 ? a.sk : a.sq;
+__device__ __forceinline__ void load_part_a(u32x4 (&r)[kRegA], const ChainSrc& src, int lt) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * br + j;
-    pf.kq[j] = (r < nval) ? *reinterpret_cast<const u16x8*>(src + (tokbase + r) * st + hk * DK + 8 * bc)
-                          : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  for (int m = 0; m < kRegA; ++m) {
+    const unsigned char* p = m < 8 ? src.wsk + 32768 + 16 * (lt + 128 * m)              // K^T fragments
+                                   : src.wsh + 12288 + 16 * (lt + 128 * (m - 8));       // P | scalings
+    r[m] = *reinterpret_cast<const u32x4*>(p);
   }
-  const uint16_t* gv = static_cast<const uint16_t*>(a.v);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int vi = tid + 256 * j;
-    const int r = vi >> 3, c8 = (vi & 7) * 8;
-    pf.v[j] = (r < nval) ? *reinterpret_cast<const u16x8*>(gv + (tokbase + r) * a.sv + h * DK + slice * DVS + c8)
-                         : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int j = 0; j < 6; ++j) pf.tp[j] = reinterpret_cast<const u32x4*>(wsc)[tid + 256 * j];
-  if (tid < 64) pf.sc = reinterpret_cast<const floatx4*>(wsc + WS_TP)[tid];
 }
 
-__device__ __forceinline__ void chain_stage(const ChainPrefetch& pf, unsigned char* smem, int tid) {
-  using L = ChainLds;
-  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + L::kK);
-  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + L::kQ);
-  uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + L::kKt);
-  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + L::kV);
-  const int which = tid >> 7, blk = tid & 127;
-  const int br = blk >> 4, bc = blk & 15;
-  uint16_t* dst = which == 0 ? sK : sQ;
+__device__ __forceinline__ void store_part_a(const u32x4 (&r)[kRegA], unsigned char* alt, int lt) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) *reinterpret_cast<u16x8*>(dst + (8 * br + j) * KP + 8 * bc) = pf.kq[j];
-  if (which == 0) {  // K^T: transpose the 8x8 block in registers
+  for (int m = 0; m < kRegA; ++m) reinterpret_cast<u32x4*>(alt)[lt + 128 * m] = r[m];
+}
+
+__device__ __forceinline__ void load_part_b(u32x4 (&r)[kRegB], const ChainSrc& src, int lt) {
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      u16x8 col;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) col[j] = pf.kq[j][cc];
-      *reinterpret_cast<u16x8*>(sKt + (8 * bc + cc) * RP + 8 * br) = col;
+  for (int m = 0; m < kRegB; ++m) {
+    if (m < 16) {
+      r[m] = *reinterpret_cast<const u32x4*>(src.wsk + 16 * (lt + 128 * m));          // K, Q fragments
+    } else if (m < 22) {
+      r[m] = *reinterpret_cast<const u32x4*>(src.wsh + 16 * (lt + 128 * (m - 16)));   // T' fragments
+    } else {
+      const int vi = lt + 128 * (m - 22), row = vi >> 3, c8 = (vi & 7) * 8;
+      const int rr = row < src.nval ? row : src.nval - 1;                             // stays in bounds
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src.v + rr * src.sv + c8);
+      r[m] = row < src.nval ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
+}
+
+__device__ __forceinline__ void store_part_b(const u32x4 (&r)[kRegB], unsigned char* smem, int lt) {
+  using L = ChainLds;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int vi = tid + 256 * j;
-    *reinterpret_cast<u16x8*>(sV + (vi >> 3) * RP + (vi & 7) * 8) = pf.v[j];
+  for (int m = 0; m < kRegB; ++m) {
+    if (m < 22) {
+      reinterpret_cast<u32x4*>(smem + L::kK)[lt + 128 * m] = r[m];   // K | Q | T' are contiguous
+    } else {
+      const int vi = lt + 128 * (m - 22);
+      *reinterpret_cast<u32x4*>(smem + L::kV + ((vi >> 3) * RP + (vi & 7) * 8) * 2) = r[m];
+    }
   }
-#pragma unroll
-  for (int j = 0; j < 6; ++j) reinterpret_cast<u32x4*>(smem + L::kTP)[tid + 256 * j] = pf.tp[j];
-  if (tid < 64) reinterpret_cast<floatx4*>(smem + L::kSc)[tid] = pf.sc;
 }
 
 __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, const unsigned char* ws, int nwin,
                                                           const float* state_in, float* state_out) {
   using L = ChainLds;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + L::kK);
-  const uint16_t* sQ = reinterpret_cast<const uint16_t*>(smem + L::kQ);
-  const uint16_t* sKt = reinterpret_cast<const uint16_t*>(smem + L::kKt);
+  const unsigned char* sK = smem + L::kK;
+  const unsigned char* sQ = smem + L::kQ;
+  const unsigned char* sTp = smem + L::kTp;
   const uint16_t* sV = reinterpret_cast<const uint16_t*>(smem + L::kV);
-  const unsigned char* sTP = smem + L::kTP;
-  const float* sSc = reinterpret_cast<const float*>(smem + L::kSc);
   unsigned char* sMf = smem + L::kMf;
   unsigned char* sUf = smem + L::kUf;
 
@@ -438,17 +522,28 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
   const int slice = blockIdx.x, hv = blockIdx.y, b = blockIdx.z;
   const int hk = hv / a.G;
   const int bh = b * a.Hv + hv;
-  const int strip = wv & 1;                    // 32-column strip inside the slice
+  const int strip = wv & 1;                        // 32-column strip inside the slice
   const bool state_wave = wv < 2;
+  const int lt = tid - 128;                        // loader thread index (waves 2, 3)
   const int col = slice * DVS + 32 * strip + l32;  // this lane's value column (global)
   const int vcol = 32 * strip + l32;               // ... inside the V slice
   uint16_t* go = static_cast<uint16_t*>(a.o);
 
   const int nchunk = min(nwin, (a.T + CH - 1) / CH - c0);
-  auto wsc_of = [&](int cl) { return ws + (static_cast<int64_t>(bh) * nwin + cl) * WS_CHUNK; };
+  const unsigned char* regK = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WS_CHUNK;
+  auto src_of = [&](int cl) {
+    ChainSrc s;
+    s.wsh = ws + (static_cast<int64_t>(bh) * nwin + cl) * WS_CHUNK;
+    s.wsk = regK + (static_cast<int64_t>(b * a.Hk + hk) * nwin + cl) * WS_KQ;
+    const int t0 = (c0 + cl) * CH;
+    s.nval = min(CH, a.T - t0);
+    s.sv = a.sv;
+    s.v = static_cast<const uint16_t*>(a.v) + (static_cast<int64_t>(b) * a.T + t0) * a.sv + hv * DK + slice * DVS;
+    return s;
+  };
 
-  // State strip (state waves): 4 tiles of 32 key rows x 32 value columns.
   floatx16 Ms[4];
+  u32x4 regA[kRegA], regB[kRegB];
   if (state_wave) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -460,17 +555,15 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
         Ms[dt] = zero16();
       }
     }
-    // publish M as B fragments for the output waves' Q M
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       *reinterpret_cast<bf16x8*>(sMf + (strip * 8 + ks) * 1024 + lane * 16) = acc_frag(Ms[ks >> 1], ks & 1);
-  }
-
-  ChainPrefetch pf;
-  {
-    const int t0 = c0 * CH;
-    chain_prefetch(pf, a, wsc_of(0), static_cast<int64_t>(b) * a.T + t0, min(CH, a.T - t0), hk, hv, slice, tid);
-    chain_stage(pf, smem, tid);
+  } else {
+    const ChainSrc s0 = src_of(0);
+    load_part_b(regB, s0, lt);
+    load_part_a(regA, s0, lt);
+    store_part_b(regB, smem, lt);
+    store_part_a(regA, smem + L::kAlt, lt);
   }
   __syncthreads();
 
@@ -478,19 +571,28 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
     const int t0 = (c0 + cl) * CH;
     const int nval = min(CH, a.T - t0);
     const int64_t tokbase = static_cast<int64_t>(b) * a.T + t0;
-    if (cl + 1 < nchunk) {
-      const int t1 = t0 + CH;
-      chain_prefetch(pf, a, wsc_of(cl + 1), tokbase + CH, min(CH, a.T - t1), hk, hv, slice, tid);
-    }
+    const unsigned char* alt = smem + L::kAlt + (cl & 1) * L::kAltBytes;
+    const float* sSc = reinterpret_cast<const float*>(alt + L::kAltSc);
     if (state_wave) {
-      // X = V - diag(gamma rk) K M
-      floatx16 X[2] = {zero16(), zero16()};
+      // ---- phase 1: X = V - diag(gamma rk) K M ; U = T' X ; publish U ----
+      floatx16 X[2];
+      {
+        // four independent accumulation chains (row tile x even/odd k step) keep the
+        // MFMA pipe busy instead of waiting on one dependent chain
+        floatx16 Xe[2] = {zero16(), zero16()}, Xo[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 Bm = acc_frag(Ms[ks >> 1], ks & 1);
+        for (int kp = 0; kp < 4; ++kp) {
+          const bf16x8 B0 = acc_frag(Ms[kp], 0), B1 = acc_frag(Ms[kp], 1);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          X[rt] = mfma32(lds_frag32(sK + (32 * rt + l32) * KP + 16 * ks, h), Bm, X[rt]);
+          for (int rt = 0; rt < 2; ++rt) {
+            const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(sK + (rt * 8 + 2 * kp) * 1024 + lane * 16);
+            const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(sK + (rt * 8 + 2 * kp + 1) * 1024 + lane * 16);
+            Xe[rt] = mfma32(A0, B0, Xe[rt]);
+            Xo[rt] = mfma32(A1, B1, Xo[rt]);
+          }
+        }
+        X[0] = Xe[0] + Xo[0];
+        X[1] = Xe[1] + Xo[1];
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
@@ -499,23 +601,25 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
           const int r = 32 * rt + acc_row(v, h);
           X[rt][v] = bf16_bits_to_f32(sV[r * RP + vcol]) - sSc[r] * X[rt][v];
         }
-      // U = T' X
-      floatx16 U[2] = {zero16(), zero16()};
+      floatx16 U[2];
       {
         bf16x8 Xh[4], Xl[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) acc_frag_split(X[ks >> 1], ks & 1, Xh[ks], Xl[ks]);
+        // hi*hi, hi*lo and lo*hi in separate accumulators: six independent chains
+        floatx16 Uhh[2] = {zero16(), zero16()}, Uhl[2] = {zero16(), zero16()}, Ulh[2] = {zero16(), zero16()};
 #pragma unroll
         for (int f = 0; f < FT; ++f) {
           const int rt = f < 2 ? 0 : 1, ks = f < 2 ? f : f - 2;
-          const bf16x8 Ah = *reinterpret_cast<const bf16x8*>(sTP + (f * 2 + 0) * 1024 + lane * 16);
-          const bf16x8 Al = *reinterpret_cast<const bf16x8*>(sTP + (f * 2 + 1) * 1024 + lane * 16);
-          U[rt] = mfma32(Ah, Xh[ks], U[rt]);
-          U[rt] = mfma32(Ah, Xl[ks], U[rt]);
-          U[rt] = mfma32(Al, Xh[ks], U[rt]);
+          const bf16x8 Ah = *reinterpret_cast<const bf16x8*>(sTp + (f * 2 + 0) * 1024 + lane * 16);
+          const bf16x8 Al = *reinterpret_cast<const bf16x8*>(sTp + (f * 2 + 1) * 1024 + lane * 16);
+          Uhh[rt] = mfma32(Ah, Xh[ks], Uhh[rt]);
+          Uhl[rt] = mfma32(Ah, Xl[ks], Uhl[rt]);
+          Ulh[rt] = mfma32(Al, Xh[ks], Ulh[rt]);
         }
+        U[0] = Uhh[0] + (Uhl[0] + Ulh[0]);
+        U[1] = Uhh[1] + (Uhl[1] + Ulh[1]);
       }
-      // publish U (hi/lo B fragments) for P U
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         bf16x8 hi, lo;
@@ -523,9 +627,10 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
         *reinterpret_cast<bf16x8*>(sUf + ((strip * 4 + ks) * 2 + 0) * 1024 + lane * 16) = hi;
         *reinterpret_cast<bf16x8*>(sUf + ((strip * 4 + ks) * 2 + 1) * 1024 + lane * 16) = lo;
       }
-      __syncthreads();  // (1) U published; the output waves' Q M has read sMf
-      // M <- gamma_63 M + K^T diag(rk e^{g_63-g}) U
+      __syncthreads();  // B1: U published; Q M has read M
+      // ---- phase 2: M <- gamma_63 M + K^T diag(rk e^{g_63-g}) U ; publish M ----
       {
+        const unsigned char* sKt = alt + L::kAltKt;
         bf16x8 Wh[4], Wl[4];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -535,57 +640,91 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
         for (int ks = 0; ks < 4; ++ks) acc_frag_split(U[ks >> 1], ks & 1, Wh[ks], Wl[ks]);
         const float gC = sSc[192];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          Ms[dt] *= gC;
+        for (int dt = 0; dt < 4; ++dt) Ms[dt] *= gC;
+        // the lo parts accumulate apart from M: eight independent chains, four tiles wide
+        floatx16 Ml[4] = {zero16(), zero16(), zero16(), zero16()};
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 A = lds_frag32(sKt + (32 * dt + l32) * RP + 16 * ks, h);
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const bf16x8 A = *reinterpret_cast<const bf16x8*>(sKt + (dt * 4 + ks) * 1024 + lane * 16);
             Ms[dt] = mfma32(A, Wh[ks], Ms[dt]);
-            Ms[dt] = mfma32(A, Wl[ks], Ms[dt]);
+            Ml[dt] = mfma32(A, Wl[ks], Ml[dt]);
           }
-        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) Ms[dt] += Ml[dt];
       }
-      // M for the next chunk's Q M
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         *reinterpret_cast<bf16x8*>(sMf + (strip * 8 + ks) * 1024 + lane * 16) = acc_frag(Ms[ks >> 1], ks & 1);
+      __syncthreads();  // B2
     } else {
-      // output waves: O = diag(gamma rq) Q M + P U
-      floatx16 O[2] = {zero16(), zero16()};
+      // ---- phase 1: issue the next chunk's loads (part B first: it is consumed
+      //      first); O = diag(gamma rq) Q M ----
+      const bool more = cl + 1 < nchunk;
+      if (more) {
+        const ChainSrc sn = src_of(cl + 1);
+        load_part_b(regB, sn, lt);
+        load_part_a(regA, sn, lt);
+      }
+      floatx16 O[2];
+      {
+        floatx16 Oe[2] = {zero16(), zero16()}, Oo[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 Bm = *reinterpret_cast<const bf16x8*>(sMf + (strip * 8 + ks) * 1024 + lane * 16);
+        for (int kp = 0; kp < 4; ++kp) {
+          const bf16x8 B0 = *reinterpret_cast<const bf16x8*>(sMf + (strip * 8 + 2 * kp) * 1024 + lane * 16);
+          const bf16x8 B1 = *reinterpret_cast<const bf16x8*>(sMf + (strip * 8 + 2 * kp + 1) * 1024 + lane * 16);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          O[rt] = mfma32(lds_frag32(sQ + (32 * rt + l32) * KP + 16 * ks, h), Bm, O[rt]);
+          for (int rt = 0; rt < 2; ++rt) {
+            const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(sQ + (rt * 8 + 2 * kp) * 1024 + lane * 16);
+            const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(sQ + (rt * 8 + 2 * kp + 1) * 1024 + lane * 16);
+            Oe[rt] = mfma32(A0, B0, Oe[rt]);
+            Oo[rt] = mfma32(A1, B1, Oo[rt]);
+          }
+        }
+        O[0] = Oe[0] + Oo[0];
+        O[1] = Oe[1] + Oo[1];
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) O[rt][v] *= sSc[64 + 32 * rt + acc_row(v, h)];
-      __syncthreads();  // (1) wait for U
+      __syncthreads();  // B1: wait for U; the primary buffer is free
+      // ---- phase 2: stage part B of chunk cl+1 ; O += P U ; store O ; stage part A ----
+      if (more) store_part_b(regB, smem, lt);
+      {
+        const unsigned char* sP = alt + L::kAltP;
+        floatx16 Ohl[2] = {zero16(), zero16()}, Olh[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int f = 0; f < FT; ++f) {
-        const int rt = f < 2 ? 0 : 1, ks = f < 2 ? f : f - 2;
-        const bf16x8 Ph = *reinterpret_cast<const bf16x8*>(sTP + ((6 + f) * 2 + 0) * 1024 + lane * 16);
-        const bf16x8 Pl = *reinterpret_cast<const bf16x8*>(sTP + ((6 + f) * 2 + 1) * 1024 + lane * 16);
-        const bf16x8 Uh = *reinterpret_cast<const bf16x8*>(sUf + ((strip * 4 + ks) * 2 + 0) * 1024 + lane * 16);
-        const bf16x8 Ul = *reinterpret_cast<const bf16x8*>(sUf + ((strip * 4 + ks) * 2 + 1) * 1024 + lane * 16);
-        O[rt] = mfma32(Ph, Uh, O[rt]);
-        O[rt] = mfma32(Ph, Ul, O[rt]);
-        O[rt] = mfma32(Pl, Uh, O[rt]);
+        for (int f = 0; f < FT; ++f) {
+          const int rt = f < 2 ? 0 : 1, ks = f < 2 ? f : f - 2;
+          const bf16x8 Ph = *reinterpret_cast<const bf16x8*>(sP + (f * 2 + 0) * 1024 + lane * 16);
+          const bf16x8 Pl = *reinterpret_cast<const bf16x8*>(sP + (f * 2 + 1) * 1024 + lane * 16);
+          const bf16x8 Uh = *reinterpret_cast<const bf16x8*>(sUf + ((strip * 4 + ks) * 2 + 0) * 1024 + lane * 16);
+          const bf16x8 Ul = *reinterpret_cast<const bf16x8*>(sUf + ((strip * 4 + ks) * 2 + 1) * 1024 + lane * 16);
+          O[rt] = mfma32(Ph, Uh, O[rt]);
+          Ohl[rt] = mfma32(Ph, Ul, Ohl[rt]);
+          Olh[rt] = mfma32(Pl, Uh, Olh[rt]);
+        }
+        O[0] += Ohl[0] + Olh[0];
+        O[1] += Ohl[1] + Olh[1];
       }
+      // O through LDS so that HBM sees 16-byte row segments
+      uint16_t* sO = reinterpret_cast<uint16_t*>(smem + L::kO) + strip * CH * L::OP;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = 32 * rt + acc_row(v, h);
-          if (r < nval) go[(tokbase + r) * a.so + hv * DK + col] = f32_to_bf16_bits(O[rt][v]);
-        }
+        for (int v = 0; v < 16; ++v) sO[(32 * rt + acc_row(v, h)) * L::OP + l32] = f32_to_bf16_bits(O[rt][v]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int vi = lane + 64 * m, r = vi >> 2, c8 = (vi & 3) * 8;
+        if (r < nval)
+          *reinterpret_cast<u16x8*>(go + (tokbase + r) * a.so + hv * DK + slice * DVS + 32 * strip + c8) =
+              *reinterpret_cast<const u16x8*>(sO + r * L::OP + c8);
+      }
+      if (more) store_part_a(regA, smem + L::kAlt + ((cl + 1) & 1) * L::kAltBytes, lt);
+      __syncthreads();  // B2
     }
-    __syncthreads();  // (2) every wave is done with this chunk's LDS inputs
-    if (cl + 1 < nchunk) chain_stage(pf, smem, tid);
-    __syncthreads();  // (3) next chunk staged
   }
 
   if (state_wave && state_out) {
@@ -599,7 +738,9 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
 
 }  // namespace
 
-size_t chunk_ws_bytes_per_chunk(const RecArgs& a) { return static_cast<size_t>(a.B) * a.Hv * WS_CHUNK; }
+size_t chunk_ws_bytes_per_chunk(const RecArgs& a) {
+  return static_cast<size_t>(a.B) * (static_cast<size_t>(a.Hv) * WS_CHUNK + static_cast<size_t>(a.Hk) * WS_KQ);
+}
 
 size_t chunk_ws_carry_bytes(const RecArgs& a) { return static_cast<size_t>(a.B) * a.Hv * DK * DK * 4; }
 
