@@ -28,7 +28,7 @@
 //    that does not depend on the state -- row norms, the Gram products
 //    K K^T and Q K^T (MFMA), the gate prefix sums, A, the triangular inverse
 //    (fp32, blocked 16/32), T' and P -- written to the workspace as ready
-//    MFMA A-operand fragments (bf16 hi + lo pairs) plus three row-scaling
+//    MFMA A-operand fragments (fp16) plus three row-scaling
 //    vectors per (chunk, value head).
 //    The prep kernel also writes K, Q and K^T as fragments, so the chain
 //    kernel stages its inputs with plain 16-byte copies and reads every MFMA
@@ -44,13 +44,16 @@
 //    phase reads go to one of two alternating buffers at the chunk's end,
 //    the rest is restaged while the update runs.
 //
-// Precision.  MFMA operands are bf16 with fp32 accumulation.  Genuine bf16
-// inputs (K, Q, V) enter as they are.  fp32 operands whose rounding would
-// reach the state or output tolerance are split into hi + lo bf16 pairs:
-// T' and X in T'X (3 products), P and U in P U (3), U' in K^T U' (2).  M
-// enters K M and Q M as a single bf16.
+// Precision.  MFMA accumulation is fp32 throughout.  K M and Q M run on bf16
+// operands (K and Q are bf16 inputs; M is rounded once to bf16 for them).
+// T'X, P U and K^T U' run on fp16 operands: T', P and the update's K^T are
+// written as fp16 by the prep kernel (bf16 K converts exactly), X and U are
+// rounded once to fp16.  fp16 keeps 11 significant bits, which holds the
+// state within a few 1e-4 of the exact result and the outputs well inside
+// their bound; its range (|x| < 65504) bounds the values of v, the state and
+// the intra-chunk matrices this path accepts.
 //
-// MFMA layout (v_mfma_f32_32x32x16_bf16, wave64): A row = B column =
+// MFMA layout (v_mfma_f32_32x32x16_bf16 and _f16, wave64): A row = B column =
 // lane & 31; the accumulator holds column lane & 31, rows 8j + 4h + i
 // (h = lane >> 5, value index 4j + i).  The contraction index is permuted the
 // same way on A and B: inside each 16-wide k step, lane half h carries
@@ -66,6 +69,7 @@ namespace {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
 constexpr int CH = 64;    // chunk length
 constexpr int DK = 128;   // head width
@@ -74,7 +78,7 @@ constexpr int RP = 72;    // LDS row pitch (bf16) of K^T and of the V slice
 constexpr int FP = 68;    // LDS row pitch (floats) of fp32 64 x 64 matrices (16-byte rows)
 constexpr int DVS = 64;   // value columns per chain workgroup
 constexpr int FT = 6;     // 32x16 fragment tiles covering a 64x64 lower triangle
-constexpr int WS_TP = 2 * FT * 2 * 1024;  // T' and P fragments, hi and lo
+constexpr int WS_TP = 2 * FT * 1024;      // T' and P fragments (fp16)
 constexpr int WS_CHUNK = WS_TP + 2048;    // + grk[64], grq[64], drk[64], gamma_63 (2 KiB slot)
 constexpr int WS_KQ = 3 * 16 * 1024;      // per (b, key head, chunk): K, Q and K^T fragments
 
@@ -95,21 +99,26 @@ __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ floatx16 mfma32h(const halfx8& a, const halfx8& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ halfx8 acc_frag_h(const floatx16& t, int s) {
+  halfx8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<_Float16>(t[8 * s + e]);
+  return r;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
 __device__ __forceinline__ bf16x8 acc_frag(const floatx16& t, int s) {
   bf16x8 r;
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(t[8 * s + e]);
   return r;
-}
-
-__device__ __forceinline__ void acc_frag_split(const floatx16& t, int s, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = t[8 * s + e];
-    const __bf16 hb = static_cast<__bf16>(x);
-    hi[e] = hb;
-    lo[e] = static_cast<__bf16>(x - static_cast<float>(hb));
-  }
 }
 
 __device__ __forceinline__ floatx16 zero16() {
@@ -212,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       } else {
         const int d = 32 * (tile >> 2) + r32, k0 = 16 * (tile & 3);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = sK[(k0 + kperm(hh, e)) * KP + d];
+        for (int e = 0; e < 8; ++e) f[e] = f32_to_f16_bits(bf16_bits_to_f32(sK[(k0 + kperm(hh, e)) * KP + d]));
       }
       *reinterpret_cast<u16x8*>(wsk + mat * 16384 + tile * 1024 + ln * 16) = f;
     }
@@ -304,19 +313,15 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       const floatx4 qb = *reinterpret_cast<const floatx4*>(sQK + r * FP + cb);
       const floatx4 ga = *reinterpret_cast<const floatx4*>(vG + ca), gb = *reinterpret_cast<const floatx4*>(vG + cb);
       const floatx4 ka = *reinterpret_cast<const floatx4*>(vRk + ca), kb = *reinterpret_cast<const floatx4*>(vRk + cb);
-      u16x8 hi, lo;
+      u16x8 pf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = e < 4 ? ca + e : cb + e - 4;
         const float qk = e < 4 ? qa[e] : qb[e - 4], g = e < 4 ? ga[e] : gb[e - 4], rk = e < 4 ? ka[e] : kb[e - 4];
         const float x = __expf(fminf(gr - g, 0.f)) * rq * rk * qk;
-        const float pv = i <= r ? x : 0.f;
-        const __bf16 hb = static_cast<__bf16>(pv);
-        hi[e] = __builtin_bit_cast(uint16_t, hb);
-        lo[e] = f32_to_bf16_bits(pv - static_cast<float>(hb));
+        pf[e] = f32_to_f16_bits(i <= r ? x : 0.f);
       }
-      *reinterpret_cast<u16x8*>(wsc + ((6 + f) * 2 + 0) * 1024 + ln * 16) = hi;
-      *reinterpret_cast<u16x8*>(wsc + ((6 + f) * 2 + 1) * 1024 + ln * 16) = lo;
+      *reinterpret_cast<u16x8*>(wsc + (6 + f) * 1024 + ln * 16) = pf;
     }
     __syncthreads();
     // ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution ------
@@ -408,18 +413,14 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       const floatx4 ta = *reinterpret_cast<const floatx4*>(sT + r * FP + ca);
       const floatx4 tb = *reinterpret_cast<const floatx4*>(sT + r * FP + cb);
       const floatx4 ba = *reinterpret_cast<const floatx4*>(vBe + ca), bb = *reinterpret_cast<const floatx4*>(vBe + cb);
-      u16x8 hi, lo;
+      u16x8 tf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = e < 4 ? ca + e : cb + e - 4;
         const float x = e < 4 ? ta[e] * ba[e] : tb[e - 4] * bb[e - 4];
-        const float tv = i <= r ? x : 0.f;
-        const __bf16 hb = static_cast<__bf16>(tv);
-        hi[e] = __builtin_bit_cast(uint16_t, hb);
-        lo[e] = f32_to_bf16_bits(tv - static_cast<float>(hb));
+        tf[e] = f32_to_f16_bits(i <= r ? x : 0.f);
       }
-      *reinterpret_cast<u16x8*>(wsc + (f * 2 + 0) * 1024 + ln * 16) = hi;
-      *reinterpret_cast<u16x8*>(wsc + (f * 2 + 1) * 1024 + ln * 16) = lo;
+      *reinterpret_cast<u16x8*>(wsc + f * 1024 + ln * 16) = tf;
     }
     __syncthreads();  // vG, vBe, sA, sT are rewritten for the next value head
   }
@@ -434,26 +435,26 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
 struct ChainLds {
   static constexpr int kK = 0;                     // 16 fragment tiles
   static constexpr int kQ = kK + 16 * 1024;        // 16 fragment tiles
-  static constexpr int kTp = kQ + 16 * 1024;       // T' 6 tiles x hi/lo
-  static constexpr int kV = kTp + 12 * 1024;       // bf16 [64][RP]
-  static constexpr int kAlt = kV + CH * RP * 2;    // 2 x {K^T 16 tiles | P 6 x hi/lo | scalings}
-  static constexpr int kAltKt = 0, kAltP = 16 * 1024, kAltSc = 28 * 1024;
-  static constexpr int kAltBytes = 30 * 1024;
-  static constexpr int kMf = kAlt + 2 * kAltBytes;  // M B-fragments [2 strips][8 k steps][64 lanes] x 16 B
-  static constexpr int kUf = kMf + 2 * 8 * 1024;    // U B-fragments [2 strips][4 k steps][hi/lo][64] x 16 B
-  static constexpr int kO = kUf + 2 * 4 * 2 * 1024; // O staging: [2 strips][64 rows][OP] bf16
+  static constexpr int kTp = kQ + 16 * 1024;       // T' 6 fp16 tiles
+  static constexpr int kV = kTp + 6 * 1024;        // bf16 [64][RP]
+  static constexpr int kAlt = kV + CH * RP * 2;    // 2 x {K^T 16 fp16 tiles | P 6 fp16 tiles | scalings}
+  static constexpr int kAltKt = 0, kAltP = 16 * 1024, kAltSc = 22 * 1024;
+  static constexpr int kAltBytes = 24 * 1024;
+  static constexpr int kMf = kAlt + 2 * kAltBytes;  // M B-fragments (bf16) [2 strips][8 k steps][64 lanes] x 16 B
+  static constexpr int kUf = kMf + 2 * 8 * 1024;    // U B-fragments (fp16) [2 strips][4 k steps][64] x 16 B
+  static constexpr int kO = kUf + 2 * 4 * 1024;     // O staging: [2 strips][64 rows][OP] bf16
   static constexpr int OP = 40;
   static constexpr int kBytes = kO + 2 * CH * OP * 2;
 };
 
 // Loader waves (2 and 3) move a chunk's chain inputs global -> registers -> LDS in two parts:
-// part A (K^T fragments, P fragments, row scalings; 30 KiB) into the alternating buffer, and
-// part B (K, Q, T' fragments; 44 KiB; plus the 8 KiB V slice) into the primary buffer.  Both
+// part A (K^T fragments, P fragments, row scalings; 24 KiB) into the alternating buffer, and
+// part B (K, Q, T' fragments; 38 KiB; plus the 8 KiB V slice) into the primary buffer.  Both
 // parts are whole multiples of 128 16-byte vectors and every source is a compile-time function of
 // the unrolled index, so the loads carry no per-lane branches and the compiler can wait for each
 // part on its own in issue order.
-constexpr int kRegA = 15;   // 8 x 128 K^T vectors, 6 x 128 P vectors, 1 x 128 scaling vectors
-constexpr int kRegB = 26;   // 16 x 128 K|Q vectors, 6 x 128 T' vectors, 4 x 128 V vectors
+constexpr int kRegA = 12;   // 8 x 128 K^T vectors, 3 x 128 P vectors, 1 x 128 scaling vectors
+constexpr int kRegB = 23;   // 16 x 128 K|Q vectors, 3 x 128 T' vectors, 4 x 128 V vectors
 
 struct ChainSrc {
   const unsigned char* wsh;   // region H block of (b, hv, chunk)
@@ -467,7 +468,7 @@ __device__ __forceinline__ void load_part_a(u32x4 (&r)[kRegA], const ChainSrc& s
 #pragma unroll
   for (int m = 0; m < kRegA; ++m) {
     const unsigned char* p = m < 8 ? src.wsk + 32768 + 16 * (lt + 128 * m)              // K^T fragments
-                                   : src.wsh + 12288 + 16 * (lt + 128 * (m - 8));       // P | scalings
+                                   : src.wsh + 6144 + 16 * (lt + 128 * (m - 8));        // P | scalings
     r[m] = *reinterpret_cast<const u32x4*>(p);
   }
 }
@@ -482,10 +483,10 @@ __device__ __forceinline__ void load_part_b(u32x4 (&r)[kRegB], const ChainSrc& s
   for (int m = 0; m < kRegB; ++m) {
     if (m < 16) {
       r[m] = *reinterpret_cast<const u32x4*>(src.wsk + 16 * (lt + 128 * m));          // K, Q fragments
-    } else if (m < 22) {
+    } else if (m < 19) {
       r[m] = *reinterpret_cast<const u32x4*>(src.wsh + 16 * (lt + 128 * (m - 16)));   // T' fragments
     } else {
-      const int vi = lt + 128 * (m - 22), row = vi >> 3, c8 = (vi & 7) * 8;
+      const int vi = lt + 128 * (m - 19), row = vi >> 3, c8 = (vi & 7) * 8;
       const int rr = row < src.nval ? row : src.nval - 1;                             // stays in bounds
       const u32x4 x = *reinterpret_cast<const u32x4*>(src.v + rr * src.sv + c8);
       r[m] = row < src.nval ? x : u32x4{0u, 0u, 0u, 0u};
@@ -497,10 +498,10 @@ __device__ __forceinline__ void store_part_b(const u32x4 (&r)[kRegB], unsigned c
   using L = ChainLds;
 #pragma unroll
   for (int m = 0; m < kRegB; ++m) {
-    if (m < 22) {
+    if (m < 19) {
       reinterpret_cast<u32x4*>(smem + L::kK)[lt + 128 * m] = r[m];   // K | Q | T' are contiguous
     } else {
-      const int vi = lt + 128 * (m - 22);
+      const int vi = lt + 128 * (m - 19);
       *reinterpret_cast<u32x4*>(smem + L::kV + ((vi >> 3) * RP + (vi & 7) * 8) * 2) = r[m];
     }
   }
@@ -599,60 +600,50 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = 32 * rt + acc_row(v, h);
-          X[rt][v] = bf16_bits_to_f32(sV[r * RP + vcol]) - sSc[r] * X[rt][v];
+          X[rt][v] = fmaf(-sSc[r], X[rt][v], bf16_bits_to_f32(sV[r * RP + vcol]));
         }
       floatx16 U[2];
       {
-        bf16x8 Xh[4], Xl[4];
+        halfx8 Xf[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc_frag_split(X[ks >> 1], ks & 1, Xh[ks], Xl[ks]);
-        // hi*hi, hi*lo and lo*hi in separate accumulators: six independent chains
-        floatx16 Uhh[2] = {zero16(), zero16()}, Uhl[2] = {zero16(), zero16()}, Ulh[2] = {zero16(), zero16()};
+        for (int ks = 0; ks < 4; ++ks) Xf[ks] = acc_frag_h(X[ks >> 1], ks & 1);
+        // T' X in fp16 with four independent accumulators (row tile x k-step parity)
+        floatx16 Ue[2] = {zero16(), zero16()}, Uo[2] = {zero16(), zero16()};
 #pragma unroll
         for (int f = 0; f < FT; ++f) {
           const int rt = f < 2 ? 0 : 1, ks = f < 2 ? f : f - 2;
-          const bf16x8 Ah = *reinterpret_cast<const bf16x8*>(sTp + (f * 2 + 0) * 1024 + lane * 16);
-          const bf16x8 Al = *reinterpret_cast<const bf16x8*>(sTp + (f * 2 + 1) * 1024 + lane * 16);
-          Uhh[rt] = mfma32(Ah, Xh[ks], Uhh[rt]);
-          Uhl[rt] = mfma32(Ah, Xl[ks], Uhl[rt]);
-          Ulh[rt] = mfma32(Al, Xh[ks], Ulh[rt]);
+          const halfx8 At = *reinterpret_cast<const halfx8*>(sTp + f * 1024 + lane * 16);
+          if (ks & 1) Uo[rt] = mfma32h(At, Xf[ks], Uo[rt]);
+          else Ue[rt] = mfma32h(At, Xf[ks], Ue[rt]);
         }
-        U[0] = Uhh[0] + (Uhl[0] + Ulh[0]);
-        U[1] = Uhh[1] + (Uhl[1] + Ulh[1]);
+        U[0] = Ue[0] + Uo[0];
+        U[1] = Ue[1] + Uo[1];
       }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 hi, lo;
-        acc_frag_split(U[ks >> 1], ks & 1, hi, lo);
-        *reinterpret_cast<bf16x8*>(sUf + ((strip * 4 + ks) * 2 + 0) * 1024 + lane * 16) = hi;
-        *reinterpret_cast<bf16x8*>(sUf + ((strip * 4 + ks) * 2 + 1) * 1024 + lane * 16) = lo;
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        *reinterpret_cast<halfx8*>(sUf + (strip * 4 + ks) * 1024 + lane * 16) = acc_frag_h(U[ks >> 1], ks & 1);
       __syncthreads();  // B1: U published; Q M has read M
       // ---- phase 2: M <- gamma_63 M + K^T diag(rk e^{g_63-g}) U ; publish M ----
       {
         const unsigned char* sKt = alt + L::kAltKt;
-        bf16x8 Wh[4], Wl[4];
+        halfx8 Wf[4];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
           for (int v = 0; v < 16; ++v) U[rt][v] *= sSc[128 + 32 * rt + acc_row(v, h)];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc_frag_split(U[ks >> 1], ks & 1, Wh[ks], Wl[ks]);
+        for (int ks = 0; ks < 4; ++ks) Wf[ks] = acc_frag_h(U[ks >> 1], ks & 1);
         const float gC = sSc[192];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) Ms[dt] *= gC;
-        // the lo parts accumulate apart from M: eight independent chains, four tiles wide
-        floatx16 Ml[4] = {zero16(), zero16(), zero16(), zero16()};
+        // four state tiles interleaved: four independent accumulation chains
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
-            const bf16x8 A = *reinterpret_cast<const bf16x8*>(sKt + (dt * 4 + ks) * 1024 + lane * 16);
-            Ms[dt] = mfma32(A, Wh[ks], Ms[dt]);
-            Ml[dt] = mfma32(A, Wl[ks], Ml[dt]);
+            const halfx8 A = *reinterpret_cast<const halfx8*>(sKt + (dt * 4 + ks) * 1024 + lane * 16);
+            Ms[dt] = mfma32h(A, Wf[ks], Ms[dt]);
           }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) Ms[dt] += Ml[dt];
       }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
@@ -694,20 +685,17 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
       if (more) store_part_b(regB, smem, lt);
       {
         const unsigned char* sP = alt + L::kAltP;
-        floatx16 Ohl[2] = {zero16(), zero16()}, Olh[2] = {zero16(), zero16()};
+        floatx16 Op[2] = {zero16(), zero16()};
 #pragma unroll
         for (int f = 0; f < FT; ++f) {
           const int rt = f < 2 ? 0 : 1, ks = f < 2 ? f : f - 2;
-          const bf16x8 Ph = *reinterpret_cast<const bf16x8*>(sP + (f * 2 + 0) * 1024 + lane * 16);
-          const bf16x8 Pl = *reinterpret_cast<const bf16x8*>(sP + (f * 2 + 1) * 1024 + lane * 16);
-          const bf16x8 Uh = *reinterpret_cast<const bf16x8*>(sUf + ((strip * 4 + ks) * 2 + 0) * 1024 + lane * 16);
-          const bf16x8 Ul = *reinterpret_cast<const bf16x8*>(sUf + ((strip * 4 + ks) * 2 + 1) * 1024 + lane * 16);
-          O[rt] = mfma32(Ph, Uh, O[rt]);
-          Ohl[rt] = mfma32(Ph, Ul, Ohl[rt]);
-          Olh[rt] = mfma32(Pl, Uh, Olh[rt]);
+          const halfx8 Pf = *reinterpret_cast<const halfx8*>(sP + f * 1024 + lane * 16);
+          const halfx8 Uf = *reinterpret_cast<const halfx8*>(sUf + (strip * 4 + ks) * 1024 + lane * 16);
+          if (ks & 1) Op[rt] = mfma32h(Pf, Uf, Op[rt]);
+          else O[rt] = mfma32h(Pf, Uf, O[rt]);
         }
-        O[0] += Ohl[0] + Olh[0];
-        O[1] += Ohl[1] + Olh[1];
+        O[0] += Op[0];
+        O[1] += Op[1];
       }
       // O through LDS so that HBM sees 16-byte row segments
       uint16_t* sO = reinterpret_cast<uint16_t*>(smem + L::kO) + strip * CH * L::OP;
