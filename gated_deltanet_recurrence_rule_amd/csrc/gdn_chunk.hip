@@ -73,14 +73,18 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
 constexpr int CH = 64;    // chunk length
 constexpr int DK = 128;   // head width
-constexpr int KP = 136;   // LDS row pitch (bf16) of 64 x 128 K / Q tiles
-constexpr int RP = 72;    // LDS row pitch (bf16) of K^T and of the V slice
+constexpr int KP = 136;   // LDS row pitch (bf16) of 64 x 128 row tiles
 constexpr int FP = 68;    // LDS row pitch (floats) of fp32 64 x 64 matrices (16-byte rows)
-constexpr int DVS = 64;   // value columns per chain workgroup
 constexpr int FT = 6;     // 32x16 fragment tiles covering a 64x64 lower triangle
-constexpr int WS_TP = 2 * FT * 1024;      // T' and P fragments (fp16)
-constexpr int WS_CHUNK = WS_TP + 2048;    // + grk[64], grq[64], drk[64], gamma_63 (2 KiB slot)
-constexpr int WS_KQ = 3 * 16 * 1024;      // per (b, key head, chunk): K, Q and K^T fragments
+// workspace block per (batch, value head, chunk): fp16 MFMA fragments and fp32 scalings
+constexpr int WH_W = 0;        // -W = -T' diag(gamma rk) K: tile rt*8+ks (rows 32rt.., key step ks)
+constexpr int WH_KD = 16384;   // Kd = K^T diag(rk e^{g_63-g}): tile dt*4+ks (keys 32dt.., chunk step ks)
+constexpr int WH_U0 = 32768;   // U0 = T' V in accumulator layout: [value tile 4][row tile 2][lane 64][16]
+constexpr int WH_P = 49152;    // P: 6 tiles of the lower triangle
+constexpr int WH_SC = 55296;   // gamma_r (64 floats), gamma_63
+constexpr int WH_BYTES = 56320;
+// workspace block per (batch, key head, chunk): Q^ = diag(rq) Q fragments, tile rt*8+ks
+constexpr int WK_BYTES = 16384;
 
 // fragment tile f covers rows 32*kFtRt[f].., k step kFtKs[f] (16 columns)
 __device__ __forceinline__ int ft_rt(int f) { return f < 2 ? 0 : 1; }
@@ -114,13 +118,6 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
-__device__ __forceinline__ bf16x8 acc_frag(const floatx16& t, int s) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(t[8 * s + e]);
-  return r;
-}
-
 __device__ __forceinline__ floatx16 zero16() {
   floatx16 z;
 #pragma unroll
@@ -135,31 +132,31 @@ __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 *
 // prep kernel: one workgroup (4 waves) per (chunk in window, key head, batch)
 // =========================================================================
 struct PrepLds {
-  static constexpr int kKQ = 0;                       // sK, sQ bf16 [64][KP]; later sA, sT fp32
-  static constexpr int kA = 0;
-  static constexpr int kT = CH * FP * 4;
-  static constexpr int kKK = 2 * CH * KP * 2;         // fp32 [64][FP]
-  static constexpr int kQK = kKK + CH * FP * 4;
-  static constexpr int kY = kQK + CH * FP * 4;        // fp32 32 x 36 (or 2 x 16 x 20)
-  static constexpr int kVec = kY + 32 * 36 * 4;       // rk, rq, g, beta
-  static constexpr int kBytes = kVec + 4 * CH * 4;
+  static constexpr int kK = 0;                   // bf16 [64][KP]; later sA fp32 [64][FP]
+  static constexpr int kQ = CH * KP * 2;         // bf16 [64][KP]; later sT fp32 [64][FP]
+  static constexpr int kV = 2 * CH * KP * 2;     // bf16 [64][KP]: V rows of the current value head
+  static constexpr int kY = 3 * CH * KP * 2;     // fp32 32 x 36 (or 2 x 16 x 20)
+  static constexpr int kVec = kY + 32 * 36 * 4;  // rk, rq, g, beta, gamma rk, rk e^{g_63 - g}
+  static constexpr int kBytes = kVec + 6 * CH * 4;
 };
+static_assert(CH * FP * 4 <= CH * KP * 2, "sA and sT reuse the K and Q rows");
 
 __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, unsigned char* ws, int nwin) {
-  // workspace: region H = [B][Hv][nwin] x WS_CHUNK, then region K = [B][Hk][nwin] x WS_KQ
+  // workspace: region H = [B][Hv][nwin] x WH_BYTES, then region K = [B][Hk][nwin] x WK_BYTES
   using L = PrepLds;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + L::kKQ);
-  uint16_t* sQ = sK + CH * KP;
-  float* sA = reinterpret_cast<float*>(smem + L::kA);
-  float* sT = reinterpret_cast<float*>(smem + L::kT);
-  float* sKK = reinterpret_cast<float*>(smem + L::kKK);
-  float* sQK = reinterpret_cast<float*>(smem + L::kQK);
+  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + L::kK);
+  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + L::kQ);
+  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + L::kV);
+  float* sA = reinterpret_cast<float*>(smem + L::kK);
+  float* sT = reinterpret_cast<float*>(smem + L::kQ);
   float* sY = reinterpret_cast<float*>(smem + L::kY);
   float* vRk = reinterpret_cast<float*>(smem + L::kVec);
   float* vRq = vRk + CH;
   float* vG = vRk + 2 * CH;
   float* vBe = vRk + 3 * CH;
+  float* vKs = vRk + 4 * CH;
+  float* vKd = vRk + 5 * CH;
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, h = lane >> 5;
@@ -171,6 +168,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   const bool l2 = (a.flags & 1u) != 0;
   const uint16_t* gq = static_cast<const uint16_t*>(a.q);
   const uint16_t* gk = static_cast<const uint16_t*>(a.k);
+  const uint16_t* gv = static_cast<const uint16_t*>(a.v);
 
   // ---- K, Q rows and their norms ------------------------------------------
 #pragma unroll
@@ -203,52 +201,67 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   }
   __syncthreads();
 
-  // ---- K, Q and K^T as the chain kernel's MFMA A fragments ------------------
-  // K, Q (A of K M / Q M): tile (rt, ks) holds rows 32rt + (lane&31), k = 16ks + kperm;
-  // K^T (A of K^T U): tile (dt, ks) holds key rows 32dt + (lane&31), k = chunk rows 16ks + kperm.
+  // ---- Q^ = diag(rq) Q as the output product's A fragments (fp16) -----------
+  //      tile rt*8+ks holds rows 32rt + (lane&31), k = 16ks + kperm
   {
-    unsigned char* wsk = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WS_CHUNK +
-                         (static_cast<int64_t>(b * a.Hk + hk) * nwin + cl) * WS_KQ;
-    for (int slot = tid; slot < 3 * 16 * 64; slot += 256) {
-      const int mat = slot >> 10, tile = (slot >> 6) & 15, ln = slot & 63;
-      const int r32 = ln & 31, hh = ln >> 5;
+    unsigned char* wsk = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WH_BYTES +
+                         (static_cast<int64_t>(b * a.Hk + hk) * nwin + cl) * WK_BYTES;
+    for (int slot = tid; slot < 16 * 64; slot += 256) {
+      const int tile = slot >> 6, ln = slot & 63;
+      const int r = 32 * (tile >> 3) + (ln & 31), hh = ln >> 5;
+      const uint16_t* src = sQ + r * KP + 16 * (tile & 7);
+      const u16x4 lo = *reinterpret_cast<const u16x4*>(src + 4 * hh);
+      const u16x4 hi = *reinterpret_cast<const u16x4*>(src + 8 + 4 * hh);
+      const float rq = vRq[r];
       u16x8 f;
-      if (mat < 2) {
-        const uint16_t* src = (mat == 0 ? sK : sQ) + (32 * (tile >> 3) + r32) * KP + 16 * (tile & 7);
-        const u16x4 lo = *reinterpret_cast<const u16x4*>(src + 4 * hh);
-        const u16x4 hi = *reinterpret_cast<const u16x4*>(src + 8 + 4 * hh);
-        f = u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      } else {
-        const int d = 32 * (tile >> 2) + r32, k0 = 16 * (tile & 3);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = f32_to_f16_bits(bf16_bits_to_f32(sK[(k0 + kperm(hh, e)) * KP + d]));
+      for (int e = 0; e < 4; ++e) {
+        f[e] = f32_to_f16_bits(bf16_bits_to_f32(lo[e]) * rq);
+        f[4 + e] = f32_to_f16_bits(bf16_bits_to_f32(hi[e]) * rq);
       }
-      *reinterpret_cast<u16x8*>(wsk + mat * 16384 + tile * 1024 + ln * 16) = f;
+      *reinterpret_cast<u16x8*>(wsk + tile * 1024 + ln * 16) = f;
     }
   }
-
-  // ---- Gram tiles (32x32): K K^T and Q K^T, lower blocks (0,0) (1,0) (1,1) --
-  for (int job = wv; job < 6; job += 4) {
-    const int m = job / 3, tI = job % 3;
-    const int rt = tI == 0 ? 0 : 1, ct = tI == 2 ? 1 : 0;
-    const uint16_t* As = m == 0 ? sK : sQ;
-    floatx16 acc = zero16();
+  // ---- this wave's columns of K^T (key rows 32 wv + (lane&31)) at the chunk rows
+  //      of each 16-row k step, in fragment order; scaled per value head below
+  float kt[4][8];
+  {
+    const int d = 32 * wv + l32;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kt[ks][e] = bf16_bits_to_f32(sK[(16 * ks + kperm(h, e)) * KP + d]);
+  }
+  // ---- Gram tiles (32x32), kept in registers of waves 0-2 -------------------
+  //  K K^T tile (rtK, ctK) in {(0,0), (1,0), (1,1)}: element (row r, column i) = k_r . k_i
+  //  K Q^T tile (itP, rtP) in {(0,0), (0,1), (1,1)}: element (row i, column r) = k_i . q_r
+  const int rtK = wv == 0 ? 0 : 1, ctK = wv == 2 ? 1 : 0;
+  const int itP = wv == 2 ? 1 : 0, rtP = wv == 0 ? 0 : 1;
+  floatx16 gKK = zero16(), gKQ = zero16();
+  if (wv < 3) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 A = lds_frag32(As + (32 * rt + l32) * KP + 16 * ks, h);
-      const bf16x8 B = lds_frag32(sK + (32 * ct + l32) * KP + 16 * ks, h);
-      acc = mfma32(A, B, acc);
+      gKK = mfma32(lds_frag32(sK + (32 * rtK + l32) * KP + 16 * ks, h),
+                   lds_frag32(sK + (32 * ctK + l32) * KP + 16 * ks, h), gKK);
+      gKQ = mfma32(lds_frag32(sK + (32 * itP + l32) * KP + 16 * ks, h),
+                   lds_frag32(sQ + (32 * rtP + l32) * KP + 16 * ks, h), gKQ);
     }
-    float* dst = m == 0 ? sKK : sQK;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) dst[(32 * rt + acc_row(v, h)) * FP + 32 * ct + l32] = acc[v];
   }
   __syncthreads();  // sK / sQ are dead from here on: their bytes become sA / sT
 
   for (int j = 0; j < a.G; ++j) {
     const int hv = hk * a.G + j;
-    unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hv) * nwin + cl) * WS_CHUNK;
-    // ---- gates: prefix sums and the chain's row scalings ------------------
+    unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hv) * nwin + cl) * WH_BYTES;
+    // V rows of this value head (loads issued before the gate scan)
+    u32x4 vr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int vi = tid + 256 * m, r = vi >> 4, c8 = (vi & 15) * 8;
+      const int rr = r < nval ? r : nval - 1;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(gv + (tokbase + rr) * a.sv + hv * DK + c8);
+      vr[m] = r < nval ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+    // ---- gates: prefix sums and the row scalings --------------------------
     if (wv == 0) {
       float la = 0.f, be = 0.f;
       if (lane < nval) {
@@ -262,66 +275,67 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
         if (lane >= off) g += t;
       }
       const float gl = __shfl(g, 63, 64);
+      const float eg = __expf(g);
       vG[lane] = g;
       vBe[lane] = be;
-      float* sc = reinterpret_cast<float*>(wsc + WS_TP);
-      const float eg = __expf(g);
-      sc[lane] = eg * vRk[lane];
-      sc[64 + lane] = eg * vRq[lane];
-      sc[128 + lane] = __expf(gl - g) * vRk[lane];
-      if (lane == 0) sc[192] = __expf(gl);
+      vKs[lane] = eg * vRk[lane];
+      vKd[lane] = __expf(gl - g) * vRk[lane];
+      float* sc = reinterpret_cast<float*>(wsc + WH_SC);
+      sc[lane] = eg;
+      if (lane == 0) sc[64] = __expf(gl);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int vi = tid + 256 * m;
+      *reinterpret_cast<u32x4*>(sV + (vi >> 4) * KP + (vi & 15) * 8) = vr[m];
     }
     __syncthreads();
-    // ---- A (fp32, strictly lower), the P fragments, and zeros in the two ----
-    //      upper blocks of T that the block inverse reads
-    {
-      // A: thread -> row r, 16 consecutive columns; every load issued before use
-      const int r = tid >> 2, i0 = (tid & 3) * 16;
-      const float gr = vG[r], cr = vBe[r] * vRk[r];
-      floatx4 kk[4], gi[4], rki[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        kk[q] = *reinterpret_cast<const floatx4*>(sKK + r * FP + i0 + 4 * q);
-        gi[q] = *reinterpret_cast<const floatx4*>(vG + i0 + 4 * q);
-        rki[q] = *reinterpret_cast<const floatx4*>(vRk + i0 + 4 * q);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        floatx4 av;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + 4 * q + e;
-          const float x = cr * __expf(fminf(gr - gi[q][e], 0.f)) * rki[q][e] * kk[q][e];
-          av[e] = i < r ? x : 0.f;
-        }
-        *reinterpret_cast<floatx4*>(sA + r * FP + i0 + 4 * q) = av;
-      }
-      // T blocks (0,1) and (2,3) (above the diagonal, inside S0 and S1) are read as zeros
+    // ---- A (fp32, strictly lower) and the P fragments from the Gram tiles, and
+    //      zeros in the two upper 16x16 blocks of T that the block inverse reads
+    if (wv < 3) {
       {
-        const int blk = tid >> 7, e2 = (tid & 127) * 2;
-        const int rr = 32 * blk + (e2 >> 4), cc = 32 * blk + 16 + (e2 & 15);
-        sT[rr * FP + cc] = 0.f;
-        sT[rr * FP + cc + 1] = 0.f;
-      }
-    }
-    for (int slot = tid; slot < FT * 64; slot += 256) {
-      const int f = slot >> 6, ln = slot & 63;
-      const int r = 32 * ft_rt(f) + (ln & 31), hh = ln >> 5;
-      const int ca = 16 * ft_ks(f) + 4 * hh, cb = ca + 8;   // the lane's two 4-column runs
-      const float gr = vG[r], rq = vRq[r];
-      const floatx4 qa = *reinterpret_cast<const floatx4*>(sQK + r * FP + ca);
-      const floatx4 qb = *reinterpret_cast<const floatx4*>(sQK + r * FP + cb);
-      const floatx4 ga = *reinterpret_cast<const floatx4*>(vG + ca), gb = *reinterpret_cast<const floatx4*>(vG + cb);
-      const floatx4 ka = *reinterpret_cast<const floatx4*>(vRk + ca), kb = *reinterpret_cast<const floatx4*>(vRk + cb);
-      u16x8 pf;
+        const int i = 32 * ctK + l32;
+        const float gi = vG[i], rki = vRk[i];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = e < 4 ? ca + e : cb + e - 4;
-        const float qk = e < 4 ? qa[e] : qb[e - 4], g = e < 4 ? ga[e] : gb[e - 4], rk = e < 4 ? ka[e] : kb[e - 4];
-        const float x = __expf(fminf(gr - g, 0.f)) * rq * rk * qk;
-        pf[e] = f32_to_f16_bits(i <= r ? x : 0.f);
+        for (int q = 0; q < 4; ++q) {
+          const int r0 = 32 * rtK + 8 * q + 4 * h;
+          const floatx4 g4 = *reinterpret_cast<const floatx4*>(vG + r0);
+          const floatx4 b4 = *reinterpret_cast<const floatx4*>(vBe + r0);
+          const floatx4 k4 = *reinterpret_cast<const floatx4*>(vRk + r0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = r0 + e;
+            const float x = b4[e] * k4[e] * rki * __expf(fminf(g4[e] - gi, 0.f)) * gKK[4 * q + e];
+            sA[r * FP + i] = i < r ? x : 0.f;
+          }
+        }
       }
-      *reinterpret_cast<u16x8*>(wsc + (6 + f) * 1024 + ln * 16) = pf;
+      {
+        const int r = 32 * rtP + l32;
+        const float gr = vG[r], rq = vRq[r];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int f = rtP == 0 ? s2 : 2 + 2 * itP + s2;
+          const int ia = 32 * itP + 16 * s2 + 4 * h, ib = ia + 8;
+          const floatx4 ga = *reinterpret_cast<const floatx4*>(vG + ia), gb = *reinterpret_cast<const floatx4*>(vG + ib);
+          const floatx4 ka = *reinterpret_cast<const floatx4*>(vRk + ia), kb = *reinterpret_cast<const floatx4*>(vRk + ib);
+          u16x8 pf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = e < 4 ? ia + e : ib + e - 4;
+            const float gi = e < 4 ? ga[e] : gb[e - 4], rki = e < 4 ? ka[e] : kb[e - 4];
+            const float x = __expf(fminf(gr - gi, 0.f)) * rq * rki * gKQ[8 * s2 + e];
+            pf[e] = f32_to_f16_bits(i <= r ? x : 0.f);
+          }
+          *reinterpret_cast<u16x8*>(wsc + WH_P + f * 1024 + lane * 16) = pf;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int e = lane + 64 * m, blk = e >> 8;
+        sT[(32 * blk + ((e >> 4) & 15)) * FP + 32 * blk + 16 + (e & 15)] = 0.f;
+      }
     }
     __syncthreads();
     // ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution ------
@@ -405,147 +419,169 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       *reinterpret_cast<floatx4*>(sT + (32 + yr) * FP + yc) = -t;
     }
     __syncthreads();
-    // ---- T' = T diag(beta) fragments ----------------------------------------
-    for (int slot = tid; slot < FT * 64; slot += 256) {
-      const int f = slot >> 6, ln = slot & 63;
-      const int r = 32 * ft_rt(f) + (ln & 31), hh = ln >> 5;
-      const int ca = 16 * ft_ks(f) + 4 * hh, cb = ca + 8;
+    // ---- per wave: T' = T diag(beta) fragments (all six), the K^T columns of key
+    //      tile wv scaled two ways, and the V columns of value tile wv -------------
+    halfx8 tf[FT];
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+      const int r = 32 * ft_rt(f) + l32;
+      const int ca = 16 * ft_ks(f) + 4 * h, cb = ca + 8;
       const floatx4 ta = *reinterpret_cast<const floatx4*>(sT + r * FP + ca);
       const floatx4 tb = *reinterpret_cast<const floatx4*>(sT + r * FP + cb);
       const floatx4 ba = *reinterpret_cast<const floatx4*>(vBe + ca), bb = *reinterpret_cast<const floatx4*>(vBe + cb);
-      u16x8 tf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = e < 4 ? ca + e : cb + e - 4;
         const float x = e < 4 ? ta[e] * ba[e] : tb[e - 4] * bb[e - 4];
-        tf[e] = f32_to_f16_bits(i <= r ? x : 0.f);
+        tf[f][e] = static_cast<_Float16>(i <= r ? x : 0.f);
       }
-      *reinterpret_cast<u16x8*>(wsc + f * 1024 + ln * 16) = tf;
     }
-    __syncthreads();  // vG, vBe, sA, sT are rewritten for the next value head
+    {
+      // W^T tiles (key tile wv, row tile 0 / 1) = Ks^T T'^T with Ks = diag(gamma rk) K;
+      // Kd = K^T diag(rk e^{g_63 - g}) fragments go out as they are
+      floatx16 w0 = zero16(), w1 = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const floatx4 sa = *reinterpret_cast<const floatx4*>(vKs + 16 * ks + 4 * h);
+        const floatx4 sb = *reinterpret_cast<const floatx4*>(vKs + 16 * ks + 8 + 4 * h);
+        const floatx4 da = *reinterpret_cast<const floatx4*>(vKd + 16 * ks + 4 * h);
+        const floatx4 db = *reinterpret_cast<const floatx4*>(vKd + 16 * ks + 8 + 4 * h);
+        halfx8 kf, df;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kf[e] = static_cast<_Float16>(kt[ks][e] * (e < 4 ? sa[e] : sb[e - 4]));
+          df[e] = static_cast<_Float16>(kt[ks][e] * (e < 4 ? da[e] : db[e - 4]));
+        }
+        *reinterpret_cast<halfx8*>(wsc + WH_KD + (wv * 4 + ks) * 1024 + lane * 16) = df;
+        if (ks < 2) w0 = mfma32h(kf, tf[ks], w0);
+        w1 = mfma32h(kf, tf[2 + ks], w1);
+      }
+      // accumulator values [8s, 8s+8) of W^T tile (wv, rt) are the -W fragment (rt, 2 wv + s)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        halfx8 n0, n1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          n0[e] = static_cast<_Float16>(-w0[8 * s2 + e]);
+          n1[e] = static_cast<_Float16>(-w1[8 * s2 + e]);
+        }
+        *reinterpret_cast<halfx8*>(wsc + WH_W + (2 * wv + s2) * 1024 + lane * 16) = n0;
+        *reinterpret_cast<halfx8*>(wsc + WH_W + (8 + 2 * wv + s2) * 1024 + lane * 16) = n1;
+      }
+    }
+    {
+      // U0 tiles (row tile 0 / 1, value tile wv) = T' V, stored in accumulator layout
+      floatx16 u0 = zero16(), u1 = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        halfx8 vf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vf[e] = static_cast<_Float16>(bf16_bits_to_f32(sV[(16 * ks + kperm(h, e)) * KP + 32 * wv + l32]));
+        if (ks < 2) u0 = mfma32h(tf[ks], vf, u0);
+        u1 = mfma32h(tf[2 + ks], vf, u1);
+      }
+      unsigned char* du = wsc + WH_U0 + (wv * 2) * 2048 + lane * 32;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        halfx8 x0, x1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x0[e] = static_cast<_Float16>(u0[8 * s2 + e]);
+          x1[e] = static_cast<_Float16>(u1[8 * s2 + e]);
+        }
+        *reinterpret_cast<halfx8*>(du + 16 * s2) = x0;
+        *reinterpret_cast<halfx8*>(du + 2048 + 16 * s2) = x1;
+      }
+    }
+    __syncthreads();  // vG, vBe, vKs, vKd, sA, sT, sV are rewritten for the next value head
   }
 }
 
 // =========================================================================
-// chain kernel: one workgroup (4 waves) per (64-column slice, value head, batch)
+// chain kernel: one workgroup (3 waves) per (32-column strip, value head, batch)
 // =========================================================================
-// LDS: a primary buffer (K, Q, T' fragments and the V slice) restaged once per
-// chunk after the state waves' first phase, and two alternating buffers
-// (K^T and P fragments, row scalings) staged a chunk ahead.
+// LDS: two input slots (a chunk's -W, Kd, U0 strip, P, scalings and Q^, copied
+// from the workspace by the load wave one chunk ahead) and the M and U
+// fragments that the state wave publishes for the output wave.
 struct ChainLds {
-  static constexpr int kK = 0;                     // 16 fragment tiles
-  static constexpr int kQ = kK + 16 * 1024;        // 16 fragment tiles
-  static constexpr int kTp = kQ + 16 * 1024;       // T' 6 fp16 tiles
-  static constexpr int kV = kTp + 6 * 1024;        // bf16 [64][RP]
-  static constexpr int kAlt = kV + CH * RP * 2;    // 2 x {K^T 16 fp16 tiles | P 6 fp16 tiles | scalings}
-  static constexpr int kAltKt = 0, kAltP = 16 * 1024, kAltSc = 22 * 1024;
-  static constexpr int kAltBytes = 24 * 1024;
-  static constexpr int kMf = kAlt + 2 * kAltBytes;  // M B-fragments (bf16) [2 strips][8 k steps][64 lanes] x 16 B
-  static constexpr int kUf = kMf + 2 * 8 * 1024;    // U B-fragments (fp16) [2 strips][4 k steps][64] x 16 B
-  static constexpr int kO = kUf + 2 * 4 * 1024;     // O staging: [2 strips][64 rows][OP] bf16
-  static constexpr int OP = 40;
-  static constexpr int kBytes = kO + 2 * CH * OP * 2;
+  static constexpr int kW = 0, kKd = 16384, kU0 = 32768, kP = 36864, kSc = 43008, kQ = 44032;
+  static constexpr int kSlot = 60416;               // 59 blocks of 1 KiB
+  static constexpr int kMf = 2 * kSlot;             // M fragments (fp16) [k step 8][lane 64] x 16 B
+  static constexpr int kUf = kMf + 8 * 1024;        // U fragments (fp16) [k step 4][lane 64] x 16 B
+  static constexpr int kBytes = kUf + 4 * 1024;
 };
+constexpr int kSlotBlocks = 59;
 
-// Loader waves (2 and 3) move a chunk's chain inputs global -> registers -> LDS in two parts:
-// part A (K^T fragments, P fragments, row scalings; 24 KiB) into the alternating buffer, and
-// part B (K, Q, T' fragments; 38 KiB; plus the 8 KiB V slice) into the primary buffer.  Both
-// parts are whole multiples of 128 16-byte vectors and every source is a compile-time function of
-// the unrolled index, so the loads carry no per-lane branches and the compiler can wait for each
-// part on its own in issue order.
-constexpr int kRegA = 12;   // 8 x 128 K^T vectors, 3 x 128 P vectors, 1 x 128 scaling vectors
-constexpr int kRegB = 23;   // 16 x 128 K|Q vectors, 3 x 128 T' vectors, 4 x 128 V vectors
-
-struct ChainSrc {
-  const unsigned char* wsh;   // region H block of (b, hv, chunk)
-  const unsigned char* wsk;   // region K block of (b, hk, chunk)
-  const uint16_t* v;          // first V row of the chunk for this head and slice
-  int64_t sv;
-  int nval;
-};
-
-__device__ __forceinline__ void load_part_a(u32x4 (&r)[kRegA], const ChainSrc& src, int lt) {
-#pragma unroll
-  for (int m = 0; m < kRegA; ++m) {
-    const unsigned char* p = m < 8 ? src.wsk + 32768 + 16 * (lt + 128 * m)              // K^T fragments
-                                   : src.wsh + 6144 + 16 * (lt + 128 * (m - 8));        // P | scalings
-    r[m] = *reinterpret_cast<const u32x4*>(p);
-  }
+// source of 1 KiB block m of a chunk's input slot (blocks follow the slot layout)
+__device__ __forceinline__ const unsigned char* slot_src(int m, const unsigned char* wsh, const unsigned char* wsk,
+                                                         int strip) {
+  return m < 32 ? wsh + 1024 * m                                         // -W, Kd
+       : m < 36 ? wsh + WH_U0 + strip * 4096 + 1024 * (m - 32)           // U0 columns of this strip
+       : m < 43 ? wsh + WH_P + 1024 * (m - 36)                           // P, scalings
+                : wsk + 1024 * (m - 43);                                 // Q^
 }
 
-__device__ __forceinline__ void store_part_a(const u32x4 (&r)[kRegA], unsigned char* alt, int lt) {
-#pragma unroll
-  for (int m = 0; m < kRegA; ++m) reinterpret_cast<u32x4*>(alt)[lt + 128 * m] = r[m];
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// Workgroup barrier that orders LDS only: global stores and the LDS copies in
+// flight are not waited for (the copy wave waits for its own copies explicitly).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ void load_part_b(u32x4 (&r)[kRegB], const ChainSrc& src, int lt) {
-#pragma unroll
-  for (int m = 0; m < kRegB; ++m) {
-    if (m < 16) {
-      r[m] = *reinterpret_cast<const u32x4*>(src.wsk + 16 * (lt + 128 * m));          // K, Q fragments
-    } else if (m < 19) {
-      r[m] = *reinterpret_cast<const u32x4*>(src.wsh + 16 * (lt + 128 * (m - 16)));   // T' fragments
-    } else {
-      const int vi = lt + 128 * (m - 19), row = vi >> 3, c8 = (vi & 7) * 8;
-      const int rr = row < src.nval ? row : src.nval - 1;                             // stays in bounds
-      const u32x4 x = *reinterpret_cast<const u32x4*>(src.v + rr * src.sv + c8);
-      r[m] = row < src.nval ? x : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float floatx2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const floatx2v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
-__device__ __forceinline__ void store_part_b(const u32x4 (&r)[kRegB], unsigned char* smem, int lt) {
-  using L = ChainLds;
-#pragma unroll
-  for (int m = 0; m < kRegB; ++m) {
-    if (m < 19) {
-      reinterpret_cast<u32x4*>(smem + L::kK)[lt + 128 * m] = r[m];   // K | Q | T' are contiguous
-    } else {
-      const int vi = lt + 128 * (m - 19);
-      *reinterpret_cast<u32x4*>(smem + L::kV + ((vi >> 3) * RP + (vi & 7) * 8) * 2) = r[m];
-    }
-  }
-}
-
-__global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, const unsigned char* ws, int nwin,
-                                                          const float* state_in, float* state_out) {
+__global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, const unsigned char* ws, int nwin,
+                                                             const float* state_in, float* state_out) {
   using L = ChainLds;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const unsigned char* sK = smem + L::kK;
-  const unsigned char* sQ = smem + L::kQ;
-  const unsigned char* sTp = smem + L::kTp;
-  const uint16_t* sV = reinterpret_cast<const uint16_t*>(smem + L::kV);
-  unsigned char* sMf = smem + L::kMf;
-  unsigned char* sUf = smem + L::kUf;
-
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, h = lane >> 5;
-  const int slice = blockIdx.x, hv = blockIdx.y, b = blockIdx.z;
+  // Workgroups are handed to the 8 XCDs round-robin by linear index; when the
+  // (sequence, head) count is a multiple of 8, the 4 strips of a head get indices
+  // that are equal modulo 8, so they share one XCD's L2 for the head's inputs.
+  const int L0 = blockIdx.x;
+  const int nheads = a.B * a.Hv;
+  int bhv, strip;
+  if ((nheads & 7) == 0) {
+    bhv = (L0 >> 5) * 8 + (L0 & 7);
+    strip = (L0 >> 3) & 3;
+  } else {
+    bhv = L0 >> 2;
+    strip = L0 & 3;
+  }
+  const int b = bhv / a.Hv, hv = bhv - b * a.Hv;
   const int hk = hv / a.G;
-  const int bh = b * a.Hv + hv;
-  const int strip = wv & 1;                        // 32-column strip inside the slice
-  const bool state_wave = wv < 2;
-  const int lt = tid - 128;                        // loader thread index (waves 2, 3)
-  const int col = slice * DVS + 32 * strip + l32;  // this lane's value column (global)
-  const int vcol = 32 * strip + l32;               // ... inside the V slice
+  const int bh = bhv;
+  // roles (one wave per SIMD): wave 1 carries the state of the strip, wave 0 produces
+  // its outputs, wave 2 copies the next chunk's inputs into LDS
+  const int role = wv == 2 ? 2 : (wv == 1 ? 0 : 1);
+  const int col = 32 * strip + l32;  // this lane's value column
+  unsigned char* sMf = smem + L::kMf;
+  unsigned char* sUf = smem + L::kUf;
   uint16_t* go = static_cast<uint16_t*>(a.o);
 
   const int nchunk = min(nwin, (a.T + CH - 1) / CH - c0);
-  const unsigned char* regK = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WS_CHUNK;
-  auto src_of = [&](int cl) {
-    ChainSrc s;
-    s.wsh = ws + (static_cast<int64_t>(bh) * nwin + cl) * WS_CHUNK;
-    s.wsk = regK + (static_cast<int64_t>(b * a.Hk + hk) * nwin + cl) * WS_KQ;
-    const int t0 = (c0 + cl) * CH;
-    s.nval = min(CH, a.T - t0);
-    s.sv = a.sv;
-    s.v = static_cast<const uint16_t*>(a.v) + (static_cast<int64_t>(b) * a.T + t0) * a.sv + hv * DK + slice * DVS;
-    return s;
+  const unsigned char* regK = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WH_BYTES;
+  auto copy_chunk = [&](int cl, unsigned char* slot) {
+    const unsigned char* wsh = ws + (static_cast<int64_t>(bh) * nwin + cl) * WH_BYTES;
+    const unsigned char* wsk = regK + (static_cast<int64_t>(b * a.Hk + hk) * nwin + cl) * WK_BYTES;
+#pragma unroll
+    for (int m = 0; m < kSlotBlocks; ++m)
+      __builtin_amdgcn_global_load_lds(slot_src(m, wsh, wsk, strip) + 16 * lane, slot + 1024 * m, 16, 0, 0);
   };
 
   floatx16 Ms[4];
-  u32x4 regA[kRegA], regB[kRegB];
-  if (state_wave) {
+  halfx8 Mfr[8];
+  if (role == 0) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       if (state_in) {
@@ -557,165 +593,154 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      *reinterpret_cast<bf16x8*>(sMf + (strip * 8 + ks) * 1024 + lane * 16) = acc_frag(Ms[ks >> 1], ks & 1);
-  } else {
-    const ChainSrc s0 = src_of(0);
-    load_part_b(regB, s0, lt);
-    load_part_a(regA, s0, lt);
-    store_part_b(regB, smem, lt);
-    store_part_a(regA, smem + L::kAlt, lt);
+    for (int ks = 0; ks < 8; ++ks) {
+      Mfr[ks] = acc_frag_h(Ms[ks >> 1], ks & 1);
+      *reinterpret_cast<halfx8*>(sMf + ks * 1024 + lane * 16) = Mfr[ks];
+    }
+  } else if (role == 2) {
+    copy_chunk(0, smem);
+    wait_vm_all();
   }
   __syncthreads();
 
   for (int cl = 0; cl < nchunk; ++cl) {
-    const int t0 = (c0 + cl) * CH;
-    const int nval = min(CH, a.T - t0);
-    const int64_t tokbase = static_cast<int64_t>(b) * a.T + t0;
-    const unsigned char* alt = smem + L::kAlt + (cl & 1) * L::kAltBytes;
-    const float* sSc = reinterpret_cast<const float*>(alt + L::kAltSc);
-    if (state_wave) {
-      // ---- phase 1: X = V - diag(gamma rk) K M ; U = T' X ; publish U ----
-      floatx16 X[2];
-      {
-        // four independent accumulation chains (row tile x even/odd k step) keep the
-        // MFMA pipe busy instead of waiting on one dependent chain
-        floatx16 Xe[2] = {zero16(), zero16()}, Xo[2] = {zero16(), zero16()};
-#pragma unroll
-        for (int kp = 0; kp < 4; ++kp) {
-          const bf16x8 B0 = acc_frag(Ms[kp], 0), B1 = acc_frag(Ms[kp], 1);
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(sK + (rt * 8 + 2 * kp) * 1024 + lane * 16);
-            const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(sK + (rt * 8 + 2 * kp + 1) * 1024 + lane * 16);
-            Xe[rt] = mfma32(A0, B0, Xe[rt]);
-            Xo[rt] = mfma32(A1, B1, Xo[rt]);
-          }
-        }
-        X[0] = Xe[0] + Xo[0];
-        X[1] = Xe[1] + Xo[1];
-      }
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = 32 * rt + acc_row(v, h);
-          X[rt][v] = fmaf(-sSc[r], X[rt][v], bf16_bits_to_f32(sV[r * RP + vcol]));
-        }
+    unsigned char* slot = smem + (cl & 1) * L::kSlot;
+    const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
+    if (role == 0) {
+      // ---- U = U0 - W M (U0 enters as the accumulator) ; publish U ----------
       floatx16 U[2];
-      {
-        halfx8 Xf[4];
+      halfx8 Af[16];   // -W fragments, all read before the first product
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) Xf[ks] = acc_frag_h(X[ks >> 1], ks & 1);
-        // T' X in fp16 with four independent accumulators (row tile x k-step parity)
-        floatx16 Ue[2] = {zero16(), zero16()}, Uo[2] = {zero16(), zero16()};
+      for (int i = 0; i < 16; ++i) Af[i] = *reinterpret_cast<const halfx8*>(slot + L::kW + i * 1024 + lane * 16);
 #pragma unroll
-        for (int f = 0; f < FT; ++f) {
-          const int rt = f < 2 ? 0 : 1, ks = f < 2 ? f : f - 2;
-          const halfx8 At = *reinterpret_cast<const halfx8*>(sTp + f * 1024 + lane * 16);
-          if (ks & 1) Uo[rt] = mfma32h(At, Xf[ks], Uo[rt]);
-          else Ue[rt] = mfma32h(At, Xf[ks], Ue[rt]);
+      for (int rt = 0; rt < 2; ++rt) {
+        const halfx8 x0 = *reinterpret_cast<const halfx8*>(slot + L::kU0 + rt * 2048 + lane * 32);
+        const halfx8 x1 = *reinterpret_cast<const halfx8*>(slot + L::kU0 + rt * 2048 + lane * 32 + 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          U[rt][e] = static_cast<float>(x0[e]);
+          U[rt][8 + e] = static_cast<float>(x1[e]);
         }
-        U[0] = Ue[0] + Uo[0];
-        U[1] = Ue[1] + Uo[1];
       }
+      const float gC = sSc[64];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        *reinterpret_cast<halfx8*>(sUf + (strip * 4 + ks) * 1024 + lane * 16) = acc_frag_h(U[ks >> 1], ks & 1);
-      __syncthreads();  // B1: U published; Q M has read M
-      // ---- phase 2: M <- gamma_63 M + K^T diag(rk e^{g_63-g}) U ; publish M ----
-      {
-        const unsigned char* sKt = alt + L::kAltKt;
-        halfx8 Wf[4];
+      for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt) U[rt] = mfma32h(Af[rt * 8 + ks], Mfr[ks], U[rt]);
+      // the state's decay runs on the vector unit while the products occupy the
+      // matrix unit
 #pragma unroll
-          for (int v = 0; v < 16; ++v) U[rt][v] *= sSc[128 + 32 * rt + acc_row(v, h)];
+      for (int dt = 0; dt < 4; ++dt) Ms[dt] *= gC;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) Wf[ks] = acc_frag_h(U[ks >> 1], ks & 1);
-        const float gC = sSc[192];
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Kd fragments for the update, read while the last products drain
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) Ms[dt] *= gC;
-        // four state tiles interleaved: four independent accumulation chains
+      for (int i = 0; i < 16; ++i) Af[i] = *reinterpret_cast<const halfx8*>(slot + L::kKd + i * 1024 + lane * 16);
+      halfx8 Uf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        Uf[ks] = acc_frag_h(U[ks >> 1], ks & 1);
+        *reinterpret_cast<halfx8*>(sUf + ks * 1024 + lane * 16) = Uf[ks];
+      }
+      lds_sync();  // B1: U published; the output wave has read M
+      // ---- M <- gamma_63 M + Kd U, two state tiles at a time so that the first
+      //      pair's fragments are formed while the second pair runs ; publish M ----
+#pragma unroll
+      for (int dp = 0; dp < 4; dp += 2) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const halfx8 A = *reinterpret_cast<const halfx8*>(sKt + (dt * 4 + ks) * 1024 + lane * 16);
-            Ms[dt] = mfma32h(A, Wf[ks], Ms[dt]);
-          }
-      }
+          for (int dt = dp; dt < dp + 2; ++dt) Ms[dt] = mfma32h(Af[dt * 4 + ks], Uf[ks], Ms[dt]);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        *reinterpret_cast<bf16x8*>(sMf + (strip * 8 + ks) * 1024 + lane * 16) = acc_frag(Ms[ks >> 1], ks & 1);
-      __syncthreads();  // B2
-    } else {
-      // ---- phase 1: issue the next chunk's loads (part B first: it is consumed
-      //      first); O = diag(gamma rq) Q M ----
-      const bool more = cl + 1 < nchunk;
-      if (more) {
-        const ChainSrc sn = src_of(cl + 1);
-        load_part_b(regB, sn, lt);
-        load_part_a(regA, sn, lt);
-      }
-      floatx16 O[2];
-      {
-        floatx16 Oe[2] = {zero16(), zero16()}, Oo[2] = {zero16(), zero16()};
-#pragma unroll
-        for (int kp = 0; kp < 4; ++kp) {
-          const bf16x8 B0 = *reinterpret_cast<const bf16x8*>(sMf + (strip * 8 + 2 * kp) * 1024 + lane * 16);
-          const bf16x8 B1 = *reinterpret_cast<const bf16x8*>(sMf + (strip * 8 + 2 * kp + 1) * 1024 + lane * 16);
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(sQ + (rt * 8 + 2 * kp) * 1024 + lane * 16);
-            const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(sQ + (rt * 8 + 2 * kp + 1) * 1024 + lane * 16);
-            Oe[rt] = mfma32(A0, B0, Oe[rt]);
-            Oo[rt] = mfma32(A1, B1, Oo[rt]);
-          }
+        for (int ks = 2 * dp; ks < 2 * dp + 4; ++ks) {
+          Mfr[ks] = acc_frag_h(Ms[ks >> 1], ks & 1);
+          *reinterpret_cast<halfx8*>(sMf + ks * 1024 + lane * 16) = Mfr[ks];
         }
-        O[0] = Oe[0] + Oo[0];
-        O[1] = Oe[1] + Oo[1];
       }
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) O[rt][v] *= sSc[64 + 32 * rt + acc_row(v, h)];
-      __syncthreads();  // B1: wait for U; the primary buffer is free
-      // ---- phase 2: stage part B of chunk cl+1 ; O += P U ; store O ; stage part A ----
-      if (more) store_part_b(regB, smem, lt);
+      lds_sync();  // B2
+    } else if (role == 1) {
+      // ---- O^T = M^T Q^^T diag(gamma) + U^T P^T: the M and U fragments serve as A
+      //      operands and Q^, P as B operands, so each lane holds one token and
+      //      runs of four value columns ------------------------------------------
+      floatx16 O[2] = {zero16(), zero16()};
       {
-        const unsigned char* sP = alt + L::kAltP;
-        floatx16 Op[2] = {zero16(), zero16()};
+        halfx8 Am[8], Bq[16];   // all operands read before the first product
 #pragma unroll
-        for (int f = 0; f < FT; ++f) {
-          const int rt = f < 2 ? 0 : 1, ks = f < 2 ? f : f - 2;
-          const halfx8 Pf = *reinterpret_cast<const halfx8*>(sP + f * 1024 + lane * 16);
-          const halfx8 Uf = *reinterpret_cast<const halfx8*>(sUf + (strip * 4 + ks) * 1024 + lane * 16);
-          if (ks & 1) Op[rt] = mfma32h(Pf, Uf, Op[rt]);
-          else O[rt] = mfma32h(Pf, Uf, O[rt]);
-        }
-        O[0] += Op[0];
-        O[1] += Op[1];
+        for (int ks = 0; ks < 8; ++ks) Am[ks] = *reinterpret_cast<const halfx8*>(sMf + ks * 1024 + lane * 16);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(slot + L::kQ + i * 1024 + lane * 16);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) O[rt] = mfma32h(Am[ks], Bq[rt * 8 + ks], O[rt]);
       }
-      // O through LDS so that HBM sees 16-byte row segments
-      uint16_t* sO = reinterpret_cast<uint16_t*>(smem + L::kO) + strip * CH * L::OP;
+      const float g0 = sSc[l32], g1 = sSc[32 + l32];
+      O[0] *= g0;
+      O[1] *= g1;
+      lds_sync();  // B1
+      {
+        halfx8 Au[4], Bp[FT];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+        for (int ks = 0; ks < 4; ++ks) Au[ks] = *reinterpret_cast<const halfx8*>(sUf + ks * 1024 + lane * 16);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sO[(32 * rt + acc_row(v, h)) * L::OP + l32] = f32_to_bf16_bits(O[rt][v]);
+        for (int f = 0; f < FT; ++f) Bp[f] = *reinterpret_cast<const halfx8*>(slot + L::kP + f * 1024 + lane * 16);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < FT; ++f) O[ft_rt(f)] = mfma32h(Au[ft_ks(f)], Bp[f], O[ft_rt(f)]);
+      }
+      // stage the 64 x 32 bf16 tile over the (now read) U fragments: 64-byte rows,
+      // 16-byte units swizzled by the row so that the 4-column writes spread over
+      // the banks; then 16-byte stores of whole 8-column runs
+      unsigned char* sO = sUf;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int r = 32 * rt + l32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint2 w = {pack_bf16x2(O[rt][4 * j], O[rt][4 * j + 1]), pack_bf16x2(O[rt][4 * j + 2], O[rt][4 * j + 3])};
+          *reinterpret_cast<uint2*>(sO + r * 64 + ((j ^ (r & 3)) * 16) + 8 * h) = w;
+        }
+      }
+      const int t0 = (c0 + cl) * CH;
+      const int nval = min(CH, a.T - t0);
+      uint16_t* obase = go + (static_cast<int64_t>(b) * a.T + t0) * a.so + hv * DK + 32 * strip;
+      u16x8 x[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int vi = lane + 64 * m, r = vi >> 2, c8 = (vi & 3) * 8;
-        if (r < nval)
-          *reinterpret_cast<u16x8*>(go + (tokbase + r) * a.so + hv * DK + slice * DVS + 32 * strip + c8) =
-              *reinterpret_cast<const u16x8*>(sO + r * L::OP + c8);
+        const int vi = lane + 64 * m, r = vi >> 2, u = vi & 3;
+        x[m] = *reinterpret_cast<const u16x8*>(sO + r * 64 + ((u ^ (r & 3)) * 16));
       }
-      if (more) store_part_a(regA, smem + L::kAlt + ((cl + 1) & 1) * L::kAltBytes, lt);
-      __syncthreads();  // B2
+      if (nval == CH) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int vi = lane + 64 * m, r = vi >> 2, u = vi & 3;
+          *reinterpret_cast<u16x8*>(obase + static_cast<int64_t>(r) * a.so + 8 * u) = x[m];
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int vi = lane + 64 * m, r = vi >> 2, u = vi & 3;
+          if (r < nval) *reinterpret_cast<u16x8*>(obase + static_cast<int64_t>(r) * a.so + 8 * u) = x[m];
+        }
+      }
+      lds_sync();  // B2
+    } else {
+      if (cl + 1 < nchunk) copy_chunk(cl + 1, smem + ((cl + 1) & 1) * L::kSlot);
+      // B1 without a fence: this wave touches LDS only through the copies in flight,
+      // which the other waves read after B2
+      __builtin_amdgcn_s_barrier();
+      wait_vm_all();
+      lds_sync();  // B2: the next chunk's inputs are in LDS
     }
   }
 
-  if (state_wave && state_out) {
+  if (role == 0 && state_out) {
     float* sp = state_out + static_cast<int64_t>(bh) * DK * DK;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -727,7 +752,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(RecArgs a, int c0, con
 }  // namespace
 
 size_t chunk_ws_bytes_per_chunk(const RecArgs& a) {
-  return static_cast<size_t>(a.B) * (static_cast<size_t>(a.Hv) * WS_CHUNK + static_cast<size_t>(a.Hk) * WS_KQ);
+  return static_cast<size_t>(a.B) * (static_cast<size_t>(a.Hv) * WH_BYTES + static_cast<size_t>(a.Hk) * WK_BYTES);
 }
 
 size_t chunk_ws_carry_bytes(const RecArgs& a) { return static_cast<size_t>(a.B) * a.Hv * DK * DK * 4; }
@@ -767,7 +792,7 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     hipLaunchKernelGGL(chunk_prep_kernel, dim3(nw, a.Hk, a.B), dim3(256), PrepLds::kBytes, s, a, c0, wsb, nwin);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_chain_kernel, dim3(DK / DVS, a.Hv, a.B), dim3(256), ChainLds::kBytes, s, a, c0,
+    hipLaunchKernelGGL(chunk_chain_kernel, dim3(a.B * a.Hv * (DK / 32)), dim3(192), ChainLds::kBytes, s, a, c0,
                        static_cast<const unsigned char*>(wsb), nwin, sin, sout);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -121,8 +121,9 @@ gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const
  * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill wants
  * for these dims (0 when the call needs none).  The chunked kernel keeps, per
  * (sequence, value head, chunk of a window), the per-chunk matrices that do
- * not depend on the state (26 KiB, plus 48 KiB per key head for the K, Q
- * and K^T fragments); windows are sized to about 128 MiB
+ * not depend on the state (55 KiB: the -W, K^T, U0 and P operands and the
+ * row scalings, plus 16 KiB per key head for the scaled Q); windows are
+ * sized to about 256 MiB
  * and the state is carried between windows through state_out, or through a
  * carry area inside the workspace when state_out is NULL.  A smaller
  * workspace is accepted down to one chunk per window (plus the carry when

@@ -32,14 +32,14 @@ def test_library_exports_every_declared_function():
 
 def test_workspace_size():
     ws = B.gdn_prefill_workspace_size
-    # per chunk: B * (Hv * (24 KiB fragments + 2 KiB scalings) + Hk * 48 KiB K/Q/K^T fragments)
-    per_chunk = 6 * 14336 + 2 * 49152
+    # per chunk: B * (Hv * 55 KiB (-W, Kd, U0, P fragments + 1 KiB scalings) + Hk * 16 KiB Q^ fragments)
+    per_chunk = 6 * 56320 + 2 * 16384
     assert ws(dims(T=64)) == per_chunk
     assert ws(dims(T=65)) == 2 * per_chunk
     assert ws(dims(io=B.GDN_F32, D=16)) == 0            # token-serial path needs none
-    big = dims(B=4, T=32768, Hk=16, Hv=128)             # windows of ~128 MiB + a state carry
-    per = 4 * (128 * 14336 + 16 * 49152)
-    assert ws(big) == ((128 << 20) // per) * per + 4 * 128 * 128 * 128 * 4
+    big = dims(B=4, T=32768, Hk=16, Hv=128)             # windows of ~256 MiB + a state carry
+    per = 4 * (128 * 56320 + 16 * 16384)
+    assert ws(big) == ((256 << 20) // per) * per + 4 * 128 * 128 * 128 * 4
     assert ws(dims(Hv=5)) == 0                          # invalid dims
 
 

@@ -139,7 +139,7 @@ def test_prefill_small_workspace_windows(with_state_out):
     si = to_dev(p["state_in"].astype(np.float32))
     dims = G.make_dims(B, T, Hk, Hv, D, G.GDN_BF16)
     full = G.gdn_prefill_workspace_size(dims)
-    per_chunk = B * (Hv * 14336 + Hk * 49152)
+    per_chunk = B * (Hv * 56320 + Hk * 16384)
     assert full == 5 * per_chunk
     for nwin in (1, 2):
         extra = 0 if with_state_out else B * Hv * D * D * 4
