@@ -501,26 +501,29 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
 // =========================================================================
 // chain kernel: one workgroup (3 waves) per (32-column strip, value head, batch)
 // =========================================================================
-// LDS: two input slots (a chunk's -W, Kd, U0 strip, P, scalings and Q^, copied
-// from the workspace by the load wave one chunk ahead) and the M and U
-// fragments that the state wave publishes for the output wave.
+// LDS: three input slots (a chunk's -W, Kd, U0 strip and scalings, copied from
+// the workspace by the copy wave two chunks ahead) and the M and U fragments
+// that the state wave publishes for the output wave.  The output wave reads its
+// own operands (Q^ and P fragments) from the workspace straight into registers.
 struct ChainLds {
-  static constexpr int kW = 0, kKd = 16384, kU0 = 32768, kP = 36864, kSc = 43008, kQ = 44032;
-  static constexpr int kSlot = 60416;               // 59 blocks of 1 KiB
-  static constexpr int kMf = 2 * kSlot;             // M fragments (fp16) [k step 8][lane 64] x 16 B
+  static constexpr int kW = 0, kKd = 16384, kU0 = 32768, kSc = 36864;
+  static constexpr int kSlot = 37888;               // 37 blocks of 1 KiB
+  static constexpr int kNSlot = 3;
+  static constexpr int kMf = kNSlot * kSlot;        // M fragments (fp16) [k step 8][lane 64] x 16 B
   static constexpr int kUf = kMf + 8 * 1024;        // U fragments (fp16) [k step 4][lane 64] x 16 B
   static constexpr int kBytes = kUf + 4 * 1024;
 };
-constexpr int kSlotBlocks = 59;
+constexpr int kSlotBlocks = 37;
 
 // source of 1 KiB block m of a chunk's input slot (blocks follow the slot layout)
-__device__ __forceinline__ const unsigned char* slot_src(int m, const unsigned char* wsh, const unsigned char* wsk,
-                                                         int strip) {
+__device__ __forceinline__ const unsigned char* slot_src(int m, const unsigned char* wsh, int strip) {
   return m < 32 ? wsh + 1024 * m                                         // -W, Kd
        : m < 36 ? wsh + WH_U0 + strip * 4096 + 1024 * (m - 32)           // U0 columns of this strip
-       : m < 43 ? wsh + WH_P + 1024 * (m - 36)                           // P, scalings
-                : wsk + 1024 * (m - 43);                                 // Q^
+                : wsh + WH_SC;                                           // scalings
 }
+
+// s_waitcnt immediate that waits until at most n vector memory operations are outstanding
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
@@ -571,17 +574,22 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
 
   const int nchunk = min(nwin, (a.T + CH - 1) / CH - c0);
   const unsigned char* regK = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WH_BYTES;
-  auto copy_chunk = [&](int cl, unsigned char* slot) {
-    const unsigned char* wsh = ws + (static_cast<int64_t>(bh) * nwin + cl) * WH_BYTES;
-    const unsigned char* wsk = regK + (static_cast<int64_t>(b * a.Hk + hk) * nwin + cl) * WK_BYTES;
+  auto wsh_of = [&](int cl) { return ws + (static_cast<int64_t>(bh) * nwin + cl) * WH_BYTES; };
+  auto wsk_of = [&](int cl) { return regK + (static_cast<int64_t>(b * a.Hk + hk) * nwin + cl) * WK_BYTES; };
+  auto copy_chunk = [&](int cl) {
+    unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
+    const unsigned char* wsh = wsh_of(cl);
 #pragma unroll
     for (int m = 0; m < kSlotBlocks; ++m)
-      __builtin_amdgcn_global_load_lds(slot_src(m, wsh, wsk, strip) + 16 * lane, slot + 1024 * m, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(slot_src(m, wsh, strip) + 16 * lane, slot + 1024 * m, 16, 0, 0);
   };
 
-  floatx16 Ms[4];
-  halfx8 Mfr[8];
+  // Each role runs its own chunk loop (same trip count, the same two barriers per
+  // chunk), so that the registers one role carries across chunks are free in the
+  // others.
   if (role == 0) {
+    floatx16 Ms[4];
+    halfx8 Mfr[8];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       if (state_in) {
@@ -597,16 +605,10 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
       Mfr[ks] = acc_frag_h(Ms[ks >> 1], ks & 1);
       *reinterpret_cast<halfx8*>(sMf + ks * 1024 + lane * 16) = Mfr[ks];
     }
-  } else if (role == 2) {
-    copy_chunk(0, smem);
-    wait_vm_all();
-  }
-  __syncthreads();
-
-  for (int cl = 0; cl < nchunk; ++cl) {
-    unsigned char* slot = smem + (cl & 1) * L::kSlot;
-    const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
-    if (role == 0) {
+    __syncthreads();
+    for (int cl = 0; cl < nchunk; ++cl) {
+      unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
+      const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
       // ---- U = U0 - W M (U0 enters as the accumulator) ; publish U ----------
       floatx16 U[2];
       halfx8 Af[16];   // -W fragments, all read before the first product
@@ -663,36 +665,62 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
         }
       }
       lds_sync();  // B2
-    } else if (role == 1) {
+    }
+    if (state_out) {
+      float* sp = state_out + static_cast<int64_t>(bh) * DK * DK;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sp[(32 * dt + acc_row(v, h)) * DK + col] = Ms[dt][v];
+    }
+  } else if (role == 1) {
+    halfx8 Bq[16], Bp[FT];  // this chunk's Q^ and P fragments
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(wsk_of(0) + i * 1024 + lane * 16);
+#pragma unroll
+    for (int f = 0; f < FT; ++f) Bp[f] = *reinterpret_cast<const halfx8*>(wsh_of(0) + WH_P + f * 1024 + lane * 16);
+
+    __syncthreads();
+    for (int cl = 0; cl < nchunk; ++cl) {
+      unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
+      const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
       // ---- O^T = M^T Q^^T diag(gamma) + U^T P^T: the M and U fragments serve as A
       //      operands and Q^, P as B operands, so each lane holds one token and
       //      runs of four value columns ------------------------------------------
       floatx16 O[2] = {zero16(), zero16()};
+      const int cn = min(cl + 1, nchunk - 1);   // next chunk (the last one reloads itself)
       {
-        halfx8 Am[8], Bq[16];   // all operands read before the first product
+        halfx8 Am[8];   // M fragments, all read before the first product
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) Am[ks] = *reinterpret_cast<const halfx8*>(sMf + ks * 1024 + lane * 16);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(slot + L::kQ + i * 1024 + lane * 16);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) O[rt] = mfma32h(Am[ks], Bq[rt * 8 + ks], O[rt]);
       }
+      // the next chunk's Q^ fragments: a chunk ahead of their use
+      {
+        const unsigned char* wq = wsk_of(cn);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(wq + i * 1024 + lane * 16);
+      }
       const float g0 = sSc[l32], g1 = sSc[32 + l32];
       O[0] *= g0;
       O[1] *= g1;
       lds_sync();  // B1
       {
-        halfx8 Au[4], Bp[FT];
+        halfx8 Au[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) Au[ks] = *reinterpret_cast<const halfx8*>(sUf + ks * 1024 + lane * 16);
-#pragma unroll
-        for (int f = 0; f < FT; ++f) Bp[f] = *reinterpret_cast<const halfx8*>(slot + L::kP + f * 1024 + lane * 16);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int f = 0; f < FT; ++f) O[ft_rt(f)] = mfma32h(Au[ft_ks(f)], Bp[f], O[ft_rt(f)]);
+      }
+      {
+        const unsigned char* wp = wsh_of(cn) + WH_P;
+#pragma unroll
+        for (int f = 0; f < FT; ++f) Bp[f] = *reinterpret_cast<const halfx8*>(wp + f * 1024 + lane * 16);
       }
       // stage the 64 x 32 bf16 tile over the (now read) U fragments: 64-byte rows,
       // 16-byte units swizzled by the row so that the 4-column writes spread over
@@ -730,22 +758,27 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
         }
       }
       lds_sync();  // B2
+    }
+  } else {
+    copy_chunk(0);
+    if (nchunk > 1) {
+      copy_chunk(1);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSlotBlocks));
     } else {
-      if (cl + 1 < nchunk) copy_chunk(cl + 1, smem + ((cl + 1) & 1) * L::kSlot);
+      wait_vm_all();
+    }
+    __syncthreads();
+    for (int cl = 0; cl < nchunk; ++cl) {
+      // copies run two chunks ahead: slot (cl+2) % 3 was last read during chunk cl-1
+      const bool ahead = cl + 2 < nchunk;
+      if (ahead) copy_chunk(cl + 2);
       // B1 without a fence: this wave touches LDS only through the copies in flight,
       // which the other waves read after B2
       __builtin_amdgcn_s_barrier();
-      wait_vm_all();
+      if (ahead) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSlotBlocks));  // chunk cl+1 has landed
+      else wait_vm_all();
       lds_sync();  // B2: the next chunk's inputs are in LDS
     }
-  }
-
-  if (role == 0 && state_out) {
-    float* sp = state_out + static_cast<int64_t>(bh) * DK * DK;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sp[(32 * dt + acc_row(v, h)) * DK + col] = Ms[dt][v];
   }
 }
 
