@@ -135,8 +135,8 @@ struct PrepLds {
   static constexpr int kK = 0;                   // bf16 [64][KP]; later sA fp32 [64][FP]
   static constexpr int kQ = CH * KP * 2;         // bf16 [64][KP]; later sT fp32 [64][FP]
   static constexpr int kV = 2 * CH * KP * 2;     // bf16 [64][KP]: V rows of the current value head
-  static constexpr int kY = 3 * CH * KP * 2;     // fp32 32 x 36 (or 2 x 16 x 20)
-  static constexpr int kVec = kY + 32 * 36 * 4;  // rk, rq, g, beta, gamma rk, rk e^{g_63 - g}
+  static constexpr int kY = 3 * CH * KP * 2;     // fp32 2 x 16 x 20 (level 1 of the inverse)
+  static constexpr int kVec = kY + 2 * 16 * 20 * 4;  // rk, rq, g, beta, gamma rk, rk e^{g_63 - g}
   static constexpr int kBytes = kVec + 6 * CH * 4;
 };
 static_assert(CH * FP * 4 <= CH * KP * 2, "sA and sT reuse the K and Q rows");
@@ -249,25 +249,29 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   }
   __syncthreads();  // sK / sQ are dead from here on: their bytes become sA / sT
 
-  for (int j = 0; j < a.G; ++j) {
-    const int hv = hk * a.G + j;
-    unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hv) * nwin + cl) * WH_BYTES;
-    // V rows of this value head (loads issued before the gate scan)
-    u32x4 vr[4];
+  // V rows and gates of a value head are loaded one head ahead, into registers
+  // (rows past the sequence end read the last valid row and are replaced by zeros)
+  u32x4 vr[4];
+  float la = 0.f, be = 0.f;
+  auto load_head = [&](int hv) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int vi = tid + 256 * m, r = vi >> 4, c8 = (vi & 15) * 8;
       const int rr = r < nval ? r : nval - 1;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(gv + (tokbase + rr) * a.sv + hv * DK + c8);
-      vr[m] = r < nval ? x : u32x4{0u, 0u, 0u, 0u};
+      vr[m] = *reinterpret_cast<const u32x4*>(gv + (tokbase + rr) * a.sv + hv * DK + c8);
     }
+    const int tr = lane < nval ? lane : nval - 1;
+    la = a.la[(tokbase + tr) * a.Hv + hv];
+    be = a.beta[(tokbase + tr) * a.Hv + hv];
+  };
+  load_head(hk * a.G);
+
+  for (int j = 0; j < a.G; ++j) {
+    const int hv = hk * a.G + j;
+    unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hv) * nwin + cl) * WH_BYTES;
     // ---- gates: prefix sums and the row scalings --------------------------
     if (wv == 0) {
-      float la = 0.f, be = 0.f;
-      if (lane < nval) {
-        la = a.la[(tokbase + lane) * a.Hv + hv];
-        be = a.beta[(tokbase + lane) * a.Hv + hv];
-      }
+      if (lane >= nval) la = be = 0.f;
       float g = la;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -287,11 +291,12 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int vi = tid + 256 * m;
-      *reinterpret_cast<u32x4*>(sV + (vi >> 4) * KP + (vi & 15) * 8) = vr[m];
+      *reinterpret_cast<u32x4*>(sV + (vi >> 4) * KP + (vi & 15) * 8) =
+          (vi >> 4) < nval ? vr[m] : u32x4{0u, 0u, 0u, 0u};
     }
+    if (j + 1 < a.G) load_head(hv + 1);
     __syncthreads();
-    // ---- A (fp32, strictly lower) and the P fragments from the Gram tiles, and
-    //      zeros in the two upper 16x16 blocks of T that the block inverse reads
+    // ---- A (fp32, strictly lower) and the P fragments from the Gram tiles ----
     if (wv < 3) {
       {
         const int i = 32 * ctK + l32;
@@ -331,6 +336,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
         }
       }
     } else {
+      // T blocks (0,1) and (2,3) (above the diagonal, inside S0 and S1) are read as zeros
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int e = lane + 64 * m, blk = e >> 8;
@@ -393,30 +399,54 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       *reinterpret_cast<floatx2*>(sT + (16 * I + yr) * FP + 16 * J + yc) = floatx2{-t[0], -t[1]};
     }
     __syncthreads();
-    // level 2: T[32:64, 0:32] = -S1 (A[32:64, 0:32] S0), S0/S1 the 32x32 diagonal inverses
-    {
-      const int idx = tid * 4;
-      const int yr = idx >> 5, yc = idx & 31;
-      floatx4 y = {0.f, 0.f, 0.f, 0.f};
+    // level 2 on wave 0:
+    if (wv == 0) {
+      // T[32:64, 0:32] = -S1 (A[32:64, 0:32] S0) on MFMA, each fp32 operand split into
+      // fp16 hi + lo and three products kept (hi hi, hi lo, lo hi): about 22 bits
+      {
+        floatx16 Y = zero16(), Y2 = zero16();
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const floatx4 av = *reinterpret_cast<const floatx4*>(sA + (32 + yr) * FP + 4 * q);
+        for (int ks = 0; ks < 2; ++ks) {
+          const float* ar = sA + (32 + l32) * FP + 16 * ks + 4 * h;
+          const floatx4 a0 = *reinterpret_cast<const floatx4*>(ar), a1 = *reinterpret_cast<const floatx4*>(ar + 8);
+          halfx8 ahi, alo, bhi, blo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const floatx4 tv = *reinterpret_cast<const floatx4*>(sT + (4 * q + e) * FP + yc);
-          y += av[e] * tv;
+          for (int e = 0; e < 8; ++e) {
+            const float av = e < 4 ? a0[e] : a1[e - 4];
+            const float bv = sT[(16 * ks + kperm(h, e)) * FP + l32];
+            ahi[e] = static_cast<_Float16>(av);
+            alo[e] = static_cast<_Float16>(av - static_cast<float>(ahi[e]));
+            bhi[e] = static_cast<_Float16>(bv);
+            blo[e] = static_cast<_Float16>(bv - static_cast<float>(bhi[e]));
+          }
+          Y = mfma32h(ahi, bhi, Y);
+          Y2 = mfma32h(ahi, blo, Y2);
+          Y2 = mfma32h(alo, bhi, Y2);
         }
-      }
-      *reinterpret_cast<floatx4*>(sY + yr * 36 + yc) = y;
-      __syncthreads();
-      floatx4 t = {0.f, 0.f, 0.f, 0.f};
+        Y += Y2;
+        floatx16 Z = zero16(), Z2 = zero16();
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const floatx4 tv = *reinterpret_cast<const floatx4*>(sT + (32 + yr) * FP + 32 + 4 * q);
+        for (int ks = 0; ks < 2; ++ks) {
+          const float* sr = sT + (32 + l32) * FP + 32 + 16 * ks + 4 * h;
+          const floatx4 a0 = *reinterpret_cast<const floatx4*>(sr), a1 = *reinterpret_cast<const floatx4*>(sr + 8);
+          halfx8 ahi, alo, bhi, blo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t += tv[e] * *reinterpret_cast<const floatx4*>(sY + (4 * q + e) * 36 + yc);
+          for (int e = 0; e < 8; ++e) {
+            const float av = e < 4 ? a0[e] : a1[e - 4];
+            const float bv = Y[8 * ks + e];   // accumulator values [8ks, 8ks+8) are the B fragment
+            ahi[e] = static_cast<_Float16>(av);
+            alo[e] = static_cast<_Float16>(av - static_cast<float>(ahi[e]));
+            bhi[e] = static_cast<_Float16>(bv);
+            blo[e] = static_cast<_Float16>(bv - static_cast<float>(bhi[e]));
+          }
+          Z = mfma32h(ahi, bhi, Z);
+          Z2 = mfma32h(ahi, blo, Z2);
+          Z2 = mfma32h(alo, bhi, Z2);
+        }
+        Z += Z2;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sT[(32 + acc_row(v, h)) * FP + l32] = -Z[v];
       }
-      *reinterpret_cast<floatx4*>(sT + (32 + yr) * FP + yc) = -t;
     }
     __syncthreads();
     // ---- per wave: T' = T diag(beta) fragments (all six), the K^T columns of key
