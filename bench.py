@@ -11,6 +11,8 @@ prefill with the L2 flag, gated RMSNorm), the 262144-token prefill, the
 roofline of the dominant kernel, and the fp64 oracle timed on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+       python bench.py --calib-copy   (a plain device copy of 256 MiB, five times: the
+                                       reference that HBM counters are scaled by)
 """
 from __future__ import annotations
 
@@ -270,7 +272,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="headline only (no decode/block/long)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run only a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
+    if args.calib_copy:
+        import torch
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "repeats": 5}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
