@@ -20,38 +20,36 @@
 //   M    <- gamma_63 M + K^T diag(rk e^{g_63 - g}) U
 //
 // which reproduces the token-by-token rule exactly (up to rounding).  Every
-// exponent is <= 0.  K and Q stay raw bf16 MFMA operands; the L2 factors are
-// folded into fp32 row scalings.
+// exponent is <= 0.  Everything that does not depend on the state is folded
+// before the serial loop:
+//
+//   W  = T' diag(gamma rk) K,   U0 = T' V,   Kd = K^T diag(rk e^{g_63 - g}),
+//   Q^ = diag(rq) Q,            so that per chunk
+//   U  = U0 - W M,   M <- gamma_63 M + Kd U,   O = diag(gamma) Q^ M + P U.
 //
 // Two kernels per window of chunks:
-//  * prep (one workgroup per chunk and key head, fully parallel): everything
-//    that does not depend on the state -- row norms, the Gram products
-//    K K^T and Q K^T (MFMA), the gate prefix sums, A, the triangular inverse
-//    (fp32, blocked 16/32), T' and P -- written to the workspace as ready
-//    MFMA A-operand fragments (fp16) plus three row-scaling
-//    vectors per (chunk, value head).
-//    The prep kernel also writes K, Q and K^T as fragments, so the chain
-//    kernel stages its inputs with plain 16-byte copies and reads every MFMA
-//    A operand with one conflict-free 16-byte LDS read per lane.
-//  * chain (one workgroup per sequence, value head and 64 value columns,
-//    looping over the chunks): only the state-dependent products.  Columns of
-//    M evolve independently; waves 0-1 ("state") each own a 32-column strip
-//    of M in MFMA accumulators for the whole window and run the serial path
-//    K M, X, U = T'X and the update, with nothing else to do; waves 2-3
-//    ("output") compute Q M and P U for the same strips from fragments the
-//    state waves publish in LDS, and move the next chunk's inputs from HBM
-//    into LDS: loads are issued at the start of a chunk; inputs the update
-//    phase reads go to one of two alternating buffers at the chunk's end,
-//    the rest is restaged while the update runs.
+//  * prep (one workgroup per chunk and key head, fully parallel over chunks):
+//    row norms, the Gram products K K^T and K Q^T (bf16 MFMA, kept in
+//    registers), and per value head the gate prefix sums, A, the inverse
+//    (16x16 forward substitution, a 16-block merge, and the 32x32 merge on
+//    MFMA with split-fp16 operands), T', and the products -W and U0 (fp16
+//    MFMA).  All of it is written to the workspace as MFMA-ready fp16
+//    fragments; U0 in the accumulator layout of the chain's U.
+//  * chain (one workgroup per sequence, value head and 32-column strip of M,
+//    looping over the window's chunks; columns of M evolve independently).
+//    One wave carries the fp32 strip of M in registers and runs the serial
+//    path: 16 MFMAs for U = U0 - W M, 16 for the update.  A second wave forms
+//    the outputs from the M and U fragments the first publishes in LDS; a
+//    third copies the next operands from the workspace into LDS two chunks
+//    ahead with direct global-to-LDS loads.
 //
-// Precision.  MFMA accumulation is fp32 throughout.  K M and Q M run on bf16
-// operands (K and Q are bf16 inputs; M is rounded once to bf16 for them).
-// T'X, P U and K^T U' run on fp16 operands: T', P and the update's K^T are
-// written as fp16 by the prep kernel (bf16 K converts exactly), X and U are
-// rounded once to fp16.  fp16 keeps 11 significant bits, which holds the
-// state within a few 1e-4 of the exact result and the outputs well inside
-// their bound; its range (|x| < 65504) bounds the values of v, the state and
-// the intra-chunk matrices this path accepts.
+// Precision.  MFMA accumulation is fp32 throughout and the state stays fp32.
+// The Gram products take the bf16 inputs as they are; every other product
+// runs on fp16 operands, each rounded once (in prep: -W, Kd, U0, P, Q^; in
+// the chain: M and U).  fp16 keeps 11 significant bits, which holds the state
+// within a few 1e-4 of the exact result and the outputs well inside their
+// bound; its range (|x| < 65504) bounds the values of v, the state and the
+// intra-chunk matrices this path accepts.
 //
 // MFMA layout (v_mfma_f32_32x32x16_bf16 and _f16, wave64): A row = B column =
 // lane & 31; the accumulator holds column lane & 31, rows 8j + 4h + i
@@ -59,7 +57,8 @@
 // same way on A and B: inside each 16-wide k step, lane half h carries
 // k = 4h..4h+3 and 8+4h..8+4h+3.  With that permutation accumulator values
 // [8s, 8s+8) of a tile are directly the B operand for k step s of that tile,
-// so M, X and U feed the next product from registers.
+// so M and U feed the next product from registers, and a product computed in
+// transposed form (C^T = B^T A^T) leaves its result as an A fragment.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
