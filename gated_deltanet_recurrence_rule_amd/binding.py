@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libgdn.so")
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN, GDN_ERR_DEVICE = range(6)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_QK_L2NORM = 1
+GDN_FLAG_TOKEN_SERIAL = 2
 
 # Every exported symbol, in the order include/gdn.h declares them.
 EXPORTS = ("gdn_prefill", "gdn_prefill_workspace_size", "gdn_decode_step", "gdn_conv1d_silu",
@@ -124,11 +125,12 @@ def gdn_prefill_workspace_size(dims: GdnDims) -> int:
 
 def gdn_prefill(q, k, v, log_alpha, beta, state_in=None, state_out=None, o=None, *, Hk: int,
                 Hv: int, l2norm: bool = False, l2_eps: float = 1e-6, q_scale: float = 1.0,
-                workspace=None, stream=None):
+                token_serial: bool = False, workspace=None, stream=None):
     """q, k: [B, T, Hk*D] views; v: [B, T, Hv*D]; log_alpha, beta: [B, T, Hv] fp32;
     state_in / state_out: [B, Hv, D, D] fp32 or None; o: [B, T, >=Hv*D] or None
     (allocated); workspace: uint8 device tensor or None (allocated with the size
-    gdn_prefill_workspace_size asks for).  Returns o."""
+    gdn_prefill_workspace_size asks for); token_serial: GDN_FLAG_TOKEN_SERIAL.
+    Returns o."""
     import torch
     B, T = int(q.shape[0]), int(q.shape[1])
     if q.shape[2] % Hk or v.shape[2] % Hv or q.shape[2] // Hk != v.shape[2] // Hv:
@@ -139,7 +141,8 @@ def gdn_prefill(q, k, v, log_alpha, beta, state_in=None, state_out=None, o=None,
         raise ValueError("q, k, v and o must share one dtype")
     if o is None:
         o = torch.empty((B, T, Hv * D), dtype=q.dtype, device=q.device)
-    dims = make_dims(B, T, Hk, Hv, D, io, GDN_FLAG_QK_L2NORM if l2norm else 0,
+    flags = (GDN_FLAG_QK_L2NORM if l2norm else 0) | (GDN_FLAG_TOKEN_SERIAL if token_serial else 0)
+    dims = make_dims(B, T, Hk, Hv, D, io, flags,
                      _token_stride(q, B, T, Hk * D, "q"), _token_stride(k, B, T, Hk * D, "k"),
                      _token_stride(v, B, T, Hv * D, "v"), _token_stride(o, B, T, Hv * D, "o"),
                      q_scale, l2_eps)

@@ -50,7 +50,8 @@ gdn_status check_dims(const gdn_dims* d, bool T1) {
   if (d->Dk != d->Dv || !supported_d(d->Dk))
     return fail(GDN_ERR_UNSUPPORTED, "head widths Dk=%d Dv=%d: kernels take Dk == Dv in {16,32,64,128}",
                 d->Dk, d->Dv);
-  if ((d->flags & ~GDN_FLAG_QK_L2NORM) != 0) return fail(GDN_ERR_SHAPE, "unknown flag bits 0x%x", d->flags);
+  if ((d->flags & ~(GDN_FLAG_QK_L2NORM | GDN_FLAG_TOKEN_SERIAL)) != 0)
+    return fail(GDN_ERR_SHAPE, "unknown flag bits 0x%x", d->flags);
   const int64_t wq = static_cast<int64_t>(d->Hk) * d->Dk, wv = static_cast<int64_t>(d->Hv) * d->Dv;
   if (d->stride_q < wq || d->stride_k < wq)
     return fail(GDN_ERR_SHAPE, "stride_q=%lld / stride_k=%lld below Hk*Dk=%lld", (long long)d->stride_q,
@@ -64,7 +65,9 @@ gdn_status check_dims(const gdn_dims* d, bool T1) {
   return GDN_OK;
 }
 
-bool use_chunk_kernel(const gdn_dims* d) { return d->io == GDN_BF16 && d->Dk == 128 && d->T > 0; }
+bool use_chunk_kernel(const gdn_dims* d) {
+  return d->io == GDN_BF16 && d->Dk == 128 && d->T > 0 && !(d->flags & GDN_FLAG_TOKEN_SERIAL);
+}
 
 gdn::RecArgs rec_args(const gdn_dims* d, const void* q, const void* k, const void* v, const float* la,
                       const float* beta, const float* sin, float* sout, void* o) {

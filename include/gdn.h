@@ -66,6 +66,12 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 /* Flag: divide q and k of each (token, key head) by sqrt(sum of squares +
  * l2_eps) before use (per-head L2 normalisation). */
 #define GDN_FLAG_QK_L2NORM 1u
+/* Flag (gdn_prefill): run the token-by-token kernel, fp32 arithmetic
+ * throughout, instead of the chunked one.  The chunked kernel multiplies fp16
+ * operands (fp32 accumulation), which bounds the magnitudes it accepts: v, the
+ * state and the per-chunk intermediates must stay below fp16's 65504.  This
+ * flag lifts that bound at the cost of speed; it needs no workspace. */
+#define GDN_FLAG_TOKEN_SERIAL 2u
 
 /*
  * Shapes of one recurrence call.

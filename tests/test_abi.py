@@ -41,6 +41,9 @@ def test_workspace_size():
     per = 4 * (128 * 56320 + 16 * 16384)
     assert ws(big) == ((256 << 20) // per) * per + 4 * 128 * 128 * 128 * 4
     assert ws(dims(Hv=5)) == 0                          # invalid dims
+    d = dims(T=64)
+    d.flags = B.GDN_FLAG_TOKEN_SERIAL                   # token-serial path forced: none
+    assert ws(d) == 0
 
 
 def test_version_and_struct_layout():

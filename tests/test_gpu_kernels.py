@@ -20,14 +20,15 @@ def _torch():
     return torch
 
 
-def run_prefill(p, *, l2=False, q_scale=1.0, state_in=None):
+def run_prefill(p, *, l2=False, q_scale=1.0, state_in=None, token_serial=False):
     torch = _torch()
     q, k, v = to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"])
     la, be = to_dev(p["log_alpha"]), to_dev(p["beta"])
     B, Hv, D = p["B"], p["Hv"], p["D"]
     si = None if state_in is None else to_dev(state_in.astype(np.float32))
     so = torch.empty((B, Hv, D, D), dtype=torch.float32, device="cuda")
-    o = G.gdn_prefill(q, k, v, la, be, si, so, Hk=p["Hk"], Hv=Hv, l2norm=l2, q_scale=q_scale)
+    o = G.gdn_prefill(q, k, v, la, be, si, so, Hk=p["Hk"], Hv=Hv, l2norm=l2, q_scale=q_scale,
+                      token_serial=token_serial)
     torch.cuda.synchronize()
     return to_host(o).reshape(B, p["T"], Hv, D), to_host(so)
 
@@ -84,6 +85,22 @@ def test_prefill_token_serial_parity(B, T, Hk, Hv, D, io, state, l2):
     assert_state(sg, srf)
     if io == "f32":   # fp32 arithmetic end to end: far inside the bound
         assert np.abs(og - orf).max() <= 1e-4 * np.sqrt(np.mean(orf ** 2))
+
+
+@pytest.mark.parametrize("v_scale", [1.0, 4096.0])
+def test_prefill_token_serial_flag(v_scale):
+    """GDN_FLAG_TOKEN_SERIAL runs the fp32 token-serial kernel on a shape the chunked
+    kernel would take (bf16, D = 128), including values far beyond fp16's range for
+    the state (v scaled by 2^12, slowly decaying gates)."""
+    p = W.problem(77, 1, 150, 1, 3, 128, io="bf16", recipe="tiny", state="normal")
+    if v_scale != 1.0:
+        p["v"] = W.f32_to_bf16(W.bf16_to_f32(p["v"]) * np.float32(v_scale))
+        p["state_in"] = (p["state_in"] * v_scale).astype(np.float32)
+    og, sg = run_prefill(p, state_in=p["state_in"], token_serial=True)
+    orf, srf = oracle_prefill(p, state_in=p["state_in"])
+    assert_out(og, orf, bf16=True)
+    e = max(assert_state(sg[0, h], srf[0, h]) for h in range(3))
+    assert e < 1e-5, e   # fp32 arithmetic throughout
 
 
 @pytest.mark.parametrize("D,io,l2", [(128, "bf16", False), (128, "bf16", True), (16, "f32", False), (64, "bf16", False)])
