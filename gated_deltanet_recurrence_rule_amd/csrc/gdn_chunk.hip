@@ -169,6 +169,24 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   const uint16_t* gk = static_cast<const uint16_t*>(a.k);
   const uint16_t* gv = static_cast<const uint16_t*>(a.v);
 
+  // V rows and gates of a value head are loaded one head ahead, into registers
+  // (rows past the sequence end read the last valid row and are replaced by zeros);
+  // the first head's loads are issued before the K and Q rows are waited for
+  u32x4 vr[4];
+  float la = 0.f, be = 0.f;
+  auto load_head = [&](int hv) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int vi = tid + 256 * m, r = vi >> 4, c8 = (vi & 15) * 8;
+      const int rr = r < nval ? r : nval - 1;
+      vr[m] = *reinterpret_cast<const u32x4*>(gv + (tokbase + rr) * a.sv + hv * DK + c8);
+    }
+    const int tr = lane < nval ? lane : nval - 1;
+    la = a.la[(tokbase + tr) * a.Hv + hv];
+    be = a.beta[(tokbase + tr) * a.Hv + hv];
+  };
+  load_head(hk * a.G);
+
   // ---- K, Q rows and their norms ------------------------------------------
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -248,22 +266,6 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   }
   __syncthreads();  // sK / sQ are dead from here on: their bytes become sA / sT
 
-  // V rows and gates of a value head are loaded one head ahead, into registers
-  // (rows past the sequence end read the last valid row and are replaced by zeros)
-  u32x4 vr[4];
-  float la = 0.f, be = 0.f;
-  auto load_head = [&](int hv) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int vi = tid + 256 * m, r = vi >> 4, c8 = (vi & 15) * 8;
-      const int rr = r < nval ? r : nval - 1;
-      vr[m] = *reinterpret_cast<const u32x4*>(gv + (tokbase + rr) * a.sv + hv * DK + c8);
-    }
-    const int tr = lane < nval ? lane : nval - 1;
-    la = a.la[(tokbase + tr) * a.Hv + hv];
-    be = a.beta[(tokbase + tr) * a.Hv + hv];
-  };
-  load_head(hk * a.G);
 
   for (int j = 0; j < a.G; ++j) {
     const int hv = hk * a.G + j;
