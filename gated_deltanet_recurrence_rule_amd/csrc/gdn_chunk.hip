@@ -533,16 +533,18 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
 // chain kernel: one workgroup (3 waves) per (32-column strip, value head, batch)
 // =========================================================================
 // LDS: three input slots (a chunk's -W, Kd, U0 strip and scalings, copied from
-// the workspace by the copy wave two chunks ahead) and the M and U fragments
-// that the state wave publishes for the output wave.  The output wave reads its
-// own operands (Q^ and P fragments) from the workspace straight into registers.
+// the workspace by the copy wave two chunks ahead), two buffers each of the M
+// and U fragments that the state wave publishes for the output wave, and the
+// output wave's staging tile.  The output wave reads its own operands (Q^ and
+// P fragments) from the workspace straight into registers.
 struct ChainLds {
   static constexpr int kW = 0, kKd = 16384, kU0 = 32768, kSc = 36864;
   static constexpr int kSlot = 37888;               // 37 blocks of 1 KiB
   static constexpr int kNSlot = 3;
-  static constexpr int kMf = kNSlot * kSlot;        // M fragments (fp16) [k step 8][lane 64] x 16 B
-  static constexpr int kUf = kMf + 8 * 1024;        // U fragments (fp16) [k step 4][lane 64] x 16 B
-  static constexpr int kBytes = kUf + 4 * 1024;
+  static constexpr int kMf = kNSlot * kSlot;        // 2 x M fragments (fp16) [k step 8][lane 64] x 16 B
+  static constexpr int kUf = kMf + 2 * 8192;        // 2 x U fragments (fp16) [k step 4][lane 64] x 16 B
+  static constexpr int kSt = kUf + 2 * 4096;        // 64 x 32 bf16 output staging tile
+  static constexpr int kBytes = kSt + 4096;
 };
 constexpr int kSlotBlocks = 37;
 
@@ -573,6 +575,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
+// One barrier per chunk.  Between barrier c-1 and barrier c:
+//  * the state wave turns M_c into U_c and M_{c+1}, publishing U_c into U buffer
+//    c & 1 and M_{c+1} into M buffer (c+1) & 1;
+//  * the output wave forms diag(gamma) Q^ M_c from M buffer c & 1 and completes the
+//    previous chunk, O_{c-1} += P U_{c-1} from U buffer (c-1) & 1, and stores it;
+//  * the copy wave starts chunk c+2's copy into the slot chunk c-1 used and waits
+//    until chunk c+1's copy has landed.
+// Each buffer is rewritten two chunks after it was filled, by which time its
+// reader has passed the barrier in between.
 __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, const unsigned char* ws, int nwin,
                                                              const float* state_in, float* state_out) {
   using L = ChainLds;
@@ -596,11 +607,9 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
   const int hk = hv / a.G;
   const int bh = bhv;
   // roles (one wave per SIMD): wave 1 carries the state of the strip, wave 0 produces
-  // its outputs, wave 2 copies the next chunk's inputs into LDS
+  // its outputs, wave 2 copies the next chunks' inputs into LDS
   const int role = wv == 2 ? 2 : (wv == 1 ? 0 : 1);
   const int col = 32 * strip + l32;  // this lane's value column
-  unsigned char* sMf = smem + L::kMf;
-  unsigned char* sUf = smem + L::kUf;
   uint16_t* go = static_cast<uint16_t*>(a.o);
 
   const int nchunk = min(nwin, (a.T + CH - 1) / CH - c0);
@@ -615,9 +624,8 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
       __builtin_amdgcn_global_load_lds(slot_src(m, wsh, strip) + 16 * lane, slot + 1024 * m, 16, 0, 0);
   };
 
-  // Each role runs its own chunk loop (same trip count, the same two barriers per
-  // chunk), so that the registers one role carries across chunks are free in the
-  // others.
+  // Each role runs its own chunk loop (same trip count, one barrier per chunk),
+  // so that the registers one role carries across chunks are free in the others.
   if (role == 0) {
     floatx16 Ms[4];
     halfx8 Mfr[8];
@@ -634,28 +642,37 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       Mfr[ks] = acc_frag_h(Ms[ks >> 1], ks & 1);
-      *reinterpret_cast<halfx8*>(sMf + ks * 1024 + lane * 16) = Mfr[ks];
+      *reinterpret_cast<halfx8*>(smem + L::kMf + ks * 1024 + lane * 16) = Mfr[ks];
     }
     __syncthreads();
     for (int cl = 0; cl < nchunk; ++cl) {
       unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
       const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
+      unsigned char* sUf = smem + L::kUf + (cl & 1) * 4096;
+      unsigned char* sMf = smem + L::kMf + ((cl + 1) & 1) * 8192;
       // ---- U = U0 - W M (U0 enters as the accumulator) ; publish U ----------
+      // all reads are issued before the first use: the gate, U0, then the -W
+      // fragments in the order the products take them
+      const float gC = sSc[64];
+      __builtin_amdgcn_sched_barrier(0);
+      halfx8 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const halfx8*>(slot + L::kU0 + (i >> 1) * 2048 + lane * 32 + (i & 1) * 16);
+      halfx8 Af[16];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          Af[rt * 8 + ks] = *reinterpret_cast<const halfx8*>(slot + L::kW + (rt * 8 + ks) * 1024 + lane * 16);
+      __builtin_amdgcn_sched_barrier(0);
       floatx16 U[2];
-      halfx8 Af[16];   // -W fragments, all read before the first product
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Af[i] = *reinterpret_cast<const halfx8*>(slot + L::kW + i * 1024 + lane * 16);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const halfx8 x0 = *reinterpret_cast<const halfx8*>(slot + L::kU0 + rt * 2048 + lane * 32);
-        const halfx8 x1 = *reinterpret_cast<const halfx8*>(slot + L::kU0 + rt * 2048 + lane * 32 + 16);
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          U[rt][e] = static_cast<float>(x0[e]);
-          U[rt][8 + e] = static_cast<float>(x1[e]);
+          U[rt][e] = static_cast<float>(x[2 * rt][e]);
+          U[rt][8 + e] = static_cast<float>(x[2 * rt + 1][e]);
         }
-      }
-      const float gC = sSc[64];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
@@ -680,7 +697,6 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
         Uf[ks] = acc_frag_h(U[ks >> 1], ks & 1);
         *reinterpret_cast<halfx8*>(sUf + ks * 1024 + lane * 16) = Uf[ks];
       }
-      lds_sync();  // B1: U published; the output wave has read M
       // ---- M <- gamma_63 M + Kd U, two state tiles at a time so that the first
       //      pair's fragments are formed while the second pair runs ; publish M ----
 #pragma unroll
@@ -695,7 +711,7 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
           *reinterpret_cast<halfx8*>(sMf + ks * 1024 + lane * 16) = Mfr[ks];
         }
       }
-      lds_sync();  // B2
+      lds_sync();
     }
     if (state_out) {
       float* sp = state_out + static_cast<int64_t>(bh) * DK * DK;
@@ -705,42 +721,19 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
         for (int v = 0; v < 16; ++v) sp[(32 * dt + acc_row(v, h)) * DK + col] = Ms[dt][v];
     }
   } else if (role == 1) {
-    halfx8 Bq[16], Bp[FT];  // this chunk's Q^ and P fragments
+    halfx8 Bq[16], Bp[FT];  // Q^ fragments of the current chunk, P fragments of the previous one
 #pragma unroll
     for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(wsk_of(0) + i * 1024 + lane * 16);
 #pragma unroll
     for (int f = 0; f < FT; ++f) Bp[f] = *reinterpret_cast<const halfx8*>(wsh_of(0) + WH_P + f * 1024 + lane * 16);
+    unsigned char* sO = smem + L::kSt;
 
-    __syncthreads();
-    for (int cl = 0; cl < nchunk; ++cl) {
-      unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
-      const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
-      // ---- O^T = M^T Q^^T diag(gamma) + U^T P^T: the M and U fragments serve as A
-      //      operands and Q^, P as B operands, so each lane holds one token and
-      //      runs of four value columns ------------------------------------------
-      floatx16 O[2] = {zero16(), zero16()};
-      const int cn = min(cl + 1, nchunk - 1);   // next chunk (the last one reloads itself)
+    // O_c += U_c^T P_c^T, then the 64 x 32 bf16 tile is staged in LDS (64-byte rows,
+    // 16-byte units swizzled by the row so that the 4-column writes spread over the
+    // banks) and stored as 16-byte runs of 8 columns
+    auto finish = [&](floatx16 (&O)[2], int cp) {
       {
-        halfx8 Am[8];   // M fragments, all read before the first product
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) Am[ks] = *reinterpret_cast<const halfx8*>(sMf + ks * 1024 + lane * 16);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) O[rt] = mfma32h(Am[ks], Bq[rt * 8 + ks], O[rt]);
-      }
-      // the next chunk's Q^ fragments: a chunk ahead of their use
-      {
-        const unsigned char* wq = wsk_of(cn);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(wq + i * 1024 + lane * 16);
-      }
-      const float g0 = sSc[l32], g1 = sSc[32 + l32];
-      O[0] *= g0;
-      O[1] *= g1;
-      lds_sync();  // B1
-      {
+        const unsigned char* sUf = smem + L::kUf + (cp & 1) * 4096;
         halfx8 Au[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) Au[ks] = *reinterpret_cast<const halfx8*>(sUf + ks * 1024 + lane * 16);
@@ -748,15 +741,11 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
 #pragma unroll
         for (int f = 0; f < FT; ++f) O[ft_rt(f)] = mfma32h(Au[ft_ks(f)], Bp[f], O[ft_rt(f)]);
       }
-      {
-        const unsigned char* wp = wsh_of(cn) + WH_P;
+      if (cp + 1 < nchunk) {
+        const unsigned char* wp = wsh_of(cp + 1) + WH_P;
 #pragma unroll
         for (int f = 0; f < FT; ++f) Bp[f] = *reinterpret_cast<const halfx8*>(wp + f * 1024 + lane * 16);
       }
-      // stage the 64 x 32 bf16 tile over the (now read) U fragments: 64-byte rows,
-      // 16-byte units swizzled by the row so that the 4-column writes spread over
-      // the banks; then 16-byte stores of whole 8-column runs
-      unsigned char* sO = sUf;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int r = 32 * rt + l32;
@@ -766,7 +755,7 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
           *reinterpret_cast<uint2*>(sO + r * 64 + ((j ^ (r & 3)) * 16) + 8 * h) = w;
         }
       }
-      const int t0 = (c0 + cl) * CH;
+      const int t0 = (c0 + cp) * CH;
       const int nval = min(CH, a.T - t0);
       uint16_t* obase = go + (static_cast<int64_t>(b) * a.T + t0) * a.so + hv * DK + 32 * strip;
       u16x8 x[4];
@@ -788,8 +777,46 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
           if (r < nval) *reinterpret_cast<u16x8*>(obase + static_cast<int64_t>(r) * a.so + 8 * u) = x[m];
         }
       }
-      lds_sync();  // B2
+    };
+
+    floatx16 Op[2];  // the previous chunk's outputs, waiting for P U
+    __syncthreads();
+    for (int cl = 0; cl < nchunk; ++cl) {
+      unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
+      const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
+      const unsigned char* sMf = smem + L::kMf + (cl & 1) * 8192;
+      // ---- O^T = M^T Q^^T diag(gamma) + U^T P^T: the M and U fragments serve as A
+      //      operands and Q^, P as B operands, so each lane holds one token and
+      //      runs of four value columns ------------------------------------------
+      floatx16 O[2] = {zero16(), zero16()};
+      {
+        halfx8 Am[8];   // M fragments, all read before the first product
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) Am[ks] = *reinterpret_cast<const halfx8*>(sMf + ks * 1024 + lane * 16);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) O[rt] = mfma32h(Am[ks], Bq[rt * 8 + ks], O[rt]);
+      }
+      // the next chunk's Q^ fragments: a chunk ahead of their use (the last chunk
+      // reloads its own)
+      {
+        const unsigned char* wq = wsk_of(min(cl + 1, nchunk - 1));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(wq + i * 1024 + lane * 16);
+      }
+      if (cl > 0) finish(Op, cl - 1);
+      const float g0 = sSc[l32], g1 = sSc[32 + l32];
+      Op[0] = O[0] * g0;
+      Op[1] = O[1] * g1;
+      // the first chunk issues no stores; draining its loads here keeps the counts
+      // the compiler waits for at the loop head those of the later chunks, whose
+      // stores need not complete before the next chunk's products
+      if (cl == 0) wait_vm_all();
+      lds_sync();
     }
+    if (nchunk > 0) finish(Op, nchunk - 1);
   } else {
     copy_chunk(0);
     if (nchunk > 1) {
@@ -800,15 +827,16 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
     }
     __syncthreads();
     for (int cl = 0; cl < nchunk; ++cl) {
-      // copies run two chunks ahead: slot (cl+2) % 3 was last read during chunk cl-1
-      const bool ahead = cl + 2 < nchunk;
-      if (ahead) copy_chunk(cl + 2);
-      // B1 without a fence: this wave touches LDS only through the copies in flight,
-      // which the other waves read after B2
+      // slot (cl+2) % 3 was last read during chunk cl-1
+      if (cl + 2 < nchunk) {
+        copy_chunk(cl + 2);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSlotBlocks));  // chunk cl+1 has landed
+      } else {
+        wait_vm_all();
+      }
+      // barrier without a fence: this wave writes LDS only through its copies, and
+      // the vector memory count above already covers the ones the others read next
       __builtin_amdgcn_s_barrier();
-      if (ahead) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSlotBlocks));  // chunk cl+1 has landed
-      else wait_vm_all();
-      lds_sync();  // B2: the next chunk's inputs are in LDS
     }
   }
 }
