@@ -105,8 +105,7 @@ size_t gdn_prefill_workspace_size(const gdn_dims* d) {
   const gdn::RecArgs a = rec_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
   const size_t per_chunk = gdn::chunk_ws_bytes_per_chunk(a);
   const int64_t nchunks = (static_cast<int64_t>(d->T) + 63) / 64;
-  int64_t nwin = static_cast<int64_t>((size_t(256) << 20) / per_chunk);
-  if (nwin < 1) nwin = 1;
+  const int64_t nwin = gdn::chunk_window_chunks(a);
   if (nwin >= nchunks) return static_cast<size_t>(nchunks) * per_chunk;
   return static_cast<size_t>(nwin) * per_chunk + gdn::chunk_ws_carry_bytes(a);
 }

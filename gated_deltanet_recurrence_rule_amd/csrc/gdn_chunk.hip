@@ -849,6 +849,26 @@ size_t chunk_ws_bytes_per_chunk(const RecArgs& a) {
 
 size_t chunk_ws_carry_bytes(const RecArgs& a) { return static_cast<size_t>(a.B) * a.Hv * DK * DK * 4; }
 
+// Chunks per window.  The chain kernel reads a window's operands back from the
+// memory-side last-level cache (256 MB) when they are still there: with the whole
+// T=4096, 16/48-head workspace (190 MB) in one window, the prep's input reads and
+// the outputs push part of it out, and the chain runs 20 % slower than with two
+// windows of 95 MB.  So a window is about 96 MiB of workspace, unless that leaves
+// the prep kernel fewer than two (chunk, key head) workgroups per CU (512 on 256
+// CUs), and never more than 256 MiB.  Windows are then balanced.
+int chunk_window_chunks(const RecArgs& a) {
+  const int nchunks = (a.T + CH - 1) / CH;
+  const size_t per = chunk_ws_bytes_per_chunk(a);
+  const int items = a.Hk * a.B;
+  int w = static_cast<int>((size_t(96) << 20) / per);
+  w = max(w, (512 + items - 1) / items);
+  w = min(w, static_cast<int>((size_t(256) << 20) / per));
+  w = max(w, 1);
+  if (w >= nchunks) return nchunks;
+  const int nwins = (nchunks + w - 1) / w;
+  return (nchunks + nwins - 1) / nwins;
+}
+
 hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
@@ -864,13 +884,14 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
   const size_t per_chunk = chunk_ws_bytes_per_chunk(a);
   // One window when the whole sequence fits; otherwise the state is carried
   // between windows through state_out (or a carry area at the workspace end).
-  int nwin = static_cast<int>(ws_bytes / per_chunk);
+  // the preferred window, or what the workspace holds when it is smaller
+  int nwin = static_cast<int>(min(ws_bytes / per_chunk, static_cast<size_t>(chunk_window_chunks(a))));
   bool need_carry = false;
   if (nwin < nchunks) {
     need_carry = a.state_out == nullptr;
     const size_t carry_b = need_carry ? chunk_ws_carry_bytes(a) : 0;
     const size_t avail = ws_bytes > carry_b ? ws_bytes - carry_b : 0;
-    nwin = static_cast<int>(avail / per_chunk);
+    nwin = min(nwin, static_cast<int>(avail / per_chunk));
   }
   if (nwin < 1) return hipErrorInvalidValue;
   if (nwin > nchunks) nwin = nchunks;

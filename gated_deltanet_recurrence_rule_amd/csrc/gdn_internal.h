@@ -32,6 +32,8 @@ hipError_t launch_recurrent(const RecArgs& a, int io, hipStream_t s);
 // needs several windows and there is no state_out, a state carry follows.
 size_t chunk_ws_bytes_per_chunk(const RecArgs& a);
 size_t chunk_ws_carry_bytes(const RecArgs& a);
+// preferred number of chunks per window (balanced windows)
+int chunk_window_chunks(const RecArgs& a);
 hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 
 struct ConvArgs {

@@ -128,10 +128,12 @@ gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const
  * for these dims (0 when the call needs none).  The chunked kernel keeps, per
  * (sequence, value head, chunk of a window), the per-chunk matrices that do
  * not depend on the state (55 KiB: the -W, K^T, U0 and P operands and the
- * row scalings, plus 16 KiB per key head for the scaled Q); windows are
- * sized to about 256 MiB
- * and the state is carried between windows through state_out, or through a
- * carry area inside the workspace when state_out is NULL.  A smaller
+ * row scalings, plus 16 KiB per key head for the scaled Q).  Windows hold
+ * about 96 MiB of these, so that the chain kernel finds them in the GPU's
+ * last-level cache, but at least 512 / (Hk * B) chunks and at most 256 MiB;
+ * they are balanced.  The state is carried between windows through
+ * state_out, or through a carry area inside the workspace when state_out is
+ * NULL.  A smaller
  * workspace is accepted down to one chunk per window (plus the carry when
  * needed); GDN_ERR_SHAPE below that.  The workspace is caller-owned device
  * memory, 256-byte aligned, used only during the call's kernels on `stream`.

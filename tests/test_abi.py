@@ -37,9 +37,16 @@ def test_workspace_size():
     assert ws(dims(T=64)) == per_chunk
     assert ws(dims(T=65)) == 2 * per_chunk
     assert ws(dims(io=B.GDN_F32, D=16)) == 0            # token-serial path needs none
-    big = dims(B=4, T=32768, Hk=16, Hv=128)             # windows of ~256 MiB + a state carry
+    # windows of ~96 MiB, balanced: 64 chunks of 2.97 MB -> 2 windows of 32, plus a state carry
+    per = 48 * 56320 + 16 * 16384
+    assert ws(dims(T=4096, Hk=16, Hv=48)) == 32 * per + 48 * 128 * 128 * 4
+    # ... but at least 512 / (Hk B) = 8 chunks: windows of 8 (228 MiB) + a state carry
+    big = dims(B=4, T=32768, Hk=16, Hv=128)
     per = 4 * (128 * 56320 + 16 * 16384)
-    assert ws(big) == ((256 << 20) // per) * per + 4 * 128 * 128 * 128 * 4
+    assert ws(big) == 8 * per + 4 * 128 * 128 * 128 * 4
+    # long sequence: 4096 chunks in 125 balanced windows of 33
+    per = 48 * 56320 + 16 * 16384
+    assert ws(dims(T=262144, Hk=16, Hv=48)) == 33 * per + 48 * 128 * 128 * 4
     assert ws(dims(Hv=5)) == 0                          # invalid dims
     d = dims(T=64)
     d.flags = B.GDN_FLAG_TOKEN_SERIAL                   # token-serial path forced: none
