@@ -269,7 +269,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # about 40 ms of untimed calls: the GPU's clocks are still rising over the first
+    # few hundred calls (at T=4096 the mean call time falls from ~143 to ~131 us)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-extras", action="store_true", help="headline only (no decode/block/long)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu baseline")
     ap.add_argument("--calib-copy", action="store_true",

@@ -540,11 +540,14 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
 struct ChainLds {
   static constexpr int kW = 0, kKd = 16384, kU0 = 32768, kSc = 36864;
   static constexpr int kSlot = 37888;               // 37 blocks of 1 KiB
-  static constexpr int kNSlot = 3;
+#ifndef GDN_CHAIN_SLOTS
+#define GDN_CHAIN_SLOTS 2
+#endif
+  static constexpr int kNSlot = GDN_CHAIN_SLOTS;
   static constexpr int kMf = kNSlot * kSlot;        // 2 x M fragments (fp16) [k step 8][lane 64] x 16 B
-  static constexpr int kUf = kMf + 2 * 8192;        // 2 x U fragments (fp16) [k step 4][lane 64] x 16 B
-  static constexpr int kSt = kUf + 2 * 4096;        // 64 x 32 bf16 output staging tile
-  static constexpr int kBytes = kSt + 4096;
+  static constexpr int kUf = kMf + 2 * 8192;        // 2 x U fragments (fp16) [k step 4][lane 64] x 16 B;
+                                                    // once read, a U buffer stages the output tile
+  static constexpr int kBytes = kUf + 2 * 4096;
 };
 constexpr int kSlotBlocks = 37;
 
@@ -726,14 +729,15 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
     for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(wsk_of(0) + i * 1024 + lane * 16);
 #pragma unroll
     for (int f = 0; f < FT; ++f) Bp[f] = *reinterpret_cast<const halfx8*>(wsh_of(0) + WH_P + f * 1024 + lane * 16);
-    unsigned char* sO = smem + L::kSt;
 
-    // O_c += U_c^T P_c^T, then the 64 x 32 bf16 tile is staged in LDS (64-byte rows,
-    // 16-byte units swizzled by the row so that the 4-column writes spread over the
-    // banks) and stored as 16-byte runs of 8 columns
+    // O_c += U_c^T P_c^T, then the 64 x 32 bf16 tile is staged in LDS over the U
+    // fragments just read (64-byte rows, 16-byte units swizzled by the row so that the
+    // 4-column writes spread over the banks) and stored as 16-byte runs of 8 columns.
+    // The state wave refills that U buffer only after the next barrier.
     auto finish = [&](floatx16 (&O)[2], int cp) {
+      unsigned char* sO = smem + L::kUf + (cp & 1) * 4096;
       {
-        const unsigned char* sUf = smem + L::kUf + (cp & 1) * 4096;
+        const unsigned char* sUf = sO;
         halfx8 Au[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) Au[ks] = *reinterpret_cast<const halfx8*>(sUf + ks * 1024 + lane * 16);
@@ -818,8 +822,11 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
     }
     if (nchunk > 0) finish(Op, nchunk - 1);
   } else {
+    // copies run kAhead = slots - 1 chunks ahead
+    constexpr int kAhead = L::kNSlot - 1;
+    static_assert(kAhead == 1 || kAhead == 2, "one or two chunks ahead");
     copy_chunk(0);
-    if (nchunk > 1) {
+    if (kAhead == 2 && nchunk > 1) {
       copy_chunk(1);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSlotBlocks));
     } else {
@@ -827,10 +834,11 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
     }
     __syncthreads();
     for (int cl = 0; cl < nchunk; ++cl) {
-      // slot (cl+2) % 3 was last read during chunk cl-1
-      if (cl + 2 < nchunk) {
-        copy_chunk(cl + 2);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSlotBlocks));  // chunk cl+1 has landed
+      // slot (cl + kAhead) % slots was last read during chunk cl-1
+      if (cl + kAhead < nchunk) {
+        copy_chunk(cl + kAhead);
+        // chunk cl+1 has landed
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kAhead - 1) * kSlotBlocks));
       } else {
         wait_vm_all();
       }
