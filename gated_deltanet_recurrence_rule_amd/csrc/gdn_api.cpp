@@ -65,8 +65,11 @@ gdn_status check_dims(const gdn_dims* d, bool T1) {
   return GDN_OK;
 }
 
+// The chunked kernels keep the gate vectors of all value heads of a key head in
+// LDS, which bounds the heads per key head at 64.
 bool use_chunk_kernel(const gdn_dims* d) {
-  return d->io == GDN_BF16 && d->Dk == 128 && d->T > 0 && !(d->flags & GDN_FLAG_TOKEN_SERIAL);
+  return d->io == GDN_BF16 && d->Dk == 128 && d->T > 0 && d->Hv / d->Hk <= 64 &&
+         !(d->flags & GDN_FLAG_TOKEN_SERIAL);
 }
 
 gdn::RecArgs rec_args(const gdn_dims* d, const void* q, const void* k, const void* v, const float* la,

@@ -135,8 +135,8 @@ struct PrepLds {
   static constexpr int kQ = CH * KP * 2;         // bf16 [64][KP]; later sT fp32 [64][FP]
   static constexpr int kV = 2 * CH * KP * 2;     // bf16 [64][KP]: V rows of the current value head
   static constexpr int kY = 3 * CH * KP * 2;     // fp32 2 x 16 x 20 (level 1 of the inverse)
-  static constexpr int kVec = kY + 2 * 16 * 20 * 4;  // rk, rq, g, beta, gamma rk, rk e^{g_63 - g}
-  static constexpr int kBytes = kVec + 6 * CH * 4;
+  static constexpr int kVec = kY + 2 * 16 * 20 * 4;  // rk, rq; per value head: g, beta, gamma rk, rk e^{g_63 - g}
+  static constexpr int bytes(int G) { return kVec + (2 + 4 * G) * CH * 4; }
 };
 static_assert(CH * FP * 4 <= CH * KP * 2, "sA and sT reuse the K and Q rows");
 
@@ -152,10 +152,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   float* sY = reinterpret_cast<float*>(smem + L::kY);
   float* vRk = reinterpret_cast<float*>(smem + L::kVec);
   float* vRq = vRk + CH;
-  float* vG = vRk + 2 * CH;
-  float* vBe = vRk + 3 * CH;
-  float* vKs = vRk + 4 * CH;
-  float* vKd = vRk + 5 * CH;
+  // gate vectors of value head j of this key head
+  auto vgate = [&](int j) { return vRk + (2 + 4 * j) * CH; };
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, h = lane >> 5;
@@ -169,11 +167,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   const uint16_t* gk = static_cast<const uint16_t*>(a.k);
   const uint16_t* gv = static_cast<const uint16_t*>(a.v);
 
-  // V rows and gates of a value head are loaded one head ahead, into registers
-  // (rows past the sequence end read the last valid row and are replaced by zeros);
-  // the first head's loads are issued before the K and Q rows are waited for
+  // V rows of a value head are loaded one head ahead, into registers (rows past
+  // the sequence end read the last valid row and are replaced by zeros); the first
+  // head's loads are issued before the K and Q rows are waited for.  Wave w takes
+  // the gates of value heads w, w+4, ...: the first are loaded here as well.
   u32x4 vr[4];
-  float la = 0.f, be = 0.f;
   auto load_head = [&](int hv) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -181,11 +179,14 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       const int rr = r < nval ? r : nval - 1;
       vr[m] = *reinterpret_cast<const u32x4*>(gv + (tokbase + rr) * a.sv + hv * DK + c8);
     }
-    const int tr = lane < nval ? lane : nval - 1;
-    la = a.la[(tokbase + tr) * a.Hv + hv];
-    be = a.beta[(tokbase + tr) * a.Hv + hv];
   };
   load_head(hk * a.G);
+  const int tr = lane < nval ? lane : nval - 1;
+  float la = 0.f, be = 0.f;
+  if (wv < a.G) {
+    la = a.la[(tokbase + tr) * a.Hv + hk * a.G + wv];
+    be = a.beta[(tokbase + tr) * a.Hv + hk * a.G + wv];
+  }
 
   // ---- K, Q rows and their norms ------------------------------------------
 #pragma unroll
@@ -217,6 +218,31 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
     }
   }
   __syncthreads();
+
+  // ---- gates of every value head: prefix sums and the row scalings ----------
+  for (int j = wv; j < a.G; j += 4) {
+    if (j != wv) {
+      la = a.la[(tokbase + tr) * a.Hv + hk * a.G + j];
+      be = a.beta[(tokbase + tr) * a.Hv + hk * a.G + j];
+    }
+    if (lane >= nval) la = be = 0.f;
+    float g = la;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float t = __shfl_up(g, off, 64);
+      if (lane >= off) g += t;
+    }
+    const float gl = __shfl(g, 63, 64);
+    const float eg = __expf(g);
+    float* vg = vgate(j);
+    vg[lane] = g;
+    vg[CH + lane] = be;
+    vg[2 * CH + lane] = eg * vRk[lane];
+    vg[3 * CH + lane] = __expf(gl - g) * vRk[lane];
+    float* sc = reinterpret_cast<float*>(ws + (static_cast<int64_t>(b * a.Hv + hk * a.G + j) * nwin + cl) * WH_BYTES + WH_SC);
+    sc[lane] = eg;
+    if (lane == 0) sc[64] = __expf(gl);
+  }
 
   // ---- Q^ = diag(rq) Q as the output product's A fragments (fp16) -----------
   //      tile rt*8+ks holds rows 32rt + (lane&31), k = 16ks + kperm
@@ -270,25 +296,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   for (int j = 0; j < a.G; ++j) {
     const int hv = hk * a.G + j;
     unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hv) * nwin + cl) * WH_BYTES;
-    // ---- gates: prefix sums and the row scalings --------------------------
-    if (wv == 0) {
-      if (lane >= nval) la = be = 0.f;
-      float g = la;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float t = __shfl_up(g, off, 64);
-        if (lane >= off) g += t;
-      }
-      const float gl = __shfl(g, 63, 64);
-      const float eg = __expf(g);
-      vG[lane] = g;
-      vBe[lane] = be;
-      vKs[lane] = eg * vRk[lane];
-      vKd[lane] = __expf(gl - g) * vRk[lane];
-      float* sc = reinterpret_cast<float*>(wsc + WH_SC);
-      sc[lane] = eg;
-      if (lane == 0) sc[64] = __expf(gl);
-    }
+    const float* vG = vgate(j);
+    const float* vBe = vG + CH;
+    const float* vKs = vG + 2 * CH;
+    const float* vKd = vG + 3 * CH;
+    // V rows of this head to LDS (read after two barriers), the next head's loads
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int vi = tid + 256 * m;
@@ -296,7 +308,6 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
           (vi >> 4) < nval ? vr[m] : u32x4{0u, 0u, 0u, 0u};
     }
     if (j + 1 < a.G) load_head(hv + 1);
-    __syncthreads();
     // ---- A (fp32, strictly lower) and the P fragments from the Gram tiles ----
     if (wv < 3) {
       {
@@ -525,7 +536,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
         *reinterpret_cast<halfx8*>(du + 2048 + 16 * s2) = x1;
       }
     }
-    __syncthreads();  // vG, vBe, vKs, vKd, sA, sT, sV are rewritten for the next value head
+    __syncthreads();  // sA, sT, sV are rewritten for the next value head
   }
 }
 
@@ -881,7 +892,7 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_prep_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::kBytes);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds::kBytes);
@@ -910,7 +921,7 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     const int nw = min(nwin, nchunks - c0);
     const bool last = c0 + nw >= nchunks;
     float* sout = last ? a.state_out : carry;
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3(nw, a.Hk, a.B), dim3(256), PrepLds::kBytes, s, a, c0, wsb, nwin);
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3(nw, a.Hk, a.B), dim3(256), PrepLds::bytes(a.G), s, a, c0, wsb, nwin);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(chunk_chain_kernel, dim3(a.B * a.Hv * (DK / 32)), dim3(192), ChainLds::kBytes, s, a, c0,

@@ -112,8 +112,9 @@ typedef struct {
  *   o          [B, T, Hv, Dv]  io dtype, token stride stride_o;
  *              o_t = S_t q_t with S_t after token t's update
  *   workspace, workspace_bytes  device scratch, see gdn_prefill_workspace_size
- * The bf16, Dk == Dv == 128 case runs the chunked MFMA kernels (chunks of
- * 64 tokens); other supported shapes run the token-serial kernel.
+ * The bf16, Dk == Dv == 128 case with at most 64 value heads per key head
+ * runs the chunked MFMA kernels (chunks of 64 tokens); other supported shapes
+ * run the token-serial kernel.
  * Alignment: bf16 with D == 128 needs q, k, v, o 16-byte aligned and strides
  * multiples of 8; states need 16-byte alignment.
  * o must not overlap q, k or v.

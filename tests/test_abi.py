@@ -51,6 +51,8 @@ def test_workspace_size():
     d = dims(T=64)
     d.flags = B.GDN_FLAG_TOKEN_SERIAL                   # token-serial path forced: none
     assert ws(d) == 0
+    assert ws(dims(T=64, Hk=1, Hv=64)) == 64 * 56320 + 16384   # 64 value heads per key head: chunked
+    assert ws(dims(T=64, Hk=1, Hv=65)) == 0             # more: token-serial, no workspace
 
 
 def test_version_and_struct_layout():
