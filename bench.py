@@ -192,8 +192,9 @@ def bench_block(dev, steps=5, warmup=2):
     return res
 
 
-def bench_long(dev, steps=3, warmup=1):
-    """Prefill at T = 262144 (batch 1, 16/48 heads), inputs drawn on the GPU."""
+def bench_long(dev, steps=3, warmup=4):
+    """Prefill at T = 262144 (batch 1, 16/48 heads), inputs drawn on the GPU.  Four
+    untimed calls (~45 ms) let the clocks settle first."""
     import torch
     from gated_deltanet_recurrence_rule_amd import binding as G
     B, T, Hk, Hv, D = 1, 262144, 16, 48, 128
