@@ -72,6 +72,8 @@ def lib():
         L.gdn_oracle_gated_rmsnorm.argtypes = [i64, i64, i32, p, i32, p, i32, p, ctypes.c_double,
                                                i64, p, p, i32]
         L.gdn_oracle_gated_rmsnorm.restype = ctypes.c_int
+        L.gdn_oracle_gates.argtypes = [i64, i64, i64, i32, p, i32, p, p, p, p]
+        L.gdn_oracle_gates.restype = ctypes.c_int
         L.gdn_oracle_round_bf16.argtypes = [p, p, i64]
         L.gdn_oracle_round_bf16.restype = None
         _lib = L
@@ -195,6 +197,30 @@ def gated_rmsnorm(x, z, w, eps: float, *, rows=None, n_threads=0):
     if rc != 0:
         raise ValueError("gdn_oracle_gated_rmsnorm rejected its arguments")
     return y
+
+
+def gates(ba, Hv: int, A_log, dt_bias):
+    """fp64 gate activation from raw in_proj_ba outputs (gdn_oracle.c, gdn_oracle_gates).
+    ba: [..., >= 2*Hv] (beta logits in [0, Hv), alpha inputs in [Hv, 2*Hv)); A_log, dt_bias:
+    [Hv] (same dtype).  Returns (log_alpha, beta), float64 [..., Hv]."""
+    ba = np.asarray(ba)
+    lead = ba.shape[:-1]
+    ba2 = ba.reshape(-1, ba.shape[-1])
+    if ba2.strides[-1] != ba2.itemsize:
+        ba2 = np.ascontiguousarray(ba2)
+    A_log = np.ascontiguousarray(A_log)
+    dt_bias = np.ascontiguousarray(dt_bias, dtype=A_log.dtype)
+    if A_log.shape != (Hv,) or dt_bias.shape != (Hv,):
+        raise ValueError("A_log and dt_bias must be [Hv]")
+    n = ba2.shape[0]
+    la = np.empty((n, Hv), np.float64)
+    be = np.empty((n, Hv), np.float64)
+    stride = ba2.strides[0] // ba2.itemsize if n > 1 else ba2.shape[1]
+    rc = lib().gdn_oracle_gates(n, Hv, stride, _code(ba2), _ptr(ba2), _code(A_log), _ptr(A_log), _ptr(dt_bias),
+                                _ptr(la), _ptr(be))
+    if rc != 0:
+        raise ValueError("gdn_oracle_gates rejected its arguments")
+    return la.reshape(lead + (Hv,)), be.reshape(lead + (Hv,))
 
 
 def round_bf16(a: np.ndarray) -> np.ndarray:

@@ -71,7 +71,7 @@ typedef struct {
   double q_scale, l2_eps;
 } gdn_oracle_dims;
 
-int gdn_oracle_abi_version(void) { return 1; }
+int gdn_oracle_abi_version(void) { return 2; }
 
 /* Per-token L2 normalisation of one head vector: x / sqrt(sum x^2 + eps). */
 static void l2_normalise(double* x, int64_t n, double eps) {
@@ -224,6 +224,35 @@ int gdn_oracle_conv1d_silu(int64_t B, int64_t T, int64_t C, int64_t K, int64_t x
           conv_state_out[(bb * C + c) * (K - 1) + j] = xv;
         }
   }
+  return 0;
+}
+
+/*
+ * Gate activation from the raw per-value-head outputs of the in_proj_ba
+ * projection ([HYB] table "Le decompte": in_proj_ba gives beta and alpha, one
+ * each per value head, 2 x Hv outputs per token, beta first; [HYB] section
+ * "La recurrence": alpha and beta lie in ]0,1[; [BRI] section 2 table: the
+ * sigmoid as the gate that squashes into ]0,1[ and softplus(x) = log(1+e^x)).
+ * The pages do not give alpha's activation; the layer recipe used for the
+ * inputs fixes log alpha = -exp(A_h) * softplus(a + dt_bias_h):
+ *     beta_t[h]      = sigmoid(ba[t][h])
+ *     log_alpha_t[h] = -exp(A_log[h]) * log(1 + exp(ba[t][Hv + h] + dt_bias[h]))
+ * ba is [n_tok][stride] (element stride between tokens); A_log and dt_bias
+ * are [Hv]; outputs are [n_tok][Hv].
+ */
+int gdn_oracle_gates(int64_t n_tok, int64_t Hv, int64_t stride, int32_t ba_dtype, const void* ba,
+                     int32_t p_dtype, const void* A_log, const void* dt_bias, double* log_alpha,
+                     double* beta) {
+  if (n_tok < 0 || Hv < 1 || stride < 2 * Hv || !A_log || !dt_bias || (n_tok > 0 && (!ba || !log_alpha || !beta)))
+    return -1;
+  for (int64_t t = 0; t < n_tok; ++t)
+    for (int64_t h = 0; h < Hv; ++h) {
+      const double b = ld(ba, ba_dtype, t * stride + h);
+      const double a = ld(ba, ba_dtype, t * stride + Hv + h);
+      beta[t * Hv + h] = sigmoid(b);
+      /* log1p(e^x) is log(1 + e^x) without rounding 1 + e^x (exact enough down to x ~ -745) */
+      log_alpha[t * Hv + h] = -exp(ld(A_log, p_dtype, h)) * log1p(exp(a + ld(dt_bias, p_dtype, h)));
+    }
   return 0;
 }
 

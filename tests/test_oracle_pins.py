@@ -386,3 +386,48 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(oracle.round_bf16(a.astype(np.float64)), ref)
     from gated_deltanet_recurrence_rule_amd.workloads import f32_to_bf16
     np.testing.assert_array_equal(f32_to_bf16(a), ref)
+
+
+def test_gate_activation_closed_forms():
+    """Gates from raw in_proj_ba outputs: beta = sigmoid(b), log alpha = -exp(A) softplus(a + dt)
+    (page "Les briques d'un reseau de neurones", section 2 table: sigmoid and softplus; page
+    "L'attention hybride", table "Le decompte": in_proj_ba gives beta then alpha per value head)."""
+    Hv = 3
+    A = np.log(np.array([1.0, 4.0, 16.0]))
+    dt = np.array([0.0, 0.5, -1.0])
+    # a + dt = 0 and b = 0: softplus(0) = ln 2, sigmoid(0) = 1/2
+    ba = np.concatenate([np.zeros(Hv), -dt])[None]
+    la, be = oracle.gates(ba, Hv, A, dt)
+    np.testing.assert_allclose(la[0], -np.array([1.0, 4.0, 16.0]) * np.log(2.0), rtol=1e-15)
+    assert np.all(be == 0.5)
+    # worked values, written out: sigmoid(3) = 0.95257412682243..., softplus(1) = 1.31326168751822...
+    # (A = 0 on head 0), and the block order: b (beta logits) first, a second
+    ba = np.array([[3.0, 0.0, 0.0, 1.0, 0.0, 0.0]])
+    la, be = oracle.gates(ba, Hv, np.zeros(Hv), np.zeros(Hv))
+    assert abs(be[0, 0] - 0.9525741268224334) < 1e-15
+    assert abs(la[0, 0] + 1.3132616875182228) < 1e-15
+    # identities: softplus(x) - softplus(-x) = x, sigmoid(x) + sigmoid(-x) = 1
+    x = np.linspace(-30.0, 30.0, 121)
+    pos = np.concatenate([np.repeat(x[:, None], Hv, 1), np.repeat(x[:, None], Hv, 1)], 1)
+    neg = -pos
+    la_p, be_p = oracle.gates(pos, Hv, np.zeros(Hv), np.zeros(Hv))
+    la_n, be_n = oracle.gates(neg, Hv, np.zeros(Hv), np.zeros(Hv))
+    np.testing.assert_allclose(-la_p + la_n, np.repeat(x[:, None], Hv, 1), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(be_p + be_n, 1.0, rtol=0, atol=1e-15)
+    # limits: softplus(x) -> x for large x, -> e^x for very negative x
+    ba = np.array([[0.0, 0.0, 0.0, 40.0, -40.0, -700.0]])
+    la, _ = oracle.gates(ba, Hv, np.zeros(Hv), np.zeros(Hv))
+    np.testing.assert_allclose(-la[0], [40.0, np.exp(-40.0), np.exp(-700.0)], rtol=1e-14)
+    # ranges: beta in ]0,1[, log alpha < 0, decreasing in a; bf16 inputs are widened exactly
+    rng = np.random.default_rng(31)
+    raw = rng.standard_normal((50, 2 * Hv)) * 4
+    la, be = oracle.gates(raw, Hv, A, dt)
+    assert np.all((be > 0) & (be < 1)) and np.all(la < 0)
+    la2, _ = oracle.gates(raw + np.concatenate([np.zeros(Hv), np.full(Hv, 0.25)]), Hv, A, dt)
+    assert np.all(la2 < la)
+    bits = oracle.round_bf16(raw)
+    from gated_deltanet_recurrence_rule_amd.workloads import bf16_to_f32
+    la_b, be_b = oracle.gates(bits, Hv, A, dt)
+    la_f, be_f = oracle.gates(bf16_to_f32(bits).astype(np.float64), Hv, A, dt)
+    np.testing.assert_array_equal(la_b, la_f)
+    np.testing.assert_array_equal(be_b, be_f)
