@@ -21,7 +21,7 @@ GDN_FLAG_TOKEN_SERIAL = 2
 
 # Every exported symbol, in the order include/gdn.h declares them.
 EXPORTS = ("gdn_prefill", "gdn_prefill_workspace_size", "gdn_decode_step", "gdn_conv1d_silu",
-           "gdn_gated_rmsnorm", "gdn_last_error", "gdn_version")
+           "gdn_gated_rmsnorm", "gdn_gates", "gdn_decode_token", "gdn_last_error", "gdn_version")
 
 
 class GdnDims(ctypes.Structure):
@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_conv1d_silu.restype = ctypes.c_int
         L.gdn_gated_rmsnorm.argtypes = [i64, i32, i32, i32, p, i64, p, i64, p, ctypes.c_float, p, i64, p]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
+        L.gdn_gates.argtypes = [i64, i32, i32, p, i64, p, p, p, p, p]
+        L.gdn_gates.restype = ctypes.c_int
+        L.gdn_decode_token.argtypes = [ctypes.POINTER(GdnDims), p, p, p, i32, p, i64, p, p, p, p, p, p]
+        L.gdn_decode_token.restype = ctypes.c_int
         L.gdn_last_error.argtypes = []
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -229,6 +233,68 @@ def gdn_gated_rmsnorm(x, z, w, eps: float = 1e-5, y=None, *, H: int, stream=None
                                    z.stride(0) if n > 1 else H * D, _ptr(w), float(eps), _ptr(y),
                                    y.stride(0) if n > 1 else H * D, _stream(stream)))
     return y
+
+
+def _params(A_log, dt_bias, Hv: int):
+    import torch
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (Hv,):
+            raise ValueError(f"{name} must be contiguous fp32 [Hv]")
+
+
+def gdn_gates(ba, A_log, dt_bias, log_alpha=None, beta=None, *, Hv: int, stream=None):
+    """ba: [n_tok, >=2*Hv] raw in_proj_ba outputs (bf16 or fp32, contiguous columns; beta
+    logits first); A_log, dt_bias: [Hv] fp32.  Returns (log_alpha, beta), [n_tok, Hv] fp32."""
+    import torch
+    n = int(ba.shape[0])
+    if ba.dim() != 2 or ba.shape[1] < 2 * Hv or (n > 0 and ba.stride(1) != 1):
+        raise ValueError(f"ba: expected [n_tok, >={2 * Hv}] with contiguous columns")
+    _params(A_log, dt_bias, Hv)
+    if log_alpha is None:
+        log_alpha = torch.empty((n, Hv), dtype=torch.float32, device=ba.device)
+    if beta is None:
+        beta = torch.empty((n, Hv), dtype=torch.float32, device=ba.device)
+    for name, g in (("log_alpha", log_alpha), ("beta", beta)):
+        if g.dtype != torch.float32 or not g.is_contiguous() or g.numel() != n * Hv:
+            raise ValueError(f"{name} must be contiguous fp32 with n_tok * Hv elements")
+    _check(lib().gdn_gates(n, Hv, _io(ba), _ptr(ba), ba.stride(0) if n > 1 else 2 * Hv, _ptr(A_log),
+                           _ptr(dt_bias), _ptr(log_alpha), _ptr(beta), _stream(stream)))
+    return log_alpha, beta
+
+
+def gdn_decode_token(q, k, v, ba, A_log, dt_bias, state_pool, slots=None, o=None, *, Hk: int, Hv: int,
+                     l2norm: bool = False, l2_eps: float = 1e-6, q_scale: float = 1.0, stream=None):
+    """One decode token per sequence with gates formed from the raw in_proj_ba outputs
+    ba [B, >=2*Hv] (bf16 or fp32) and A_log, dt_bias [Hv] fp32, and states in a pool
+    state_pool [S, Hv, D, D] fp32 (updated in place): sequence b uses entry slots[b]
+    (slots: [B] int32 device tensor; None = entry b; negative = skipped).
+    q, k: [B, >=Hk*D]; v: [B, >=Hv*D]; o: [B, >=Hv*D] or None.  Returns o."""
+    import torch
+    B = int(q.shape[0])
+    D = int(state_pool.shape[2])
+    io = _io(q)
+    if o is None:
+        o = torch.empty((B, Hv * D), dtype=q.dtype, device=q.device)
+    for name, t, w in (("q", q, Hk * D), ("k", k, Hk * D), ("v", v, Hv * D), ("o", o, Hv * D),
+                       ("ba", ba, 2 * Hv)):
+        if t.dim() != 2 or t.shape[0] != B or t.shape[1] < w or t.stride(1) != 1:
+            raise ValueError(f"{name}: expected [B, >={w}] with contiguous rows")
+    _params(A_log, dt_bias, Hv)
+    if (state_pool.dtype != torch.float32 or not state_pool.is_contiguous() or state_pool.dim() != 4
+            or tuple(state_pool.shape[1:]) != (Hv, D, D)):
+        raise ValueError("state_pool must be contiguous fp32 [S, Hv, D, D]")
+    if slots is None and state_pool.shape[0] < B:
+        raise ValueError("without slots the pool needs at least B entries")
+    if slots is not None and (slots.dtype != torch.int32 or not slots.is_contiguous() or tuple(slots.shape) != (B,)):
+        raise ValueError("slots must be a contiguous int32 [B] tensor")
+    dims = make_dims(B, 1, Hk, Hv, D, io, GDN_FLAG_QK_L2NORM if l2norm else 0,
+                     q.stride(0) if B > 1 else Hk * D, k.stride(0) if B > 1 else Hk * D,
+                     v.stride(0) if B > 1 else Hv * D, o.stride(0) if B > 1 else Hv * D,
+                     q_scale, l2_eps)
+    _check(lib().gdn_decode_token(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _io(ba), _ptr(ba),
+                                  ba.stride(0) if B > 1 else 2 * Hv, _ptr(A_log), _ptr(dt_bias),
+                                  _ptr(state_pool), _ptr(slots), _ptr(o), _stream(stream)))
+    return o
 
 
 def gdn_version() -> int:

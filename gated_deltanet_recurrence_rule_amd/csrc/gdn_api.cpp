@@ -228,8 +228,59 @@ gdn_status gdn_gated_rmsnorm(int64_t n_tok, int32_t H, int32_t D, int32_t dtype,
   return from_hip(gdn::launch_gated_rmsnorm(a, dtype, static_cast<hipStream_t>(stream)), "gdn_gated_rmsnorm");
 }
 
+gdn_status gdn_gates(int64_t n_tok, int32_t Hv, int32_t dtype, const void* ba, int64_t stride_ba,
+                     const float* A_log, const float* dt_bias, float* log_alpha, float* beta, void* stream) {
+  if (n_tok < 0 || Hv < 1) return fail(GDN_ERR_SHAPE, "n_tok=%lld Hv=%d", (long long)n_tok, Hv);
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_SHAPE, "dtype %d unknown", dtype);
+  if (stride_ba < 2 * static_cast<int64_t>(Hv))
+    return fail(GDN_ERR_SHAPE, "stride_ba=%lld below 2*Hv=%d", (long long)stride_ba, 2 * Hv);
+  if (n_tok == 0) return ok();
+  if (!ba || !A_log || !dt_bias || !log_alpha || !beta)
+    return fail(GDN_ERR_NULL, "ba, A_log, dt_bias, log_alpha and beta are required");
+  if (!aligned(ba, dtype == GDN_BF16 ? 2 : 4) || !aligned(A_log, 4) || !aligned(dt_bias, 4) ||
+      !aligned(log_alpha, 4) || !aligned(beta, 4))
+    return fail(GDN_ERR_ALIGN, "pointers must be aligned to their element size");
+  gdn::GateArgs a;
+  a.n_tok = n_tok;
+  a.Hv = Hv;
+  a.sba = stride_ba;
+  a.ba = ba;
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.la = log_alpha;
+  a.beta = beta;
+  return from_hip(gdn::launch_gates(a, dtype, static_cast<hipStream_t>(stream)), "gdn_gates");
+}
+
+gdn_status gdn_decode_token(const gdn_dims* d, const void* q, const void* k, const void* v, int32_t ba_dtype,
+                            const void* ba, int64_t stride_ba, const float* A_log, const float* dt_bias,
+                            float* state_pool, const int32_t* slots, void* o, void* stream) {
+  gdn_status st = check_dims(d, true);
+  if (st != GDN_OK) return st;
+  if (ba_dtype != GDN_F32 && ba_dtype != GDN_BF16) return fail(GDN_ERR_SHAPE, "ba dtype %d unknown", ba_dtype);
+  if (stride_ba < 2 * static_cast<int64_t>(d->Hv))
+    return fail(GDN_ERR_SHAPE, "stride_ba=%lld below 2*Hv=%d", (long long)stride_ba, 2 * d->Hv);
+  if (d->B == 0) return ok();
+  if (!q || !k || !v || !ba || !A_log || !dt_bias || !state_pool || !o)
+    return fail(GDN_ERR_NULL, "q, k, v, ba, A_log, dt_bias, state_pool and o are required");
+  if (!aligned(state_pool, 16)) return fail(GDN_ERR_ALIGN, "state_pool must be 16-byte aligned");
+  const size_t es = d->io == GDN_BF16 ? 2 : 4;
+  if (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(o, es) ||
+      !aligned(ba, ba_dtype == GDN_BF16 ? 2 : 4) || !aligned(A_log, 4) || !aligned(dt_bias, 4) ||
+      !aligned(slots, 4))
+    return fail(GDN_ERR_ALIGN, "pointers must be aligned to their element size");
+  gdn::RecArgs a = rec_args(d, q, k, v, nullptr, nullptr, state_pool, state_pool, o);
+  a.ba = ba;
+  a.sba = stride_ba;
+  a.ba_io = ba_dtype;
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.slots = slots;
+  return from_hip(gdn::launch_recurrent(a, d->io, static_cast<hipStream_t>(stream)), "gdn_decode_token");
+}
+
 const char* gdn_last_error(void) { return g_err; }
 
-int32_t gdn_version(void) { return 100; /* 0.1.0 */ }
+int32_t gdn_version(void) { return 200; /* 0.2.0 */ }
 
 }  // extern "C"

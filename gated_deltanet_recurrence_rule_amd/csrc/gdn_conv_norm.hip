@@ -12,6 +12,10 @@
 // D-row ("Les briques", section 4; "L'attention hybride", swish output gate
 // and one 128-weight norm shared by the heads).  D/8 lanes own one row, 8
 // elements each, and reduce the sum of squares with lane shuffles.
+//
+// gates: beta and log alpha of every (token, value head) from the raw
+// in_proj_ba outputs ("L'attention hybride", table "Le decompte": one beta and
+// one alpha per value head, beta first), one element per thread.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -151,7 +155,31 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(NormArgs a) {
   if (live) Vec8<IO>::store(a.y, t * a.sy + static_cast<int64_t>(h) * D + c, y);
 }
 
+template <typename IO>
+__global__ __launch_bounds__(256) void gates_kernel(GateArgs a) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= a.n_tok * a.Hv) return;
+  const int64_t t = i / a.Hv;
+  const int h = static_cast<int>(i - t * a.Hv);
+  float la, be;
+  gate_activation(IoTraits<IO>::load(a.ba, t * a.sba + h), IoTraits<IO>::load(a.ba, t * a.sba + a.Hv + h),
+                  a.A_log[h], a.dt_bias[h], la, be);
+  a.la[i] = la;
+  a.beta[i] = be;
+}
+
 }  // namespace
+
+hipError_t launch_gates(const GateArgs& a, int io, hipStream_t s) {
+  const int64_t n = a.n_tok * a.Hv;
+  if (n == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  if (io == 1)
+    hipLaunchKernelGGL(gates_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(gates_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_conv1d_silu(const ConvArgs& a, int io, hipStream_t s) {
   const int groups = (a.C + 7) / 8;

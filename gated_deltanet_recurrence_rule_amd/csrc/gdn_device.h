@@ -55,4 +55,18 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// Gate activation of one value head from its raw in_proj_ba outputs b (beta
+// logit) and a (alpha input): beta = sigmoid(b), log alpha = -exp(A_log) *
+// softplus(a + dt_bias) ("Les briques d'un reseau de neurones", section 2
+// table: sigmoid and softplus(x) = log(1 + e^x); the alpha recipe of the layer
+// inputs).  softplus is evaluated as max(x, 0) + log1p(e^-|x|) and sigmoid
+// from e^-|x|, so neither overflows.
+__device__ __forceinline__ void gate_activation(float b, float a, float A_log, float dt_bias, float& log_alpha,
+                                                float& beta) {
+  const float eb = __expf(-fabsf(b));
+  beta = b >= 0.f ? 1.0f / (1.0f + eb) : eb / (1.0f + eb);
+  const float x = a + dt_bias;
+  log_alpha = -__expf(A_log) * (fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))));
+}
+
 }  // namespace gdn

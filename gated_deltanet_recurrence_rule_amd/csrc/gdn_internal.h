@@ -22,6 +22,17 @@ struct RecArgs {
   const float* state_in;   // may be null (zero state)
   float* state_out;        // may be null
   void* o;
+  // Token-serial kernel only.  When ba is set, the gates are formed from the raw
+  // in_proj_ba outputs ([token][sba], beta logits at [0, Hv), alpha inputs at
+  // [Hv, 2 Hv), dtype ba_io) with A_log and dt_bias [Hv], instead of read from
+  // la / beta.  When slots is set, row b of the batch keeps its state in entry
+  // slots[b] of state_in / state_out (a pool); a negative slot skips the row.
+  const void* ba = nullptr;
+  int64_t sba = 0;
+  int32_t ba_io = 0;
+  const float* A_log = nullptr;
+  const float* dt_bias = nullptr;
+  const int32_t* slots = nullptr;
 };
 
 // io: 0 = fp32, 1 = bf16 (same codes as gdn_dtype).
@@ -58,5 +69,17 @@ struct NormArgs {
   void* y;
 };
 hipError_t launch_gated_rmsnorm(const NormArgs& a, int io, hipStream_t s);
+
+struct GateArgs {
+  int64_t n_tok;
+  int32_t Hv;
+  int64_t sba;
+  const void* ba;
+  const float* A_log;
+  const float* dt_bias;
+  float* la;
+  float* beta;
+};
+hipError_t launch_gates(const GateArgs& a, int io, hipStream_t s);
 
 }  // namespace gdn

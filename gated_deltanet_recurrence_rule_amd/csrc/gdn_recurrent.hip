@@ -50,10 +50,17 @@ __global__ __launch_bounds__(RecShape<D>::NT) void recurrent_kernel(RecArgs a) {
   const int tid = threadIdx.x;
   const int cg = tid % TPR, rg = tid / TPR;
   const int c0 = cg * 4;
+  // state entry of this (sequence, head): its own, or pool slot slots[b]
+  int64_t sidx = bh;
+  if (a.slots) {
+    const int slot = a.slots[b];
+    if (slot < 0) return;  // the whole workgroup skips the row
+    sidx = static_cast<int64_t>(slot) * a.Hv + h;
+  }
 
   floatx4 M[RPT];
   if (a.state_in) {
-    const float* sp = a.state_in + static_cast<int64_t>(bh) * D * D;
+    const float* sp = a.state_in + sidx * D * D;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) M[r] = *reinterpret_cast<const floatx4*>(sp + (rg + RG * r) * D + c0);
   } else {
@@ -94,8 +101,21 @@ __global__ __launch_bounds__(RecShape<D>::NT) void recurrent_kernel(RecArgs a) {
       }
       if (tid == 0) {
         s_scal[0] = sqk * rq * rk;  // (k^ . q^)
-        s_scal[1] = __expf(a.la[tok * a.Hv + h]);
-        s_scal[2] = a.beta[tok * a.Hv + h];
+        if (a.ba) {
+          float la, be;
+          const int64_t r = tok * a.sba;
+          if (a.ba_io == 1)
+            gate_activation(IoTraits<uint16_t>::load(a.ba, r + h), IoTraits<uint16_t>::load(a.ba, r + a.Hv + h),
+                            a.A_log[h], a.dt_bias[h], la, be);
+          else
+            gate_activation(IoTraits<float>::load(a.ba, r + h), IoTraits<float>::load(a.ba, r + a.Hv + h),
+                            a.A_log[h], a.dt_bias[h], la, be);
+          s_scal[1] = __expf(la);
+          s_scal[2] = be;
+        } else {
+          s_scal[1] = __expf(a.la[tok * a.Hv + h]);
+          s_scal[2] = a.beta[tok * a.Hv + h];
+        }
       }
     }
     __syncthreads();
@@ -133,7 +153,7 @@ __global__ __launch_bounds__(RecShape<D>::NT) void recurrent_kernel(RecArgs a) {
   }
 
   if (a.state_out) {
-    float* sp = a.state_out + static_cast<int64_t>(bh) * D * D;
+    float* sp = a.state_out + sidx * D * D;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) *reinterpret_cast<floatx4*>(sp + (rg + RG * r) * D + c0) = M[r];
   }

@@ -192,6 +192,48 @@ gdn_status gdn_gated_rmsnorm(int64_t n_tok, int32_t H, int32_t D, int32_t dtype,
                              int64_t stride_x, const void* z, int64_t stride_z, const void* w,
                              float eps, void* y, int64_t stride_y, void* stream);
 
+/*
+ * gdn_gates -- beta and log alpha of every (token, value head) from the raw
+ * outputs of the in_proj_ba projection ("L'attention hybride", table "Le
+ * decompte": one beta and one alpha per value head, 2*Hv outputs per token,
+ * beta first; "Les briques", section 2 table: sigmoid, softplus(x) =
+ * log(1 + e^x)).  The pages leave alpha's activation open; the layer recipe
+ * log alpha = -exp(A_log) * softplus(a + dt_bias) is used:
+ *     beta[t][h]      = sigmoid(ba[t][h])
+ *     log_alpha[t][h] = -exp(A_log[h]) * softplus(ba[t][Hv + h] + dt_bias[h])
+ *   ba        [n_tok, stride_ba] dtype (stride_ba >= 2*Hv), element-aligned
+ *   A_log, dt_bias [Hv] fp32 (per-head parameters of the layer)
+ *   log_alpha, beta [n_tok, Hv] fp32, contiguous: the gate inputs of
+ *                   gdn_prefill and gdn_decode_step
+ * fp32 arithmetic; softplus and sigmoid are evaluated without overflow for
+ * any finite input.  n_tok == 0 is a no-op.
+ */
+gdn_status gdn_gates(int64_t n_tok, int32_t Hv, int32_t dtype, const void* ba, int64_t stride_ba,
+                     const float* A_log, const float* dt_bias, float* log_alpha, float* beta, void* stream);
+
+/*
+ * gdn_decode_token -- one decode token per sequence, for a serving loop
+ * ("Chapitre 16", 16.3: decode reads the fixed per-request state, produces
+ * the token's output and updates the state; 16.2 and "L'etat, en memoire":
+ * the state is per request and has a fixed size).  Same step as
+ * gdn_decode_step, with two differences:
+ *   - the gates are formed in the kernel from the raw in_proj_ba outputs
+ *     exactly as gdn_gates does: ba [B, stride_ba] in ba_dtype (bf16 or
+ *     fp32), A_log and dt_bias [Hv] fp32;
+ *   - the states live in a caller-owned pool state_pool [S, Hv, Dk, Dv] fp32
+ *     (16-byte aligned): sequence b uses entry slots[b] (slots: [B] int32,
+ *     device memory), or entry b when slots is NULL.  A negative slot skips
+ *     the sequence: neither its state nor its output row is touched.  Two
+ *     sequences of one call must not share a slot (their updates would race).
+ *     Slot values are not checked against S on the host (they are device
+ *     data): every non-negative slot must be < S.
+ * dims->T must be 1; q, k, v, o and flags (GDN_FLAG_QK_L2NORM) as for
+ * gdn_decode_step.
+ */
+gdn_status gdn_decode_token(const gdn_dims* dims, const void* q, const void* k, const void* v, int32_t ba_dtype,
+                            const void* ba, int64_t stride_ba, const float* A_log, const float* dt_bias,
+                            float* state_pool, const int32_t* slots, void* o, void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  The string
  * is owned by the library and valid until the next call on this thread. */
 const char* gdn_last_error(void);

@@ -56,7 +56,7 @@ def test_workspace_size():
 
 
 def test_version_and_struct_layout():
-    assert B.gdn_version() == 100
+    assert B.gdn_version() == 200
     # gdn_dims: 8 x int32, 4 x int64, 2 x float -> 72 bytes with natural alignment
     assert ctypes.sizeof(B.GdnDims) == 72
     assert B.GdnDims.stride_q.offset == 32 and B.GdnDims.q_scale.offset == 64
@@ -155,6 +155,35 @@ def test_conv_and_norm_argument_errors():
     assert norm(z=None) == B.GDN_ERR_NULL
     assert norm(y=FAKE_ODD) == B.GDN_ERR_ALIGN
     assert norm(n=0) == B.GDN_OK
+
+
+def test_gates_and_decode_token_argument_errors():
+    L = B.lib()
+
+    def gates(**kw):
+        return L.gdn_gates(kw.get("n", 4), kw.get("Hv", 48), kw.get("dt", B.GDN_BF16), kw.get("ba", FAKE),
+                           kw.get("s", 96), kw.get("A", FAKE), kw.get("dtb", FAKE), kw.get("la", FAKE),
+                           kw.get("be", FAKE), None)
+    assert gates(Hv=0) == B.GDN_ERR_SHAPE
+    assert gates(n=-1) == B.GDN_ERR_SHAPE
+    assert gates(s=95) == B.GDN_ERR_SHAPE                    # stride below 2*Hv
+    assert gates(dt=7) == B.GDN_ERR_SHAPE
+    assert gates(A=None) == B.GDN_ERR_NULL
+    assert gates(la=FAKE_ODD) == B.GDN_ERR_ALIGN
+    assert gates(n=0, ba=None) == B.GDN_OK                   # nothing to do
+
+    def tok(d, **kw):
+        return L.gdn_decode_token(ctypes.byref(d), FAKE, FAKE, FAKE, kw.get("bdt", B.GDN_BF16), kw.get("ba", FAKE),
+                                  kw.get("s", 12), kw.get("A", FAKE), kw.get("dtb", FAKE), kw.get("pool", FAKE),
+                                  kw.get("slots", None), FAKE, None)
+    assert tok(dims(T=2)) == B.GDN_ERR_SHAPE                  # one token per sequence
+    assert tok(dims(T=1), s=11) == B.GDN_ERR_SHAPE            # stride_ba below 2*Hv (Hv = 6)
+    assert tok(dims(T=1), bdt=5) == B.GDN_ERR_SHAPE
+    assert tok(dims(T=1), pool=None) == B.GDN_ERR_NULL
+    assert tok(dims(T=1), dtb=None) == B.GDN_ERR_NULL
+    assert tok(dims(T=1), pool=ctypes.c_void_p(0x10008)) == B.GDN_ERR_ALIGN
+    assert tok(dims(T=1), slots=FAKE_ODD) == B.GDN_ERR_ALIGN
+    assert tok(dims(T=1, B=0)) == B.GDN_OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -298,3 +298,111 @@ def test_gated_rmsnorm_parity(io, H, D):
     G.gdn_gated_rmsnorm(xd, zd, to_dev(wh), 1e-5, y=xd, H=H)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_host(xd).reshape(n * H, D), yg)
+
+
+def _raw_ba(seed, n, Hv):
+    """Raw in_proj_ba outputs: N(0, 2^2) draws plus fixed extreme values on the first rows."""
+    rng = np.random.default_rng(seed)
+    ba = (rng.standard_normal((n, 2 * Hv)) * 2.0).astype(np.float32)
+    ext = np.array([0.0, 40.0, -40.0, 100.0, -100.0, 7.5, -7.5, 1e-3], np.float32)
+    for i, x in enumerate(ext[: min(n, ext.size)]):
+        ba[i, :] = x
+    return ba
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_gates_parity(io):
+    """gdn_gates against the oracle's fp64 activation.  fp32 arithmetic: the fast exponential
+    scales its argument by log2(e) in fp32, so e^x carries a relative error up to about
+    |x| * 2^-24; with |x| <= 100 here every output is within 1e-5 relative."""
+    torch = _torch()
+    n, Hv = 1003, 48
+    rng = np.random.default_rng(51)
+    A = np.log(rng.uniform(1.0, 16.0, Hv)).astype(np.float32)
+    dt = (rng.standard_normal(Hv) * 0.5).astype(np.float32)
+    ba = _raw_ba(52, n, Hv)
+    if io == "bf16":
+        ba = W.f32_to_bf16(ba)
+    # a strided view: rows of 2*Hv + 8 elements
+    pad = np.zeros((n, 2 * Hv + 8), ba.dtype)
+    pad[:, : 2 * Hv] = ba
+    dev = to_dev(pad)[:, : 2 * Hv]
+    la, be = G.gdn_gates(dev, to_dev(A), to_dev(dt), Hv=Hv)
+    torch.cuda.synchronize()
+    la_ref, be_ref = oracle.gates(ba, Hv, A, dt)
+    np.testing.assert_allclose(to_host(la), la_ref, rtol=1e-5, atol=1e-37)
+    np.testing.assert_allclose(to_host(be), be_ref, rtol=1e-5, atol=1e-37)
+    assert np.all(to_host(la) <= 0) and np.all((to_host(be) >= 0) & (to_host(be) <= 1))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("l2", [False, True])
+@pytest.mark.parametrize("ba_io", ["bf16", "f32"])
+def test_decode_token_gates_and_slots(l2, ba_io):
+    """gdn_decode_token: gates formed in the kernel from raw in_proj_ba outputs, states in a
+    pool addressed by a slot table (a permutation with one skipped sequence), against the oracle's
+    activation followed by its recurrence on the gathered states; untouched pool entries and the
+    skipped output row must stay bit-identical."""
+    torch = _torch()
+    B, Hk, Hv, D, S, steps = 5, 2, 6, 128, 8, 3
+    slots = np.array([6, -1, 2, 0, 7], np.int32)
+    rng = np.random.default_rng(53)
+    A = np.log(rng.uniform(1.0, 16.0, Hv)).astype(np.float32)
+    dt = (rng.standard_normal(Hv) * 0.5).astype(np.float32)
+    p = W.problem(5100, B, steps, Hk, Hv, D, io="bf16", recipe="qwen", state="normal", normalise=not l2)
+    pool = (rng.standard_normal((S, Hv, D, D)) * 0.02).astype(np.float32)
+    pool_dev = to_dev(pool)
+    ref_pool = pool.astype(np.float64)
+    q, k, v = to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"])
+    for s in range(steps):
+        ba = _raw_ba(5200 + s, B, Hv)
+        ba_in = W.f32_to_bf16(ba) if ba_io == "bf16" else ba
+        o = torch.full((B, Hv * D), 7.0, dtype=torch.bfloat16, device="cuda")
+        G.gdn_decode_token(q[:, s].contiguous(), k[:, s].contiguous(), v[:, s].contiguous(), to_dev(ba_in),
+                           to_dev(A), to_dev(dt), pool_dev, to_dev(slots), o, Hk=Hk, Hv=Hv, l2norm=l2)
+        torch.cuda.synchronize()
+        la, be = oracle.gates(ba_in, Hv, A, dt)
+        live = slots >= 0
+        c = np.ascontiguousarray
+        sl = slice(s, s + 1)
+        orf, srf = oracle.recurrence(c(p["q"][live][:, sl]), c(p["k"][live][:, sl]), c(p["v"][live][:, sl]),
+                                     c(la[live][:, None]), c(be[live][:, None]), Hk, Hv,
+                                     c(ref_pool[slots[live]]), l2norm=l2, l2_eps=1e-6)
+        ref_pool[slots[live]] = srf.reshape(-1, Hv, D, D)
+        oh = to_host(o).reshape(B, Hv, D)
+        assert_out(oh[live], orf.reshape(-1, Hv, D), bf16=True)
+        assert np.all(oh[~live] == 7.0)
+        ph = to_host(pool_dev)
+        for sidx in range(S):
+            if sidx in slots[live]:
+                assert_state(ph[sidx], ref_pool[sidx])
+            else:
+                np.testing.assert_array_equal(ph[sidx], pool[sidx])
+
+
+@pytest.mark.gpu
+def test_conv_single_token_steps_roll_the_window():
+    """Decode front end: T single-token conv calls, each handing its 3-input window to the next,
+    equal one conv over the T tokens (and the oracle)."""
+    torch = _torch()
+    B, T, C = 3, 9, 10240
+    rng = np.random.default_rng(54)
+    x = W.f32_to_bf16(rng.standard_normal((B, T, C)).astype(np.float32))
+    w = W.f32_to_bf16((rng.standard_normal((C, 4)) * 0.5).astype(np.float32))
+    cs0 = W.f32_to_bf16(rng.standard_normal((B, C, 3)).astype(np.float32))
+    xd, wd = to_dev(x), to_dev(w)
+    full = G.gdn_conv1d_silu(xd, wd, to_dev(cs0))
+    cs = to_dev(cs0)
+    steps = []
+    for t in range(T):
+        nxt = torch.empty_like(cs)
+        steps.append(G.gdn_conv1d_silu(xd[:, t:t + 1], wd, cs, nxt))
+        cs = nxt
+    torch.cuda.synchronize()
+    y_steps = np.concatenate([to_host(y) for y in steps], axis=1)
+    np.testing.assert_array_equal(y_steps, to_host(full))
+    ref = np.stack([oracle.conv1d_silu(x, w, cs0, b=b)[0] for b in range(B)])
+    assert_out(y_steps, ref, bf16=True)
+    # the window handed on after the last step holds the last three inputs, oldest first
+    np.testing.assert_array_equal(to_host(cs), W.bf16_to_f32(np.ascontiguousarray(x[:, T - 3:].transpose(0, 2, 1))))
