@@ -136,6 +136,61 @@ def bench_decode(dev, n_steps=256, pools=1):
                 bytes_per_step=per, GBs=per / (med_ms * 1e-3) / 1e9)
 
 
+def bench_decode_front(dev, n_steps=256, n_inputs=32):
+    """One layer's decode token for 64 sequences, front to back: single-token conv+SiLU over the
+    q|k|v channels with the window handed on, gdn_decode_token (L2 flag, gates formed from raw
+    in_proj_ba outputs, states in a 64-entry pool through a shuffled slot table), gated RMSNorm.
+    n_inputs distinct per-step inputs are staged in HBM and cycled."""
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding as G
+    B, Hk, Hv, D = 64, 16, 48, 128
+    C = (2 * Hk + Hv) * D
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+    bf = torch.bfloat16
+    xs = [torch.randn((B, 1, C), generator=g, device=dev).to(bf) for _ in range(n_inputs)]
+    bas = [torch.randn((B, 2 * Hv), generator=g, device=dev).to(bf) for _ in range(n_inputs)]
+    zs = [torch.randn((B, Hv * D), generator=g, device=dev).to(bf) for _ in range(n_inputs)]
+    w = (0.5 * torch.randn((C, 4), generator=g, device=dev)).to(bf)
+    nw = (1.0 + 0.1 * torch.randn((D,), generator=g, device=dev)).to(bf)
+    A_log = torch.rand((Hv,), generator=g, device=dev) * float(np.log(16.0))
+    dt_bias = 0.5 * torch.randn((Hv,), generator=g, device=dev)
+    cs = [torch.zeros((B, C, 3), dtype=bf, device=dev) for _ in range(2)]
+    pool = 0.02 * torch.randn((B, Hv, D, D), generator=g, device=dev)
+    slots = torch.randperm(B, generator=g, device=dev).to(torch.int32)
+    y = torch.empty((B, 1, C), dtype=bf, device=dev)
+    o = torch.empty((B, Hv * D), dtype=bf, device=dev)
+    out = torch.empty((B, Hv * D), dtype=bf, device=dev)
+    stream = torch.cuda.current_stream()
+    i = [0]
+
+    def step():
+        s = i[0] % n_inputs
+        G.gdn_conv1d_silu(xs[s], w, cs[i[0] % 2], cs[(i[0] + 1) % 2], y, stream=stream)
+        y2 = y[:, 0]
+        G.gdn_decode_token(y2[:, :Hk * D], y2[:, Hk * D:2 * Hk * D], y2[:, 2 * Hk * D:], bas[s], A_log, dt_bias,
+                           pool, slots, o, Hk=Hk, Hv=Hv, l2norm=True, stream=stream)
+        G.gdn_gated_rmsnorm(o, zs[s], nw, 1e-6, out, H=Hv, stream=stream)
+        i[0] += 1
+
+    def token_only():
+        s = i[0] % n_inputs
+        y2 = y[:, 0]
+        G.gdn_decode_token(y2[:, :Hk * D], y2[:, Hk * D:2 * Hk * D], y2[:, 2 * Hk * D:], bas[s], A_log, dt_bias,
+                           pool, slots, o, Hk=Hk, Hv=Hv, l2norm=True, stream=stream)
+        i[0] += 1
+
+    torch.cuda.synchronize()
+    _, mean_ms, med_ms = timed_launches(step, n_steps, 300, stream)
+    _, _, tok_med = timed_launches(token_only, n_steps, 8, stream)
+    conv_b = B * (2 * C * 2 + 2 * 3 * C * 2) + C * 4 * 2
+    tok_b = B * (2 * Hv * D * D * 4 + 2 * Hk * D * 2 + 2 * Hv * D * 2 + 2 * Hv * 2) + 4 * B
+    norm_b = B * 3 * Hv * D * 2 + D * 2
+    return dict(median_us=med_ms * 1e3, mean_us=mean_ms * 1e3, bytes_per_step=conv_b + tok_b + norm_b,
+                GBs=(conv_b + tok_b + norm_b) / (med_ms * 1e-3) / 1e9, token_median_us=tok_med * 1e3,
+                token_GBs=tok_b / (tok_med * 1e-3) / 1e9)
+
+
 def bench_block(dev, steps=5, warmup=2):
     """Block front end at batch 4, T = 32768, 16 key / 128 value heads: conv+SiLU over
     [q|k|v] (20480 channels), prefill on strided views with the L2 flag, gated
@@ -345,6 +400,14 @@ def main():
                           "GBs": dec["GBs"], "hbm_frac": dec["GBs"] / HBM_PEAK_GBS,
                           "bytes_per_step": dec["bytes_per_step"],
                           "two_pools_GBs": dec2["GBs"], "two_pools_median_us": dec2["median_ms"] * 1e3}
+        fr = bench_decode_front(dev)
+        print(f"[bench] decode front end: {fr['median_us']:.1f} us/step (token {fr['token_median_us']:.1f} us)",
+              file=sys.stderr, flush=True)
+        line["decode_front_end"] = {
+            "config": "64 sequences, one layer token: conv+SiLU over 10240 q|k|v channels (window rolled), "
+                      "gdn_decode_token (L2 flag, gates from raw in_proj_ba, 64-entry state pool via a shuffled "
+                      "slot table), gated RMSNorm over 48 x 128",
+            **fr, "hbm_frac": fr["GBs"] / HBM_PEAK_GBS, "token_hbm_frac": fr["token_GBs"] / HBM_PEAK_GBS}
         blk = bench_block(dev)
         print(f"[bench] block: {blk['block_ms']:.2f} ms", file=sys.stderr, flush=True)
         line["block"] = {"config": "batch 4, T=32768, 16 key / 128 value heads: conv+SiLU, prefill (L2 flag), "
