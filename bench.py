@@ -180,15 +180,29 @@ def bench_decode_front(dev, n_steps=256, n_inputs=32):
                            pool, slots, o, Hk=Hk, Hv=Hv, l2norm=True, stream=stream)
         i[0] += 1
 
+    # the same token through the fused kernel: window pools [S, C, 3] swapped each step
+    xs2 = [x[:, 0] for x in xs]
+    pools_cs = [torch.zeros((B, C, 3), dtype=bf, device=dev) for _ in range(2)]
+    out2 = torch.empty((B, Hv * D), dtype=bf, device=dev)
+
+    def fused():
+        s = i[0] % n_inputs
+        G.gdn_decode_layer(xs2[s], w, pools_cs[i[0] % 2], pools_cs[(i[0] + 1) % 2], bas[s], A_log, dt_bias, pool,
+                           zs[s], nw, slots, out2, Hk=Hk, Hv=Hv, l2norm=True, stream=stream)
+        i[0] += 1
+
     torch.cuda.synchronize()
     _, mean_ms, med_ms = timed_launches(step, n_steps, 300, stream)
     _, _, tok_med = timed_launches(token_only, n_steps, 8, stream)
+    _, _, fused_med = timed_launches(fused, n_steps, 8, stream)
     conv_b = B * (2 * C * 2 + 2 * 3 * C * 2) + C * 4 * 2
     tok_b = B * (2 * Hv * D * D * 4 + 2 * Hk * D * 2 + 2 * Hv * D * 2 + 2 * Hv * 2) + 4 * B
     norm_b = B * 3 * Hv * D * 2 + D * 2
+    fused_b = B * (C * 2 + 2 * 3 * C * 2 + 2 * Hv * 2 + 2 * Hv * D * D * 4 + 2 * Hv * D * 2) + C * 4 * 2 + 4 * B
     return dict(median_us=med_ms * 1e3, mean_us=mean_ms * 1e3, bytes_per_step=conv_b + tok_b + norm_b,
                 GBs=(conv_b + tok_b + norm_b) / (med_ms * 1e-3) / 1e9, token_median_us=tok_med * 1e3,
-                token_GBs=tok_b / (tok_med * 1e-3) / 1e9)
+                token_GBs=tok_b / (tok_med * 1e-3) / 1e9, fused_median_us=fused_med * 1e3,
+                fused_bytes_per_step=fused_b, fused_GBs=fused_b / (fused_med * 1e-3) / 1e9)
 
 
 def bench_block(dev, steps=5, warmup=2):
@@ -401,13 +415,15 @@ def main():
                           "bytes_per_step": dec["bytes_per_step"],
                           "two_pools_GBs": dec2["GBs"], "two_pools_median_us": dec2["median_ms"] * 1e3}
         fr = bench_decode_front(dev)
-        print(f"[bench] decode front end: {fr['median_us']:.1f} us/step (token {fr['token_median_us']:.1f} us)",
+        print(f"[bench] decode front end: {fr['median_us']:.1f} us/step (token {fr['token_median_us']:.1f} us, "
+              f"fused layer {fr['fused_median_us']:.1f} us)",
               file=sys.stderr, flush=True)
         line["decode_front_end"] = {
             "config": "64 sequences, one layer token: conv+SiLU over 10240 q|k|v channels (window rolled), "
                       "gdn_decode_token (L2 flag, gates from raw in_proj_ba, 64-entry state pool via a shuffled "
                       "slot table), gated RMSNorm over 48 x 128",
-            **fr, "hbm_frac": fr["GBs"] / HBM_PEAK_GBS, "token_hbm_frac": fr["token_GBs"] / HBM_PEAK_GBS}
+            **fr, "hbm_frac": fr["GBs"] / HBM_PEAK_GBS, "token_hbm_frac": fr["token_GBs"] / HBM_PEAK_GBS,
+            "fused_hbm_frac": fr["fused_GBs"] / HBM_PEAK_GBS}
         blk = bench_block(dev)
         print(f"[bench] block: {blk['block_ms']:.2f} ms", file=sys.stderr, flush=True)
         line["block"] = {"config": "batch 4, T=32768, 16 key / 128 value heads: conv+SiLU, prefill (L2 flag), "

@@ -21,7 +21,8 @@ GDN_FLAG_TOKEN_SERIAL = 2
 
 # Every exported symbol, in the order include/gdn.h declares them.
 EXPORTS = ("gdn_prefill", "gdn_prefill_workspace_size", "gdn_decode_step", "gdn_conv1d_silu",
-           "gdn_gated_rmsnorm", "gdn_gates", "gdn_decode_token", "gdn_last_error", "gdn_version")
+           "gdn_gated_rmsnorm", "gdn_gates", "gdn_decode_token", "gdn_decode_layer", "gdn_last_error",
+           "gdn_version")
 
 
 class GdnDims(ctypes.Structure):
@@ -33,6 +34,20 @@ class GdnDims(ctypes.Structure):
         ("stride_v", ctypes.c_int64), ("stride_o", ctypes.c_int64),
         ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
     ]
+
+
+class GdnDecodeLayerArgs(ctypes.Structure):
+    p = ctypes.c_void_p
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hk", ctypes.c_int32), ("Hv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
+        ("norm_eps", ctypes.c_float),
+        ("x", p), ("stride_x", ctypes.c_int64), ("conv_w", p), ("conv_state_in", p), ("conv_state_out", p),
+        ("ba", p), ("stride_ba", ctypes.c_int64), ("A_log", p), ("dt_bias", p), ("state_pool", p),
+        ("slots", p), ("z", p), ("stride_z", ctypes.c_int64), ("norm_w", p), ("out", p),
+        ("stride_out", ctypes.c_int64), ("o", p), ("stride_o", ctypes.c_int64),
+    ]
+    del p
 
 
 class GdnError(RuntimeError):
@@ -67,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_gates.restype = ctypes.c_int
         L.gdn_decode_token.argtypes = [ctypes.POINTER(GdnDims), p, p, p, i32, p, i64, p, p, p, p, p, p]
         L.gdn_decode_token.restype = ctypes.c_int
+        L.gdn_decode_layer.argtypes = [ctypes.POINTER(GdnDecodeLayerArgs), p]
+        L.gdn_decode_layer.restype = ctypes.c_int
         L.gdn_last_error.argtypes = []
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -295,6 +312,51 @@ def gdn_decode_token(q, k, v, ba, A_log, dt_bias, state_pool, slots=None, o=None
                                   ba.stride(0) if B > 1 else 2 * Hv, _ptr(A_log), _ptr(dt_bias),
                                   _ptr(state_pool), _ptr(slots), _ptr(o), _stream(stream)))
     return o
+
+
+def gdn_decode_layer(x, conv_w, conv_state_in, conv_state_out, ba, A_log, dt_bias, state_pool, z, norm_w,
+                     slots=None, out=None, o=None, *, Hk: int, Hv: int, l2norm: bool = True,
+                     l2_eps: float = 1e-6, q_scale: float = 1.0, norm_eps: float = 1e-6, stream=None):
+    """One fused decode token of the layer (bf16, D = 128).  x: [B, >=C] pre-conv q|k|v channels
+    (C = (2*Hk + Hv)*128); conv_w: [C, 4]; conv_state_in / _out: [S, C, 3] window pools (distinct);
+    ba: [B, >=2*Hv]; A_log, dt_bias: [Hv] fp32; state_pool: [S, Hv, 128, 128] fp32 (in place);
+    z: [B, >=Hv*128]; norm_w: [128]; slots: [B] int32 or None; out: [B, >=Hv*128] or None;
+    o: optional pre-norm output.  Returns out."""
+    import torch
+    D = 128
+    B = int(x.shape[0])
+    C = (2 * Hk + Hv) * D
+    if out is None:
+        out = torch.empty((B, Hv * D), dtype=torch.bfloat16, device=x.device)
+    for name, t, wdt in (("x", x, C), ("ba", ba, 2 * Hv), ("z", z, Hv * D), ("out", out, Hv * D)) + \
+            ((("o", o, Hv * D),) if o is not None else ()):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.shape[0] != B or t.shape[1] < wdt or t.stride(1) != 1:
+            raise ValueError(f"{name}: expected bf16 [B, >={wdt}] with contiguous rows")
+    for name, t in (("conv_w", conv_w), ("norm_w", norm_w), ("conv_state_in", conv_state_in),
+                    ("conv_state_out", conv_state_out)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous bf16")
+    if tuple(conv_w.shape) != (C, 4) or tuple(norm_w.shape) != (D,):
+        raise ValueError("conv_w must be [C, 4] and norm_w [128]")
+    S = int(state_pool.shape[0])
+    if tuple(conv_state_in.shape) != (S, C, 3) or tuple(conv_state_out.shape) != (S, C, 3):
+        raise ValueError("conv states must be [S, C, 3] with the state pool's S")
+    _params(A_log, dt_bias, Hv)
+    if (state_pool.dtype != torch.float32 or not state_pool.is_contiguous()
+            or tuple(state_pool.shape[1:]) != (Hv, D, D)):
+        raise ValueError("state_pool must be contiguous fp32 [S, Hv, 128, 128]")
+    if slots is None and S < B:
+        raise ValueError("without slots the pools need at least B entries")
+    if slots is not None and (slots.dtype != torch.int32 or not slots.is_contiguous() or tuple(slots.shape) != (B,)):
+        raise ValueError("slots must be a contiguous int32 [B] tensor")
+    st = lambda t, wdt: t.stride(0) if B > 1 else wdt
+    a = GdnDecodeLayerArgs(B, Hk, Hv, D, GDN_FLAG_QK_L2NORM if l2norm else 0, q_scale, l2_eps, norm_eps,
+                           _ptr(x), st(x, C), _ptr(conv_w), _ptr(conv_state_in), _ptr(conv_state_out),
+                           _ptr(ba), st(ba, 2 * Hv), _ptr(A_log), _ptr(dt_bias), _ptr(state_pool), _ptr(slots),
+                           _ptr(z), st(z, Hv * D), _ptr(norm_w), _ptr(out), st(out, Hv * D), _ptr(o),
+                           st(o, Hv * D) if o is not None else 0)
+    _check(lib().gdn_decode_layer(ctypes.byref(a), _stream(stream)))
+    return out
 
 
 def gdn_version() -> int:

@@ -279,6 +279,60 @@ gdn_status gdn_decode_token(const gdn_dims* d, const void* q, const void* k, con
   return from_hip(gdn::launch_recurrent(a, d->io, static_cast<hipStream_t>(stream)), "gdn_decode_token");
 }
 
+gdn_status gdn_decode_layer(const gdn_decode_layer_args* p, void* stream) {
+  if (!p) return fail(GDN_ERR_NULL, "args is NULL");
+  if (p->B < 0 || p->Hk < 1 || p->Hv < 1 || p->Hv % p->Hk)
+    return fail(GDN_ERR_SHAPE, "B=%d Hk=%d Hv=%d (Hv must be a multiple of Hk)", p->B, p->Hk, p->Hv);
+  if (p->D != 128) return fail(GDN_ERR_UNSUPPORTED, "D=%d: the fused decode layer takes D=128", p->D);
+  if (p->flags & ~static_cast<uint32_t>(GDN_FLAG_QK_L2NORM))
+    return fail(GDN_ERR_SHAPE, "flags 0x%x: only GDN_FLAG_QK_L2NORM applies", p->flags);
+  if (!(p->l2_eps >= 0.0f) || !(p->norm_eps >= 0.0f)) return fail(GDN_ERR_SHAPE, "eps values must be >= 0");
+  const int64_t C = static_cast<int64_t>(2 * p->Hk + p->Hv) * p->D, W = static_cast<int64_t>(p->Hv) * p->D;
+  if (p->stride_x < C || p->stride_ba < 2 * static_cast<int64_t>(p->Hv) || p->stride_z < W || p->stride_out < W ||
+      (p->o && p->stride_o < W))
+    return fail(GDN_ERR_SHAPE, "row strides below the row widths (x %lld, ba %d, z/out/o %lld)", (long long)C,
+                2 * p->Hv, (long long)W);
+  if (p->B == 0) return ok();
+  if (!p->x || !p->conv_w || !p->conv_state_in || !p->conv_state_out || !p->ba || !p->A_log || !p->dt_bias ||
+      !p->state_pool || !p->z || !p->norm_w || !p->out)
+    return fail(GDN_ERR_NULL, "x, conv_w, conv states, ba, A_log, dt_bias, state_pool, z, norm_w, out are required");
+  if (p->conv_state_in == p->conv_state_out) return fail(GDN_ERR_SHAPE, "conv_state_out must not alias conv_state_in");
+  if (!aligned(p->x, 4) || (p->stride_x % 2) || !aligned(p->conv_w, 16) || !aligned(p->conv_state_in, 4) ||
+      !aligned(p->conv_state_out, 4) || !aligned(p->ba, 2) || !aligned(p->A_log, 4) || !aligned(p->dt_bias, 4) ||
+      !aligned(p->state_pool, 16) || !aligned(p->slots, 4) || !aligned(p->z, 2) || !aligned(p->norm_w, 2) ||
+      !aligned(p->out, 2) || !aligned(p->o, 2))
+    return fail(GDN_ERR_ALIGN, "alignment: state_pool and conv_w 16 bytes, x and the conv states 4 bytes "
+                               "(stride_x even), the rest their element size");
+  gdn::LayerArgs a;
+  a.B = p->B;
+  a.Hk = p->Hk;
+  a.Hv = p->Hv;
+  a.G = p->Hv / p->Hk;
+  a.flags = p->flags;
+  a.q_scale = p->q_scale;
+  a.l2_eps = p->l2_eps;
+  a.norm_eps = p->norm_eps;
+  a.x = static_cast<const uint16_t*>(p->x);
+  a.sx = p->stride_x;
+  a.conv_w = static_cast<const uint16_t*>(p->conv_w);
+  a.cs_in = static_cast<const uint16_t*>(p->conv_state_in);
+  a.cs_out = static_cast<uint16_t*>(p->conv_state_out);
+  a.ba = static_cast<const uint16_t*>(p->ba);
+  a.sba = p->stride_ba;
+  a.A_log = p->A_log;
+  a.dt_bias = p->dt_bias;
+  a.pool = p->state_pool;
+  a.slots = p->slots;
+  a.z = static_cast<const uint16_t*>(p->z);
+  a.sz = p->stride_z;
+  a.norm_w = static_cast<const uint16_t*>(p->norm_w);
+  a.out = static_cast<uint16_t*>(p->out);
+  a.sout = p->stride_out;
+  a.o = static_cast<uint16_t*>(p->o);
+  a.so = p->stride_o;
+  return from_hip(gdn::launch_decode_layer(a, static_cast<hipStream_t>(stream)), "gdn_decode_layer");
+}
+
 const char* gdn_last_error(void) { return g_err; }
 
 int32_t gdn_version(void) { return 200; /* 0.2.0 */ }

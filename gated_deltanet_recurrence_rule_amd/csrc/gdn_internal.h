@@ -37,6 +37,35 @@ struct RecArgs {
 
 // io: 0 = fp32, 1 = bf16 (same codes as gdn_dtype).
 hipError_t launch_recurrent(const RecArgs& a, int io, hipStream_t s);
+
+// One decode token of a whole layer's mixer (bf16 I/O, head width 128): conv +
+// SiLU of the token's q|k|v channels against a window pool, L2 norm of q and k,
+// gates from raw in_proj_ba outputs, the recurrence on a state pool, and the
+// gated RMSNorm of the output.  Pools are indexed by slots[b] (or b).
+struct LayerArgs {
+  int32_t B, Hk, Hv, G;
+  uint32_t flags;
+  float q_scale, l2_eps, norm_eps;
+  const uint16_t* x;          // [B][sx]: the token's pre-conv q | k | v channels
+  int64_t sx;
+  const uint16_t* conv_w;     // [C][4]
+  const uint16_t* cs_in;      // [S][C][3] window pool read
+  uint16_t* cs_out;           // [S][C][3] window pool written (distinct from cs_in)
+  const uint16_t* ba;         // [B][sba] raw beta logits | alpha inputs
+  int64_t sba;
+  const float* A_log;
+  const float* dt_bias;
+  float* pool;                // [S][Hv][128][128]
+  const int32_t* slots;       // [B] or null
+  const uint16_t* z;          // [B][sz]
+  int64_t sz;
+  const uint16_t* norm_w;     // [128]
+  uint16_t* out;              // [B][sout]
+  int64_t sout;
+  uint16_t* o;                // [B][so] pre-norm output, or null
+  int64_t so;
+};
+hipError_t launch_decode_layer(const LayerArgs& a, hipStream_t s);
 // Chunked prefill: a prep kernel and a chain kernel per window of chunks.
 // The workspace holds, per (b, value head, chunk of the window), the
 // fragments and row scalings the prep kernel produces; when the sequence

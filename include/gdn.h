@@ -234,6 +234,59 @@ gdn_status gdn_decode_token(const gdn_dims* dims, const void* q, const void* k, 
                             const void* ba, int64_t stride_ba, const float* A_log, const float* dt_bias,
                             float* state_pool, const int32_t* slots, void* o, void* stream);
 
+/*
+ * gdn_decode_layer -- one decode token of a whole Gated DeltaNet mixer layer,
+ * fused into one kernel per (sequence, value head): depthwise causal conv +
+ * SiLU of the token's q | k | v channels against their rolling window, L2
+ * norm of q and k (GDN_FLAG_QK_L2NORM), gates from the raw in_proj_ba outputs
+ * (as gdn_gates), the gated delta rule on the pooled state (as
+ * gdn_decode_token), and the gated RMSNorm x swish(z) of the head's output
+ * (as gdn_gated_rmsnorm).  ("L'attention hybride", table "Le decompte": the
+ * q|k|v|z split of the projection, kernel-4 conv over q, k, v, one beta and
+ * one alpha per value head, the 128-weight norm; config block: swish output
+ * gate; "Chapitre 16", 16.3: a decode step reads the per-request state,
+ * emits the token's output and updates the state.)  bf16 I/O, Dk = Dv = D = 128.
+ * With C = (2*Hk + Hv)*D channels and S pool entries:
+ *   x [B, >= C] (row stride stride_x): the token's channels before the conv
+ *   conv_w [C, 4]; conv_state_in / conv_state_out [S, C, 3]: the window pool,
+ *     read from _in and written to _out (distinct buffers; a serving loop
+ *     swaps them each step); the key head's q and k windows are written once
+ *   ba [B, >= 2*Hv] (stride_ba); A_log, dt_bias [Hv] fp32
+ *   state_pool [S, Hv, D, D] fp32, updated in place
+ *   slots [B] int32 device memory or NULL (entry b); a negative slot skips the
+ *     sequence (nothing of it is read or written); slots must be distinct and
+ *     < S (device data, not checked on the host)
+ *   z [B, >= Hv*D] (stride_z); norm_w [D]; out [B, >= Hv*D] (stride_out)
+ *   o [B, >= Hv*D] (stride_o) receives the output before the norm, or NULL
+ * Alignment: state_pool and conv_w 16 bytes; x, conv_state_in and
+ * conv_state_out 4 bytes with stride_x even; the rest their element size.
+ */
+typedef struct {
+  int32_t B, Hk, Hv, D;
+  uint32_t flags;               /* GDN_FLAG_QK_L2NORM or 0 */
+  float q_scale, l2_eps, norm_eps;
+  const void* x;
+  int64_t stride_x;
+  const void* conv_w;
+  const void* conv_state_in;
+  void* conv_state_out;
+  const void* ba;
+  int64_t stride_ba;
+  const float* A_log;
+  const float* dt_bias;
+  float* state_pool;
+  const int32_t* slots;
+  const void* z;
+  int64_t stride_z;
+  const void* norm_w;
+  void* out;
+  int64_t stride_out;
+  void* o;
+  int64_t stride_o;
+} gdn_decode_layer_args;
+
+gdn_status gdn_decode_layer(const gdn_decode_layer_args* args, void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  The string
  * is owned by the library and valid until the next call on this thread. */
 const char* gdn_last_error(void);

@@ -186,6 +186,35 @@ def test_gates_and_decode_token_argument_errors():
     assert tok(dims(T=1, B=0)) == B.GDN_OK
 
 
+def test_decode_layer_arguments():
+    L = B.lib()
+    # gdn_decode_layer_args: 4 x int32, uint32, 3 x float, then 18 pointer / int64 fields
+    assert ctypes.sizeof(B.GdnDecodeLayerArgs) == 176
+    assert B.GdnDecodeLayerArgs.x.offset == 32 and B.GdnDecodeLayerArgs.stride_o.offset == 168
+
+    def args(**kw):
+        a = B.GdnDecodeLayerArgs(2, 2, 6, 128, 1, 1.0, 1e-6, 1e-6, FAKE, 10 * 128, FAKE, FAKE,
+                                 ctypes.c_void_p(0x20000), FAKE, 12, FAKE, FAKE, FAKE, None, FAKE, 768, FAKE, FAKE,
+                                 768, None, 0)
+        for k_, v_ in kw.items():
+            setattr(a, k_, v_)
+        return L.gdn_decode_layer(ctypes.byref(a), None)
+    assert L.gdn_decode_layer(None, None) == B.GDN_ERR_NULL
+    assert args(D=64) == B.GDN_ERR_UNSUPPORTED
+    assert args(Hv=5) == B.GDN_ERR_SHAPE
+    assert args(flags=2) == B.GDN_ERR_SHAPE
+    assert args(stride_x=10 * 128 - 1) == B.GDN_ERR_SHAPE
+    assert args(stride_ba=11) == B.GDN_ERR_SHAPE
+    assert args(norm_eps=-1.0) == B.GDN_ERR_SHAPE
+    assert args(z=None) == B.GDN_ERR_NULL
+    assert args(conv_state_out=FAKE.value) == B.GDN_ERR_SHAPE     # aliases conv_state_in
+    assert args(state_pool=0x10008) == B.GDN_ERR_ALIGN
+    assert args(out=0x10001) == B.GDN_ERR_ALIGN                    # bf16 needs 2-byte alignment
+    assert args(conv_w=0x10008) == B.GDN_ERR_ALIGN                 # conv weights: 16 bytes
+    assert args(stride_x=10 * 128 + 1) == B.GDN_ERR_ALIGN          # word loads of channel pairs
+    assert args(B=0) == B.GDN_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))

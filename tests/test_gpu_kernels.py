@@ -406,3 +406,74 @@ def test_conv_single_token_steps_roll_the_window():
     assert_out(y_steps, ref, bf16=True)
     # the window handed on after the last step holds the last three inputs, oldest first
     np.testing.assert_array_equal(to_host(cs), W.bf16_to_f32(np.ascontiguousarray(x[:, T - 3:].transpose(0, 2, 1))))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("l2", [True, False])
+def test_decode_layer_fused_parity(l2):
+    """gdn_decode_layer (conv window, L2 norm, gates from raw in_proj_ba, recurrence on a pooled
+    state, gated RMSNorm) against the oracle's conv, gate activation, recurrence and norm applied
+    in turn in fp64, over three tokens with the window pools swapped each step and a slot table
+    with one skipped sequence.  Moved window entries are bf16 copies and must match exactly."""
+    torch = _torch()
+    B, Hk, Hv, D, S, steps = 5, 2, 6, 128, 8, 3
+    C = (2 * Hk + Hv) * D
+    slots = np.array([3, 7, -1, 0, 5], np.int32)
+    live = slots >= 0
+    rng = np.random.default_rng(61)
+    bf = lambda a: W.f32_to_bf16(np.asarray(a, np.float32))
+    A = np.log(rng.uniform(1.0, 16.0, Hv)).astype(np.float32)
+    dt = (rng.standard_normal(Hv) * 0.5).astype(np.float32)
+    cw = bf(rng.standard_normal((C, 4)) * 0.5)
+    nw = bf(1.0 + 0.1 * rng.standard_normal(D))
+    cs = [bf(rng.standard_normal((S, C, 3))), bf(np.full((S, C, 3), 3.0))]
+    pool = (rng.standard_normal((S, Hv, D, D)) * 0.02).astype(np.float32)
+    ref_pool = pool.astype(np.float64)
+    ref_cs = cs[0].copy()
+    d_cs = [to_dev(cs[0]), to_dev(cs[1])]
+    d_pool, d_cw, d_nw, d_A, d_dt, d_slots = to_dev(pool), to_dev(cw), to_dev(nw), to_dev(A), to_dev(dt), to_dev(slots)
+    eps = 1e-6
+    for s in range(steps):
+        x = bf(rng.standard_normal((B, C)))
+        ba = bf(rng.standard_normal((B, 2 * Hv)) * 2.0)
+        z = bf(rng.standard_normal((B, Hv * D)))
+        out = torch.full((B, Hv * D), 5.0, dtype=torch.bfloat16, device="cuda")
+        o = torch.full((B, Hv * D), 5.0, dtype=torch.bfloat16, device="cuda")
+        G.gdn_decode_layer(to_dev(x), d_cw, d_cs[s % 2], d_cs[(s + 1) % 2], to_dev(ba), d_A, d_dt, d_pool, to_dev(z),
+                           d_nw, d_slots, out, o, Hk=Hk, Hv=Hv, l2norm=l2, norm_eps=eps)
+        torch.cuda.synchronize()
+        # oracle, sequence by sequence: conv with the pooled window, gates, recurrence, norm
+        la, be = oracle.gates(ba, Hv, A, dt)
+        outs, pres = [], []
+        for b in np.nonzero(live)[0]:
+            sl = slots[b]
+            y, win = oracle.conv1d_silu(x[b][None, None], cw, ref_cs[sl][None], want_state=True)
+            y = y[0]
+            q, k, v = y[:Hk * D], y[Hk * D:2 * Hk * D], y[2 * Hk * D:]
+            orf, srf = oracle.recurrence(q[None, None], k[None, None], v[None, None], la[b][None, None],
+                                         be[b][None, None], Hk, Hv, ref_pool[sl][None], l2norm=l2, l2_eps=1e-6)
+            ref_pool[sl] = srf.reshape(Hv, D, D)
+            ref_cs[sl] = W.f32_to_bf16(win[0].astype(np.float32))
+            pre = orf.reshape(Hv, D)
+            pres.append(pre)
+            outs.append(oracle.gated_rmsnorm(pre, W.bf16_to_f32(z[b]).reshape(Hv, D).astype(np.float64),
+                                             W.bf16_to_f32(nw).astype(np.float64), eps))
+        oh, ph = to_host(out).reshape(B, Hv, D), to_host(o).reshape(B, Hv, D)
+        assert_out(ph[live], np.stack(pres), bf16=True, what="o")
+        assert_out(oh[live], np.stack(outs), bf16=True, what="out")
+        assert np.all(oh[~live] == 5.0) and np.all(ph[~live] == 5.0)
+        hp = to_host(d_pool)
+        for sl in range(S):
+            if sl in slots[live]:
+                assert_state(hp[sl], ref_pool[sl])
+            else:
+                np.testing.assert_array_equal(hp[sl], pool[sl])
+        # window pools: entries of live slots moved on exactly; the others untouched
+        written = d_cs[(s + 1) % 2].view(torch.int16).cpu().numpy().view(np.uint16)
+        before = cs[(s + 1) % 2]
+        for sl in range(S):
+            if sl in slots[live]:
+                np.testing.assert_array_equal(written[sl], ref_cs[sl])
+            else:
+                np.testing.assert_array_equal(written[sl], before[sl])
+        cs[(s + 1) % 2] = written.copy()
