@@ -12,7 +12,11 @@
 //     o = alpha w + (k . q) d                    (= M'^T q, read after update)
 // This is the decode-step kernel (T = 1: one HBM read and one HBM write of the
 // 64 KiB state, 128-bit coalesced) and the prefill kernel for shapes the
-// chunked MFMA kernel does not take (fp32 I/O, head widths 16..64).
+// chunked MFMA kernel does not take (fp32 I/O, head widths 16..64).  It can
+// form the gates from raw in_proj_ba outputs and address its state through a
+// slot table into a pool (the serving decode token).  decode_layer_kernel
+// below fuses a whole layer's decode token: conv window, L2 norm, gates, this
+// update and the gated output norm.
 //
 // Thread layout: TPR = D/4 threads cover one row of M with a float4 each;
 // RG = NT/TPR row groups take rows rg, rg+RG, ... so that one wave's loads
