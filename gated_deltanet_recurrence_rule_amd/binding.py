@@ -20,7 +20,8 @@ GDN_FLAG_QK_L2NORM = 1
 GDN_FLAG_TOKEN_SERIAL = 2
 
 # Every exported symbol, in the order include/gdn.h declares them.
-EXPORTS = ("gdn_prefill", "gdn_prefill_workspace_size", "gdn_decode_step", "gdn_conv1d_silu",
+EXPORTS = ("gdn_prefill", "gdn_prefill_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_size",
+           "gdn_decode_step", "gdn_conv1d_silu",
            "gdn_gated_rmsnorm", "gdn_gates", "gdn_decode_token", "gdn_decode_layer", "gdn_last_error",
            "gdn_version")
 
@@ -72,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnDims)]
         L.gdn_prefill_workspace_size.restype = ctypes.c_size_t
+        L.gdn_prefill_varlen.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p, p, p, ctypes.c_size_t, p]
+        L.gdn_prefill_varlen.restype = ctypes.c_int
+        L.gdn_prefill_varlen_workspace_size.argtypes = [ctypes.POINTER(GdnDims)]
+        L.gdn_prefill_varlen_workspace_size.restype = ctypes.c_size_t
         L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p]
         L.gdn_decode_step.restype = ctypes.c_int
         L.gdn_conv1d_silu.argtypes = [i32, i32, i32, i32, i32, p, i64, p, p, p, p, i64, p]
@@ -181,6 +186,55 @@ def gdn_prefill(q, k, v, log_alpha, beta, state_in=None, state_out=None, o=None,
     _check(lib().gdn_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                              _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o), _ptr(workspace),
                              ws_len, _stream(stream)))
+    return o
+
+
+def gdn_prefill_varlen_workspace_size(dims: GdnDims) -> int:
+    return int(lib().gdn_prefill_varlen_workspace_size(ctypes.byref(dims)))
+
+
+def gdn_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, state_in=None, state_out=None, o=None, *, Hk: int,
+                       Hv: int, l2norm: bool = False, l2_eps: float = 1e-6, q_scale: float = 1.0,
+                       token_serial: bool = False, workspace=None, stream=None):
+    """Packed sequences: q, k [T, Hk*D]; v [T, Hv*D]; log_alpha, beta [T, Hv] fp32; cu_seqlens [B+1]
+    int32 device tensor (sequence s = tokens cu[s]..cu[s+1]); states [B, Hv, D, D] or None;
+    o [T, >=Hv*D] or None.  Returns o."""
+    import torch
+    T = int(q.shape[0])
+    nseq = int(cu_seqlens.shape[0]) - 1
+    if q.shape[1] % Hk or v.shape[1] % Hv or q.shape[1] // Hk != v.shape[1] // Hv:
+        raise ValueError("q must be [T, Hk*D] and v [T, Hv*D]")
+    D = int(q.shape[1]) // Hk
+    io = _io(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or (o is not None and o.dtype != q.dtype):
+        raise ValueError("q, k, v and o must share one dtype")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous() or cu_seqlens.dim() != 1 or nseq < 0:
+        raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor")
+    if cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be on the device of q")
+    if o is None:
+        o = torch.empty((T, Hv * D), dtype=q.dtype, device=q.device)
+    for name, t, w in (("q", q, Hk * D), ("k", k, Hk * D), ("v", v, Hv * D), ("o", o, Hv * D)):
+        if t.dim() != 2 or t.shape[0] != T or t.shape[1] < w or (T > 0 and t.stride(1) != 1):
+            raise ValueError(f"{name}: expected [T, >={w}] with contiguous rows")
+    for name, g in (("log_alpha", log_alpha), ("beta", beta)):
+        if g.dtype != torch.float32 or not g.is_contiguous() or tuple(g.shape) != (T, Hv):
+            raise ValueError(f"{name} must be contiguous fp32 [T, Hv]")
+    for name, s_ in (("state_in", state_in), ("state_out", state_out)):
+        if s_ is not None and (s_.dtype != torch.float32 or not s_.is_contiguous()
+                               or tuple(s_.shape) != (nseq, Hv, D, D)):
+            raise ValueError(f"{name} must be contiguous fp32 [B, Hv, D, D]")
+    flags = (GDN_FLAG_QK_L2NORM if l2norm else 0) | (GDN_FLAG_TOKEN_SERIAL if token_serial else 0)
+    st = lambda t, w: t.stride(0) if T > 1 else w
+    dims = make_dims(nseq, T, Hk, Hv, D, io, flags, st(q, Hk * D), st(k, Hk * D), st(v, Hv * D), st(o, Hv * D),
+                     q_scale, l2_eps)
+    ws_bytes = gdn_prefill_varlen_workspace_size(dims)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gdn_prefill_varlen(ctypes.byref(dims), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(log_alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o),
+                                    _ptr(workspace), ws_len, _stream(stream)))
     return o
 
 

@@ -99,24 +99,36 @@ gdn::RecArgs rec_args(const gdn_dims* d, const void* q, const void* k, const voi
   return a;
 }
 
-}  // namespace
+// Marks a packed (variable-length) batch in the workspace-size query, where
+// cu_seqlens is not known; only its being non-null is looked at on the host.
+const int32_t kPackedMarker[1] = {0};
 
-extern "C" {
+// Arguments of the chunked path.  A packed batch is one token stream (B = 1 for
+// the workspace layout) of d->B sequences.
+gdn::RecArgs chunk_args(const gdn_dims* d, const int32_t* cu, const void* q, const void* k, const void* v,
+                        const float* la, const float* beta, const float* sin, float* sout, void* o) {
+  gdn::RecArgs a = rec_args(d, q, k, v, la, beta, sin, sout, o);
+  if (cu) {
+    a.B = 1;
+    a.cu_seqlens = cu;
+    a.nseq = d->B;
+  }
+  return a;
+}
 
-size_t gdn_prefill_workspace_size(const gdn_dims* d) {
+size_t workspace_size(const gdn_dims* d, const int32_t* cu) {
   if (check_dims(d, false) != GDN_OK || d->B == 0 || !use_chunk_kernel(d)) return 0;
-  const gdn::RecArgs a = rec_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  const gdn::RecArgs a = chunk_args(d, cu, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
   const size_t per_chunk = gdn::chunk_ws_bytes_per_chunk(a);
-  const int64_t nchunks = (static_cast<int64_t>(d->T) + 63) / 64;
+  const int64_t nchunks = gdn::chunk_count(a);
   const int64_t nwin = gdn::chunk_window_chunks(a);
   if (nwin >= nchunks) return static_cast<size_t>(nchunks) * per_chunk;
   return static_cast<size_t>(nwin) * per_chunk + gdn::chunk_ws_carry_bytes(a);
 }
 
-gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const void* v,
-                       const float* log_alpha, const float* beta, const float* state_in,
-                       float* state_out, void* o, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+gdn_status prefill(const gdn_dims* d, const int32_t* cu, const void* q, const void* k, const void* v,
+                   const float* log_alpha, const float* beta, const float* state_in, float* state_out, void* o,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   gdn_status st = check_dims(d, false);
   if (st != GDN_OK) return st;
   if (d->B == 0) return ok();
@@ -130,9 +142,9 @@ gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const vo
       return fail(GDN_ERR_ALIGN, "bf16 q, k, v, o must be 16-byte aligned");
     if ((d->stride_q % 8) || (d->stride_k % 8) || (d->stride_v % 8) || (d->stride_o % 8))
       return fail(GDN_ERR_ALIGN, "bf16 strides of q, k, v, o must be multiples of 8 elements");
-    const gdn::RecArgs a = rec_args(d, q, k, v, log_alpha, beta, state_in, state_out, o);
+    const gdn::RecArgs a = chunk_args(d, cu, q, k, v, log_alpha, beta, state_in, state_out, o);
     const size_t per_chunk = gdn::chunk_ws_bytes_per_chunk(a);
-    const int64_t nchunks = (static_cast<int64_t>(d->T) + 63) / 64;
+    const int64_t nchunks = gdn::chunk_count(a);
     const size_t need_min =
         per_chunk + ((nchunks > 1 && !state_out) ? gdn::chunk_ws_carry_bytes(a) : 0);
     if (!workspace) return fail(GDN_ERR_NULL, "the chunked prefill needs a workspace");
@@ -145,9 +157,38 @@ gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const vo
   const size_t es = d->io == GDN_BF16 ? 2 : 4;
   if (d->T > 0 && (!aligned(q, es) || !aligned(k, es) || !aligned(v, es) || !aligned(o, es)))
     return fail(GDN_ERR_ALIGN, "q, k, v, o must be aligned to their element size");
-  return from_hip(gdn::launch_recurrent(rec_args(d, q, k, v, log_alpha, beta, state_in, state_out, o),
-                                        d->io, static_cast<hipStream_t>(stream)),
+  gdn::RecArgs a = rec_args(d, q, k, v, log_alpha, beta, state_in, state_out, o);
+  if (cu) {
+    a.B = 1;
+    a.cu_seqlens = cu;
+    a.nseq = d->B;
+  }
+  return from_hip(gdn::launch_recurrent(a, d->io, static_cast<hipStream_t>(stream)),
                   "gdn_prefill (token-serial kernel)");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_prefill_workspace_size(const gdn_dims* d) { return workspace_size(d, nullptr); }
+
+size_t gdn_prefill_varlen_workspace_size(const gdn_dims* d) { return workspace_size(d, kPackedMarker); }
+
+gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const float* state_in,
+                       float* state_out, void* o, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return prefill(d, nullptr, q, k, v, log_alpha, beta, state_in, state_out, o, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_varlen(const gdn_dims* d, const int32_t* cu_seqlens, const void* q, const void* k,
+                              const void* v, const float* log_alpha, const float* beta, const float* state_in,
+                              float* state_out, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return fail(GDN_ERR_NULL, "cu_seqlens is required");
+  if (!aligned(cu_seqlens, 4)) return fail(GDN_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+  return prefill(d, cu_seqlens, q, k, v, log_alpha, beta, state_in, state_out, o, workspace, workspace_bytes,
+                 stream);
 }
 
 gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, const void* v,

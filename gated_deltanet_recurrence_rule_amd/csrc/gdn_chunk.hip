@@ -159,9 +159,27 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   const int l32 = lane & 31, h = lane >> 5;
   const int cl = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int c = c0 + cl;
-  const int t0 = c * CH;
-  const int nval = min(CH, a.T - t0);
-  const int64_t tokbase = static_cast<int64_t>(b) * a.T + t0;
+  int nval;
+  int64_t tokbase;
+  if (a.cu_seqlens) {
+    // packed sequences: global chunk c is chunk c - (chunks before s) of sequence s
+    int acc = 0, s = 0, len = 0;
+    int64_t start = 0;
+    for (; s < a.nseq; ++s) {
+      packed_range(a.cu_seqlens, s, a.T, start, len);
+      const int n = (len + CH - 1) / CH;
+      if (c < acc + n) break;
+      acc += n;
+    }
+    if (s == a.nseq) return;  // past the last chunk: the whole workgroup leaves
+    const int t0 = (c - acc) * CH;
+    tokbase = start + t0;
+    nval = min(CH, len - t0);
+  } else {
+    const int t0 = c * CH;
+    nval = min(CH, a.T - t0);
+    tokbase = static_cast<int64_t>(b) * a.T + t0;
+  }
   const bool l2 = (a.flags & 1u) != 0;
   const uint16_t* gq = static_cast<const uint16_t*>(a.q);
   const uint16_t* gk = static_cast<const uint16_t*>(a.k);
@@ -598,8 +616,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 //    until chunk c+1's copy has landed.
 // Each buffer is rewritten two chunks after it was filled, by which time its
 // reader has passed the barrier in between.
+// Chunks [cs, ce) of sequence b in the window numbering, the token index of its
+// first token and its length.  Fixed-length batches: every sequence has chunks
+// [0, ceil(T/64)) and starts at token b*T.
+__device__ __forceinline__ void seq_chunks(const RecArgs& a, int b, int& cs, int& ce, int64_t& tok0, int& len) {
+  if (!a.cu_seqlens) {
+    cs = 0;
+    ce = (a.T + CH - 1) / CH;
+    tok0 = static_cast<int64_t>(b) * a.T;
+    len = a.T;
+    return;
+  }
+  int acc = 0;
+  for (int i = 0; i < b; ++i) {
+    packed_range(a.cu_seqlens, i, a.T, tok0, len);
+    acc += (len + CH - 1) / CH;
+  }
+  cs = acc;
+  packed_range(a.cu_seqlens, b, a.T, tok0, len);
+  ce = cs + (len + CH - 1) / CH;
+}
+
+// The window holds chunks [c0, c0 + nw) (workspace stride nwin).  A sequence's
+// state comes from state_in at its first chunk and from `carry` otherwise, and
+// goes to state_out after its last chunk and to `carry` otherwise.
 __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, const unsigned char* ws, int nwin,
-                                                             const float* state_in, float* state_out) {
+                                                             int nw, float* carry) {
   using L = ChainLds;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
@@ -608,7 +650,7 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
   // (sequence, head) count is a multiple of 8, the 4 strips of a head get indices
   // that are equal modulo 8, so they share one XCD's L2 for the head's inputs.
   const int L0 = blockIdx.x;
-  const int nheads = a.B * a.Hv;
+  const int nheads = (a.cu_seqlens ? a.nseq : a.B) * a.Hv;
   int bhv, strip;
   if ((nheads & 7) == 0) {
     bhv = (L0 >> 5) * 8 + (L0 & 7);
@@ -617,19 +659,39 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
     bhv = L0 >> 2;
     strip = L0 & 3;
   }
-  const int b = bhv / a.Hv, hv = bhv - b * a.Hv;
+  const int b = bhv / a.Hv, hv = bhv - b * a.Hv;   // sequence, value head
   const int hk = hv / a.G;
-  const int bh = bhv;
+  const int bw = a.cu_seqlens ? 0 : b;               // batch index inside the workspace
+  const int bh = bw * a.Hv + hv;
+  int cs, ce, len;
+  int64_t tok0;
+  seq_chunks(a, b, cs, ce, tok0, len);
+  const int lo = max(cs, c0), hi = min(ce, c0 + nw);
+  if (lo >= hi) {
+    // no chunk of this sequence in the window: the whole workgroup leaves; an empty
+    // sequence hands its state on unchanged (in the first window)
+    if (len == 0 && c0 == 0 && a.state_out) {
+      const int64_t base = static_cast<int64_t>(bhv) * DK * DK + 32 * strip;
+      for (int i = tid; i < DK * 32; i += 192) {
+        const int64_t e = base + (i >> 5) * DK + (i & 31);
+        a.state_out[e] = a.state_in ? a.state_in[e] : 0.f;
+      }
+    }
+    return;
+  }
+  const int lofs = lo - c0;
+  const float* state_in = lo == cs ? a.state_in : carry;
+  float* state_out = hi == ce ? a.state_out : carry;
   // roles (one wave per SIMD): wave 1 carries the state of the strip, wave 0 produces
   // its outputs, wave 2 copies the next chunks' inputs into LDS
   const int role = wv == 2 ? 2 : (wv == 1 ? 0 : 1);
   const int col = 32 * strip + l32;  // this lane's value column
   uint16_t* go = static_cast<uint16_t*>(a.o);
 
-  const int nchunk = min(nwin, (a.T + CH - 1) / CH - c0);
+  const int nchunk = hi - lo;
   const unsigned char* regK = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WH_BYTES;
-  auto wsh_of = [&](int cl) { return ws + (static_cast<int64_t>(bh) * nwin + cl) * WH_BYTES; };
-  auto wsk_of = [&](int cl) { return regK + (static_cast<int64_t>(b * a.Hk + hk) * nwin + cl) * WK_BYTES; };
+  auto wsh_of = [&](int cl) { return ws + (static_cast<int64_t>(bh) * nwin + lofs + cl) * WH_BYTES; };
+  auto wsk_of = [&](int cl) { return regK + (static_cast<int64_t>(bw * a.Hk + hk) * nwin + lofs + cl) * WK_BYTES; };
   auto copy_chunk = [&](int cl) {
     unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
     const unsigned char* wsh = wsh_of(cl);
@@ -646,7 +708,7 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       if (state_in) {
-        const float* sp = state_in + static_cast<int64_t>(bh) * DK * DK;
+        const float* sp = state_in + static_cast<int64_t>(bhv) * DK * DK;
 #pragma unroll
         for (int v = 0; v < 16; ++v) Ms[dt][v] = sp[(32 * dt + acc_row(v, h)) * DK + col];
       } else {
@@ -728,7 +790,7 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
       lds_sync();
     }
     if (state_out) {
-      float* sp = state_out + static_cast<int64_t>(bh) * DK * DK;
+      float* sp = state_out + static_cast<int64_t>(bhv) * DK * DK;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -770,9 +832,9 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
           *reinterpret_cast<uint2*>(sO + r * 64 + ((j ^ (r & 3)) * 16) + 8 * h) = w;
         }
       }
-      const int t0 = (c0 + cp) * CH;
-      const int nval = min(CH, a.T - t0);
-      uint16_t* obase = go + (static_cast<int64_t>(b) * a.T + t0) * a.so + hv * DK + 32 * strip;
+      const int ci = lo - cs + cp;   // chunk index inside the sequence
+      const int nval = min(CH, len - ci * CH);
+      uint16_t* obase = go + (tok0 + static_cast<int64_t>(ci) * CH) * a.so + hv * DK + 32 * strip;
       u16x8 x[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -866,7 +928,13 @@ size_t chunk_ws_bytes_per_chunk(const RecArgs& a) {
   return static_cast<size_t>(a.B) * (static_cast<size_t>(a.Hv) * WH_BYTES + static_cast<size_t>(a.Hk) * WK_BYTES);
 }
 
-size_t chunk_ws_carry_bytes(const RecArgs& a) { return static_cast<size_t>(a.B) * a.Hv * DK * DK * 4; }
+size_t chunk_ws_carry_bytes(const RecArgs& a) {
+  return static_cast<size_t>(a.cu_seqlens ? a.nseq : a.B) * a.Hv * DK * DK * 4;
+}
+
+// Chunks the windows run over: ceil(T/64) per sequence, or for packed sequences at
+// most ceil(T/64) + nseq (each sequence ends in at most one partial chunk).
+int chunk_count(const RecArgs& a) { return (a.T + CH - 1) / CH + (a.cu_seqlens ? a.nseq : 0); }
 
 // Chunks per window.  The chain kernel reads a window's operands back from the
 // memory-side last-level cache (256 MB) when they are still there: with the whole
@@ -876,7 +944,7 @@ size_t chunk_ws_carry_bytes(const RecArgs& a) { return static_cast<size_t>(a.B) 
 // the prep kernel fewer than two (chunk, key head) workgroups per CU (512 on 256
 // CUs), and never more than 256 MiB.  Windows are then balanced.
 int chunk_window_chunks(const RecArgs& a) {
-  const int nchunks = (a.T + CH - 1) / CH;
+  const int nchunks = chunk_count(a);
   const size_t per = chunk_ws_bytes_per_chunk(a);
   const int items = a.Hk * a.B;
   int w = static_cast<int>((size_t(96) << 20) / per);
@@ -899,7 +967,8 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int nchunks = (a.T + CH - 1) / CH;
+  const int nchunks = chunk_count(a);
+  if (nchunks == 0) return hipSuccess;
   const size_t per_chunk = chunk_ws_bytes_per_chunk(a);
   // One window when the whole sequence fits; otherwise the state is carried
   // between windows through state_out (or a carry area at the workspace end).
@@ -916,19 +985,16 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
   if (nwin > nchunks) nwin = nchunks;
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   float* carry = need_carry ? reinterpret_cast<float*>(wsb + static_cast<size_t>(nwin) * per_chunk) : a.state_out;
-  const float* sin = a.state_in;
+  const int nseqs = a.cu_seqlens ? a.nseq : a.B;
   for (int c0 = 0; c0 < nchunks; c0 += nwin) {
     const int nw = min(nwin, nchunks - c0);
-    const bool last = c0 + nw >= nchunks;
-    float* sout = last ? a.state_out : carry;
     hipLaunchKernelGGL(chunk_prep_kernel, dim3(nw, a.Hk, a.B), dim3(256), PrepLds::bytes(a.G), s, a, c0, wsb, nwin);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_chain_kernel, dim3(a.B * a.Hv * (DK / 32)), dim3(192), ChainLds::kBytes, s, a, c0,
-                       static_cast<const unsigned char*>(wsb), nwin, sin, sout);
+    hipLaunchKernelGGL(chunk_chain_kernel, dim3(nseqs * a.Hv * (DK / 32)), dim3(192), ChainLds::kBytes, s, a, c0,
+                       static_cast<const unsigned char*>(wsb), nwin, nw, carry);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    sin = sout;
   }
   return hipSuccess;
 }

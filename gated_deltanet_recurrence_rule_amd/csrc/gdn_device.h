@@ -47,6 +47,16 @@ struct IoTraits<uint16_t> {  // bf16 bit patterns
 };
 
 // Sum over the 64 lanes of a wave (result in every lane).
+// Token range of sequence s of a packed batch: [cu[s], cu[s+1]), clamped into
+// [0, T] and to a non-negative length, so that a malformed offset table can
+// give wrong results but never send a kernel outside the token arrays.
+__device__ __forceinline__ void packed_range(const int32_t* cu, int s, int T, int64_t& start, int& len) {
+  const int lo = min(max(cu[s], 0), T);
+  const int hi = min(max(cu[s + 1], lo), T);
+  start = lo;
+  len = hi - lo;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);

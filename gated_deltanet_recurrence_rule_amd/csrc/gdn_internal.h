@@ -33,6 +33,11 @@ struct RecArgs {
   const float* A_log = nullptr;
   const float* dt_bias = nullptr;
   const int32_t* slots = nullptr;
+  // Variable-length batch: nseq sequences packed along the token axis, sequence s
+  // holding tokens [cu_seqlens[s], cu_seqlens[s+1]).  The chunked kernels then see
+  // B == 1 (one packed token stream); chunks never span two sequences.
+  const int32_t* cu_seqlens = nullptr;
+  int32_t nseq = 0;
 };
 
 // io: 0 = fp32, 1 = bf16 (same codes as gdn_dtype).
@@ -72,7 +77,8 @@ hipError_t launch_decode_layer(const LayerArgs& a, hipStream_t s);
 // needs several windows and there is no state_out, a state carry follows.
 size_t chunk_ws_bytes_per_chunk(const RecArgs& a);
 size_t chunk_ws_carry_bytes(const RecArgs& a);
-// preferred number of chunks per window (balanced windows)
+// chunks the windows run over, and the preferred number per window (balanced)
+int chunk_count(const RecArgs& a);
 int chunk_window_chunks(const RecArgs& a);
 hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 

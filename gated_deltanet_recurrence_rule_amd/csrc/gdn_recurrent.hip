@@ -72,8 +72,12 @@ __global__ __launch_bounds__(RecShape<D>::NT) void recurrent_kernel(RecArgs a) {
     for (int r = 0; r < RPT; ++r) M[r] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int t = 0; t < a.T; ++t) {
-    const int64_t tok = static_cast<int64_t>(b) * a.T + t;
+  // tokens of this sequence: [b*T, b*T + T), or its packed range
+  int64_t tbase = static_cast<int64_t>(b) * a.T;
+  int ntok = a.T;
+  if (a.cu_seqlens) packed_range(a.cu_seqlens, b, a.T, tbase, ntok);
+  for (int t = 0; t < ntok; ++t) {
+    const int64_t tok = tbase + t;
     if (tid < 64) {
       float qv[QPL], kv[QPL];
       float sqq = 0.f, skk = 0.f, sqk = 0.f;
@@ -347,7 +351,8 @@ __global__ __launch_bounds__(256) void decode_layer_kernel(LayerArgs a) {
 
 template <int D, typename IO>
 hipError_t launch_rec(const RecArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.B * a.Hv));
+  const dim3 grid(static_cast<unsigned>((a.cu_seqlens ? a.nseq : a.B) * a.Hv));
+  if (grid.x == 0) return hipSuccess;
   hipLaunchKernelGGL((recurrent_kernel<D, IO>), grid, dim3(RecShape<D>::NT), 0, s, a);
   return hipGetLastError();
 }

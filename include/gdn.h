@@ -142,6 +142,33 @@ gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const
 size_t gdn_prefill_workspace_size(const gdn_dims* dims);
 
 /*
+ * gdn_prefill_varlen -- prefill of dims->B sequences of different lengths
+ * packed along the token axis (a continuous-batching prefill; "Chapitre 16",
+ * 16.2: each request's prompt is processed block by block and its state is
+ * handed from block to block; "L'etat, en memoire": one fixed-size state per
+ * request).  Sequence s holds tokens [cu_seqlens[s], cu_seqlens[s+1]) of the
+ * packed tensors; dims->T is the total token count.
+ *   cu_seqlens  [B+1] int32 DEVICE memory: cu_seqlens[0] = 0, non-decreasing,
+ *               cu_seqlens[B] = T (device data: not checked on the host; the
+ *               kernels clamp every range into [0, T], so a malformed table
+ *               gives unspecified results but no access outside the arrays);
+ *               empty sequences are allowed and pass their state through
+ *   q, k [T, Hk, Dk]; v, o [T, Hv, Dv]; log_alpha, beta [T, Hv]: as gdn_prefill
+ *               with B = 1 (token strides stride_q/k/v/o)
+ *   state_in / state_out [B, Hv, Dk, Dv] fp32 per sequence, as gdn_prefill
+ *   workspace   gdn_prefill_varlen_workspace_size bytes (or fewer, down to one
+ *               chunk per window plus the state carry)
+ * Chunks never span two sequences; every other rule is gdn_prefill's.
+ */
+gdn_status gdn_prefill_varlen(const gdn_dims* dims, const int32_t* cu_seqlens, const void* q, const void* k,
+                              const void* v, const float* log_alpha, const float* beta, const float* state_in,
+                              float* state_out, void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* gdn_prefill_varlen_workspace_size -- workspace bytes gdn_prefill_varlen wants
+ * for these dims (B sequences, T tokens in all), whatever the lengths. */
+size_t gdn_prefill_varlen_workspace_size(const gdn_dims* dims);
+
+/*
  * gdn_decode_step -- one token per sequence from a resident state
  * ("Chapitre 16", 16.3).  dims->T must be 1.
  *   q, k [B, Hk, Dk]; v, o [B, Hv, Dv] (io dtype, per-sequence strides

@@ -55,6 +55,22 @@ def test_workspace_size():
     assert ws(dims(T=64, Hk=1, Hv=65)) == 0             # more: token-serial, no workspace
 
 
+def test_varlen_workspace_size_and_errors():
+    ws = B.gdn_prefill_varlen_workspace_size
+    # 3 packed sequences, 4096 tokens: at most 64 + 3 chunks, balanced windows of 23, a carry per sequence
+    per = 48 * 56320 + 16 * 16384
+    assert ws(dims(B=3, T=4096, Hk=16, Hv=48)) == 23 * per + 3 * 48 * 128 * 128 * 4
+    assert ws(dims(B=2, T=100, Hk=2, Hv=6)) == 4 * (6 * 56320 + 2 * 16384)   # one window of 2 + 2 chunks
+    assert ws(dims(B=0, T=0)) == 0
+    L = B.lib()
+    call = lambda cu, d=None: L.gdn_prefill_varlen(ctypes.byref(d or dims(B=2, T=100)), cu, FAKE, FAKE, FAKE, FAKE,
+                                                   FAKE, None, None, FAKE, ctypes.c_void_p(0x100000), 1 << 30, None)
+    assert call(None) == B.GDN_ERR_NULL
+    assert call(ctypes.c_void_p(0x10002)) == B.GDN_ERR_ALIGN
+    assert call(FAKE, dims(B=2, T=100, Hv=5)) == B.GDN_ERR_SHAPE
+    assert call(FAKE, dims(B=0, T=0)) == B.GDN_OK
+
+
 def test_version_and_struct_layout():
     assert B.gdn_version() == 200
     # gdn_dims: 8 x int32, 4 x int64, 2 x float -> 72 bytes with natural alignment
