@@ -296,6 +296,70 @@ def bench_long(dev, steps=3, warmup=4):
                 hbm_frac=by / (med * 1e-3) / (HBM_PEAK_GBS * 1e9))
 
 
+def varlen_lengths(n=32, lo=16, hi=8192, seed=6):
+    """Lengths of a continuous-batching prefill: n requests, log-uniform on [lo, hi]."""
+    rng = np.random.default_rng(seed)
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), n)).astype(np.int64)
+
+
+def bench_varlen(dev, steps=20, warmup=20):
+    """Packed prefill of 32 requests of log-uniform lengths (16 to 8192 tokens,
+    seeded), 16/48 heads, one gdn_prefill_varlen call per step, final states into a
+    [32, 48, 128, 128] pool; beside it, the same requests as one gdn_prefill call
+    each.  Inputs drawn on the GPU."""
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding as G
+    lens = varlen_lengths()
+    Hk, Hv, D = 16, 48, 128
+    T = int(lens.sum())
+    cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu = torch.from_numpy(cu_h).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+
+    def unit(h):
+        a = torch.randn((T, h, D), generator=g, device=dev)
+        return (a / a.norm(dim=-1, keepdim=True)).reshape(T, h * D).to(torch.bfloat16)
+
+    q, k = unit(Hk), unit(Hk)
+    v = torch.randn((T, Hv * D), generator=g, device=dev).to(torch.bfloat16)
+    A = torch.rand((Hv,), generator=g, device=dev) * float(np.log(16.0))
+    dt = 0.5 * torch.randn((Hv,), generator=g, device=dev)
+    la = (-torch.exp(A) * torch.nn.functional.softplus(torch.randn((T, Hv), generator=g, device=dev) + dt)).contiguous()
+    be = torch.sigmoid(torch.randn((T, Hv), generator=g, device=dev)).contiguous()
+    o = torch.empty_like(v)
+    n = len(lens)
+    so = torch.empty((n, Hv, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(G.gdn_prefill_varlen_workspace_size(G.make_dims(n, T, Hk, Hv, D, G.GDN_BF16)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    fn = lambda: G.gdn_prefill_varlen(q, k, v, la, be, cu, None, so, o, Hk=Hk, Hv=Hv, workspace=ws, stream=stream)
+    _, _, med = timed_launches(fn, steps, warmup, stream)
+    # the same requests, one call each (views into the packed tensors; per-call workspaces)
+    views = []
+    for s in range(n):
+        a, b = int(cu_h[s]), int(cu_h[s + 1])
+        L = b - a
+        wsz = G.gdn_prefill_workspace_size(G.make_dims(1, L, Hk, Hv, D, G.GDN_BF16))
+        assert wsz <= ws.numel()
+        views.append((q[a:b].unsqueeze(0), k[a:b].unsqueeze(0), v[a:b].unsqueeze(0), la[a:b].unsqueeze(0),
+                      be[a:b].unsqueeze(0), so[s:s + 1], o[a:b].unsqueeze(0), ws[:wsz]))
+
+    def each():
+        for qq, kk, vv, ll, bb, ss, oo, ww in views:
+            G.gdn_prefill(qq, kk, vv, ll, bb, None, ss, oo, Hk=Hk, Hv=Hv, workspace=ww, stream=stream)
+
+    _, _, med_each = timed_launches(each, max(steps // 4, 3), 3, stream)
+    fl = prefill_flops(1, T, Hk, Hv, D)
+    by = prefill_bytes(1, T, Hk, Hv, D) + (n - 1) * Hv * D * D * 4
+    del q, k, v, o, ws
+    torch.cuda.empty_cache()
+    return dict(n_seq=n, tokens=T, min_len=int(lens.min()), max_len=int(lens.max()), ms=med,
+                tokens_per_s=T / (med * 1e-3), hbm_frac=by / (med * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                mfma_frac=fl / (med * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                one_call_per_seq_ms=med_each, one_call_per_seq_tokens_per_s=T / (med_each * 1e-3))
+
+
 def cpu_baseline(reps=2):
     """The fp64 oracle (gdn_oracle.c, OpenMP) on the headline workload: all 48 value
     heads over all 4096 tokens, timed on this host's cores."""
@@ -431,6 +495,11 @@ def main():
         lg = bench_long(dev)
         print(f"[bench] long: {lg['ms']:.2f} ms", file=sys.stderr, flush=True)
         line["long"] = {"config": "batch 1, T=262144, 16 key / 48 value heads", **lg}
+        vl = bench_varlen(dev)
+        print(f"[bench] varlen: {vl['ms']:.3f} ms for {vl['tokens']} tokens in {vl['n_seq']} sequences "
+              f"({vl['one_call_per_seq_ms']:.3f} ms as one call each)", file=sys.stderr, flush=True)
+        line["varlen"] = {"config": "32 packed requests, log-uniform lengths 16..8192 (seed 6), 16 key / 48 value "
+                                    "heads, final states into a 32-entry pool", **vl}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

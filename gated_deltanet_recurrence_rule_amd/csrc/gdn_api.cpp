@@ -122,8 +122,9 @@ size_t workspace_size(const gdn_dims* d, const int32_t* cu) {
   const size_t per_chunk = gdn::chunk_ws_bytes_per_chunk(a);
   const int64_t nchunks = gdn::chunk_count(a);
   const int64_t nwin = gdn::chunk_window_chunks(a);
-  if (nwin >= nchunks) return static_cast<size_t>(nchunks) * per_chunk;
-  return static_cast<size_t>(nwin) * per_chunk + gdn::chunk_ws_carry_bytes(a);
+  const size_t maps = gdn::chunk_map_bytes(a);
+  if (nwin >= nchunks) return maps + static_cast<size_t>(nchunks) * per_chunk;
+  return maps + static_cast<size_t>(nwin) * per_chunk + gdn::chunk_ws_carry_bytes(a);
 }
 
 gdn_status prefill(const gdn_dims* d, const int32_t* cu, const void* q, const void* k, const void* v,
@@ -145,11 +146,12 @@ gdn_status prefill(const gdn_dims* d, const int32_t* cu, const void* q, const vo
     const gdn::RecArgs a = chunk_args(d, cu, q, k, v, log_alpha, beta, state_in, state_out, o);
     const size_t per_chunk = gdn::chunk_ws_bytes_per_chunk(a);
     const int64_t nchunks = gdn::chunk_count(a);
+    const size_t maps = gdn::chunk_map_bytes(a);
     const size_t need_min =
-        per_chunk + ((nchunks > 1 && !state_out) ? gdn::chunk_ws_carry_bytes(a) : 0);
+        maps + per_chunk + ((nchunks > 1 && !state_out) ? gdn::chunk_ws_carry_bytes(a) : 0);
     if (!workspace) return fail(GDN_ERR_NULL, "the chunked prefill needs a workspace");
     if (!aligned(workspace, 256)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
-    if (workspace_bytes < need_min && workspace_bytes < static_cast<size_t>(nchunks) * per_chunk)
+    if (workspace_bytes < need_min && workspace_bytes < maps + static_cast<size_t>(nchunks) * per_chunk)
       return fail(GDN_ERR_SHAPE, "workspace of %zu bytes is below the minimum %zu", workspace_bytes, need_min);
     return from_hip(gdn::launch_chunk_prefill(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
                     "gdn_prefill (chunk kernels)");

@@ -162,17 +162,13 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   int nval;
   int64_t tokbase;
   if (a.cu_seqlens) {
-    // packed sequences: global chunk c is chunk c - (chunks before s) of sequence s
-    int acc = 0, s = 0, len = 0;
-    int64_t start = 0;
-    for (; s < a.nseq; ++s) {
-      packed_range(a.cu_seqlens, s, a.T, start, len);
-      const int n = (len + CH - 1) / CH;
-      if (c < acc + n) break;
-      acc += n;
-    }
-    if (s == a.nseq) return;  // past the last chunk: the whole workgroup leaves
-    const int t0 = (c - acc) * CH;
+    // packed sequences: global chunk c is chunk c - chunk_start[s] of sequence s
+    const int s = a.chunk_seq[c];
+    if (s >= a.nseq) return;  // past the last chunk: the whole workgroup leaves
+    int len;
+    int64_t start;
+    packed_range(a.cu_seqlens, s, a.T, start, len);
+    const int t0 = (c - a.chunk_start[s]) * CH;
     tokbase = start + t0;
     nval = min(CH, len - t0);
   } else {
@@ -627,12 +623,7 @@ __device__ __forceinline__ void seq_chunks(const RecArgs& a, int b, int& cs, int
     len = a.T;
     return;
   }
-  int acc = 0;
-  for (int i = 0; i < b; ++i) {
-    packed_range(a.cu_seqlens, i, a.T, tok0, len);
-    acc += (len + CH - 1) / CH;
-  }
-  cs = acc;
+  cs = a.chunk_start[b];
   packed_range(a.cu_seqlens, b, a.T, tok0, len);
   ce = cs + (len + CH - 1) / CH;
 }
@@ -647,19 +638,28 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, h = lane >> 5;
   // Workgroups are handed to the 8 XCDs round-robin by linear index; when the
-  // (sequence, head) count is a multiple of 8, the 4 strips of a head get indices
+  // (slot, head) count is a multiple of 8, the 4 strips of a head get indices
   // that are equal modulo 8, so they share one XCD's L2 for the head's inputs.
   const int L0 = blockIdx.x;
-  const int nheads = (a.cu_seqlens ? a.nseq : a.B) * a.Hv;
-  int bhv, strip;
+  const int nheads = static_cast<int>(gridDim.x) >> 2;
+  int jh, strip;
   if ((nheads & 7) == 0) {
-    bhv = (L0 >> 5) * 8 + (L0 & 7);
+    jh = (L0 >> 5) * 8 + (L0 & 7);
     strip = (L0 >> 3) & 3;
   } else {
-    bhv = L0 >> 2;
+    jh = L0 >> 2;
     strip = L0 & 3;
   }
-  const int b = bhv / a.Hv, hv = bhv - b * a.Hv;   // sequence, value head
+  const int j = jh / a.Hv, hv = jh - j * a.Hv;   // slot, value head
+  int b = j;                                      // sequence
+  if (a.cu_seqlens) {
+    // packed batch: slot j stands for chunk c0 + j of the window and runs the
+    // sequence of that chunk when the sequence's part of the window starts there
+    const int c = c0 + j;
+    b = a.chunk_seq[c];
+    if (b >= a.nseq || (j > 0 && a.chunk_seq[c - 1] == b)) return;
+  }
+  const int bhv = b * a.Hv + hv;
   const int hk = hv / a.G;
   const int bw = a.cu_seqlens ? 0 : b;               // batch index inside the workspace
   const int bh = bw * a.Hv + hv;
@@ -667,18 +667,7 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
   int64_t tok0;
   seq_chunks(a, b, cs, ce, tok0, len);
   const int lo = max(cs, c0), hi = min(ce, c0 + nw);
-  if (lo >= hi) {
-    // no chunk of this sequence in the window: the whole workgroup leaves; an empty
-    // sequence hands its state on unchanged (in the first window)
-    if (len == 0 && c0 == 0 && a.state_out) {
-      const int64_t base = static_cast<int64_t>(bhv) * DK * DK + 32 * strip;
-      for (int i = tid; i < DK * 32; i += 192) {
-        const int64_t e = base + (i >> 5) * DK + (i & 31);
-        a.state_out[e] = a.state_in ? a.state_in[e] : 0.f;
-      }
-    }
-    return;
-  }
+  if (lo >= hi) return;
   const int lofs = lo - c0;
   const float* state_in = lo == cs ? a.state_in : carry;
   float* state_out = hi == ce ? a.state_out : carry;
@@ -922,10 +911,84 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
   }
 }
 
+// Packed batches: an empty sequence hands its state on unchanged (the zero state
+// without state_in).  One workgroup per (sequence, value head); the others leave.
+__global__ __launch_bounds__(256) void empty_state_kernel(RecArgs a) {
+  const int bhv = blockIdx.x, b = bhv / a.Hv;
+  int64_t st;
+  int len;
+  packed_range(a.cu_seqlens, b, a.T, st, len);
+  if (len) return;
+  const int64_t base = static_cast<int64_t>(bhv) * DK * DK;
+  const floatx4* src = reinterpret_cast<const floatx4*>(a.state_in + base);
+  floatx4* dst = reinterpret_cast<floatx4*>(a.state_out + base);
+  for (int i = threadIdx.x; i < DK * DK / 4; i += 256)
+    dst[i] = a.state_in ? src[i] : floatx4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Chunk maps of a packed batch, for the prep and chain kernels: one workgroup
+// scans the per-sequence chunk counts ceil(len/64) into chunk_start, then finds
+// each chunk's sequence by binary search (the last s with chunk_start[s] <= c, so
+// that empty sequences, which share their successor's start, are passed over).
+__global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* cu, int nseq, int T, int ncap,
+                                                         int32_t* chunk_start, int32_t* chunk_seq) {
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < nseq; base += 1024) {
+    const int s = base + tid;
+    int n = 0;
+    if (s < nseq) {
+      int64_t st;
+      int len;
+      packed_range(cu, s, T, st, len);
+      n = (len + CH - 1) / CH;
+    }
+    int x = n;  // inclusive scan inside the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      before += i < wv ? wsum[i] : 0;
+      total += wsum[i];
+    }
+    if (s < nseq) chunk_start[s] = carry + before + x - n;
+    carry += total;
+    __syncthreads();  // wsum is rewritten by the next block of sequences
+  }
+  if (tid == 0) chunk_start[nseq] = carry;
+  __syncthreads();  // chunk_start is complete and visible to the workgroup
+  for (int c = tid; c < ncap; c += 1024) {
+    int sq = nseq;
+    if (c < carry) {
+      int lo = 0, hi = nseq - 1;  // chunk_start[0] = 0 <= c
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_start[mid] <= c) lo = mid;
+        else hi = mid - 1;
+      }
+      sq = lo;
+    }
+    chunk_seq[c] = sq;
+  }
+}
+
 }  // namespace
 
 size_t chunk_ws_bytes_per_chunk(const RecArgs& a) {
   return static_cast<size_t>(a.B) * (static_cast<size_t>(a.Hv) * WH_BYTES + static_cast<size_t>(a.Hk) * WK_BYTES);
+}
+
+size_t chunk_map_bytes(const RecArgs& a) {
+  if (!a.cu_seqlens) return 0;
+  const size_t b = (static_cast<size_t>(a.nseq) + 1 + chunk_count(a)) * 4;
+  return (b + 255) & ~size_t(255);
 }
 
 size_t chunk_ws_carry_bytes(const RecArgs& a) {
@@ -936,19 +999,24 @@ size_t chunk_ws_carry_bytes(const RecArgs& a) {
 // most ceil(T/64) + nseq (each sequence ends in at most one partial chunk).
 int chunk_count(const RecArgs& a) { return (a.T + CH - 1) / CH + (a.cu_seqlens ? a.nseq : 0); }
 
+// Prep workgroups resident at once on the 256 CUs: their LDS lets two share a CU
+// up to 24 value heads per key head, one beyond.
+int prep_slots(int G) { return 256 * max(1, min(2, (160 * 1024) / PrepLds::bytes(G))); }
+
 // Chunks per window.  The chain kernel reads a window's operands back from the
 // memory-side last-level cache (256 MB) when they are still there: with the whole
 // T=4096, 16/48-head workspace (190 MB) in one window, the prep's input reads and
 // the outputs push part of it out, and the chain runs 20 % slower than with two
-// windows of 95 MB.  So a window is about 96 MiB of workspace, unless that leaves
-// the prep kernel fewer than two (chunk, key head) workgroups per CU (512 on 256
-// CUs), and never more than 256 MiB.  Windows are then balanced.
+// windows of 95 MB.  The prep kernel costs about one workgroup's latency per round
+// of resident workgroups, so a window is a whole number of rounds (at least one):
+// as many as keep it within about 96 MiB of workspace, and never more than
+// 256 MiB.  Windows are then balanced, which never adds a round.
 int chunk_window_chunks(const RecArgs& a) {
   const int nchunks = chunk_count(a);
   const size_t per = chunk_ws_bytes_per_chunk(a);
-  const int items = a.Hk * a.B;
-  int w = static_cast<int>((size_t(96) << 20) / per);
-  w = max(w, (512 + items - 1) / items);
+  const int round = max(1, prep_slots(a.G) / (a.Hk * a.B));   // chunks one round of prep covers
+  const int fit = static_cast<int>((size_t(96) << 20) / per);
+  int w = max(1, fit / round) * round;
   w = min(w, static_cast<int>((size_t(256) << 20) / per));
   w = max(w, 1);
   if (w >= nchunks) return nchunks;
@@ -969,6 +1037,27 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
   }
   const int nchunks = chunk_count(a);
   if (nchunks == 0) return hipSuccess;
+  RecArgs r = a;
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  if (a.cu_seqlens) {
+    // packed batch: chunk maps first, at the workspace start
+    const size_t mb = chunk_map_bytes(a);
+    if (ws_bytes < mb) return hipErrorInvalidValue;
+    int32_t* cstart = reinterpret_cast<int32_t*>(wsb);
+    int32_t* cseq = cstart + a.nseq + 1;
+    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, s, a.cu_seqlens, a.nseq, a.T, nchunks, cstart, cseq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.state_out) {
+      hipLaunchKernelGGL(empty_state_kernel, dim3(a.nseq * a.Hv), dim3(256), 0, s, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    r.chunk_start = cstart;
+    r.chunk_seq = cseq;
+    wsb += mb;
+    ws_bytes -= mb;
+  }
   const size_t per_chunk = chunk_ws_bytes_per_chunk(a);
   // One window when the whole sequence fits; otherwise the state is carried
   // between windows through state_out (or a carry area at the workspace end).
@@ -983,15 +1072,17 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
   }
   if (nwin < 1) return hipErrorInvalidValue;
   if (nwin > nchunks) nwin = nchunks;
-  unsigned char* wsb = static_cast<unsigned char*>(ws);
   float* carry = need_carry ? reinterpret_cast<float*>(wsb + static_cast<size_t>(nwin) * per_chunk) : a.state_out;
-  const int nseqs = a.cu_seqlens ? a.nseq : a.B;
   for (int c0 = 0; c0 < nchunks; c0 += nwin) {
     const int nw = min(nwin, nchunks - c0);
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3(nw, a.Hk, a.B), dim3(256), PrepLds::bytes(a.G), s, a, c0, wsb, nwin);
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3(nw, a.Hk, a.B), dim3(256), PrepLds::bytes(a.G), s, r, c0, wsb, nwin);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_chain_kernel, dim3(nseqs * a.Hv * (DK / 32)), dim3(192), ChainLds::kBytes, s, a, c0,
+    // chain workgroups per (sequence, value head, strip); for a packed batch per
+    // (chunk slot of the window, value head, strip), since at most nw sequences
+    // have chunks in the window
+    const int slots = a.cu_seqlens ? nw : a.B;
+    hipLaunchKernelGGL(chunk_chain_kernel, dim3(slots * a.Hv * (DK / 32)), dim3(192), ChainLds::kBytes, s, r, c0,
                        static_cast<const unsigned char*>(wsb), nwin, nw, carry);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -38,6 +38,12 @@ struct RecArgs {
   // B == 1 (one packed token stream); chunks never span two sequences.
   const int32_t* cu_seqlens = nullptr;
   int32_t nseq = 0;
+  // Chunked kernels on a packed batch: chunk_start[s] is the first chunk of
+  // sequence s in the window numbering ([nseq + 1] entries), chunk_seq[c] the
+  // sequence of chunk c (nseq past the last chunk).  Written into the workspace
+  // by the launcher's map kernel.
+  const int32_t* chunk_start = nullptr;
+  const int32_t* chunk_seq = nullptr;
 };
 
 // io: 0 = fp32, 1 = bf16 (same codes as gdn_dtype).
@@ -72,11 +78,14 @@ struct LayerArgs {
 };
 hipError_t launch_decode_layer(const LayerArgs& a, hipStream_t s);
 // Chunked prefill: a prep kernel and a chain kernel per window of chunks.
-// The workspace holds, per (b, value head, chunk of the window), the
-// fragments and row scalings the prep kernel produces; when the sequence
-// needs several windows and there is no state_out, a state carry follows.
+// The workspace holds the chunk maps of a packed batch, then, per (b, value
+// head, chunk of the window), the fragments and row scalings the prep kernel
+// produces; when the sequence needs several windows and there is no state_out,
+// a state carry follows.
 size_t chunk_ws_bytes_per_chunk(const RecArgs& a);
 size_t chunk_ws_carry_bytes(const RecArgs& a);
+// packed batches: the chunk maps at the workspace start (a multiple of 256 bytes; 0 otherwise)
+size_t chunk_map_bytes(const RecArgs& a);
 // chunks the windows run over, and the preferred number per window (balanced)
 int chunk_count(const RecArgs& a);
 int chunk_window_chunks(const RecArgs& a);

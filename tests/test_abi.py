@@ -40,13 +40,17 @@ def test_workspace_size():
     # windows of ~96 MiB, balanced: 64 chunks of 2.97 MB -> 2 windows of 32, plus a state carry
     per = 48 * 56320 + 16 * 16384
     assert ws(dims(T=4096, Hk=16, Hv=48)) == 32 * per + 48 * 128 * 128 * 4
-    # ... but at least 512 / (Hk B) = 8 chunks: windows of 8 (228 MiB) + a state carry
+    # ... but at least one round of prep workgroups, 512 / (Hk B) = 8 chunks: windows of 8 (228 MiB) + a carry
     big = dims(B=4, T=32768, Hk=16, Hv=128)
     per = 4 * (128 * 56320 + 16 * 16384)
     assert ws(big) == 8 * per + 4 * 128 * 128 * 128 * 4
-    # long sequence: 4096 chunks in 125 balanced windows of 33
+    # long sequence: 4096 chunks in 128 windows of 32 (one round of 512 prep workgroups each)
     per = 48 * 56320 + 16 * 16384
-    assert ws(dims(T=262144, Hk=16, Hv=48)) == 33 * per + 48 * 128 * 128 * 4
+    assert ws(dims(T=262144, Hk=16, Hv=48)) == 32 * per + 48 * 128 * 128 * 4
+    # 32 value heads per key head: one prep workgroup per CU, a round is 256 chunks; the
+    # 256 MiB cap gives 147 chunks, balanced over 300 chunks: 3 windows of 100
+    per = 32 * 56320 + 16384
+    assert ws(dims(T=64 * 300, Hk=1, Hv=32)) == 100 * per + 32 * 128 * 128 * 4
     assert ws(dims(Hv=5)) == 0                          # invalid dims
     d = dims(T=64)
     d.flags = B.GDN_FLAG_TOKEN_SERIAL                   # token-serial path forced: none
@@ -57,10 +61,11 @@ def test_workspace_size():
 
 def test_varlen_workspace_size_and_errors():
     ws = B.gdn_prefill_varlen_workspace_size
-    # 3 packed sequences, 4096 tokens: at most 64 + 3 chunks, balanced windows of 23, a carry per sequence
+    # 3 packed sequences, 4096 tokens: chunk maps ((3 + 1) + 67 int32, rounded up to 256 bytes),
+    # at most 64 + 3 chunks in balanced windows of 23, a carry per sequence
     per = 48 * 56320 + 16 * 16384
-    assert ws(dims(B=3, T=4096, Hk=16, Hv=48)) == 23 * per + 3 * 48 * 128 * 128 * 4
-    assert ws(dims(B=2, T=100, Hk=2, Hv=6)) == 4 * (6 * 56320 + 2 * 16384)   # one window of 2 + 2 chunks
+    assert ws(dims(B=3, T=4096, Hk=16, Hv=48)) == 512 + 23 * per + 3 * 48 * 128 * 128 * 4
+    assert ws(dims(B=2, T=100, Hk=2, Hv=6)) == 256 + 4 * (6 * 56320 + 2 * 16384)   # one window of 2 + 2 chunks
     assert ws(dims(B=0, T=0)) == 0
     L = B.lib()
     call = lambda cu, d=None: L.gdn_prefill_varlen(ctypes.byref(d or dims(B=2, T=100)), cu, FAKE, FAKE, FAKE, FAKE,

@@ -119,9 +119,10 @@ def test_varlen_small_workspace_windows(with_state_out):
     dims = G.make_dims(len(LENS), p["T"], Hk, Hv, D, G.GDN_BF16)
     per_chunk = Hv * 56320 + Hk * 16384
     nchunks = (p["T"] + 63) // 64 + len(LENS)
-    assert G.gdn_prefill_varlen_workspace_size(dims) == nchunks * per_chunk
+    maps = -(-(len(LENS) + 1 + nchunks) * 4 // 256) * 256   # chunk maps at the workspace start
+    assert G.gdn_prefill_varlen_workspace_size(dims) == maps + nchunks * per_chunk
     for nwin in (1, 2, 3):
-        extra = 0 if with_state_out else len(LENS) * Hv * D * D * 4
+        extra = maps + (0 if with_state_out else len(LENS) * Hv * D * D * 4)
         ws = torch.empty(nwin * per_chunk + extra, dtype=torch.uint8, device="cuda")
         og, sg = run_packed(p, st, cu, with_state_out=with_state_out, workspace=ws)
         assert_out(og, orf, bf16=True)
@@ -157,3 +158,32 @@ def test_varlen_all_empty_and_no_sequences():
     assert torch.count_nonzero(so).item() == 0
     G.gdn_prefill_varlen(z, z, zv, g, g, to_dev(np.zeros(1, dtype=np.int32)), None, None, Hk=Hk, Hv=Hv)
     torch.cuda.synchronize()
+
+
+def test_varlen_many_sequences():
+    """1100 sequences (more than the map kernel's 1024 threads scan at once), many of
+    them empty or one chunk long, one of 300 tokens, with windows of four chunks."""
+    torch = _torch()
+    Hk, Hv, D = 1, 1, 128
+    rng = np.random.default_rng(5600)
+    lens = rng.integers(0, 20, 1100)
+    lens[rng.choice(1100, 150, replace=False)] = 0
+    lens[500] = 300
+    lens = [int(x) for x in lens]
+    p, st, cu = packed_problem(5600, lens, Hk, Hv, D, "bf16")
+    orf, srf = oracle_packed(p, st, cu)
+    og, sg = run_packed(p, st, cu)
+    assert_out(og, orf, bf16=True)
+    check_states(sg, srf, lens)
+    dims = G.make_dims(len(lens), p["T"], Hk, Hv, D, G.GDN_BF16)
+    full = G.gdn_prefill_varlen_workspace_size(dims)
+    nchunks = (p["T"] + 63) // 64 + len(lens)
+    maps = -(-(len(lens) + 1 + nchunks) * 4 // 256) * 256
+    # windows of 1024 chunks (two rounds of 512 prep workgroups, 71 MiB) balanced over 1245: two of 623,
+    # plus a state carry per sequence
+    assert nchunks == 1245
+    assert full == maps + 623 * (56320 + 16384) + len(lens) * D * D * 4
+    ws = torch.empty(maps + 4 * (56320 + 16384), dtype=torch.uint8, device="cuda")
+    og2, sg2 = run_packed(p, st, cu, workspace=ws)
+    np.testing.assert_array_equal(og2, og)   # windows do not change the arithmetic
+    np.testing.assert_array_equal(sg2, sg)
