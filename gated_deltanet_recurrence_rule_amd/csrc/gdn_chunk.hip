@@ -1009,16 +1009,20 @@ int prep_slots(int G) { return 256 * max(1, min(2, (160 * 1024) / PrepLds::bytes
 // the outputs push part of it out, and the chain runs 20 % slower than with two
 // windows of 95 MB.  The prep kernel costs about one workgroup's latency per round
 // of resident workgroups, so a window is a whole number of rounds (at least one):
-// as many as keep it within about 96 MiB of workspace, and never more than
-// 256 MiB.  Windows are then balanced, which never adds a round.
+// as many as keep it within about 96 MiB of workspace.  When one round alone
+// exceeds that, the cache cannot hold a window anyway and each window only adds
+// launches (batch 4, T=32768, 16/128 heads: 13.7 ms with windows of 8 chunks,
+// 10.7 ms with 64), so windows then take as many rounds as fit in 2 GiB.
+// Windows are then balanced, which never adds a round.
 int chunk_window_chunks(const RecArgs& a) {
   const int nchunks = chunk_count(a);
   const size_t per = chunk_ws_bytes_per_chunk(a);
   const int round = max(1, prep_slots(a.G) / (a.Hk * a.B));   // chunks one round of prep covers
-  const int fit = static_cast<int>((size_t(96) << 20) / per);
+  const size_t cache = size_t(96) << 20;
+  const size_t budget = static_cast<size_t>(round) * per <= cache ? cache : size_t(2) << 30;
+  const int fit = static_cast<int>(min(budget / per, static_cast<size_t>(1) << 30));
   int w = max(1, fit / round) * round;
-  w = min(w, static_cast<int>((size_t(256) << 20) / per));
-  w = max(w, 1);
+  w = max(1, min(w, fit));
   if (w >= nchunks) return nchunks;
   const int nwins = (nchunks + w - 1) / w;
   return (nchunks + nwins - 1) / nwins;

@@ -40,17 +40,19 @@ def test_workspace_size():
     # windows of ~96 MiB, balanced: 64 chunks of 2.97 MB -> 2 windows of 32, plus a state carry
     per = 48 * 56320 + 16 * 16384
     assert ws(dims(T=4096, Hk=16, Hv=48)) == 32 * per + 48 * 128 * 128 * 4
-    # ... but at least one round of prep workgroups, 512 / (Hk B) = 8 chunks: windows of 8 (228 MiB) + a carry
+    # one round of prep workgroups, 512 / (Hk B) = 8 chunks, is already 228 MiB here: the cache cannot
+    # hold a window, so windows take as many rounds as fit in 2 GiB: 64 chunks (1.78 GiB) + a carry
     big = dims(B=4, T=32768, Hk=16, Hv=128)
     per = 4 * (128 * 56320 + 16 * 16384)
-    assert ws(big) == 8 * per + 4 * 128 * 128 * 128 * 4
+    assert ws(big) == 64 * per + 4 * 128 * 128 * 128 * 4
     # long sequence: 4096 chunks in 128 windows of 32 (one round of 512 prep workgroups each)
     per = 48 * 56320 + 16 * 16384
     assert ws(dims(T=262144, Hk=16, Hv=48)) == 32 * per + 48 * 128 * 128 * 4
-    # 32 value heads per key head: one prep workgroup per CU, a round is 256 chunks; the
-    # 256 MiB cap gives 147 chunks, balanced over 300 chunks: 3 windows of 100
+    # 32 value heads per key head: one prep workgroup per CU, a round is 256 chunks (466 MB), so
+    # windows fill 2 GiB: 1024 chunks, and all 300 chunks fit in one window
     per = 32 * 56320 + 16384
-    assert ws(dims(T=64 * 300, Hk=1, Hv=32)) == 100 * per + 32 * 128 * 128 * 4
+    assert ws(dims(T=64 * 300, Hk=1, Hv=32)) == 300 * per
+    assert ws(dims(T=64 * 2000, Hk=1, Hv=32)) == 1000 * per + 32 * 128 * 128 * 4   # 2 windows of 1000
     assert ws(dims(Hv=5)) == 0                          # invalid dims
     d = dims(T=64)
     d.flags = B.GDN_FLAG_TOKEN_SERIAL                   # token-serial path forced: none
