@@ -1,4 +1,4 @@
-"""ctypes binding of libgdn (include/gdn.h): argument marshalling only.
+"""ctypes binding of libgdn (include/gdn.h, include/gdn_attn.h): argument marshalling only.
 
 Each function takes torch tensors, checks their layout enough to build the C
 arguments (pointers, element strides, the current HIP stream) and calls the
@@ -19,11 +19,12 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_QK_L2NORM = 1
 GDN_FLAG_TOKEN_SERIAL = 2
 
-# Every exported symbol, in the order include/gdn.h declares them.
+# Every exported symbol, in the order include/gdn.h, then include/gdn_attn.h declare them.
 EXPORTS = ("gdn_prefill", "gdn_prefill_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_size",
            "gdn_decode_step", "gdn_conv1d_silu",
            "gdn_gated_rmsnorm", "gdn_gates", "gdn_decode_token", "gdn_decode_layer", "gdn_last_error",
-           "gdn_version")
+           "gdn_version",
+           "gdn_attn_prefill", "gdn_attn_prefill_workspace_size", "gdn_attn_decode", "gdn_attn_decode_workspace_size")
 
 
 class GdnDims(ctypes.Structure):
@@ -49,6 +50,16 @@ class GdnDecodeLayerArgs(ctypes.Structure):
         ("stride_out", ctypes.c_int64), ("o", p), ("stride_o", ctypes.c_int64),
     ]
     del p
+
+
+class GdnAttnDims(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("rot_dim", ctypes.c_int32), ("S_max", ctypes.c_int32),
+        ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float), ("scale", ctypes.c_float),
+        ("stride_qg", ctypes.c_int64), ("stride_k", ctypes.c_int64), ("stride_v", ctypes.c_int64),
+        ("stride_o", ctypes.c_int64),
+    ]
 
 
 class GdnError(RuntimeError):
@@ -89,6 +100,15 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_token.restype = ctypes.c_int
         L.gdn_decode_layer.argtypes = [ctypes.POINTER(GdnDecodeLayerArgs), p]
         L.gdn_decode_layer.restype = ctypes.c_int
+        AD = ctypes.POINTER(GdnAttnDims)
+        L.gdn_attn_prefill.argtypes = [AD, p, p, p, p, p, p, p, p, p, ctypes.c_size_t, p]
+        L.gdn_attn_prefill.restype = ctypes.c_int
+        L.gdn_attn_prefill_workspace_size.argtypes = [AD]
+        L.gdn_attn_prefill_workspace_size.restype = ctypes.c_size_t
+        L.gdn_attn_decode.argtypes = [AD, p, p, p, p, p, p, p, p, p, p, ctypes.c_size_t, p]
+        L.gdn_attn_decode.restype = ctypes.c_int
+        L.gdn_attn_decode_workspace_size.argtypes = [AD]
+        L.gdn_attn_decode_workspace_size.restype = ctypes.c_size_t
         L.gdn_last_error.argtypes = []
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_version.argtypes = []
@@ -419,3 +439,95 @@ def gdn_version() -> int:
 
 def gdn_last_error() -> str:
     return lib().gdn_last_error().decode()
+
+
+# -- full-attention layer (include/gdn_attn.h) ---------------------------------
+
+def make_attn_dims(B: int, T: int, Hq: int, Hkv: int, D: int = 256, S_max: int = 64, rot_dim: int = 64,
+                   rope_theta: float = 1e7, norm_eps: float = 1e-6, scale: float | None = None,
+                   stride_qg: int | None = None, stride_k: int | None = None, stride_v: int | None = None,
+                   stride_o: int | None = None) -> GdnAttnDims:
+    return GdnAttnDims(B, T, Hq, Hkv, D, rot_dim, S_max, rope_theta, norm_eps,
+                       D ** -0.5 if scale is None else scale,
+                       2 * Hq * D if stride_qg is None else stride_qg, Hkv * D if stride_k is None else stride_k,
+                       Hkv * D if stride_v is None else stride_v, Hq * D if stride_o is None else stride_o)
+
+
+def attn_cache(B: int, Hkv: int, S_max: int, D: int = 256, device="cuda"):
+    """Zeroed key and value caches in the layout gdn_attn.h describes:
+    k [B, Hkv, S_max, D] and v [B, Hkv, S_max // 64, D, 64], bf16."""
+    import torch
+    k = torch.zeros((B, Hkv, S_max, D), dtype=torch.bfloat16, device=device)
+    v = torch.zeros((B, Hkv, S_max // 64, D, 64), dtype=torch.bfloat16, device=device)
+    return k, v
+
+
+def _rows(t, lead: int, width: int, name: str) -> int:
+    """Token stride of a bf16 tensor whose first `lead` dims index tokens (batch-major, the
+    token rows evenly spaced) and whose remaining dims are `width` contiguous elements."""
+    import torch
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16")
+    inner = 1
+    for n in t.shape[lead:]:
+        inner *= int(n)
+    if inner != width or (width and not t[(0,) * lead].is_contiguous() if t.numel() else False):
+        raise ValueError(f"{name}: each token row must be {width} contiguous elements")
+    st = int(t.stride(lead - 1))
+    if lead == 2 and t.shape[1] > 0 and int(t.stride(0)) != st * int(t.shape[1]):
+        raise ValueError(f"{name}: the sequence stride must be T times the token stride")
+    return st if t.numel() else width
+
+
+def gdn_attn_prefill(qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, o=None, *, rot_dim: int = 64,
+                     rope_theta: float = 1e7, norm_eps: float = 1e-6, scale: float | None = None,
+                     workspace=None, stream=None):
+    """qg [B, T, Hq, 2, D] (query then gate per head); k, v [B, T, Hkv, D]; q_norm_w, k_norm_w [D];
+    k_cache, v_cache from attn_cache (positions [0, T) are written); o [B, T, Hq, D] or None.
+    Returns o."""
+    import torch
+    B, T, Hq, two, D = (int(x) for x in qg.shape)
+    Hkv = int(k.shape[2])
+    if two != 2 or tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D):
+        raise ValueError("qg must be [B, T, Hq, 2, D] and k, v [B, T, Hkv, D]")
+    S_max = int(k_cache.shape[2])
+    if o is None:
+        o = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device=qg.device)
+    dims = make_attn_dims(B, T, Hq, Hkv, D, S_max, rot_dim, rope_theta, norm_eps, scale,
+                          _rows(qg, 2, 2 * Hq * D, "qg"), _rows(k, 2, Hkv * D, "k"), _rows(v, 2, Hkv * D, "v"),
+                          _rows(o, 2, Hq * D, "o"))
+    need = int(lib().gdn_attn_prefill_workspace_size(ctypes.byref(dims)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qg.device)
+    ws_len = 0 if workspace is None else workspace.numel()
+    _check(lib().gdn_attn_prefill(ctypes.byref(dims), _ptr(qg), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w),
+                                  _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(workspace), ws_len, _stream(stream)))
+    return o
+
+
+def gdn_attn_decode(qg, k, v, q_norm_w, k_norm_w, cache_len, k_cache, v_cache, o=None, *, rot_dim: int = 64,
+                    rope_theta: float = 1e7, norm_eps: float = 1e-6, scale: float | None = None,
+                    workspace=None, stream=None):
+    """One token per sequence: qg [B, Hq, 2, D]; k, v [B, Hkv, D]; cache_len [B] int32 on the device
+    (the new token's position); caches from attn_cache.  Returns o [B, Hq, D]."""
+    import torch
+    B, Hq, two, D = (int(x) for x in qg.shape)
+    Hkv = int(k.shape[1])
+    if two != 2 or tuple(k.shape) != (B, Hkv, D) or tuple(v.shape) != (B, Hkv, D):
+        raise ValueError("qg must be [B, Hq, 2, D] and k, v [B, Hkv, D]")
+    if cache_len.dtype != torch.int32 or tuple(cache_len.shape) != (B,) or cache_len.device != qg.device:
+        raise ValueError("cache_len must be an int32 [B] tensor on the device of qg")
+    S_max = int(k_cache.shape[2])
+    if o is None:
+        o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=qg.device)
+    dims = make_attn_dims(B, 1, Hq, Hkv, D, S_max, rot_dim, rope_theta, norm_eps, scale,
+                          _rows(qg, 1, 2 * Hq * D, "qg"), _rows(k, 1, Hkv * D, "k"), _rows(v, 1, Hkv * D, "v"),
+                          _rows(o, 1, Hq * D, "o"))
+    need = int(lib().gdn_attn_decode_workspace_size(ctypes.byref(dims)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qg.device)
+    ws_len = 0 if workspace is None else workspace.numel()
+    _check(lib().gdn_attn_decode(ctypes.byref(dims), _ptr(qg), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w),
+                                 _ptr(cache_len), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(workspace), ws_len,
+                                 _stream(stream)))
+    return o

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_chunk.hip", "gdn_conv_norm.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_chunk.hip", "gdn_conv_norm.hip", "gdn_attn.hip"]
 
 
 def hipcc() -> str:

@@ -1,11 +1,13 @@
 // gdn_api.cpp -- the extern "C" entry points of libgdn (declared in
-// include/gdn.h): argument validation on the host, kernel dispatch, status
+// include/gdn.h and include/gdn_attn.h): argument validation on the host, kernel dispatch, status
 // codes and the thread-local error message.  Validation happens before any
 // HIP call, so argument errors are reported even on a machine without a GPU.
 #include "../../include/gdn.h"
+#include "../../include/gdn_attn.h"
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -167,6 +169,82 @@ gdn_status prefill(const gdn_dims* d, const int32_t* cu, const void* q, const vo
   }
   return from_hip(gdn::launch_recurrent(a, d->io, static_cast<hipStream_t>(stream)),
                   "gdn_prefill (token-serial kernel)");
+}
+
+}  // namespace
+
+namespace {
+
+// Full-attention layer: checks shared by prefill and decode.
+gdn_status check_attn(const gdn_attn_dims* d, bool decode) {
+  if (!d) return fail(GDN_ERR_NULL, "dims is NULL");
+  if (d->B < 0 || d->T < 0) return fail(GDN_ERR_SHAPE, "B=%d T=%d must be >= 0", d->B, d->T);
+  if (decode && d->T != 1) return fail(GDN_ERR_SHAPE, "decode needs T == 1 (got %d)", d->T);
+  if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv)
+    return fail(GDN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", d->Hq, d->Hkv);
+  if (decode && d->Hq / d->Hkv > 8)
+    return fail(GDN_ERR_UNSUPPORTED, "decode takes at most 8 query heads per key/value head (got %d)",
+                d->Hq / d->Hkv);
+  if (d->D != 256) return fail(GDN_ERR_UNSUPPORTED, "head width D=%d: the kernels take 256", d->D);
+  if (d->rot_dim < 0 || d->rot_dim > d->D || d->rot_dim % 8)
+    return fail(GDN_ERR_SHAPE, "rot_dim=%d must be a multiple of 8 in [0, D]", d->rot_dim);
+  if (d->S_max < 64 || d->S_max % 64) return fail(GDN_ERR_SHAPE, "S_max=%d must be a positive multiple of 64",
+                                                  d->S_max);
+  if (!decode && d->T > d->S_max) return fail(GDN_ERR_SHAPE, "T=%d exceeds S_max=%d", d->T, d->S_max);
+  if (!(d->rope_theta > 0.0f) || !(d->norm_eps >= 0.0f) || !(d->scale > 0.0f) || std::isinf(d->scale))
+    return fail(GDN_ERR_SHAPE, "rope_theta and scale must be > 0 (finite), norm_eps >= 0");
+  const int64_t wq = 2LL * d->Hq * d->D, wkv = static_cast<int64_t>(d->Hkv) * d->D;
+  if (d->stride_qg < wq || d->stride_k < wkv || d->stride_v < wkv || d->stride_o < wq / 2)
+    return fail(GDN_ERR_SHAPE, "strides below the rows: qg %lld (>= %lld), k %lld, v %lld (>= %lld), o %lld (>= %lld)",
+                (long long)d->stride_qg, (long long)wq, (long long)d->stride_k, (long long)d->stride_v,
+                (long long)wkv, (long long)d->stride_o, (long long)(wq / 2));
+  if ((d->stride_qg | d->stride_k | d->stride_v | d->stride_o) % 4)
+    return fail(GDN_ERR_ALIGN, "strides must be multiples of 4 elements");
+  return GDN_OK;
+}
+
+gdn::AttnArgs attn_args(const gdn_attn_dims* d, const void* qg, const void* k, const void* v, const void* qw,
+                        const void* kw, void* kc, void* vc, void* o) {
+  gdn::AttnArgs a{};
+  a.B = d->B;
+  a.T = d->T;
+  a.Hq = d->Hq;
+  a.Hkv = d->Hkv;
+  a.rot_dim = d->rot_dim;
+  a.S_max = d->S_max;
+  a.theta = d->rope_theta;
+  a.eps = d->norm_eps;
+  a.scale = d->scale;
+  a.sqg = d->stride_qg;
+  a.sk = d->stride_k;
+  a.sv = d->stride_v;
+  a.so = d->stride_o;
+  a.qg = static_cast<const uint16_t*>(qg);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.qw = static_cast<const uint16_t*>(qw);
+  a.kw = static_cast<const uint16_t*>(kw);
+  a.kc = static_cast<uint16_t*>(kc);
+  a.vc = static_cast<uint16_t*>(vc);
+  a.o = static_cast<uint16_t*>(o);
+  return a;
+}
+
+gdn_status check_attn_pointers(const void* qg, const void* k, const void* v, const void* qw, const void* kw,
+                               const void* kc, const void* vc, const void* o, const void* ws) {
+  if (!qg || !k || !v || !qw || !kw || !kc || !vc || !o || !ws)
+    return fail(GDN_ERR_NULL, "qg, k, v, the norm weights, both caches, o and the workspace are required");
+  if (!aligned(qg, 8) || !aligned(k, 8) || !aligned(v, 8) || !aligned(qw, 8) || !aligned(kw, 8) || !aligned(o, 8))
+    return fail(GDN_ERR_ALIGN, "qg, k, v, o and the norm weights must be 8-byte aligned");
+  if (!aligned(kc, 16) || !aligned(vc, 16)) return fail(GDN_ERR_ALIGN, "the caches must be 16-byte aligned");
+  if (!aligned(ws, 256)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return GDN_OK;
+}
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+size_t attn_qrot_bytes(const gdn_attn_dims* d) {
+  return round256(static_cast<size_t>(d->B) * d->T * d->Hq * d->D * 2);
 }
 
 }  // namespace
@@ -374,6 +452,51 @@ gdn_status gdn_decode_layer(const gdn_decode_layer_args* p, void* stream) {
   a.o = static_cast<uint16_t*>(p->o);
   a.so = p->stride_o;
   return from_hip(gdn::launch_decode_layer(a, static_cast<hipStream_t>(stream)), "gdn_decode_layer");
+}
+
+size_t gdn_attn_prefill_workspace_size(const gdn_attn_dims* d) {
+  if (check_attn(d, false) != GDN_OK) return 0;
+  return attn_qrot_bytes(d);
+}
+
+gdn_status gdn_attn_prefill(const gdn_attn_dims* d, const void* qg, const void* k, const void* v,
+                            const void* q_norm_w, const void* k_norm_w, void* k_cache, void* v_cache, void* o,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  gdn_status st = check_attn(d, false);
+  if (st != GDN_OK) return st;
+  if (d->B == 0 || d->T == 0) return ok();
+  st = check_attn_pointers(qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, o, workspace);
+  if (st != GDN_OK) return st;
+  if (workspace_bytes < attn_qrot_bytes(d))
+    return fail(GDN_ERR_SHAPE, "workspace of %zu bytes is below %zu", workspace_bytes, attn_qrot_bytes(d));
+  gdn::AttnArgs a = attn_args(d, qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, o);
+  a.qrot = static_cast<uint16_t*>(workspace);
+  return from_hip(gdn::launch_attn_prefill(a, static_cast<hipStream_t>(stream)), "gdn_attn_prefill");
+}
+
+size_t gdn_attn_decode_workspace_size(const gdn_attn_dims* d) {
+  if (check_attn(d, true) != GDN_OK) return 0;
+  return attn_qrot_bytes(d) + static_cast<size_t>(d->B) * d->Hq * gdn::attn_splits(d->S_max) *
+                                  gdn::kAttnPartFloats * sizeof(float);
+}
+
+gdn_status gdn_attn_decode(const gdn_attn_dims* d, const void* qg, const void* k, const void* v,
+                           const void* q_norm_w, const void* k_norm_w, const int32_t* cache_len, void* k_cache,
+                           void* v_cache, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  gdn_status st = check_attn(d, true);
+  if (st != GDN_OK) return st;
+  if (d->B == 0) return ok();
+  st = check_attn_pointers(qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, o, workspace);
+  if (st != GDN_OK) return st;
+  if (!cache_len) return fail(GDN_ERR_NULL, "cache_len is required");
+  if (!aligned(cache_len, 4)) return fail(GDN_ERR_ALIGN, "cache_len must be 4-byte aligned");
+  const size_t need = gdn_attn_decode_workspace_size(d);
+  if (workspace_bytes < need) return fail(GDN_ERR_SHAPE, "workspace of %zu bytes is below %zu", workspace_bytes, need);
+  gdn::AttnArgs a = attn_args(d, qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, o);
+  a.cache_len = cache_len;
+  a.qrot = static_cast<uint16_t*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + attn_qrot_bytes(d));
+  return from_hip(gdn::launch_attn_decode(a, static_cast<hipStream_t>(stream)), "gdn_attn_decode");
 }
 
 const char* gdn_last_error(void) { return g_err; }

@@ -126,4 +126,30 @@ struct GateArgs {
 };
 hipError_t launch_gates(const GateArgs& a, int io, hipStream_t s);
 
+// Full-attention layer (gdn_attn.hip).  Prefill: tokens [0, T) of B sequences;
+// decode: T == 1 at position cache_len[b].  qrot is the normalised, rotated
+// queries [B*T][Hq][256] bf16; part the decode partials.
+struct AttnArgs {
+  int32_t B, T, Hq, Hkv, rot_dim, S_max;
+  float theta, eps, scale;
+  int64_t sqg, sk, sv, so;
+  const uint16_t* qg;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* qw;
+  const uint16_t* kw;
+  const int32_t* cache_len;   // decode only
+  uint16_t* kc;
+  uint16_t* vc;
+  uint16_t* o;
+  uint16_t* qrot;
+  float* part;                // decode only
+};
+// the decode splits: keys per workgroup, and floats per partial result
+constexpr int kAttnSplit = 256;
+constexpr int kAttnPartFloats = 260;
+__host__ __device__ inline int attn_splits(int S_max) { return (S_max + kAttnSplit - 1) / kAttnSplit; }
+hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
+
 }  // namespace gdn

@@ -18,7 +18,9 @@ Shapes follow the layer described on the page "L'attention hybride"
 DeltaNet" and table "Le decompte": 16 key heads and 48 value heads of width
 128, conv kernel 4 over the q|k|v channels, one 128-weight output norm; and
 the larger variant of section "La dissymetrie 16 / 48" (16 key heads for
-128 value heads).
+128 value heads).  The full-attention inputs follow section "Les 16 couches
+d'attention complete" of the same page: 24 query heads (each with its gate)
+and 4 key/value heads of width 256.
 """
 from __future__ import annotations
 
@@ -31,6 +33,7 @@ SLAB = 4096
 _TAGS = {
     "q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "A": 6, "dt_bias": 7, "state": 8,
     "conv_w": 9, "norm_w": 10, "z": 11, "x": 12, "conv_state": 13, "step": 14,
+    "attn_qg": 15, "attn_k": 16, "attn_v": 17, "attn_qw": 18, "attn_kw": 19, "attn_cache": 20,
 }
 
 
@@ -194,3 +197,16 @@ def block_inputs(B: int = 4, T: int = 32768, Hk: int = 16, Hv: int = 128, D: int
         z = z.reshape(B, T, Hv * D)
     return dict(B=B, T=T, Hk=Hk, Hv=Hv, D=D, C=C, x=x, conv_w=cw, norm_w=nw, z=z,
                 log_alpha=la, beta=be)
+
+
+def attn_problem(seed: int, B: int, T: int, Hq: int = 24, Hkv: int = 4, D: int = 256, sub: int = 0) -> dict:
+    """Full-attention layer inputs, bf16 bits: qg [B, T, Hq, 2, D] (query then gate per head),
+    k, v [B, T, Hkv, D], all N(0, 1) (projection outputs before the q/k norms); q_norm_w,
+    k_norm_w [D] ~ N(1, 0.1^2)."""
+    qg = normal_tokens(seed, "attn_qg", B * T, Hq * 2 * D, sub=sub, post=f32_to_bf16, out_dtype=np.uint16)
+    k = normal_tokens(seed, "attn_k", B * T, Hkv * D, sub=sub, post=f32_to_bf16, out_dtype=np.uint16)
+    v = normal_tokens(seed, "attn_v", B * T, Hkv * D, sub=sub, post=f32_to_bf16, out_dtype=np.uint16)
+    qw = normal_tokens(seed, "attn_qw", 1, D, loc=1.0, scale=0.1, post=f32_to_bf16, out_dtype=np.uint16)[0]
+    kw = normal_tokens(seed, "attn_kw", 1, D, loc=1.0, scale=0.1, post=f32_to_bf16, out_dtype=np.uint16)[0]
+    return dict(B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, qg=qg.reshape(B, T, Hq, 2, D), k=k.reshape(B, T, Hkv, D),
+                v=v.reshape(B, T, Hkv, D), q_norm_w=qw, k_norm_w=kw)

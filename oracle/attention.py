@@ -22,7 +22,11 @@ and "Le RoPE partiel"; RMSNorm as in "Les briques d'un reseau de neurones", 4:
 * grouped-query attention: 24 query heads, 4 key/value heads, query head h
   reads key/value head h // 6; causal softmax(q k^T * scale) v with scale
   1/sqrt(D) (reading A5);
-* the output of each query head is multiplied by sigmoid(gate) (reading A1).
+* the output of each query head is multiplied by sigmoid(gate) (reading A1);
+* q and k enter the attention products as bf16 values, rounded once to
+  nearest-even after norm and RoPE: the page's "Le float32 n'est pas un
+  detail" keeps only the recurrent state in float32 and the rest of the model
+  in BF16 (reading A6).  ``qk_bf16=False`` keeps them in fp64.
 
 Inputs may be float64, float32, or uint16 holding bf16 bit patterns (widened
 exactly).
@@ -62,13 +66,22 @@ def rope(x, pos, rot_dim=64, theta=1e7):
     return y
 
 
-def prepare(qg, k, v, q_norm_w, k_norm_w, pos, *, rot_dim=64, theta=1e7, eps=1e-6):
+def to_bf16(x):
+    """x rounded once to the nearest bf16 value (ties to even), as float64."""
+    from oracle import round_bf16
+    return widen(round_bf16(x))
+
+
+def prepare(qg, k, v, q_norm_w, k_norm_w, pos, *, rot_dim=64, theta=1e7, eps=1e-6, qk_bf16=True):
     """Per-head norm and RoPE of q and k.  qg [B, T, Hq, 2, D]; k, v [B, T, Hkv, D];
-    pos [B, T] or [T].  Returns (q, gate, k, v) as float64 with q and k rotated."""
+    pos [B, T] or [T].  Returns (q, gate, k, v) as float64 with q and k rotated (and
+    rounded to bf16 values when ``qk_bf16``)."""
     qg = widen(qg)
     q, gate = qg[..., 0, :], qg[..., 1, :]
     q = rope(rms_norm(q, q_norm_w, eps), pos, rot_dim, theta)
     kr = rope(rms_norm(k, k_norm_w, eps), pos, rot_dim, theta)
+    if qk_bf16:
+        q, kr = to_bf16(q), to_bf16(kr)
     return q, gate, kr, widen(v)
 
 
@@ -86,14 +99,16 @@ def attend(q, gate, k, v, n_keys, scale):
     return out / (1.0 + np.exp(-gate))
 
 
-def prefill(qg, k, v, q_norm_w, k_norm_w, *, rot_dim=64, theta=1e7, eps=1e-6, scale=None, rows=None):
+def prefill(qg, k, v, q_norm_w, k_norm_w, *, rot_dim=64, theta=1e7, eps=1e-6, scale=None, rows=None,
+            qk_bf16=True):
     """Causal prefill of B sequences of T tokens from position 0.  Returns
     (o [B, T, Hq, D] (only ``rows``, a list of (b, t), when given: [n, Hq, D]),
     k_cache [B, T, Hkv, D] rotated keys, v [B, T, Hkv, D])."""
     qg = widen(qg)
     B, T, Hq, _, D = qg.shape
     scale = 1.0 / np.sqrt(D) if scale is None else scale
-    q, gate, kr, vv = prepare(qg, k, v, q_norm_w, k_norm_w, np.arange(T), rot_dim=rot_dim, theta=theta, eps=eps)
+    q, gate, kr, vv = prepare(qg, k, v, q_norm_w, k_norm_w, np.arange(T), rot_dim=rot_dim, theta=theta, eps=eps,
+                              qk_bf16=qk_bf16)
     if rows is not None:
         return np.stack([attend(q[b, t], gate[b, t], kr[b], vv[b], t + 1, scale) for b, t in rows]), kr, vv
     o = np.empty((B, T, Hq, D))
@@ -103,7 +118,8 @@ def prefill(qg, k, v, q_norm_w, k_norm_w, *, rot_dim=64, theta=1e7, eps=1e-6, sc
     return o, kr, vv
 
 
-def decode(qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, lens, *, rot_dim=64, theta=1e7, eps=1e-6, scale=None):
+def decode(qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, lens, *, rot_dim=64, theta=1e7, eps=1e-6, scale=None,
+           qk_bf16=True):
     """One new token per sequence at position lens[b]: qg [B, Hq, 2, D]; k, v
     [B, Hkv, D]; k_cache, v_cache [B, S, Hkv, D] (rotated keys, values) holding
     lens[b] tokens.  Returns (o [B, Hq, D], new rotated key [B, Hkv, D])."""
@@ -116,7 +132,8 @@ def decode(qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, lens, *, rot_dim=64, 
     for b in range(B):
         n = int(lens[b])
         q, gate, kr, vv = prepare(qg[b][None, None], widen(k)[b][None, None], widen(v)[b][None, None],
-                                  q_norm_w, k_norm_w, np.array([n]), rot_dim=rot_dim, theta=theta, eps=eps)
+                                  q_norm_w, k_norm_w, np.array([n]), rot_dim=rot_dim, theta=theta, eps=eps,
+                                  qk_bf16=qk_bf16)
         keys = np.concatenate([kc[b, :n], kr[0]], axis=0)
         vals = np.concatenate([vc[b, :n], vv[0]], axis=0)
         o[b] = attend(q[0, 0], gate[0, 0], keys, vals, n + 1, scale)

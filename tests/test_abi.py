@@ -2,6 +2,7 @@
 include/gdn.h declares, and rejects bad arguments on the host with the
 documented status before any device work."""
 import ctypes
+import glob
 import os
 import re
 
@@ -17,9 +18,11 @@ FAKE_ODD = ctypes.c_void_p(0x10002)   # 2-byte aligned only
 
 
 def header_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -243,3 +246,59 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+def adims(**kw):
+    d = dict(B=2, T=100, Hq=24, Hkv=4, D=256, S_max=128)
+    d.update(kw)
+    return B.make_attn_dims(**d)
+
+
+def test_attention_workspace_sizes():
+    assert B.lib().gdn_attn_prefill_workspace_size(ctypes.byref(adims())) == 2 * 100 * 24 * 256 * 2
+    assert B.lib().gdn_attn_prefill_workspace_size(ctypes.byref(adims(T=1, B=1, Hq=1, Hkv=1))) == 512
+    # decode: the rotated queries (rounded up to 256 bytes), then per (sequence, query head, 256-position
+    # split of the cache) a partial result of 260 floats
+    d = adims(T=1, S_max=4096)
+    assert B.lib().gdn_attn_decode_workspace_size(ctypes.byref(d)) == 2 * 24 * 512 + 2 * 24 * 16 * 260 * 4
+    d = adims(T=1, S_max=320)                           # 2 splits, the second partial
+    assert B.lib().gdn_attn_decode_workspace_size(ctypes.byref(d)) == 2 * 24 * 512 + 2 * 24 * 2 * 260 * 4
+    assert B.lib().gdn_attn_decode_workspace_size(ctypes.byref(adims(T=2))) == 0      # invalid: T != 1
+    assert B.lib().gdn_attn_prefill_workspace_size(ctypes.byref(adims(D=128))) == 0   # unsupported
+
+
+def test_attention_argument_errors():
+    L = B.lib()
+    ws = ctypes.c_void_p(0x100000)
+    big = 1 << 30
+
+    def pre(d, qg=FAKE, k=FAKE, kc=FAKE, ws_=ws, n=big):
+        return L.gdn_attn_prefill(ctypes.byref(d) if d is not None else None, qg, k, FAKE, FAKE, FAKE, kc, FAKE,
+                                  FAKE, ws_, n, None)
+
+    def dec(d, cl=FAKE, qg=FAKE, n=big):
+        return L.gdn_attn_decode(ctypes.byref(d), qg, FAKE, FAKE, FAKE, FAKE, cl, FAKE, FAKE, FAKE, ws, n, None)
+
+    assert pre(None) == B.GDN_ERR_NULL
+    assert pre(adims(D=128)) == B.GDN_ERR_UNSUPPORTED
+    assert pre(adims(rot_dim=12)) == B.GDN_ERR_SHAPE
+    assert pre(adims(rot_dim=264)) == B.GDN_ERR_SHAPE
+    assert pre(adims(S_max=100)) == B.GDN_ERR_SHAPE
+    assert pre(adims(T=129)) == B.GDN_ERR_SHAPE         # beyond the cache
+    assert pre(adims(Hq=10)) == B.GDN_ERR_SHAPE         # not a multiple of Hkv
+    assert pre(adims(scale=0.0)) == B.GDN_ERR_SHAPE
+    assert pre(adims(stride_qg=2 * 24 * 256 - 4)) == B.GDN_ERR_SHAPE
+    assert pre(adims(stride_o=24 * 256 + 2)) == B.GDN_ERR_ALIGN
+    assert pre(adims(), qg=None) == B.GDN_ERR_NULL
+    assert pre(adims(), k=ctypes.c_void_p(0x10004)) == B.GDN_ERR_ALIGN       # 4-byte aligned only
+    assert pre(adims(), k=ctypes.c_void_p(0x10002)) == B.GDN_ERR_ALIGN
+    assert pre(adims(), kc=ctypes.c_void_p(0x10008)) == B.GDN_ERR_ALIGN       # caches need 16 bytes
+    assert pre(adims(), ws_=ctypes.c_void_p(0x100010)) == B.GDN_ERR_ALIGN
+    assert pre(adims(), n=1000) == B.GDN_ERR_SHAPE                             # workspace too small
+    assert pre(adims(B=0)) == B.GDN_OK and pre(adims(T=0)) == B.GDN_OK        # nothing to do
+    assert dec(adims(T=2)) == B.GDN_ERR_SHAPE
+    assert dec(adims(T=1, Hq=36, Hkv=4)) == B.GDN_ERR_UNSUPPORTED              # 9 query heads per group
+    assert dec(adims(T=1), cl=None) == B.GDN_ERR_NULL
+    assert dec(adims(T=1), cl=ctypes.c_void_p(0x10002)) == B.GDN_ERR_ALIGN
+    assert dec(adims(T=1), n=1000) == B.GDN_ERR_SHAPE
+    assert dec(adims(T=1, B=0)) == B.GDN_OK

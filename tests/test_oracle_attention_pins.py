@@ -143,3 +143,19 @@ def test_kv_cache_size_the_pages_print():
     # 24-head (no GQA) case and says that is six times more
     assert A.kv_cache_bytes_per_token(24, 256) == 24576
     assert A.kv_cache_bytes_per_token(4, 256) * 6 == 24576
+
+
+def test_bf16_operands():
+    # with qk_bf16 (the default) the rotated q and k are bf16 values within half an ulp of the fp64
+    # ones; the cache keys returned are those rounded keys
+    qg, k, v, wq, wk = problem(7, 1, 5, 6, 1, 256)
+    q64, _, k64, _ = A.prepare(qg, k, v, wq, wk, np.arange(5), qk_bf16=False)
+    q16, _, k16, _ = A.prepare(qg, k, v, wq, wk, np.arange(5))
+    for x64, x16 in ((q64, q16), (k64, k16)):
+        f32 = x16.astype(np.float32)
+        assert np.array_equal(f32.astype(np.float64), x16)
+        assert np.all((f32.view(np.uint32) & 0xFFFF) == 0)               # bf16-representable
+        m, e = np.frexp(np.abs(x64))
+        assert np.all(np.abs(x16 - x64) <= np.ldexp(1.0, e - 9))          # half an ulp (8 significant bits)
+    _, kr, _ = A.prefill(qg, k, v, wq, wk)
+    np.testing.assert_array_equal(kr, k16)
