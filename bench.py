@@ -17,6 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-c
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -296,6 +297,55 @@ def bench_long(dev, steps=3, warmup=4):
                 hbm_frac=by / (med * 1e-3) / (HBM_PEAK_GBS * 1e9))
 
 
+def attn_prefill_flops(B, T, Hq, D):
+    """Causal attention: query row t meets t + 1 keys, two products of 2 D flops each."""
+    return 4.0 * D * Hq * B * T * (T + 1) / 2
+
+
+def bench_attention(dev, steps=20, warmup=20):
+    """The hybrid's full-attention layer (24 query / 4 key-value heads of 256, RoPE on 64
+    dimensions, output gate).  Prefill: batch 1, T = 4096, one gdn_attn_prefill call (norm,
+    RoPE, cache writes, attention).  Decode: 64 sequences with 4095 cached positions each,
+    one gdn_attn_decode call (the new token's prep, split attention, combine).  Inputs drawn
+    on the GPU; the decode caches hold random rotated keys and values."""
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding as G
+    Hq, Hkv, D = 24, 4, 256
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    bf = lambda *shape: torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    qw = (1 + 0.1 * torch.randn((D,), generator=g, device=dev)).to(torch.bfloat16)
+    kw = (1 + 0.1 * torch.randn((D,), generator=g, device=dev)).to(torch.bfloat16)
+    T = 4096
+    qg, k, v = bf(1, T, Hq, 2, D), bf(1, T, Hkv, D), bf(1, T, Hkv, D)
+    kc, vc = G.attn_cache(1, Hkv, T, D, device=dev)
+    o = torch.empty((1, T, Hq, D), dtype=torch.bfloat16, device=dev)
+    dims = G.make_attn_dims(1, T, Hq, Hkv, D, T)
+    ws = torch.empty(G.lib().gdn_attn_prefill_workspace_size(ctypes.byref(dims)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    fn = lambda: G.gdn_attn_prefill(qg, k, v, qw, kw, kc, vc, o, workspace=ws, stream=stream)
+    _, _, med_p = timed_launches(fn, steps, warmup, stream)
+    fl = attn_prefill_flops(1, T, Hq, D)
+    del qg, k, v, kc, vc, o, ws
+    B, S = 64, 4096
+    kc = torch.randn((B, Hkv, S, D), generator=g, device=dev).to(torch.bfloat16)
+    vc = torch.randn((B, Hkv, S // 64, D, 64), generator=g, device=dev).to(torch.bfloat16)
+    lens = torch.full((B,), S - 1, dtype=torch.int32, device=dev)
+    qg, k, v = bf(B, Hq, 2, D), bf(B, Hkv, D), bf(B, Hkv, D)
+    o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    dims = G.make_attn_dims(B, 1, Hq, Hkv, D, S)
+    ws = torch.empty(G.lib().gdn_attn_decode_workspace_size(ctypes.byref(dims)), dtype=torch.uint8, device=dev)
+    fn = lambda: G.gdn_attn_decode(qg, k, v, qw, kw, lens, kc, vc, o, workspace=ws, stream=stream)
+    _, _, med_d = timed_launches(fn, steps * 5, warmup, stream)
+    by = B * Hkv * S * D * 2 * 2 + B * (Hq * 2 * D + 2 * Hkv * D + Hq * D) * 2
+    del kc, vc
+    torch.cuda.empty_cache()
+    return dict(prefill_T=T, prefill_us=med_p * 1e3, prefill_tflops=fl / (med_p * 1e-3) / 1e12,
+                prefill_mfma_frac=fl / (med_p * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                decode_B=B, decode_cached=S, decode_us=med_d * 1e3, decode_bytes=by,
+                decode_GBs=by / (med_d * 1e-3) / 1e9, decode_hbm_frac=by / (med_d * 1e-3) / (HBM_PEAK_GBS * 1e9))
+
+
 def varlen_lengths(n=32, lo=16, hi=8192, seed=6):
     """Lengths of a continuous-batching prefill: n requests, log-uniform on [lo, hi]."""
     rng = np.random.default_rng(seed)
@@ -495,6 +545,12 @@ def main():
         lg = bench_long(dev)
         print(f"[bench] long: {lg['ms']:.2f} ms", file=sys.stderr, flush=True)
         line["long"] = {"config": "batch 1, T=262144, 16 key / 48 value heads", **lg}
+        at = bench_attention(dev)
+        print(f"[bench] attention: prefill {at['prefill_us']:.1f} us ({at['prefill_tflops']:.0f} TFLOP/s), "
+              f"decode {at['decode_us']:.1f} us ({at['decode_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
+        line["attention"] = {"config": "full-attention layer, 24 query / 4 key-value heads of 256, RoPE on 64 "
+                                       "dims, output gate: prefill batch 1 T=4096; decode 64 sequences x 4095 "
+                                       "cached positions", **at}
         vl = bench_varlen(dev)
         print(f"[bench] varlen: {vl['ms']:.3f} ms for {vl['tokens']} tokens in {vl['n_seq']} sequences "
               f"({vl['one_call_per_seq_ms']:.3f} ms as one call each)", file=sys.stderr, flush=True)

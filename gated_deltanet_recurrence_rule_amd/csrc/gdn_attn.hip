@@ -5,7 +5,7 @@
 // ("Le facteur 2 sur W_Q", "GQA a 6:1", "Le RoPE partiel").
 //
 // Kernels:
-//  * attn_prep_kernel: one wave per 256-wide row of a token.  Query rows are
+//  * attn_prep_kernel: one workgroup per token, a wave per 256-wide row.  Query rows are
 //    normalised and rotated into the qrot scratch; key rows likewise into the
 //    key cache at the token's position; value rows are copied into the value
 //    cache, whose 64-position blocks are stored transposed ([256][64]) so that
@@ -19,11 +19,13 @@
 //    of the accumulator rows is the k order of the operand).  Key and value
 //    blocks are staged through LDS, double-buffered, with the next block's
 //    loads in flight during the products.
-//  * attn_decode_kernel: one workgroup per (256 cached positions, key/value
-//    head, sequence) scores the group's query heads (one position per thread,
-//    fp32), and accumulates the softmax-weighted values (one dimension per
-//    thread); attn_combine_kernel merges the partial maxima, sums and outputs
-//    of a head and applies the gate.
+//  * attn_decode_kernel: one wave per (256 cached positions, key/value head,
+//    sequence) runs the same products with the group's query heads as the
+//    MFMA columns, reading keys and values straight from the caches;
+//    attn_combine_kernel merges the partial maxima, sums and outputs of a head
+//    and applies the gate.
+#include <cmath>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -35,10 +37,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int AD = 256;      // head width
 constexpr int QB = 128;      // query rows per prefill workgroup (4 waves x 32)
 constexpr int KB = 64;       // keys per block
-constexpr int KPITCH = 264;  // LDS row pitch (bf16) of a key block [64][256]
-constexpr int VPITCH = 72;   // LDS row pitch (bf16) of a transposed value block [256][64]
-constexpr int KBUF = KB * KPITCH * 2;
-constexpr int VBUF = AD * VPITCH * 2;
+constexpr int KBUF = KB * AD * 2;   // LDS key block: 64 rows of 512 bytes
+constexpr int VBUF = AD * KB * 2;   // LDS transposed value block: 256 rows of 128 bytes
 constexpr int kFwdLds = 2 * (KBUF + VBUF);
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -47,6 +47,11 @@ __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, con
 }
 // row of value v of a 32x32 accumulator in lane half h
 __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
+// Key held by row r of a 32-key S^T tile: rows 16a + 8b + 4h + c hold key
+// 16a + 8h + 4b + c (bits 2 and 3 swapped).  The accumulator values 8s..8s+7
+// of lane half h, which become the k slots of the P^T operand, then hold the 8
+// consecutive keys 16s + 8h.., so a value operand is one 16-byte read.
+__device__ __forceinline__ int key_of_row(int r) { return (r & ~12) | ((r & 8) >> 1) | ((r & 4) << 1); }
 
 __device__ __forceinline__ int64_t kc_index(const AttnArgs& a, int b, int j, int pos) {
   return ((static_cast<int64_t>(b) * a.Hkv + j) * a.S_max + pos) * AD;
@@ -59,114 +64,130 @@ __device__ __forceinline__ int64_t vc_block(const AttnArgs& a, int b, int j, int
 // ---------------------------------------------------------------------------
 // prep: rows are, per token, Hq query rows, Hkv key rows, Hkv value rows
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_prep_kernel(AttnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int R = a.Hq + 2 * a.Hkv;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= static_cast<int64_t>(a.B) * a.T * R) return;
-  const int64_t tok = row / R;
-  const int r = static_cast<int>(row - tok * R);
+__global__ __launch_bounds__(256) void attn_prep_kernel(AttnArgs a, RopeTable rt) {
+  // one workgroup per token; wave w takes the token's rows w, w + 4, ...
+  const int64_t tok = blockIdx.x;
   const int b = static_cast<int>(tok / a.T), t = static_cast<int>(tok - static_cast<int64_t>(b) * a.T);
   const int pos = a.cache_len ? min(max(a.cache_len[b], 0), a.S_max - 1) : t;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d0 = 4 * lane;
-  if (r >= a.Hq + a.Hkv) {
-    const int j = r - a.Hq - a.Hkv;
-    const u16x4 x = *reinterpret_cast<const u16x4*>(a.v + tok * a.sv + static_cast<int64_t>(j) * AD + d0);
-    uint16_t* dst = a.vc + vc_block(a, b, j, pos) + pos % KB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(d0 + i) * KB] = x[i];
-    return;
-  }
-  const bool isq = r < a.Hq;
-  const uint16_t* src = isq ? a.qg + tok * a.sqg + static_cast<int64_t>(r) * 2 * AD
-                            : a.k + tok * a.sk + static_cast<int64_t>(r - a.Hq) * AD;
-  const uint16_t* w = isq ? a.qw : a.kw;
-  const u16x4 x4 = *reinterpret_cast<const u16x4*>(src + d0);
-  const u16x4 w4 = *reinterpret_cast<const u16x4*>(w + d0);
-  float y[4];
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    y[i] = bf16_bits_to_f32(x4[i]);
-    ss += y[i] * y[i];
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / AD + a.eps);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) y[i] = y[i] * inv * bf16_bits_to_f32(w4[i]);
+  const int R = a.Hq + (a.cache_len ? 2 : 1) * a.Hkv;   // prefill values go through attn_vblock_kernel
   // RoPE: dimension i < half pairs with i + half; half is a multiple of 4, so a
-  // lane's partner lane is half/4 away
+  // lane's partner lane is half/4 away.  The angle and its reduction to
+  // [-pi, pi] are fp64 (positions reach 10^5 and more, where an fp32 angle would
+  // be off by ~1e-2 rad); sin and cos are fp32, once per lane and token.
   const int half = a.rot_dim / 2, lo = half / 4;
   const int pl = lane < lo ? lane + lo : lane - lo;
-  float p[4];
+  const bool rot = d0 < a.rot_dim, first = d0 < half;
+  float cs[4], sn[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = __shfl(y[i], pl, 64);
-  if (d0 < a.rot_dim) {
-    const bool first = d0 < half;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = (first ? d0 : d0 - half) + i;
-      // the angle in fp64: positions reach 10^5 and more, where fp32 would lose ~1e-2 rad
-      const double ang = static_cast<double>(pos) * pow(static_cast<double>(a.theta), -2.0 * f / a.rot_dim);
-      double sn, cs;
-      sincos(ang, &sn, &cs);
-      const float c = static_cast<float>(cs), s = static_cast<float>(sn);
-      y[i] = first ? y[i] * c - p[i] * s : y[i] * c + p[i] * s;
+  for (int i = 0; i < 4; ++i) {
+    cs[i] = 1.f;
+    sn[i] = 0.f;
+    if (rot) {
+      const double ang = static_cast<double>(pos) * rt.inv_freq[(first ? d0 : d0 - half) + i];
+      const double turns = rint(ang * 0.15915494309189535);
+      sincosf(static_cast<float>(fma(-turns, 6.283185307179586, ang)), &sn[i], &cs[i]);
     }
   }
-  u16x4 out;
+  auto src_of = [&](int r) -> const uint16_t* {
+    if (r < a.Hq) return a.qg + tok * a.sqg + static_cast<int64_t>(r) * 2 * AD;
+    if (r < a.Hq + a.Hkv) return a.k + tok * a.sk + static_cast<int64_t>(r - a.Hq) * AD;
+    return a.v + tok * a.sv + static_cast<int64_t>(r - a.Hq - a.Hkv) * AD;
+  };
+  const u16x4 wq = *reinterpret_cast<const u16x4*>(a.qw + d0);
+  const u16x4 wk = *reinterpret_cast<const u16x4*>(a.kw + d0);
+  u16x4 nxt = w < R ? *reinterpret_cast<const u16x4*>(src_of(w) + d0) : u16x4{0, 0, 0, 0};
+  for (int r = w; r < R; r += 4) {
+    const u16x4 x4 = nxt;
+    if (r + 4 < R) nxt = *reinterpret_cast<const u16x4*>(src_of(r + 4) + d0);   // next row in flight
+    if (r >= a.Hq + a.Hkv) {   // decode only: the token's value, into its transposed block
+      const int j = r - a.Hq - a.Hkv;
+      uint16_t* dst = a.vc + vc_block(a, b, j, pos) + pos % KB;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = f32_to_bf16_bits(y[i]);
-  uint16_t* dst = isq ? a.qrot + (tok * a.Hq + r) * AD : a.kc + kc_index(a, b, r - a.Hq, pos);
-  *reinterpret_cast<u16x4*>(dst + d0) = out;
+      for (int i = 0; i < 4; ++i) dst[(d0 + i) * KB] = x4[i];
+      continue;
+    }
+    const bool isq = r < a.Hq;
+    const u16x4 w4 = isq ? wq : wk;
+    float y[4];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[i] = bf16_bits_to_f32(x4[i]);
+      ss += y[i] * y[i];
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / AD + a.eps);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = y[i] * inv * bf16_bits_to_f32(w4[i]);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __shfl(y[i], pl, 64);
+    if (rot) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = first ? y[i] * cs[i] - p[i] * sn[i] : y[i] * cs[i] + p[i] * sn[i];
+    }
+    u16x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = f32_to_bf16_bits(y[i]);
+    uint16_t* dst = isq ? a.qrot + (tok * a.Hq + r) * AD : a.kc + kc_index(a, b, r - a.Hq, pos);
+    *reinterpret_cast<u16x4*>(dst + d0) = out;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // prefill attention
 // ---------------------------------------------------------------------------
-// 16-byte chunk i (of 2048) of key block kb and of value block kb, into registers
-struct BlockRegs {
-  u16x8 k[8], v[8];
-};
-
-__device__ __forceinline__ void load_block(const AttnArgs& a, int b, int j, int kb, int tid, BlockRegs& r) {
-  const uint16_t* ks = a.kc + kc_index(a, b, j, kb * KB);
-  const uint16_t* vs = a.vc + vc_block(a, b, j, kb * KB);
+// LDS layout of a block.  Row m of key tile u (rows 32u..32u+31) holds key
+// 32u + key_of_row(m), so the A operand's lane m reads LDS row 32u + m.  The
+// 16-byte chunk c (keys: dims 8c..; values: positions 8c..) of key row r sits
+// at chunk position c ^ (r & 15), of value row r at c ^ ((r >> 1) & 7): sixteen
+// consecutive rows, read by sixteen consecutive lanes, then fall on distinct
+// 16-byte bank groups of a 256-byte bank line (5 % faster than swizzling with
+// r & 7).  A block is 32 + 32 pieces of 1 KiB copied straight from the caches
+// into LDS (lane i of a piece fills bytes 16i..16i+15 of it), 16 per wave.
+__device__ __forceinline__ void copy_block(const AttnArgs& a, int b, int j, int kb, int w, int lane,
+                                           unsigned char* kbuf, unsigned char* vbuf) {
+  const unsigned char* ks = reinterpret_cast<const unsigned char*>(a.kc + kc_index(a, b, j, kb * KB));
+  const unsigned char* vs = reinterpret_cast<const unsigned char*>(a.vc + vc_block(a, b, j, kb * KB));
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int c = tid + 256 * i;
-    r.k[i] = *reinterpret_cast<const u16x8*>(ks + 8 * c);   // key row c/32, dims 8 (c%32)..
-    r.v[i] = *reinterpret_cast<const u16x8*>(vs + 8 * c);   // dim row c/8, keys 8 (c%8)..
+    const int pc = 8 * w + i;
+    const int r = 2 * pc + (lane >> 5), c = (lane & 31) ^ (r & 15);
+    const int key = 32 * (r >> 5) + key_of_row(r & 31);
+    __builtin_amdgcn_global_load_lds(ks + key * (AD * 2) + 16 * c, kbuf + 1024 * pc, 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int pc = 8 * w + i;
+    const int r = 8 * pc + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+    __builtin_amdgcn_global_load_lds(vs + r * (KB * 2) + 16 * c, vbuf + 1024 * pc, 16, 0, 0);
   }
 }
 
-// Keys at or beyond `valid` in the block are zeroed: cache positions past the
-// written ones hold arbitrary bits, and a NaN there would survive a zero weight.
-__device__ __forceinline__ void store_block(unsigned char* kbuf, unsigned char* vbuf, int tid, BlockRegs& r,
-                                            int valid) {
-  uint16_t* sk = reinterpret_cast<uint16_t*>(kbuf);
-  uint16_t* sv = reinterpret_cast<uint16_t*>(vbuf);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + 256 * i;
-    u16x8 kk = r.k[i], vv = r.v[i];
-    if (valid < KB) {
-      if (c / 32 >= valid) kk = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (8 * (c % 8) + e >= valid) vv[e] = 0;
-    }
-    *reinterpret_cast<u16x8*>(sk + (c / 32) * KPITCH + 8 * (c % 32)) = kk;
-    *reinterpret_cast<u16x8*>(sv + (c / 8) * VPITCH + 8 * (c % 8)) = vv;
-  }
-}
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
 __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // Workgroup -> (sequence, query head, query block).  The 8 XCDs take linear
+  // indices round-robin; indices are re-ordered so that each XCD runs a
+  // contiguous range of (key/value group, query block, head) work, i.e. the
+  // query heads of one group, whose keys and values then stay in that XCD's
+  // L2.  Inside a group the query blocks go long, short, long, short ...
+  // (31, 0, 30, 1, ... for 32 blocks), so that any contiguous range of them,
+  // and thus each XCD's share, holds about the same causal work.
   const int nqb = (a.T + QB - 1) / QB;
-  const int qb = nqb - 1 - static_cast<int>(blockIdx.x);  // the longest rows first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int j = h / (a.Hq / a.Hkv);
+  const int G = a.Hq / a.Hkv;
+  const int N = static_cast<int>(gridDim.x), L = static_cast<int>(blockIdx.x);
+  const int N8 = N / 8 * 8;
+  const int idx = L < N8 ? (L % 8) * (N8 / 8) + L / 8 : L;
+  const int per_group = nqb * G;
+  const int grp = idx / per_group, rr = idx - grp * per_group;
+  const int pos = rr / G;
+  const int qb = (pos & 1) ? pos >> 1 : nqb - 1 - (pos >> 1);
+  const int b = grp / a.Hkv, j = grp - b * a.Hkv;
+  const int h = j * G + rr % G;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int q0 = qb * QB + 32 * w;  // the wave's first query
   const int qi = q0 + l32;          // the lane's query
@@ -185,31 +206,59 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int v = 0; v < 16; ++v) O[t][v] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float m = 0.f, l = 0.f;
+  bool over = false;
   const float sl2 = a.scale * kLog2e;
 
+  // blocks: keys past T are zero in the caches (the value block kernel writes
+  // whole blocks), and masked as later than every query
   const int last_key = min(qb * QB + QB, a.T) - 1;   // the largest key any row here sees
   const int nkb = last_key / KB + 1;
-  BlockRegs br;
-  load_block(a, b, j, 0, tid, br);
-  store_block(smem, smem + 2 * KBUF, tid, br, min(KB, a.T));
+  const int xk = l32 & 15, xv = (l32 >> 1) & 7;   // this lane's chunk swizzles (key rows, value rows)
+  copy_block(a, b, j, 0, w, lane, smem, smem + 2 * KBUF);
+  wait_vm_all();
   __syncthreads();
+  // The softmax reference of a row is the maximum of its scores in the first
+  // block (which holds key 0, seen by every row), and it stays fixed: the
+  // output then only ever accumulates in the matrix cores, with no rescaling.
+  // Weights 2^(s - m) are fp32 and bf16 numbers, whose range is the same, and
+  // stay far inside it unless a later score exceeds the reference by more than
+  // 96 (base 2); a wave that sees one redoes its rows exactly after the loop.
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1;
-    const uint16_t* sk = reinterpret_cast<const uint16_t*>(smem + cur * KBUF);
-    const uint16_t* sv = reinterpret_cast<const uint16_t*>(smem + 2 * KBUF + cur * VBUF);
-    if (kb + 1 < nkb) load_block(a, b, j, kb + 1, tid, br);
+    const unsigned char* sk = smem + cur * KBUF;
+    const unsigned char* sv = smem + 2 * KBUF + cur * VBUF;
+    if (kb + 1 < nkb) copy_block(a, b, j, kb + 1, w, lane, smem + (cur ^ 1) * KBUF, smem + 2 * KBUF + (cur ^ 1) * VBUF);
 
-    // S^T tiles u = keys 32u.. of the block
+    // S^T tiles u = keys 32u.. of the block; key fragments are read from LDS eight
+    // at a time, one group ahead of the products
     floatx16 S[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int v = 0; v < 16; ++v) S[u][v] = 0.f;
-      const uint16_t* kr = sk + (32 * u + l32) * KPITCH + 8 * hh;
+    {
+      const unsigned char* kr = sk + l32 * (AD * 2);
+      u16x8 kf[2][8];
+      auto kload = [&](int g, u16x8* dst) {
 #pragma unroll
-      for (int s = 0; s < 16; ++s)
-        S[u] = mfma32(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr + 16 * s)), Qf[s], S[u]);
+        for (int i = 0; i < 8; ++i) {
+          const int st = 4 * g + (i >> 1), u = i & 1;
+          dst[i] = *reinterpret_cast<const u16x8*>(kr + 32 * u * (AD * 2) + 16 * ((2 * st + hh) ^ xk));
+        }
+      };
+      kload(0, kf[0]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (g < 3) kload(g + 1, kf[(g + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int st = 4 * g + (i >> 1), u = i & 1;
+          S[u] = mfma32(__builtin_bit_cast(bf16x8, kf[g & 1][i]), Qf[st], S[u]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // scale to base 2, mask keys after the query, block maximum
     const int kbase = kb * KB;
@@ -220,23 +269,15 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float x = S[u][v] * sl2;
-        if (diag && kbase + 32 * u + acc_row(v, hh) > qi) x = -INFINITY;
+        if (diag && kbase + 32 * u + key_of_row(acc_row(v, hh)) > qi) x = -INFINITY;
         S[u][v] = x;
         mx = fmaxf(mx, x);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);        // finite: key 0 precedes every query
-    const float c = exp2f(m - mn);
-    m = mn;
-    l *= c;
-    if (__builtin_amdgcn_ballot_w64(c != 1.0f)) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) O[t][v] *= c;
-    }
+    if (kb == 0) m = mx;            // finite: key 0 precedes every query
+    over |= mx > m + 96.0f;
     // P^T fragments: accumulator values 8s2..8s2+7 of tile u are keys
-    // 32u + 16 s2 + {4hh..4hh+3, 8+4hh..8+4hh+3}
+    // 32u + 16 s2 + 8hh + 0..7
     bf16x8 P[4];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -244,28 +285,88 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = exp2f(S[u][8 * s2 + e] - mn);
+          const float p = __builtin_amdgcn_exp2f(S[u][8 * s2 + e] - m);
           l += p;
           P[2 * u + s2][e] = static_cast<__bf16>(p);
         }
-    // O^T += V^T P^T: A operand rows = dims 32t + l32, k = the same key order
+    // O^T += V^T P^T: A operand rows = dims 32t + l32, k = the same key order;
+    // value fragments eight at a time (one k step), one group ahead
+    {
+      const unsigned char* vr = sv + l32 * (KB * 2);
+      u16x8 vf[2][8];
+      auto vload = [&](int ks, u16x8* dst) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint16_t* vr = sv + l32 * VPITCH + 16 * ks + 4 * hh;
+        for (int t = 0; t < 8; ++t)
+          dst[t] = *reinterpret_cast<const u16x8*>(vr + 32 * t * (KB * 2) + 16 * ((2 * ks + hh) ^ xv));
+      };
+      vload(0, vf[0]);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint16_t* vt = vr + 32 * t * VPITCH;
-        const u16x4 lo = *reinterpret_cast<const u16x4*>(vt);
-        const u16x4 hi = *reinterpret_cast<const u16x4*>(vt + 8);
-        const u16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        O[t] = mfma32(__builtin_bit_cast(bf16x8, vv), P[ks], O[t]);
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) vload(ks + 1, vf[(ks + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) O[t] = mfma32(__builtin_bit_cast(bf16x8, vf[ks & 1][t]), P[ks], O[t]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (kb + 1 < nkb) {
-      const int nxt = cur ^ 1;
-      store_block(smem + nxt * KBUF, smem + 2 * KBUF + nxt * VBUF, tid, br, min(KB, a.T - (kb + 1) * KB));
-    }
+    wait_vm_all();   // this wave's pieces of the next block are in LDS
     __syncthreads();
+  }
+  if (__builtin_amdgcn_ballot_w64(over)) {
+    // Exact redo of this wave's rows, straight from the caches: the row maxima
+    // over all visible keys first, then the weights and values against them.
+    const unsigned char* kcb = reinterpret_cast<const unsigned char*>(a.kc + kc_index(a, b, j, 0));
+    auto scores = [&](int kb, floatx16* Sx) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) Sx[u][v] = 0.f;
+        const unsigned char* kr = kcb + static_cast<int64_t>(kb * KB + 32 * u + key_of_row(l32)) * (AD * 2) + 16 * hh;
+#pragma unroll
+        for (int st = 0; st < 16; ++st)
+          Sx[u] = mfma32(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr + 32 * st)), Qf[st], Sx[u]);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          Sx[u][v] = kb * KB + 32 * u + key_of_row(acc_row(v, hh)) > qi ? -INFINITY : Sx[u][v] * sl2;
+      }
+    };
+    float m2 = -INFINITY;
+    for (int kb = 0; kb < nkb; ++kb) {
+      floatx16 Sx[2];
+      scores(kb, Sx);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) m2 = fmaxf(m2, Sx[u][v]);
+    }
+    m = fmaxf(m2, __shfl_xor(m2, 32, 64));
+    l = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) O[t][v] = 0.f;
+    for (int kb = 0; kb < nkb; ++kb) {
+      floatx16 Sx[2];
+      scores(kb, Sx);
+      bf16x8 P[4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(Sx[u][8 * s2 + e] - m);
+            l += p;
+            P[2 * u + s2][e] = static_cast<__bf16>(p);
+          }
+      const uint16_t* vb = a.vc + vc_block(a, b, j, kb * KB) + l32 * KB + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          O[t] = mfma32(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(vb + 32 * t * KB + 16 * ks)),
+                        P[ks], O[t]);
+    }
   }
   // epilogue: normalise, gate, store (rows past T are not stored)
   l += __shfl_xor(l, 32, 64);
@@ -289,118 +390,190 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------
-constexpr int kMaxGroup = 8;
-
-__device__ __forceinline__ float block_max(float x, float* red) {
-#pragma unroll
-  for (int mm = 32; mm >= 1; mm >>= 1) x = fmaxf(x, __shfl_xor(x, mm, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  x = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return x;
-}
-__device__ __forceinline__ float block_sum(float x, float* red) {
-  x = wave_sum(x);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  x = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
-  return x;
-}
-
-__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a) {
-  __shared__ float qs[kMaxGroup][AD];
-  __shared__ float ps[kMaxGroup][kAttnSplit];
-  __shared__ float red[4];
+// One wave per (256 cached positions, key/value head, sequence): the group's
+// query heads are the columns of the B operand (the columns past the group are
+// zero), keys and values are read straight from the caches as MFMA operands,
+// 64 positions at a time with an online softmax; the partial maximum, sum and
+// unnormalised output of each query head go to the workspace.
+__global__ __launch_bounds__(64) void attn_decode_kernel(AttnArgs a) {
   const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int n = min(max(a.cache_len[b], 0), a.S_max - 1) + 1;   // positions [0, n)
   const int k0 = sp * kAttnSplit;
   if (k0 >= n) return;   // the combine reads ceil(n / 256) splits only
-  const int tid = threadIdx.x;
-  for (int i = tid; i < G * AD; i += 256)
-    qs[i / AD][i % AD] = bf16_bits_to_f32(a.qrot[(static_cast<int64_t>(b) * a.Hq + j * G + i / AD) * AD + i % AD]);
-  __syncthreads();
-  // scores: one position per thread
-  const int key = k0 + tid;
-  float s[kMaxGroup];
+  const int lane = threadIdx.x, l32 = lane & 31, hh = lane >> 5;
+  bf16x8 Qf[16];
+  {
+    const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    const uint16_t* qr = a.qrot + (static_cast<int64_t>(b) * a.Hq + j * G + min(l32, G - 1)) * AD + 8 * hh;
 #pragma unroll
-  for (int g = 0; g < kMaxGroup; ++g) s[g] = 0.f;
-  if (key < n) {
-    const uint16_t* kr = a.kc + kc_index(a, b, j, key);
-    for (int c = 0; c < AD / 8; ++c) {
-      const u16x8 kv = *reinterpret_cast<const u16x8*>(kr + 8 * c);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kf = bf16_bits_to_f32(kv[e]);
-#pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g)
-          if (g < G) s[g] += kf * qs[g][8 * c + e];
-      }
-    }
+    for (int s = 0; s < 16; ++s)
+      Qf[s] = __builtin_bit_cast(bf16x8, l32 < G ? *reinterpret_cast<const u16x8*>(qr + 16 * s) : z);
   }
+  floatx16 O[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) O[t][v] = 0.f;
+  float m = -INFINITY, l = 0.f;
   const float sl2 = a.scale * kLog2e;
-  float* part = a.part + ((static_cast<int64_t>(b) * a.Hq + j * G) * attn_splits(a.S_max) + sp) * kAttnPartFloats;
-  const int64_t gstride = static_cast<int64_t>(attn_splits(a.S_max)) * kAttnPartFloats;
-  for (int g = 0; g < G; ++g) {
-    const float x = key < n ? s[g] * sl2 : -INFINITY;
-    const float mg = block_max(x, red);
-    const float p = key < n ? exp2f(x - mg) : 0.f;
-    ps[g][tid] = p;
-    const float lg = block_sum(p, red);
-    if (tid == 0) {
-      part[g * gstride + 0] = mg;
-      part[g * gstride + 1] = lg;
+  const int nblk = min(kAttnSplit / KB, (n - k0 + KB - 1) / KB);
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int kb0 = k0 + KB * blk;             // kb0 + 63 < S_max: S_max is a multiple of 64
+    const int valid = min(KB, n - kb0);
+    floatx16 S[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint16_t* kr = a.kc + kc_index(a, b, j, kb0 + 32 * u + key_of_row(l32)) + 8 * hh;
+      bf16x8 Kf[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) Kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr + 16 * s));
+#pragma unroll
+      for (int v = 0; v < 16; ++v) S[u][v] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) S[u] = mfma32(Kf[s], Qf[s], S[u]);
     }
-  }
-  __syncthreads();
-  // weighted values: one dimension per thread; positions past n are skipped
-  float o[kMaxGroup];
+    float mx = -INFINITY;
 #pragma unroll
-  for (int g = 0; g < kMaxGroup; ++g) o[g] = 0.f;
-  const int d = tid;
-  for (int blk = 0; blk < kAttnSplit / KB && k0 + KB * blk < n; ++blk) {
-    const uint16_t* vr = a.vc + vc_block(a, b, j, k0 + KB * blk) + d * KB;
-    const int valid = min(KB, n - k0 - KB * blk);
-    for (int c = 0; c < KB / 8; ++c) {
-      const u16x8 vv = *reinterpret_cast<const u16x8*>(vr + 8 * c);
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = 8 * c + e;
-        const float vf = kk < valid ? bf16_bits_to_f32(vv[e]) : 0.f;
-#pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g)
-          if (g < G) o[g] += ps[g][KB * blk + kk] * vf;
+      for (int v = 0; v < 16; ++v) {
+        const float x = 32 * u + key_of_row(acc_row(v, hh)) < valid ? S[u][v] * sl2 : -INFINITY;
+        S[u][v] = x;
+        mx = fmaxf(mx, x);
       }
-    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);             // finite: position kb0 is valid
+    const float c = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    l *= c;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) O[t][v] *= c;
+    bf16x8 P[4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(S[u][8 * s2 + e] - mn);
+          l += p;
+          P[2 * u + s2][e] = static_cast<__bf16>(p);
+        }
+    // values: k step ks holds positions 16 ks + 8 hh + 0..7; positions past n may
+    // hold arbitrary bits (a NaN would survive a zero weight), so they are zeroed
+    const uint16_t* vb = a.vc + vc_block(a, b, j, kb0) + l32 * KB + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        u16x8 vv = *reinterpret_cast<const u16x8*>(vb + 32 * t * KB + 16 * ks);
+        if (valid < KB) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (16 * ks + 8 * hh + e >= valid) vv[e] = 0;
+        }
+        O[t] = mfma32(__builtin_bit_cast(bf16x8, vv), P[ks], O[t]);
+      }
   }
-  for (int g = 0; g < G; ++g) part[g * gstride + 4 + d] = o[g];
+  l += __shfl_xor(l, 32, 64);
+  if (l32 >= G) return;
+  float* part = a.part + ((static_cast<int64_t>(b) * a.Hq + j * G + l32) * attn_splits(a.S_max) + sp) *
+                             kAttnPartFloats;
+  if (hh == 0) {
+    part[0] = m;
+    part[1] = l;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<floatx4*>(part + 4 + 32 * t + 8 * q4 + 4 * hh) =
+          floatx4{O[t][4 * q4], O[t][4 * q4 + 1], O[t][4 * q4 + 2], O[t][4 * q4 + 3]};
 }
 
+// Merges the partial results of a query head: M = max m_s, L = sum 2^(m_s - M) l_s,
+// o = sum 2^(m_s - M) o_s / L, then the gate.  One thread per dimension.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float wsp[256];
+  __shared__ float red[4];
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int n = min(max(a.cache_len[b], 0), a.S_max - 1) + 1;
   const int nsp = (n + kAttnSplit - 1) / kAttnSplit;
   const float* part = a.part + (static_cast<int64_t>(b) * a.Hq + h) * attn_splits(a.S_max) * kAttnPartFloats;
-  float M = -INFINITY;
-  for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, part[sp * kAttnPartFloats]);
-  float L = 0.f, o = 0.f;
-  for (int sp = 0; sp < nsp; ++sp) {
-    const float* pp = part + sp * kAttnPartFloats;
-    const float c = exp2f(pp[0] - M);
-    L += c * pp[1];
-    o += c * pp[4 + d];
+  float mloc = -INFINITY;
+  for (int sp = d; sp < nsp; sp += 256) mloc = fmaxf(mloc, part[sp * kAttnPartFloats]);
+#pragma unroll
+  for (int mm = 32; mm >= 1; mm >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, mm, 64));
+  if ((d & 63) == 0) red[d >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float Lloc = 0.f, o = 0.f;
+  for (int base = 0; base < nsp; base += 256) {
+    __syncthreads();   // red and wsp are rewritten
+    const int sp = base + d;
+    if (sp < nsp) {
+      const float wgt = exp2f(part[sp * kAttnPartFloats] - M);
+      wsp[d] = wgt;
+      Lloc += wgt * part[sp * kAttnPartFloats + 1];
+    }
+    __syncthreads();
+    const int cnt = min(256, nsp - base);
+    const float* pp = part + static_cast<int64_t>(base) * kAttnPartFloats + 4 + d;
+#pragma unroll 8
+    for (int i = 0; i < cnt; ++i) o += wsp[i] * pp[i * kAttnPartFloats];
   }
+  Lloc = wave_sum(Lloc);
+  __syncthreads();
+  if ((d & 63) == 0) red[d >> 6] = Lloc;
+  __syncthreads();
+  const float L = red[0] + red[1] + red[2] + red[3];
   const int64_t tok = b;   // T == 1
   const float g = bf16_bits_to_f32(a.qg[tok * a.sqg + static_cast<int64_t>(h) * 2 * AD + AD + d]);
   a.o[tok * a.so + static_cast<int64_t>(h) * AD + d] = f32_to_bf16_bits(o / L * sigmoidf_(g));
 }
 
+// Prefill: the values of 64 positions of one key/value head go into their
+// transposed cache block through LDS.  Positions past T are written as zeros,
+// values and keys, so that the attention kernel can read whole blocks.
+__global__ __launch_bounds__(256) void attn_vblock_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sv[KB][AD + 8];
+  const int blk = blockIdx.x, j = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int p0 = blk * KB;
+  const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + 256 * i;   // position c / 32, dims 8 (c % 32)..
+    const int p = c / 32, d = 8 * (c % 32);
+    u16x8 x = zero;
+    if (p0 + p < a.T)
+      x = *reinterpret_cast<const u16x8*>(a.v + (static_cast<int64_t>(b) * a.T + p0 + p) * a.sv +
+                                          static_cast<int64_t>(j) * AD + d);
+    else
+      *reinterpret_cast<u16x8*>(a.kc + kc_index(a, b, j, p0 + p) + d) = zero;
+    *reinterpret_cast<u16x8*>(&sv[p][d]) = x;
+  }
+  __syncthreads();
+  uint16_t* dst = a.vc + vc_block(a, b, j, p0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + 256 * i;   // dim c / 8, positions 8 (c % 8)..
+    const int d = c / 8, p = 8 * (c % 8);
+    u16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = sv[p + e][d];
+    *reinterpret_cast<u16x8*>(dst + d * KB + p) = y;
+  }
+}
+
 hipError_t launch_prep(const AttnArgs& a, hipStream_t s) {
-  const int64_t rows = static_cast<int64_t>(a.B) * a.T * (a.Hq + 2 * a.Hkv);
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_prep_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, a);
+  const int64_t ntok = static_cast<int64_t>(a.B) * a.T;
+  if (ntok == 0) return hipSuccess;
+  RopeTable rt{};
+  for (int f = 0; f < a.rot_dim / 2; ++f) rt.inv_freq[f] = std::pow(static_cast<double>(a.theta), -2.0 * f / a.rot_dim);
+  hipLaunchKernelGGL(attn_prep_kernel, dim3(static_cast<unsigned>(ntok)), dim3(256), 0, s, a, rt);
   return hipGetLastError();
 }
 
@@ -417,7 +590,10 @@ hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return hipSuccess;
   hipError_t e = launch_prep(a, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((a.T + QB - 1) / QB, a.Hq, a.B), dim3(256), kFwdLds, s, a);
+  hipLaunchKernelGGL(attn_vblock_kernel, dim3((a.T + KB - 1) / KB, a.Hkv, a.B), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((a.T + QB - 1) / QB * a.Hq * a.B), dim3(256), kFwdLds, s, a);
   return hipGetLastError();
 }
 
@@ -425,7 +601,7 @@ hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   hipError_t e = launch_prep(a, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_decode_kernel, dim3(attn_splits(a.S_max), a.Hkv, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_decode_kernel, dim3(attn_splits(a.S_max), a.Hkv, a.B), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(a.Hq, a.B), dim3(256), 0, s, a);

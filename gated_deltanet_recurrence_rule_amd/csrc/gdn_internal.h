@@ -145,6 +145,10 @@ struct AttnArgs {
   uint16_t* qrot;
   float* part;                // decode only
 };
+// RoPE inverse frequencies theta^(-2f/rot_dim), f < rot_dim/2, computed on the host in fp64
+struct RopeTable {
+  double inv_freq[128];
+};
 // the decode splits: keys per workgroup, and floats per partial result
 constexpr int kAttnSplit = 256;
 constexpr int kAttnPartFloats = 260;
