@@ -20,8 +20,9 @@
 //    blocks are staged through LDS, double-buffered, with the next block's
 //    loads in flight during the products.
 //  * attn_decode_kernel: one wave per (256 cached positions, key/value head,
-//    sequence) runs the same products with the group's query heads as the
-//    MFMA columns, reading keys and values straight from the caches;
+//    sequence) runs the same products on 16x16x32 tiles with the group's query
+//    heads as the MFMA columns, reading keys and values straight from the
+//    caches;
 //    attn_combine_kernel merges the partial maxima, sums and outputs of a head
 //    and applies the gate.
 #include <cmath>
@@ -390,108 +391,136 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------
-// One wave per (256 cached positions, key/value head, sequence): the group's
-// query heads are the columns of the B operand (the columns past the group are
-// zero), keys and values are read straight from the caches as MFMA operands,
-// 64 positions at a time with an online softmax; the partial maximum, sum and
-// unnormalised output of each query head go to the workspace.
-__global__ __launch_bounds__(64) void attn_decode_kernel(AttnArgs a) {
+// One wave per (256 cached positions, key/value head, sequence), on 16x16x32
+// bf16 MFMA: the group's query heads are the 16 columns of the B operand (the
+// columns past the group are zero).  Keys and values stream through the wave's
+// own 32 KiB of LDS, 32 positions at a time, copied with whole-row 16-byte
+// direct loads (1 KiB per instruction); five such waves share a CU, so one
+// wave's copies overlap the others' products.  A 16x16 accumulator gives lane l
+// column l % 16 and rows 4 (l / 16) .. + 3; the key rows of the two score tiles
+// are ordered so that these eight values of a lane are eight consecutive
+// positions, which are then the k slots of the weight operand and one 16-byte
+// read of the transposed values.  Online softmax over the blocks; the partial
+// maximum, sum and unnormalised output of each query head go to the workspace.
+__device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int DB = 32;                       // positions per decode block
+constexpr int kDecLds = DB * AD * 2 * 2;     // keys 16 KiB + transposed values 16 KiB
+
+__global__ __launch_bounds__(64, 2) void attn_decode_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* sk = smem;                  // 32 rows of 512 B: row 16 kt + r holds score tile kt's row r
+  unsigned char* sv = smem + DB * AD * 2;    // 256 rows (dims) of 64 B (32 positions)
   const int sp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int n = min(max(a.cache_len[b], 0), a.S_max - 1) + 1;   // positions [0, n)
   const int k0 = sp * kAttnSplit;
   if (k0 >= n) return;   // the combine reads ceil(n / 256) splits only
-  const int lane = threadIdx.x, l32 = lane & 31, hh = lane >> 5;
-  bf16x8 Qf[16];
+  const int lane = threadIdx.x, c16 = lane & 15, g4 = lane >> 4;
+  // queries: k step s = dims 32s.., lane group g4 holds 8 consecutive dims
+  bf16x8 Qf[8];
   {
-    const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-    const uint16_t* qr = a.qrot + (static_cast<int64_t>(b) * a.Hq + j * G + min(l32, G - 1)) * AD + 8 * hh;
+    const uint16_t* qr = a.qrot + (static_cast<int64_t>(b) * a.Hq + j * G + min(c16, G - 1)) * AD + 8 * g4;
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
-      Qf[s] = __builtin_bit_cast(bf16x8, l32 < G ? *reinterpret_cast<const u16x8*>(qr + 16 * s) : z);
+    for (int s = 0; s < 8; ++s) {
+      u16x8 x = *reinterpret_cast<const u16x8*>(qr + 32 * s);
+      if (c16 >= G) x = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      Qf[s] = __builtin_bit_cast(bf16x8, x);
+    }
   }
-  floatx16 O[8];
+  floatx4 O[16];
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) O[t][v] = 0.f;
+  for (int t = 0; t < 16; ++t) O[t] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
   const float sl2 = a.scale * kLog2e;
-  const int nblk = min(kAttnSplit / KB, (n - k0 + KB - 1) / KB);
+  const unsigned char* kcb = reinterpret_cast<const unsigned char*>(a.kc + kc_index(a, b, j, 0));
+  const int nblk = min(kAttnSplit / DB, (n - k0 + DB - 1) / DB);
   for (int blk = 0; blk < nblk; ++blk) {
-    const int kb0 = k0 + KB * blk;             // kb0 + 63 < S_max: S_max is a multiple of 64
-    const int valid = min(KB, n - kb0);
-    floatx16 S[2];
+    const int kb0 = k0 + DB * blk;           // kb0 + 31 < S_max: S_max is a multiple of 64
+    const int valid = min(DB, n - kb0);
+    // Copy.  Key row r = 16 kt + m of LDS holds position 8 (m / 4) + 4 kt + m % 4, its
+    // 16-byte chunk c at chunk position c ^ (r & 15); value row d (64 B) holds
+    // positions kb0.. kb0+31 of dim d, chunk c at c ^ ((d / 4) & 3).  (Copying the
+    // next block's keys and values while this one is worked on timed the same.)
+    __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the previous block's LDS reads are done
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint16_t* kr = a.kc + kc_index(a, b, j, kb0 + 32 * u + key_of_row(l32)) + 8 * hh;
-      bf16x8 Kf[16];
+    for (int q = 0; q < 16; ++q) {
+      const int r = 2 * q + (lane >> 5), cp = lane & 31;
+      const int kt = r >> 4, mm = r & 15;
+      const int pos = kb0 + 8 * (mm >> 2) + 4 * kt + (mm & 3);
+      __builtin_amdgcn_global_load_lds(kcb + static_cast<int64_t>(pos) * (AD * 2) + 16 * (cp ^ (r & 15)),
+                                       sk + 1024 * q, 16, 0, 0);
+    }
+    const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(a.vc + vc_block(a, b, j, kb0)) +
+                                2 * (kb0 % KB);
 #pragma unroll
-      for (int s = 0; s < 16; ++s) Kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr + 16 * s));
+    for (int q = 0; q < 16; ++q) {
+      const int d = 16 * q + (lane >> 2), cp = lane & 3;
+      __builtin_amdgcn_global_load_lds(vsrc + d * (KB * 2) + 16 * (cp ^ ((d >> 2) & 3)), sv + 1024 * q, 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0): the block is in LDS
+    floatx4 S[2];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) S[u][v] = 0.f;
+    for (int kt = 0; kt < 2; ++kt) {
+      const unsigned char* kr = sk + (16 * kt + c16) * (AD * 2);
+      S[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 16; ++s) S[u] = mfma32(Kf[s], Qf[s], S[u]);
+      for (int s = 0; s < 8; ++s)
+        S[kt] = mfma16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(kr + 16 * ((4 * s + g4) ^ c16))),
+                       Qf[s], S[kt]);
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float x = 32 * u + key_of_row(acc_row(v, hh)) < valid ? S[u][v] * sl2 : -INFINITY;
-        S[u][v] = x;
+      for (int i = 0; i < 4; ++i) {
+        const float x = 8 * g4 + 4 * kt + i < valid ? S[kt][i] * sl2 : -INFINITY;   // row 4 g4 + i of tile kt
+        S[kt][i] = x;
         mx = fmaxf(mx, x);
       }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);             // finite: position kb0 is valid
+    const float mn = fmaxf(m, mx);           // finite: position kb0 is valid
     const float c = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
     l *= c;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 16; ++t) O[t] *= c;
+    // weights: lane group g4 holds positions 8 g4 + 0..7 (tile 0 rows, then tile 1 rows)
+    bf16x8 P;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) O[t][v] *= c;
-    bf16x8 P[4];
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(S[e >> 2][e & 3] - mn);
+      l += p;
+      P[e] = static_cast<__bf16>(p);
+    }
+    // values: rows = dims 16 dt + c16; positions past n may hold arbitrary bits
+    // (a NaN would survive a zero weight), so they are zeroed
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int dt = 0; dt < 16; ++dt) {
+      const int d = 16 * dt + c16;
+      u16x8 vv = *reinterpret_cast<const u16x8*>(sv + d * (DB * 2) + 16 * (g4 ^ ((d >> 2) & 3)));
+      if (valid < DB) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(S[u][8 * s2 + e] - mn);
-          l += p;
-          P[2 * u + s2][e] = static_cast<__bf16>(p);
-        }
-    // values: k step ks holds positions 16 ks + 8 hh + 0..7; positions past n may
-    // hold arbitrary bits (a NaN would survive a zero weight), so they are zeroed
-    const uint16_t* vb = a.vc + vc_block(a, b, j, kb0) + l32 * KB + 8 * hh;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        u16x8 vv = *reinterpret_cast<const u16x8*>(vb + 32 * t * KB + 16 * ks);
-        if (valid < KB) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (16 * ks + 8 * hh + e >= valid) vv[e] = 0;
-        }
-        O[t] = mfma32(__builtin_bit_cast(bf16x8, vv), P[ks], O[t]);
+        for (int e = 0; e < 8; ++e)
+          if (8 * g4 + e >= valid) vv[e] = 0;
       }
+      O[dt] = mfma16(__builtin_bit_cast(bf16x8, vv), P, O[dt]);
+    }
   }
+  l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (l32 >= G) return;
-  float* part = a.part + ((static_cast<int64_t>(b) * a.Hq + j * G + l32) * attn_splits(a.S_max) + sp) *
+  if (c16 >= G) return;
+  float* part = a.part + ((static_cast<int64_t>(b) * a.Hq + j * G + c16) * attn_splits(a.S_max) + sp) *
                              kAttnPartFloats;
-  if (hh == 0) {
+  if (g4 == 0) {
     part[0] = m;
     part[1] = l;
   }
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<floatx4*>(part + 4 + 32 * t + 8 * q4 + 4 * hh) =
-          floatx4{O[t][4 * q4], O[t][4 * q4 + 1], O[t][4 * q4 + 2], O[t][4 * q4 + 3]};
+  for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<floatx4*>(part + 4 + 16 * dt + 4 * g4) = O[dt];
 }
 
 // Merges the partial results of a query head: M = max m_s, L = sum 2^(m_s - M) l_s,
@@ -601,7 +630,7 @@ hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   hipError_t e = launch_prep(a, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_decode_kernel, dim3(attn_splits(a.S_max), a.Hkv, a.B), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(attn_decode_kernel, dim3(attn_splits(a.S_max), a.Hkv, a.B), dim3(64), kDecLds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(a.Hq, a.B), dim3(256), 0, s, a);
