@@ -149,3 +149,43 @@ def test_decode_full_size_sampled_sequences():
                          new["k_norm_w"], kc[b:b + 1].transpose(0, 2, 1, 3), vc[b:b + 1].transpose(0, 2, 1, 3),
                          lens[b:b + 1])
         assert_out_rows(og[b:b + 1], ow)
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,rot,S_max", [(2, 128, 4, 4, 64, 192), (1, 96, 8, 1, 0, 128),
+                                                  (1, 70, 16, 2, 256, 128), (3, 256, 6, 3, 64, 320)])
+def test_prefill_shapes_and_rotations(B, T, Hq, Hkv, rot, S_max):
+    """One key/value head per query head, 8 query heads per group, no rotation, every
+    dimension rotated, exact block multiples, and caches with spare room."""
+    torch = _torch()
+    p = W.attn_problem(760 + T + rot, B, T, Hq, Hkv)
+    d = dev_problem(p)
+    kc, vc = G.attn_cache(B, Hkv, S_max)
+    o = G.gdn_attn_prefill(d["qg"], d["k"], d["v"], d["q_norm_w"], d["k_norm_w"], kc, vc, rot_dim=rot)
+    torch.cuda.synchronize()
+    orf, kr, _ = A.prefill(p["qg"], p["k"], p["v"], p["q_norm_w"], p["k_norm_w"], rot_dim=rot)
+    assert_out_rows(to_host(o), orf)
+    kg, vg = cache_views(kc, vc, S_max)
+    assert np.all(np.abs(kg[:, :T] - kr) <= ulp_bf16(kr) + 2.0 ** -12 * np.abs(kr).max(axis=-1, keepdims=True))
+    np.testing.assert_array_equal(vg[:, :T], A.widen(p["v"]))
+    tail = ((T + 63) // 64) * 64
+    assert np.all(kg[:, T:tail] == 0) and np.all(vg[:, T:tail] == 0)   # the partial block's tail is zeroed
+
+
+@pytest.mark.parametrize("G_,rot", [(8, 64), (1, 0)])
+def test_decode_group_sizes(G_, rot):
+    torch = _torch()
+    B, Hkv, T0 = 2, 2, 100
+    Hq = G_ * Hkv
+    p = W.attn_problem(780 + G_, B, T0 + 1, Hq, Hkv)
+    head = {k: (v[:, :T0].copy() if k in ("qg", "k", "v") else v) for k, v in p.items()}
+    head["T"] = T0
+    d0 = dev_problem(head)
+    kc, vc = G.attn_cache(B, Hkv, 128)
+    G.gdn_attn_prefill(d0["qg"], d0["k"], d0["v"], d0["q_norm_w"], d0["k_norm_w"], kc, vc, rot_dim=rot)
+    d = dev_problem(p)
+    lens = torch.full((B,), T0, dtype=torch.int32, device="cuda")
+    o = G.gdn_attn_decode(d["qg"][:, T0].contiguous(), d["k"][:, T0].contiguous(), d["v"][:, T0].contiguous(),
+                          d["q_norm_w"], d["k_norm_w"], lens, kc, vc, rot_dim=rot)
+    torch.cuda.synchronize()
+    orf, _, _ = A.prefill(p["qg"], p["k"], p["v"], p["q_norm_w"], p["k_norm_w"], rot_dim=rot)
+    assert_out_rows(to_host(o), orf[:, T0])
