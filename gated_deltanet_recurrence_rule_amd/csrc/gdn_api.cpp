@@ -182,8 +182,8 @@ gdn_status check_attn(const gdn_attn_dims* d, bool decode) {
   if (decode && d->T != 1) return fail(GDN_ERR_SHAPE, "decode needs T == 1 (got %d)", d->T);
   if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv)
     return fail(GDN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", d->Hq, d->Hkv);
-  if (decode && d->Hq / d->Hkv > 8)
-    return fail(GDN_ERR_UNSUPPORTED, "decode takes at most 8 query heads per key/value head (got %d)",
+  if (decode && d->Hq / d->Hkv > 16)
+    return fail(GDN_ERR_UNSUPPORTED, "decode takes at most 16 query heads per key/value head (got %d)",
                 d->Hq / d->Hkv);
   if (d->D != 256) return fail(GDN_ERR_UNSUPPORTED, "head width D=%d: the kernels take 256", d->D);
   if (d->rot_dim < 0 || d->rot_dim > d->D || d->rot_dim % 8)

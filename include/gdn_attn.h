@@ -91,7 +91,8 @@ size_t gdn_attn_prefill_workspace_size(const gdn_attn_dims* dims);
  * attends to positions [0, cache_len[b]].
  *   qg [B, Hq, 2, D], k, v [B, Hkv, D] (sequence strides stride_qg, stride_k,
  *      stride_v); o [B, Hq D] (stride_o)
- * Hq/Hkv must be at most 8.
+ * Hq/Hkv must be at most 16 (the query heads of a group are the 16 columns of
+ * the decode kernel's matrix products).
  *   cache_len [B] int32 DEVICE memory: tokens already cached per sequence,
  *      0 <= cache_len[b] < S_max (device data: not checked on the host; the
  *      kernels clamp it into that range); not modified -- the caller advances

@@ -297,7 +297,7 @@ def test_attention_argument_errors():
     assert pre(adims(), n=1000) == B.GDN_ERR_SHAPE                             # workspace too small
     assert pre(adims(B=0)) == B.GDN_OK and pre(adims(T=0)) == B.GDN_OK        # nothing to do
     assert dec(adims(T=2)) == B.GDN_ERR_SHAPE
-    assert dec(adims(T=1, Hq=36, Hkv=4)) == B.GDN_ERR_UNSUPPORTED              # 9 query heads per group
+    assert dec(adims(T=1, Hq=68, Hkv=4)) == B.GDN_ERR_UNSUPPORTED              # 17 query heads per group
     assert dec(adims(T=1), cl=None) == B.GDN_ERR_NULL
     assert dec(adims(T=1), cl=ctypes.c_void_p(0x10002)) == B.GDN_ERR_ALIGN
     assert dec(adims(T=1), n=1000) == B.GDN_ERR_SHAPE

@@ -171,7 +171,7 @@ def test_prefill_shapes_and_rotations(B, T, Hq, Hkv, rot, S_max):
     assert np.all(kg[:, T:tail] == 0) and np.all(vg[:, T:tail] == 0)   # the partial block's tail is zeroed
 
 
-@pytest.mark.parametrize("G_,rot", [(8, 64), (1, 0)])
+@pytest.mark.parametrize("G_,rot", [(16, 64), (8, 64), (1, 0)])
 def test_decode_group_sizes(G_, rot):
     torch = _torch()
     B, Hkv, T0 = 2, 2, 100
