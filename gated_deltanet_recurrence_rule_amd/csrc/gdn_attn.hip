@@ -5,24 +5,24 @@
 // ("Le facteur 2 sur W_Q", "GQA a 6:1", "Le RoPE partiel").
 //
 // Kernels:
-//  * attn_prep_kernel: one workgroup per token, a wave per 256-wide row.  Query rows are
-//    normalised and rotated into the qrot scratch; key rows likewise into the
-//    key cache at the token's position; value rows are copied into the value
-//    cache, whose 64-position blocks are stored transposed ([256][64]) so that
-//    the products read them as MFMA operands with keys along k.
+//  * attn_prep_kernel: one workgroup per token, a wave per 256-wide row.  Query
+//    rows are normalised and rotated into the qrot scratch, key rows likewise
+//    into the key cache at the token's position; a decode token's value row is
+//    copied into the value cache, whose 64-position blocks are stored transposed
+//    ([256][64]) so that the products read them as MFMA operands with positions
+//    along k.  attn_vblock_kernel writes a prefill's values a block at a time.
 //  * attn_fwd_kernel (prefill): 4 waves x 32 query rows of one query head.
 //    Per block of 64 keys: S^T = K Q^T on 32x32x16 bf16 MFMA (keys on the MFMA
 //    rows, queries on its columns, so each lane holds one query's scores and
 //    the softmax statistics are per lane plus one exchange across the two lane
-//    halves), the online softmax in base 2, then O^T += V^T P^T, whose
-//    B operand is the score accumulator itself rounded to bf16 (the key order
-//    of the accumulator rows is the k order of the operand).  Key and value
-//    blocks are staged through LDS, double-buffered, with the next block's
-//    loads in flight during the products.
+//    halves), the weights 2^(s - m) against a fixed per-row reference m, then
+//    O^T += V^T P^T, whose B operand is the score accumulator itself rounded to
+//    bf16 (the key order of the accumulator rows is the k order of the operand).
+//    Key and value blocks are copied into LDS, double-buffered, with the next
+//    block's copies in flight during the products.
 //  * attn_decode_kernel: one wave per (256 cached positions, key/value head,
 //    sequence) runs the same products on 16x16x32 tiles with the group's query
-//    heads as the MFMA columns, reading keys and values straight from the
-//    caches;
+//    heads as the MFMA columns, streaming keys and values through its own LDS;
 //    attn_combine_kernel merges the partial maxima, sums and outputs of a head
 //    and applies the gate.
 #include <cmath>
@@ -63,7 +63,8 @@ __device__ __forceinline__ int64_t vc_block(const AttnArgs& a, int b, int j, int
 }
 
 // ---------------------------------------------------------------------------
-// prep: rows are, per token, Hq query rows, Hkv key rows, Hkv value rows
+// prep: rows are, per token, Hq query rows and Hkv key rows, then (decode only)
+// Hkv value rows
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_prep_kernel(AttnArgs a, RopeTable rt) {
   // one workgroup per token; wave w takes the token's rows w, w + 4, ...
@@ -577,10 +578,12 @@ __global__ __launch_bounds__(256) void attn_vblock_kernel(AttnArgs a) {
     const int c = tid + 256 * i;   // position c / 32, dims 8 (c % 32)..
     const int p = c / 32, d = 8 * (c % 32);
     u16x8 x = zero;
-    if (p0 + p < a.T)
-      x = *reinterpret_cast<const u16x8*>(a.v + (static_cast<int64_t>(b) * a.T + p0 + p) * a.sv +
-                                          static_cast<int64_t>(j) * AD + d);
-    else
+    if (p0 + p < a.T) {
+      // two 8-byte loads: v rows are 8-byte aligned (strides are multiples of 4)
+      const uint16_t* src = a.v + (static_cast<int64_t>(b) * a.T + p0 + p) * a.sv + static_cast<int64_t>(j) * AD + d;
+      const u16x4 lo = *reinterpret_cast<const u16x4*>(src), hi = *reinterpret_cast<const u16x4*>(src + 4);
+      x = u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else
       *reinterpret_cast<u16x8*>(a.kc + kc_index(a, b, j, p0 + p) + d) = zero;
     *reinterpret_cast<u16x8*>(&sv[p][d]) = x;
   }

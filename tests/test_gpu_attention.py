@@ -189,3 +189,29 @@ def test_decode_group_sizes(G_, rot):
     torch.cuda.synchronize()
     orf, _, _ = A.prefill(p["qg"], p["k"], p["v"], p["q_norm_w"], p["k_norm_w"], rot_dim=rot)
     assert_out_rows(to_host(o), orf[:, T0])
+
+
+def test_prefill_padded_strides():
+    """qg, k, v and o as views with token strides 4 elements wider than their rows (8-byte but
+    not 16-byte aligned rows, the weakest alignment the ABI accepts)."""
+    torch = _torch()
+    B, T, Hq, Hkv, D = 2, 100, 6, 1, 256
+    p = W.attn_problem(790, B, T, Hq, Hkv)
+    d = dev_problem(p)
+
+    def padded(x, lead_shape, width):
+        wide = torch.zeros(lead_shape + (width + 4,), dtype=torch.bfloat16, device="cuda")
+        wide[..., :width] = x.reshape(lead_shape + (width,))
+        return wide[..., :width]
+
+    qg = padded(d["qg"], (B, T), 2 * Hq * D).view(B, T, Hq, 2, D)
+    k = padded(d["k"], (B, T), Hkv * D).view(B, T, Hkv, D)
+    v = padded(d["v"], (B, T), Hkv * D).view(B, T, Hkv, D)
+    o = torch.zeros((B, T, Hq * D + 4), dtype=torch.bfloat16, device="cuda")[..., :Hq * D].view(B, T, Hq, D)
+    kc, vc = G.attn_cache(B, Hkv, 128)
+    G.gdn_attn_prefill(qg, k, v, d["q_norm_w"], d["k_norm_w"], kc, vc, o)
+    torch.cuda.synchronize()
+    orf, _, _ = A.prefill(p["qg"], p["k"], p["v"], p["q_norm_w"], p["k_norm_w"])
+    assert_out_rows(to_host(o), orf)
+    _, vg = cache_views(kc, vc, T)
+    np.testing.assert_array_equal(vg, A.widen(p["v"]))
