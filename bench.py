@@ -346,12 +346,6 @@ def bench_attention(dev, steps=20, warmup=20):
                 decode_GBs=by / (med_d * 1e-3) / 1e9, decode_hbm_frac=by / (med_d * 1e-3) / (HBM_PEAK_GBS * 1e9))
 
 
-def varlen_lengths(n=32, lo=16, hi=8192, seed=6):
-    """Lengths of a continuous-batching prefill: n requests, log-uniform on [lo, hi]."""
-    rng = np.random.default_rng(seed)
-    return np.exp(rng.uniform(np.log(lo), np.log(hi), n)).astype(np.int64)
-
-
 def bench_varlen(dev, steps=20, warmup=20):
     """Packed prefill of 32 requests of log-uniform lengths (16 to 8192 tokens,
     seeded), 16/48 heads, one gdn_prefill_varlen call per step, final states into a
@@ -359,7 +353,8 @@ def bench_varlen(dev, steps=20, warmup=20):
     each.  Inputs drawn on the GPU."""
     import torch
     from gated_deltanet_recurrence_rule_amd import binding as G
-    lens = varlen_lengths()
+    from gated_deltanet_recurrence_rule_amd import workloads as W
+    lens = W.varlen_lengths()
     Hk, Hv, D = 16, 48, 128
     T = int(lens.sum())
     cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)

@@ -210,3 +210,10 @@ def attn_problem(seed: int, B: int, T: int, Hq: int = 24, Hkv: int = 4, D: int =
     kw = normal_tokens(seed, "attn_kw", 1, D, loc=1.0, scale=0.1, post=f32_to_bf16, out_dtype=np.uint16)[0]
     return dict(B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, qg=qg.reshape(B, T, Hq, 2, D), k=k.reshape(B, T, Hkv, D),
                 v=v.reshape(B, T, Hkv, D), q_norm_w=qw, k_norm_w=kw)
+
+
+def varlen_lengths(n: int = 32, lo: int = 16, hi: int = 8192, seed: int = 6) -> np.ndarray:
+    """Request lengths of a continuous-batching prefill: n draws, log-uniform on [lo, hi]
+    (numpy default_rng(seed)), truncated to integers."""
+    rng = np.random.default_rng(seed)
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), n)).astype(np.int64)

@@ -187,3 +187,29 @@ def test_varlen_many_sequences():
     og2, sg2 = run_packed(p, st, cu, workspace=ws)
     np.testing.assert_array_equal(og2, og)   # windows do not change the arithmetic
     np.testing.assert_array_equal(sg2, sg)
+
+
+def test_varlen_bench_workload_sampled():
+    """The packed workload the bench times (32 requests of log-uniform lengths, 38,693 tokens,
+    16/48 heads, D = 128, final states into a 32-entry pool), checked on sampled (request,
+    value head) pairs that the oracle recomputes over the whole request (heads are
+    independent, so a sampled head is exact).  The longest and the shortest requests are
+    among them."""
+    torch = _torch()
+    lens = [int(x) for x in W.varlen_lengths()]
+    Hk, Hv, D = 16, 48, 128
+    p, st, cu = packed_problem(5700, lens, Hk, Hv, D, "bf16", state=False)
+    q, k, v = (to_dev(p[x][0]) for x in ("q", "k", "v"))
+    la, be = to_dev(p["log_alpha"][0]), to_dev(p["beta"][0])
+    so = torch.empty((len(lens), Hv, D, D), dtype=torch.float32, device="cuda")
+    o = G.gdn_prefill_varlen(q, k, v, la, be, to_dev(cu), None, so, Hk=Hk, Hv=Hv)
+    torch.cuda.synchronize()
+    og, sg = to_host(o).reshape(p["T"], Hv, D), to_host(so)
+    longest, shortest = int(np.argmax(lens)), int(np.argmin(lens))
+    for s, h in [(longest, 0), (longest, 47), (shortest, 5), (3, 17), (20, 30), (31, 44)]:
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = lambda x: np.ascontiguousarray(x[:, a:b])
+        orf, srf = oracle.recurrence(sl(p["q"]), sl(p["k"]), sl(p["v"]), sl(p["log_alpha"]), sl(p["beta"]),
+                                     Hk, Hv, None, sel=[h])
+        assert_out(og[a:b, h], orf[0], bf16=True)
+        assert_state(sg[s, h], srf[0])
