@@ -612,13 +612,12 @@ hipError_t launch_prep(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kFwdLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static PerDeviceOnce attrs;
+  hipError_t ea = attrs.run([] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kFwdLds);
+  });
+  if (ea != hipSuccess) return ea;
   if (a.B == 0 || a.T == 0) return hipSuccess;
   hipError_t e = launch_prep(a, s);
   if (e != hipSuccess) return e;

@@ -1029,16 +1029,15 @@ int chunk_window_chunks(const RecArgs& a) {
 }
 
 hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  static PerDeviceOnce attrs;
+  hipError_t ea = attrs.run([] {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_prep_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds::kBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds::kBytes);
+  });
+  if (ea != hipSuccess) return ea;
   const int nchunks = chunk_count(a);
   if (nchunks == 0) return hipSuccess;
   RecArgs r = a;

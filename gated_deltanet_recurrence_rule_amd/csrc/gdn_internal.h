@@ -6,7 +6,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace gdn {
+
+// One-time set-up of a launcher (kernel attributes such as the dynamic LDS
+// size), which HIP keeps per device: runs `f` on the first call on each device,
+// or on every call for a device index past the table.  Concurrent first calls
+// may both run `f`, which must be idempotent.
+struct PerDeviceOnce {
+  std::atomic<bool> done[64] = {};
+  template <typename F>
+  hipError_t run(F&& f) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool tracked = dev >= 0 && dev < 64;
+    if (tracked && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+    e = f();
+    if (e == hipSuccess && tracked) done[dev].store(true, std::memory_order_release);
+    return e;
+  }
+};
 
 // Arguments of the recurrence kernels (prefill and decode share them).
 struct RecArgs {
