@@ -129,15 +129,17 @@ gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const
  * for these dims (0 when the call needs none).  The chunked kernel keeps, per
  * (sequence, value head, chunk of a window), the per-chunk matrices that do
  * not depend on the state (55 KiB: the -W, K^T, U0 and P operands and the
- * row scalings, plus 16 KiB per key head for the scaled Q).  Windows hold
- * about 96 MiB of these, so that the chain kernel finds them in the GPU's
- * last-level cache, but at least 512 / (Hk * B) chunks and at most 256 MiB;
- * they are balanced.  The state is carried between windows through
- * state_out, or through a carry area inside the workspace when state_out is
- * NULL.  A smaller
- * workspace is accepted down to one chunk per window (plus the carry when
- * needed); GDN_ERR_SHAPE below that.  The workspace is caller-owned device
- * memory, 256-byte aligned, used only during the call's kernels on `stream`.
+ * row scalings, plus 16 KiB per key head for the scaled Q).  A window is a
+ * whole number of rounds of resident prep workgroups (512 (chunk, key head)
+ * pairs at up to 24 value heads per key head): as many rounds as keep it
+ * within about 96 MiB, so that the chain kernel finds its operands in the
+ * GPU's last-level cache, or, when one round alone is larger, as many as fit
+ * in 2 GiB; windows are then balanced.  The state is carried between windows
+ * through state_out, or through a carry area inside the workspace when
+ * state_out is NULL.  A smaller workspace is accepted down to one chunk per
+ * window (plus the carry when needed); GDN_ERR_SHAPE below that.  The
+ * workspace is caller-owned device memory, 256-byte aligned, used only during
+ * the call's kernels on `stream`.
  */
 size_t gdn_prefill_workspace_size(const gdn_dims* dims);
 
@@ -156,8 +158,10 @@ size_t gdn_prefill_workspace_size(const gdn_dims* dims);
  *   q, k [T, Hk, Dk]; v, o [T, Hv, Dv]; log_alpha, beta [T, Hv]: as gdn_prefill
  *               with B = 1 (token strides stride_q/k/v/o)
  *   state_in / state_out [B, Hv, Dk, Dv] fp32 per sequence, as gdn_prefill
- *   workspace   gdn_prefill_varlen_workspace_size bytes (or fewer, down to one
- *               chunk per window plus the state carry)
+ *   workspace   gdn_prefill_varlen_workspace_size bytes (or fewer, down to the
+ *               chunk maps, one chunk per window and the state carry).  Its
+ *               head holds the chunk maps, (B + 1 + ceil(T/64) + B) int32
+ *               rounded up to 256 bytes, written by the call's first kernel
  * Chunks never span two sequences; every other rule is gdn_prefill's.
  */
 gdn_status gdn_prefill_varlen(const gdn_dims* dims, const int32_t* cu_seqlens, const void* q, const void* k,
