@@ -18,6 +18,11 @@ import numpy as np
 OUT_TOL = 2e-2
 STATE_TOL = 1e-3
 
+# Prefill workspace per chunk: per value head the -W, Kd and U0 fragments (16 KiB each), the P
+# fragments (6 KiB) and 1 KiB of scalings; per key head the Q^ fragments (16 KiB).
+WS_VALUE_HEAD = 56320
+WS_KEY_HEAD = 16384
+
 
 def to_dev(a: np.ndarray, device="cuda"):
     import torch

@@ -9,6 +9,7 @@ import re
 import pytest
 
 from gated_deltanet_recurrence_rule_amd import binding as B
+from helpers import WS_KEY_HEAD, WS_VALUE_HEAD
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
@@ -36,31 +37,31 @@ def test_library_exports_every_declared_function():
 def test_workspace_size():
     ws = B.gdn_prefill_workspace_size
     # per chunk: B * (Hv * 55 KiB (-W, Kd, U0, P fragments + 1 KiB scalings) + Hk * 16 KiB Q^ fragments)
-    per_chunk = 6 * 56320 + 2 * 16384
+    per_chunk = 6 * WS_VALUE_HEAD + 2 * WS_KEY_HEAD
     assert ws(dims(T=64)) == per_chunk
     assert ws(dims(T=65)) == 2 * per_chunk
     assert ws(dims(io=B.GDN_F32, D=16)) == 0            # token-serial path needs none
     # windows of ~96 MiB, balanced: 64 chunks of 2.97 MB -> 2 windows of 32, plus a state carry
-    per = 48 * 56320 + 16 * 16384
+    per = 48 * WS_VALUE_HEAD + 16 * WS_KEY_HEAD
     assert ws(dims(T=4096, Hk=16, Hv=48)) == 32 * per + 48 * 128 * 128 * 4
     # one round of prep workgroups, 512 / (Hk B) = 8 chunks, is already 228 MiB here: the cache cannot
     # hold a window, so windows take as many rounds as fit in 2 GiB: 64 chunks (1.78 GiB) + a carry
     big = dims(B=4, T=32768, Hk=16, Hv=128)
-    per = 4 * (128 * 56320 + 16 * 16384)
+    per = 4 * (128 * WS_VALUE_HEAD + 16 * WS_KEY_HEAD)
     assert ws(big) == 64 * per + 4 * 128 * 128 * 128 * 4
     # long sequence: 4096 chunks in 128 windows of 32 (one round of 512 prep workgroups each)
-    per = 48 * 56320 + 16 * 16384
+    per = 48 * WS_VALUE_HEAD + 16 * WS_KEY_HEAD
     assert ws(dims(T=262144, Hk=16, Hv=48)) == 32 * per + 48 * 128 * 128 * 4
     # 32 value heads per key head: one prep workgroup per CU, a round is 256 chunks (466 MB), so
     # windows fill 2 GiB: 1024 chunks, and all 300 chunks fit in one window
-    per = 32 * 56320 + 16384
+    per = 32 * WS_VALUE_HEAD + WS_KEY_HEAD
     assert ws(dims(T=64 * 300, Hk=1, Hv=32)) == 300 * per
     assert ws(dims(T=64 * 2000, Hk=1, Hv=32)) == 1000 * per + 32 * 128 * 128 * 4   # 2 windows of 1000
     assert ws(dims(Hv=5)) == 0                          # invalid dims
     d = dims(T=64)
     d.flags = B.GDN_FLAG_TOKEN_SERIAL                   # token-serial path forced: none
     assert ws(d) == 0
-    assert ws(dims(T=64, Hk=1, Hv=64)) == 64 * 56320 + 16384   # 64 value heads per key head: chunked
+    assert ws(dims(T=64, Hk=1, Hv=64)) == 64 * WS_VALUE_HEAD + WS_KEY_HEAD   # 64 value heads per key head: chunked
     assert ws(dims(T=64, Hk=1, Hv=65)) == 0             # more: token-serial, no workspace
 
 
@@ -68,9 +69,9 @@ def test_varlen_workspace_size_and_errors():
     ws = B.gdn_prefill_varlen_workspace_size
     # 3 packed sequences, 4096 tokens: chunk maps ((3 + 1) + 67 int32, rounded up to 256 bytes),
     # at most 64 + 3 chunks in balanced windows of 23, a carry per sequence
-    per = 48 * 56320 + 16 * 16384
+    per = 48 * WS_VALUE_HEAD + 16 * WS_KEY_HEAD
     assert ws(dims(B=3, T=4096, Hk=16, Hv=48)) == 512 + 23 * per + 3 * 48 * 128 * 128 * 4
-    assert ws(dims(B=2, T=100, Hk=2, Hv=6)) == 256 + 4 * (6 * 56320 + 2 * 16384)   # one window of 2 + 2 chunks
+    assert ws(dims(B=2, T=100, Hk=2, Hv=6)) == 256 + 4 * (6 * WS_VALUE_HEAD + 2 * WS_KEY_HEAD)   # one window of 2 + 2 chunks
     assert ws(dims(B=0, T=0)) == 0
     L = B.lib()
     call = lambda cu, d=None: L.gdn_prefill_varlen(ctypes.byref(d or dims(B=2, T=100)), cu, FAKE, FAKE, FAKE, FAKE,

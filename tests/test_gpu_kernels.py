@@ -10,7 +10,7 @@ import pytest
 import oracle
 from gated_deltanet_recurrence_rule_amd import binding as G
 from gated_deltanet_recurrence_rule_amd import workloads as W
-from helpers import assert_out, assert_state, to_dev, to_host
+from helpers import WS_KEY_HEAD, WS_VALUE_HEAD, assert_out, assert_state, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -156,7 +156,7 @@ def test_prefill_small_workspace_windows(with_state_out):
     si = to_dev(p["state_in"].astype(np.float32))
     dims = G.make_dims(B, T, Hk, Hv, D, G.GDN_BF16)
     full = G.gdn_prefill_workspace_size(dims)
-    per_chunk = B * (Hv * 56320 + Hk * 16384)
+    per_chunk = B * (Hv * WS_VALUE_HEAD + Hk * WS_KEY_HEAD)
     assert full == 5 * per_chunk
     for nwin in (1, 2):
         extra = 0 if with_state_out else B * Hv * D * D * 4

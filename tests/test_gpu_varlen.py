@@ -9,7 +9,7 @@ import pytest
 import oracle
 from gated_deltanet_recurrence_rule_amd import binding as G
 from gated_deltanet_recurrence_rule_amd import workloads as W
-from helpers import assert_out, assert_state, to_dev, to_host
+from helpers import WS_KEY_HEAD, WS_VALUE_HEAD, assert_out, assert_state, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -117,7 +117,7 @@ def test_varlen_small_workspace_windows(with_state_out):
     p, st, cu = packed_problem(5300, LENS, Hk, Hv, D, "bf16")
     orf, srf = oracle_packed(p, st, cu)
     dims = G.make_dims(len(LENS), p["T"], Hk, Hv, D, G.GDN_BF16)
-    per_chunk = Hv * 56320 + Hk * 16384
+    per_chunk = Hv * WS_VALUE_HEAD + Hk * WS_KEY_HEAD
     nchunks = (p["T"] + 63) // 64 + len(LENS)
     maps = -(-(len(LENS) + 1 + nchunks) * 4 // 256) * 256   # chunk maps at the workspace start
     assert G.gdn_prefill_varlen_workspace_size(dims) == maps + nchunks * per_chunk
@@ -182,8 +182,8 @@ def test_varlen_many_sequences():
     # windows of 1024 chunks (two rounds of 512 prep workgroups, 71 MiB) balanced over 1245: two of 623,
     # plus a state carry per sequence
     assert nchunks == 1245
-    assert full == maps + 623 * (56320 + 16384) + len(lens) * D * D * 4
-    ws = torch.empty(maps + 4 * (56320 + 16384), dtype=torch.uint8, device="cuda")
+    assert full == maps + 623 * (WS_VALUE_HEAD + WS_KEY_HEAD) + len(lens) * D * D * 4
+    ws = torch.empty(maps + 4 * (WS_VALUE_HEAD + WS_KEY_HEAD), dtype=torch.uint8, device="cuda")
     og2, sg2 = run_packed(p, st, cu, workspace=ws)
     np.testing.assert_array_equal(og2, og)   # windows do not change the arithmetic
     np.testing.assert_array_equal(sg2, sg)
