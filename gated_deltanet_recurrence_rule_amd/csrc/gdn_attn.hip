@@ -27,6 +27,8 @@
 //    and applies the gate.
 #include <cmath>
 
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -226,7 +228,11 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   // Weights 2^(s - m) are fp32 and bf16 numbers, whose range is the same, and
   // stay far inside it unless a later score exceeds the reference by more than
   // 96 (base 2); a wave that sees one redoes its rows exactly after the loop.
-  for (int kb = 0; kb < nkb; ++kb) {
+  // Blocks that end before the wave's first query need no causal mask: they run
+  // through a copy of the body without it.  Every wave runs nkb bodies, one
+  // barrier each.
+  auto body = [&](int kb, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
     const int cur = kb & 1;
     const unsigned char* sk = smem + cur * KBUF;
     const unsigned char* sv = smem + 2 * KBUF + cur * VBUF;
@@ -262,20 +268,21 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // scale to base 2, mask keys after the query, block maximum
+    // mask keys after the query (blocks that reach past the wave's first query
+    // only), block maximum of the raw scores; the weights are 2^(s sl2 - m)
     const int kbase = kb * KB;
-    const bool diag = kbase + KB - 1 > q0;
+    float sc[2][16];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        sc[u][v] = kMasked && kbase + 32 * u + key_of_row(acc_row(v, hh)) > qi ? -INFINITY : S[u][v];
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = S[u][v] * sl2;
-        if (diag && kbase + 32 * u + key_of_row(acc_row(v, hh)) > qi) x = -INFINITY;
-        S[u][v] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[u][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
     if (kb == 0) m = mx;            // finite: key 0 precedes every query
     over |= mx > m + 96.0f;
     // P^T fragments: accumulator values 8s2..8s2+7 of tile u are keys
@@ -287,7 +294,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(S[u][8 * s2 + e] - m);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[u][8 * s2 + e], sl2, -m));
           l += p;
           P[2 * u + s2][e] = static_cast<__bf16>(p);
         }
@@ -313,7 +320,11 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
     }
     wait_vm_all();   // this wave's pieces of the next block are in LDS
     __syncthreads();
-  }
+  };
+  // blocks whose keys all precede the wave's first query (uniform over the wave)
+  const int nfree = __builtin_amdgcn_readfirstlane(min(nkb, (q0 + 1) / KB));
+  for (int kb = 0; kb < nfree; ++kb) body(kb, std::false_type{});
+  for (int kb = nfree; kb < nkb; ++kb) body(kb, std::true_type{});
   if (__builtin_amdgcn_ballot_w64(over)) {
     // Exact redo of this wave's rows, straight from the caches: the row maxima
     // over all visible keys first, then the weights and values against them.
