@@ -468,8 +468,8 @@ def main():
         print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "repeats": 5}))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU: libgdn runs on a single GPU and has no multi-GPU path "
+              f"(asked for {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import torch
