@@ -557,18 +557,19 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
 // =========================================================================
 // chain kernel: one workgroup (3 waves) per (32-column strip, value head, batch)
 // =========================================================================
-// LDS: three input slots (a chunk's -W, Kd, U0 strip and scalings, copied from
-// the workspace by the copy wave two chunks ahead), two buffers each of the M
-// and U fragments that the state wave publishes for the output wave, and the
-// output wave's staging tile.  The output wave reads its own operands (Q^ and
-// P fragments) from the workspace straight into registers.
+// LDS: NS input slots (a chunk's -W, Kd, U0 strip and scalings, copied from the
+// workspace by the copy wave, NS - 1 chunks ahead, or with one slot once the
+// chunk's operands have been read), two buffers each of the M and U fragments
+// that the state wave publishes for the output wave, and the output wave's
+// staging tile.  The output wave reads its own operands (Q^ and P fragments)
+// from the workspace straight into registers.  Two slots take 98 KiB, so one
+// workgroup per CU; one slot 61 KiB, so two share a CU and cover each other's
+// copies when the grid holds more workgroups than there are CUs.
+template <int NS>
 struct ChainLds {
   static constexpr int kW = 0, kKd = 16384, kU0 = 32768, kSc = 36864;
   static constexpr int kSlot = 37888;               // 37 blocks of 1 KiB
-#ifndef GDN_CHAIN_SLOTS
-#define GDN_CHAIN_SLOTS 2
-#endif
-  static constexpr int kNSlot = GDN_CHAIN_SLOTS;
+  static constexpr int kNSlot = NS;
   static constexpr int kMf = kNSlot * kSlot;        // 2 x M fragments (fp16) [k step 8][lane 64] x 16 B
   static constexpr int kUf = kMf + 2 * 8192;        // 2 x U fragments (fp16) [k step 4][lane 64] x 16 B;
                                                     // once read, a U buffer stages the output tile
@@ -631,9 +632,17 @@ __device__ __forceinline__ void seq_chunks(const RecArgs& a, int b, int& cs, int
 // The window holds chunks [c0, c0 + nw) (workspace stride nwin).  A sequence's
 // state comes from state_in at its first chunk and from `carry` otherwise, and
 // goes to state_out after its last chunk and to `carry` otherwise.
+// With one slot the copy of chunk c+1 waits for a second barrier per chunk, which
+// each wave reaches once it has read chunk c's slot.
+__device__ __forceinline__ void slot_read_done() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads have returned
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int NS>
 __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, const unsigned char* ws, int nwin,
                                                              int nw, float* carry) {
-  using L = ChainLds;
+  using L = ChainLds<NS>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, h = lane >> 5;
@@ -756,6 +765,7 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
       // Kd fragments for the update, read while the last products drain
 #pragma unroll
       for (int i = 0; i < 16; ++i) Af[i] = *reinterpret_cast<const halfx8*>(slot + L::kKd + i * 1024 + lane * 16);
+      if constexpr (NS == 1) slot_read_done();
       halfx8 Uf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -851,6 +861,8 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
       unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
       const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
       const unsigned char* sMf = smem + L::kMf + (cl & 1) * 8192;
+      const float g0 = sSc[l32], g1 = sSc[32 + l32];
+      if constexpr (NS == 1) slot_read_done();
       // ---- O^T = M^T Q^^T diag(gamma) + U^T P^T: the M and U fragments serve as A
       //      operands and Q^, P as B operands, so each lane holds one token and
       //      runs of four value columns ------------------------------------------
@@ -873,7 +885,6 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
         for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(wq + i * 1024 + lane * 16);
       }
       if (cl > 0) finish(Op, cl - 1);
-      const float g0 = sSc[l32], g1 = sSc[32 + l32];
       Op[0] = O[0] * g0;
       Op[1] = O[1] * g1;
       // the first chunk issues no stores; draining its loads here keeps the counts
@@ -883,6 +894,19 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
       lds_sync();
     }
     if (nchunk > 0) finish(Op, nchunk - 1);
+  } else if constexpr (NS == 1) {
+    // one slot: chunk cl+1 is copied once every wave has read chunk cl's
+    copy_chunk(0);
+    wait_vm_all();
+    __syncthreads();
+    for (int cl = 0; cl < nchunk; ++cl) {
+      __builtin_amdgcn_s_barrier();
+      if (cl + 1 < nchunk) {
+        copy_chunk(cl + 1);
+        wait_vm_all();
+      }
+      __builtin_amdgcn_s_barrier();
+    }
   } else {
     // copies run kAhead = slots - 1 chunks ahead
     constexpr int kAhead = L::kNSlot - 1;
@@ -1034,8 +1058,11 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_prep_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds::kBytes);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<2>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<2>::kBytes);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<1>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<1>::kBytes);
   });
   if (ea != hipSuccess) return ea;
   const int nchunks = chunk_count(a);
@@ -1085,8 +1112,17 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     // (chunk slot of the window, value head, strip), since at most nw sequences
     // have chunks in the window
     const int slots = a.cu_seqlens ? nw : a.B;
-    hipLaunchKernelGGL(chunk_chain_kernel, dim3(slots * a.Hv * (DK / 32)), dim3(192), ChainLds::kBytes, s, r, c0,
-                       static_cast<const unsigned char*>(wsb), nwin, nw, carry);
+    // With more workgroups than CUs the one-slot kernel lets two share a CU (batch
+    // 4, 128 value heads: 9.9 ms of prefill against 10.7 ms).  A packed batch
+    // runs one slot per sequence with chunks in the window, which the host does
+    // not know; the few it has per window run better with two slots.
+    const dim3 grid(slots * a.Hv * (DK / 32));
+    if (!a.cu_seqlens && a.B * a.Hv * (DK / 32) > 256)
+      hipLaunchKernelGGL(chunk_chain_kernel<1>, grid, dim3(192), ChainLds<1>::kBytes, s, r, c0,
+                         static_cast<const unsigned char*>(wsb), nwin, nw, carry);
+    else
+      hipLaunchKernelGGL(chunk_chain_kernel<2>, grid, dim3(192), ChainLds<2>::kBytes, s, r, c0,
+                         static_cast<const unsigned char*>(wsb), nwin, nw, carry);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -169,6 +169,28 @@ def test_prefill_small_workspace_windows(with_state_out):
             assert_state(to_host(so), srf)
 
 
+def test_prefill_one_slot_chain():
+    # 3 x 24 value heads x 4 strips = 288 chain workgroups, more than the 256 CUs: the chain runs
+    # with one input slot per workgroup and a second barrier per chunk.  Checked with the whole
+    # workspace (one window) and with one chunk of workspace and no state_out (the state crosses
+    # the four windows through the carry area).
+    torch = _torch()
+    B, T, Hk, Hv, D = 3, 200, 8, 24, 128
+    p = W.problem(4006, B, T, Hk, Hv, D, io="bf16", recipe="qwen", state="normal")
+    orf, srf = oracle_prefill(p, state_in=p["state_in"])
+    o, so = run_prefill(p, state_in=p["state_in"])
+    assert_out(o, orf, bf16=True)
+    assert_state(so, srf)
+    q, k, v = to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"])
+    la, be = to_dev(p["log_alpha"]), to_dev(p["beta"])
+    si = to_dev(p["state_in"].astype(np.float32))
+    per_chunk = B * (Hv * WS_VALUE_HEAD + Hk * WS_KEY_HEAD)
+    ws = torch.empty(per_chunk + B * Hv * D * D * 4, dtype=torch.uint8, device="cuda")
+    o2 = G.gdn_prefill(q, k, v, la, be, si, None, Hk=Hk, Hv=Hv, workspace=ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(o2).reshape(B, T, Hv, D), o)   # windows do not change the arithmetic
+
+
 def test_decode_steps_equal_prefill():
     torch = _torch()
     B, T, Hk, Hv, D = 2, 40, 1, 3, 128
