@@ -31,10 +31,12 @@
 //  * prep (one workgroup per chunk and key head, fully parallel over chunks):
 //    row norms, the Gram products K K^T and K Q^T (bf16 MFMA, kept in
 //    registers), and per value head the gate prefix sums, A, the inverse
-//    (16x16 forward substitution, a 16-block merge, and the 32x32 merge on
-//    MFMA with split-fp16 operands), T', and the products -W and U0 (fp16
-//    MFMA).  All of it is written to the workspace as MFMA-ready fp16
-//    fragments; U0 in the accumulator layout of the chain's U.
+//    (16x16 forward substitution, a 16-block merge on fp32 MFMA, and the
+//    32x32 merge on MFMA with split-fp16 operands), T', and the products -W
+//    and U0 (fp16 MFMA).  The value heads of a key head are inverted up to
+//    three at a time, each on its own wave and in place.  All of it is
+//    written to the workspace as MFMA-ready fp16 fragments; U0 in the
+//    accumulator layout of the chain's U.
 //  * chain (one workgroup per sequence, value head and 32-column strip of M,
 //    looping over the window's chunks; columns of M evolve independently).
 //    One wave carries the fp32 strip of M in registers and runs the serial
@@ -130,30 +132,156 @@ __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 *
 // =========================================================================
 // prep kernel: one workgroup (4 waves) per (chunk in window, key head, batch)
 // =========================================================================
+// LDS: the chunk's K and Q rows (bf16, padded rows) while the norms, the Q^
+// fragments and the Gram products are formed; then, over the same bytes, one
+// fp32 64 x 64 matrix per value head of the current group of up to three,
+// stored as its three lower 32 x 32 tiles (0,0), (1,0), (1,1): A, which the
+// wave owning the head turns into T = (I + A)^-1 in place.  After them each
+// wave's tile of a value head's V (64 rows x its 32 columns), then the row
+// scalings rk, rq and per value head the gate vectors.
 struct PrepLds {
-  static constexpr int kK = 0;                   // bf16 [64][KP]; later sA fp32 [64][FP]
-  static constexpr int kQ = CH * KP * 2;         // bf16 [64][KP]; later sT fp32 [64][FP]
-  static constexpr int kV = 2 * CH * KP * 2;     // bf16 [64][KP]: V rows of the current value head
-  static constexpr int kY = 3 * CH * KP * 2;     // fp32 2 x 16 x 20 (level 1 of the inverse)
-  static constexpr int kVec = kY + 2 * 16 * 20 * 4;  // rk, rq; per value head: g, beta, gamma rk, rk e^{g_63 - g}
+  static constexpr int kNH = 3;                   // value heads per group (waves 0-2 invert one each)
+  static constexpr int kTP = 36;                  // tile row pitch in floats (16-byte rows)
+  static constexpr int kTile = 32 * kTP;          // floats per tile
+  static constexpr int kMat = 3 * kTile * 4;      // bytes per head
+  static constexpr int kK = 0;                    // bf16 [64][KP]
+  static constexpr int kQ = CH * KP * 2;          // bf16 [64][KP]
+  static constexpr int kVP = 40;                  // V tile row pitch (bf16): 80-byte rows
+  static constexpr int kV = kNH * kMat > 2 * CH * KP * 2 ? kNH * kMat : 2 * CH * KP * 2;
+  static constexpr int kVec = kV + 4 * CH * kVP * 2;
   static constexpr int bytes(int G) { return kVec + (2 + 4 * G) * CH * 4; }
 };
-static_assert(CH * FP * 4 <= CH * KP * 2, "sA and sT reuse the K and Q rows");
 
+// Orders one wave's LDS accesses across its lanes: the wave's LDS instructions
+// execute in program order, so only the compiler has to keep them there.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ floatx4 mfma16f32(float a, float b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// T = (I + A)^-1 of one 64 x 64 strictly lower A (tiles of pitch kTP), in place,
+// by one wave.  Unit lower-triangular blocks: the four diagonal 16 x 16 blocks by
+// forward substitution, then T_IJ = -T_II A_IJ T_JJ for the 16-blocks (1,0) and
+// (3,2), then the same for the 32-blocks, T_10 = -T_11 A_10 T_00.
+__device__ __forceinline__ void invert_unit_lower(float* M, int lane) {
+  using L = PrepLds;
+  const int l32 = lane & 31, h = lane >> 5;
+  {
+    // lane = (block, column jc): x = column jc of the block's inverse,
+    // x_s = [s == jc] - sum_{r<s} A_sr x_r, taking the columns of A four at a time
+    const int blk = lane >> 4, jc = lane & 15;
+    float* D = M + (blk >> 1) * 2 * L::kTile + (blk & 1) * 16 * (L::kTP + 1);
+    float x[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) x[s] = s == jc ? 1.f : 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      floatx4 ap[16];
+#pragma unroll
+      for (int s = 4 * p + 1; s < 16; ++s) ap[s] = *reinterpret_cast<const floatx4*>(D + s * L::kTP + 4 * p);
+#pragma unroll
+      for (int s = 4 * p + 1; s < 16; ++s)
+#pragma unroll
+        for (int r = 4 * p; r < (s < 4 * p + 4 ? s : 4 * p + 4); ++r) x[s] = fmaf(-ap[s][r - 4 * p], x[r], x[s]);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int s = 0; s < 16; ++s) D[s * L::kTP + jc] = x[s];
+  }
+  wave_lds_sync();
+  {
+    // 16-blocks (1,0) in tile (0,0) and (3,2) in tile (1,1), each at rows 16.., columns
+    // 0.. of its tile, on fp32 MFMA (16x16x4: A row = B column = lane & 15, k = lane >> 4;
+    // the result holds column lane & 15, rows 4 (lane >> 4) + v).  Y = A_IJ T_JJ; in the
+    // second product the k index runs over 4 (lane >> 4) + s so that Y's values are
+    // its B operand as they stand.
+    const int q = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float* Tt = M + 2 * m * L::kTile;
+      floatx4 Y = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Y = mfma16f32(Tt[(16 + n) * L::kTP + 4 * s + q], Tt[(4 * s + q) * L::kTP + n], Y);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Z = mfma16f32(Tt[(16 + n) * L::kTP + 16 + 4 * q + s], Y[s], Z);
+      wave_lds_sync();
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Tt[(16 + 4 * q + v) * L::kTP + n] = -Z[v];
+    }
+  }
+  wave_lds_sync();
+  {
+    // 32-blocks: tile (1,0) <- -T_11 (A_10 T_00) on MFMA, each fp32 operand split into
+    // fp16 hi + lo and three products kept (hi hi, hi lo, lo hi): about 22 bits
+    const float* T0 = M;
+    float* T1 = M + L::kTile;
+    const float* T2 = M + 2 * L::kTile;
+    floatx16 Y = zero16(), Y2 = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const float* ar = T1 + l32 * L::kTP + 16 * ks + 4 * h;
+      const floatx4 a0 = *reinterpret_cast<const floatx4*>(ar), a1 = *reinterpret_cast<const floatx4*>(ar + 8);
+      halfx8 ahi, alo, bhi, blo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float av = e < 4 ? a0[e] : a1[e - 4];
+        const float bv = T0[(16 * ks + kperm(h, e)) * L::kTP + l32];
+        ahi[e] = static_cast<_Float16>(av);
+        alo[e] = static_cast<_Float16>(av - static_cast<float>(ahi[e]));
+        bhi[e] = static_cast<_Float16>(bv);
+        blo[e] = static_cast<_Float16>(bv - static_cast<float>(bhi[e]));
+      }
+      Y = mfma32h(ahi, bhi, Y);
+      Y2 = mfma32h(ahi, blo, Y2);
+      Y2 = mfma32h(alo, bhi, Y2);
+    }
+    Y += Y2;
+    floatx16 Z = zero16(), Z2 = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const float* sr = T2 + l32 * L::kTP + 16 * ks + 4 * h;
+      const floatx4 a0 = *reinterpret_cast<const floatx4*>(sr), a1 = *reinterpret_cast<const floatx4*>(sr + 8);
+      halfx8 ahi, alo, bhi, blo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float av = e < 4 ? a0[e] : a1[e - 4];
+        const float bv = Y[8 * ks + e];   // accumulator values [8ks, 8ks+8) are the B fragment
+        ahi[e] = static_cast<_Float16>(av);
+        alo[e] = static_cast<_Float16>(av - static_cast<float>(ahi[e]));
+        bhi[e] = static_cast<_Float16>(bv);
+        blo[e] = static_cast<_Float16>(bv - static_cast<float>(bhi[e]));
+      }
+      Z = mfma32h(ahi, bhi, Z);
+      Z2 = mfma32h(ahi, blo, Z2);
+      Z2 = mfma32h(alo, bhi, Z2);
+    }
+    Z += Z2;
+    wave_lds_sync();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) T1[acc_row(v, h) * L::kTP + l32] = -Z[v];
+  }
+}
+
+// kOneGroup: at most kNH value heads per key head, so that the Gram tiles die
+// after the first group's A and P.
+template <bool kOneGroup>
 __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, unsigned char* ws, int nwin) {
   // workspace: region H = [B][Hv][nwin] x WH_BYTES, then region K = [B][Hk][nwin] x WK_BYTES
   using L = PrepLds;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sK = reinterpret_cast<uint16_t*>(smem + L::kK);
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + L::kQ);
-  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + L::kV);
-  float* sA = reinterpret_cast<float*>(smem + L::kK);
-  float* sT = reinterpret_cast<float*>(smem + L::kQ);
-  float* sY = reinterpret_cast<float*>(smem + L::kY);
   float* vRk = reinterpret_cast<float*>(smem + L::kVec);
   float* vRq = vRk + CH;
   // gate vectors of value head j of this key head
   auto vgate = [&](int j) { return vRk + (2 + 4 * j) * CH; };
+  // matrix of head jj of the current group
+  auto mat = [&](int jj) { return reinterpret_cast<float*>(smem + jj * L::kMat); };
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, h = lane >> 5;
@@ -181,20 +309,23 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   const uint16_t* gk = static_cast<const uint16_t*>(a.k);
   const uint16_t* gv = static_cast<const uint16_t*>(a.v);
 
-  // V rows of a value head are loaded one head ahead, into registers (rows past
-  // the sequence end read the last valid row and are replaced by zeros); the first
-  // head's loads are issued before the K and Q rows are waited for.  Wave w takes
-  // the gates of value heads w, w+4, ...: the first are loaded here as well.
+  // The V values this wave needs for a value head's U0 product are its value
+  // tile, columns 32 wv.. of the 64 rows: loaded into registers one head ahead,
+  // 16 bytes a lane, rows 16 m + (lane >> 2) (rows past the sequence end read the
+  // last valid row and are replaced by zeros), and staged through the wave's own
+  // LDS tile, from which the k-ordered B operand is read.  The first head's loads
+  // are issued before the K and Q rows are waited for, and wave w loads the gates
+  // of value head w as well.
   u32x4 vr[4];
-  auto load_head = [&](int hv) {
+  auto load_v = [&](int hv) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int vi = tid + 256 * m, r = vi >> 4, c8 = (vi & 15) * 8;
-      const int rr = r < nval ? r : nval - 1;
-      vr[m] = *reinterpret_cast<const u32x4*>(gv + (tokbase + rr) * a.sv + hv * DK + c8);
+      const int r = 16 * m + (lane >> 2), rr = r < nval ? r : nval - 1;
+      vr[m] = *reinterpret_cast<const u32x4*>(gv + (tokbase + rr) * a.sv + hv * DK + 32 * wv + 8 * (lane & 3));
     }
   };
-  load_head(hk * a.G);
+  uint16_t* sVw = reinterpret_cast<uint16_t*>(smem + L::kV) + wv * CH * L::kVP;
+  load_v(hk * a.G);
   const int tr = lane < nval ? lane : nval - 1;
   float la = 0.f, be = 0.f;
   if (wv < a.G) {
@@ -281,16 +412,17 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   }
   // ---- this wave's columns of K^T (key rows 32 wv + (lane&31)) at the chunk rows
   //      of each 16-row k step, in fragment order; scaled per value head below
-  float kt[4][8];
+  u16x8 kt[4];
   {
     const int d = 32 * wv + l32;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kt[ks][e] = bf16_bits_to_f32(sK[(16 * ks + kperm(h, e)) * KP + d]);
+      for (int e = 0; e < 8; ++e) kt[ks][e] = sK[(16 * ks + kperm(h, e)) * KP + d];
   }
   // ---- Gram tiles (32x32), kept in registers of waves 0-2 -------------------
-  //  K K^T tile (rtK, ctK) in {(0,0), (1,0), (1,1)}: element (row r, column i) = k_r . k_i
+  //  K K^T tile (rtK, ctK) in {(0,0), (1,0), (1,1)} -- tile wv of the lower
+  //  triangle: element (row r, column i) = k_r . k_i
   //  K Q^T tile (itP, rtP) in {(0,0), (0,1), (1,1)}: element (row i, column r) = k_i . q_r
   const int rtK = wv == 0 ? 0 : 1, ctK = wv == 2 ? 1 : 0;
   const int itP = wv == 2 ? 1 : 0, rtP = wv == 0 ? 0 : 1;
@@ -304,255 +436,164 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
                    lds_frag32(sQ + (32 * rtP + l32) * KP + 16 * ks, h), gKQ);
     }
   }
-  __syncthreads();  // sK / sQ are dead from here on: their bytes become sA / sT
+  __syncthreads();  // the K and Q rows are dead from here on: their bytes hold the matrices
 
-
-  for (int j = 0; j < a.G; ++j) {
-    const int hv = hk * a.G + j;
-    unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hv) * nwin + cl) * WH_BYTES;
-    const float* vG = vgate(j);
-    const float* vBe = vG + CH;
-    const float* vKs = vG + 2 * CH;
-    const float* vKd = vG + 3 * CH;
-    // V rows of this head to LDS (read after two barriers), the next head's loads
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int vi = tid + 256 * m;
-      *reinterpret_cast<u32x4*>(sV + (vi >> 4) * KP + (vi & 15) * 8) =
-          (vi >> 4) < nval ? vr[m] : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (j + 1 < a.G) load_head(hv + 1);
-    // ---- A (fp32, strictly lower) and the P fragments from the Gram tiles ----
+  // Value heads in groups of up to kNH: A and P of the group from the Gram tiles,
+  // then each head's inverse on its own wave, then the products of each head.
+  for (int j0 = 0; j0 < (kOneGroup ? 1 : a.G); j0 += L::kNH) {
+    const int ng = kOneGroup ? a.G : min(L::kNH, a.G - j0);
+    // ---- A (fp32, strictly lower; tile wv) and the P fragments --------------
     if (wv < 3) {
-      {
-        const int i = 32 * ctK + l32;
-        const float gi = vG[i], rki = vRk[i];
+      for (int jj = 0; jj < ng; ++jj) {
+        const int j = j0 + jj;
+        const float* vG = vgate(j);
+        const float* vBe = vG + CH;
+        {
+          float* At = mat(jj) + wv * L::kTile;
+          const int i = 32 * ctK + l32;
+          const float gi = vG[i], rki = vRk[i];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r0 = 32 * rtK + 8 * q + 4 * h;
-          const floatx4 g4 = *reinterpret_cast<const floatx4*>(vG + r0);
-          const floatx4 b4 = *reinterpret_cast<const floatx4*>(vBe + r0);
-          const floatx4 k4 = *reinterpret_cast<const floatx4*>(vRk + r0);
+          for (int q = 0; q < 4; ++q) {
+            const int r0 = 32 * rtK + 8 * q + 4 * h;
+            const floatx4 g4 = *reinterpret_cast<const floatx4*>(vG + r0);
+            const floatx4 b4 = *reinterpret_cast<const floatx4*>(vBe + r0);
+            const floatx4 k4 = *reinterpret_cast<const floatx4*>(vRk + r0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = r0 + e;
-            const float x = b4[e] * k4[e] * rki * __expf(fminf(g4[e] - gi, 0.f)) * gKK[4 * q + e];
-            sA[r * FP + i] = i < r ? x : 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int r = r0 + e;
+              const float x = b4[e] * k4[e] * rki * __expf(fminf(g4[e] - gi, 0.f)) * gKK[4 * q + e];
+              At[(8 * q + 4 * h + e) * L::kTP + l32] = i < r ? x : 0.f;
+            }
+          }
+        }
+        {
+          unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hk * a.G + j) * nwin + cl) * WH_BYTES;
+          const int r = 32 * rtP + l32;
+          const float gr = vG[r], rq = vRq[r];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int f = rtP == 0 ? s2 : 2 + 2 * itP + s2;
+            const int ia = 32 * itP + 16 * s2 + 4 * h, ib = ia + 8;
+            const floatx4 ga = *reinterpret_cast<const floatx4*>(vG + ia), gb = *reinterpret_cast<const floatx4*>(vG + ib);
+            const floatx4 ka = *reinterpret_cast<const floatx4*>(vRk + ia), kb = *reinterpret_cast<const floatx4*>(vRk + ib);
+            u16x8 pf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int i = e < 4 ? ia + e : ib + e - 4;
+              const float gi = e < 4 ? ga[e] : gb[e - 4], rki = e < 4 ? ka[e] : kb[e - 4];
+              const float x = __expf(fminf(gr - gi, 0.f)) * rq * rki * gKQ[8 * s2 + e];
+              pf[e] = f32_to_f16_bits(i <= r ? x : 0.f);
+            }
+            *reinterpret_cast<u16x8*>(wsc + WH_P + f * 1024 + lane * 16) = pf;
           }
         }
       }
-      {
-        const int r = 32 * rtP + l32;
-        const float gr = vG[r], rq = vRq[r];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int f = rtP == 0 ? s2 : 2 + 2 * itP + s2;
-          const int ia = 32 * itP + 16 * s2 + 4 * h, ib = ia + 8;
-          const floatx4 ga = *reinterpret_cast<const floatx4*>(vG + ia), gb = *reinterpret_cast<const floatx4*>(vG + ib);
-          const floatx4 ka = *reinterpret_cast<const floatx4*>(vRk + ia), kb = *reinterpret_cast<const floatx4*>(vRk + ib);
-          u16x8 pf;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = e < 4 ? ia + e : ib + e - 4;
-            const float gi = e < 4 ? ga[e] : gb[e - 4], rki = e < 4 ? ka[e] : kb[e - 4];
-            const float x = __expf(fminf(gr - gi, 0.f)) * rq * rki * gKQ[8 * s2 + e];
-            pf[e] = f32_to_f16_bits(i <= r ? x : 0.f);
-          }
-          *reinterpret_cast<u16x8*>(wsc + WH_P + f * 1024 + lane * 16) = pf;
-        }
-      }
-    } else {
-      // T blocks (0,1) and (2,3) (above the diagonal, inside S0 and S1) are read as zeros
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int e = lane + 64 * m, blk = e >> 8;
-        sT[(32 * blk + ((e >> 4) & 15)) * FP + 32 * blk + 16 + (e & 15)] = 0.f;
-      }
     }
     __syncthreads();
-    // ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution ------
-    if (wv == 0) {
-      const int blk = lane >> 4, jc = lane & 15;
-      const float* Ab = sA + (16 * blk) * FP + 16 * blk;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < r; ++i) s = fmaf(Ab[r * FP + i], x[i], s);
-        x[r] = (r < jc) ? 0.f : ((r == jc) ? 1.f : -s);
-      }
-      float* Tb = sT + (16 * blk) * FP + 16 * blk;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Tb[r * FP + jc] = x[r];
-    }
+    // ---- T = (I + A)^-1, head j0 + wv on wave wv ----------------------------
+    if (wv < ng) invert_unit_lower(mat(wv), lane);
     __syncthreads();
-    // level 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (128 threads each)
-    {
-      const int half = tid >> 7, idx = (tid & 127) * 2;
-      const int yr = idx >> 4, yc = idx & 15;
-      const int I = 2 * half + 1, J = 2 * half;
-      float arow[16];
+    // ---- per head, all waves: T' = T diag(beta) fragments (all six), the K^T
+    //      columns of key tile wv scaled two ways, and the V columns of value tile wv
+    for (int jj = 0; jj < ng; ++jj) {
+      const int j = j0 + jj, hv = hk * a.G + j;
+      unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hv) * nwin + cl) * WH_BYTES;
+      const float* vBe = vgate(j) + CH;
+      const float* vKs = vgate(j) + 2 * CH;
+      const float* vKd = vgate(j) + 3 * CH;
+      // this head's V tile through the wave's LDS tile, then the next head's loads
+      wave_lds_sync();   // the previous head's reads of the tile are done
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const floatx4 av = *reinterpret_cast<const floatx4*>(sA + (16 * I + yr) * FP + 16 * J + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) arow[4 * q + e] = av[e];
+      for (int m = 0; m < 4; ++m) {
+        const int r = 16 * m + (lane >> 2);
+        *reinterpret_cast<u32x4*>(sVw + r * L::kVP + 8 * (lane & 3)) = r < nval ? vr[m] : u32x4{0u, 0u, 0u, 0u};
       }
-      floatx2 y = {0.f, 0.f};
+      if (j + 1 < a.G) load_v(hv + 1);
+      wave_lds_sync();
+      halfx8 vf[4];
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const floatx2 tv = *reinterpret_cast<const floatx2*>(sT + (16 * J + m) * FP + 16 * J + yc);
-        y[0] = fmaf(arow[m], tv[0], y[0]);
-        y[1] = fmaf(arow[m], tv[1], y[1]);
-      }
-      *reinterpret_cast<floatx2*>(sY + half * 16 * 20 + yr * 20 + yc) = y;
-      __syncthreads();
-      float trow[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const floatx4 tv = *reinterpret_cast<const floatx4*>(sT + (16 * I + yr) * FP + 16 * I + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) trow[4 * q + e] = tv[e];
-      }
-      floatx2 t = {0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const floatx2 yv = *reinterpret_cast<const floatx2*>(sY + half * 16 * 20 + m * 20 + yc);
-        t[0] = fmaf(trow[m], yv[0], t[0]);
-        t[1] = fmaf(trow[m], yv[1], t[1]);
-      }
-      *reinterpret_cast<floatx2*>(sT + (16 * I + yr) * FP + 16 * J + yc) = floatx2{-t[0], -t[1]};
-    }
-    __syncthreads();
-    // level 2 on wave 0:
-    if (wv == 0) {
-      // T[32:64, 0:32] = -S1 (A[32:64, 0:32] S0) on MFMA, each fp32 operand split into
-      // fp16 hi + lo and three products kept (hi hi, hi lo, lo hi): about 22 bits
-      {
-        floatx16 Y = zero16(), Y2 = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const float* ar = sA + (32 + l32) * FP + 16 * ks + 4 * h;
-          const floatx4 a0 = *reinterpret_cast<const floatx4*>(ar), a1 = *reinterpret_cast<const floatx4*>(ar + 8);
-          halfx8 ahi, alo, bhi, blo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float av = e < 4 ? a0[e] : a1[e - 4];
-            const float bv = sT[(16 * ks + kperm(h, e)) * FP + l32];
-            ahi[e] = static_cast<_Float16>(av);
-            alo[e] = static_cast<_Float16>(av - static_cast<float>(ahi[e]));
-            bhi[e] = static_cast<_Float16>(bv);
-            blo[e] = static_cast<_Float16>(bv - static_cast<float>(bhi[e]));
-          }
-          Y = mfma32h(ahi, bhi, Y);
-          Y2 = mfma32h(ahi, blo, Y2);
-          Y2 = mfma32h(alo, bhi, Y2);
-        }
-        Y += Y2;
-        floatx16 Z = zero16(), Z2 = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const float* sr = sT + (32 + l32) * FP + 32 + 16 * ks + 4 * h;
-          const floatx4 a0 = *reinterpret_cast<const floatx4*>(sr), a1 = *reinterpret_cast<const floatx4*>(sr + 8);
-          halfx8 ahi, alo, bhi, blo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float av = e < 4 ? a0[e] : a1[e - 4];
-            const float bv = Y[8 * ks + e];   // accumulator values [8ks, 8ks+8) are the B fragment
-            ahi[e] = static_cast<_Float16>(av);
-            alo[e] = static_cast<_Float16>(av - static_cast<float>(ahi[e]));
-            bhi[e] = static_cast<_Float16>(bv);
-            blo[e] = static_cast<_Float16>(bv - static_cast<float>(bhi[e]));
-          }
-          Z = mfma32h(ahi, bhi, Z);
-          Z2 = mfma32h(ahi, blo, Z2);
-          Z2 = mfma32h(alo, bhi, Z2);
-        }
-        Z += Z2;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sT[(32 + acc_row(v, h)) * FP + l32] = -Z[v];
-      }
-    }
-    __syncthreads();
-    // ---- per wave: T' = T diag(beta) fragments (all six), the K^T columns of key
-    //      tile wv scaled two ways, and the V columns of value tile wv -------------
-    halfx8 tf[FT];
-#pragma unroll
-    for (int f = 0; f < FT; ++f) {
-      const int r = 32 * ft_rt(f) + l32;
-      const int ca = 16 * ft_ks(f) + 4 * h, cb = ca + 8;
-      const floatx4 ta = *reinterpret_cast<const floatx4*>(sT + r * FP + ca);
-      const floatx4 tb = *reinterpret_cast<const floatx4*>(sT + r * FP + cb);
-      const floatx4 ba = *reinterpret_cast<const floatx4*>(vBe + ca), bb = *reinterpret_cast<const floatx4*>(vBe + cb);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = e < 4 ? ca + e : cb + e - 4;
-        const float x = e < 4 ? ta[e] * ba[e] : tb[e - 4] * bb[e - 4];
-        tf[f][e] = static_cast<_Float16>(i <= r ? x : 0.f);
-      }
-    }
-    {
-      // W^T tiles (key tile wv, row tile 0 / 1) = Ks^T T'^T with Ks = diag(gamma rk) K;
-      // Kd = K^T diag(rk e^{g_63 - g}) fragments go out as they are
-      floatx16 w0 = zero16(), w1 = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const floatx4 sa = *reinterpret_cast<const floatx4*>(vKs + 16 * ks + 4 * h);
-        const floatx4 sb = *reinterpret_cast<const floatx4*>(vKs + 16 * ks + 8 + 4 * h);
-        const floatx4 da = *reinterpret_cast<const floatx4*>(vKd + 16 * ks + 4 * h);
-        const floatx4 db = *reinterpret_cast<const floatx4*>(vKd + 16 * ks + 8 + 4 * h);
-        halfx8 kf, df;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kf[e] = static_cast<_Float16>(kt[ks][e] * (e < 4 ? sa[e] : sb[e - 4]));
-          df[e] = static_cast<_Float16>(kt[ks][e] * (e < 4 ? da[e] : db[e - 4]));
-        }
-        *reinterpret_cast<halfx8*>(wsc + WH_KD + (wv * 4 + ks) * 1024 + lane * 16) = df;
-        if (ks < 2) w0 = mfma32h(kf, tf[ks], w0);
-        w1 = mfma32h(kf, tf[2 + ks], w1);
-      }
-      // accumulator values [8s, 8s+8) of W^T tile (wv, rt) are the -W fragment (rt, 2 wv + s)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        halfx8 n0, n1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          n0[e] = static_cast<_Float16>(-w0[8 * s2 + e]);
-          n1[e] = static_cast<_Float16>(-w1[8 * s2 + e]);
-        }
-        *reinterpret_cast<halfx8*>(wsc + WH_W + (2 * wv + s2) * 1024 + lane * 16) = n0;
-        *reinterpret_cast<halfx8*>(wsc + WH_W + (8 + 2 * wv + s2) * 1024 + lane * 16) = n1;
-      }
-    }
-    {
-      // U0 tiles (row tile 0 / 1, value tile wv) = T' V, stored in accumulator layout
-      floatx16 u0 = zero16(), u1 = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        halfx8 vf;
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          vf[e] = static_cast<_Float16>(bf16_bits_to_f32(sV[(16 * ks + kperm(h, e)) * KP + 32 * wv + l32]));
-        if (ks < 2) u0 = mfma32h(tf[ks], vf, u0);
-        u1 = mfma32h(tf[2 + ks], vf, u1);
-      }
-      unsigned char* du = wsc + WH_U0 + (wv * 2) * 2048 + lane * 32;
+          vf[ks][e] = static_cast<_Float16>(bf16_bits_to_f32(sVw[(16 * ks + kperm(h, e)) * L::kVP + l32]));
+      const float* M = mat(jj);
+      halfx8 tf[FT];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        halfx8 x0, x1;
+      for (int f = 0; f < FT; ++f) {
+        // tile (0,0) for the row tile 0 fragments, (1,0) and (1,1) for row tile 1
+        const int r = 32 * ft_rt(f) + l32;
+        const float* tr4 = M + (f < 2 ? 0 : (f < 4 ? 1 : 2)) * L::kTile + l32 * L::kTP + 16 * (ft_ks(f) & 1) + 4 * h;
+        const int ca = 16 * ft_ks(f) + 4 * h, cb = ca + 8;
+        const floatx4 ta = *reinterpret_cast<const floatx4*>(tr4);
+        const floatx4 tb = *reinterpret_cast<const floatx4*>(tr4 + 8);
+        const floatx4 ba = *reinterpret_cast<const floatx4*>(vBe + ca), bb = *reinterpret_cast<const floatx4*>(vBe + cb);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          x0[e] = static_cast<_Float16>(u0[8 * s2 + e]);
-          x1[e] = static_cast<_Float16>(u1[8 * s2 + e]);
+          const int i = e < 4 ? ca + e : cb + e - 4;
+          const float x = e < 4 ? ta[e] * ba[e] : tb[e - 4] * bb[e - 4];
+          tf[f][e] = static_cast<_Float16>(i <= r ? x : 0.f);
         }
-        *reinterpret_cast<halfx8*>(du + 16 * s2) = x0;
-        *reinterpret_cast<halfx8*>(du + 2048 + 16 * s2) = x1;
+      }
+      {
+        // W^T tiles (key tile wv, row tile 0 / 1) = Ks^T T'^T with Ks = diag(gamma rk) K;
+        // Kd = K^T diag(rk e^{g_63 - g}) fragments go out as they are
+        floatx16 w0 = zero16(), w1 = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const floatx4 sa = *reinterpret_cast<const floatx4*>(vKs + 16 * ks + 4 * h);
+          const floatx4 sb = *reinterpret_cast<const floatx4*>(vKs + 16 * ks + 8 + 4 * h);
+          const floatx4 da = *reinterpret_cast<const floatx4*>(vKd + 16 * ks + 4 * h);
+          const floatx4 db = *reinterpret_cast<const floatx4*>(vKd + 16 * ks + 8 + 4 * h);
+          halfx8 kf, df;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float kv = bf16_bits_to_f32(kt[ks][e]);
+            kf[e] = static_cast<_Float16>(kv * (e < 4 ? sa[e] : sb[e - 4]));
+            df[e] = static_cast<_Float16>(kv * (e < 4 ? da[e] : db[e - 4]));
+          }
+          *reinterpret_cast<halfx8*>(wsc + WH_KD + (wv * 4 + ks) * 1024 + lane * 16) = df;
+          if (ks < 2) w0 = mfma32h(kf, tf[ks], w0);
+          w1 = mfma32h(kf, tf[2 + ks], w1);
+        }
+        // accumulator values [8s, 8s+8) of W^T tile (wv, rt) are the -W fragment (rt, 2 wv + s)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          halfx8 n0, n1;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            n0[e] = static_cast<_Float16>(-w0[8 * s2 + e]);
+            n1[e] = static_cast<_Float16>(-w1[8 * s2 + e]);
+          }
+          *reinterpret_cast<halfx8*>(wsc + WH_W + (2 * wv + s2) * 1024 + lane * 16) = n0;
+          *reinterpret_cast<halfx8*>(wsc + WH_W + (8 + 2 * wv + s2) * 1024 + lane * 16) = n1;
+        }
+      }
+      {
+        // U0 tiles (row tile 0 / 1, value tile wv) = T' V, stored in accumulator layout
+        floatx16 u0 = zero16(), u1 = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          if (ks < 2) u0 = mfma32h(tf[ks], vf[ks], u0);
+          u1 = mfma32h(tf[2 + ks], vf[ks], u1);
+        }
+        unsigned char* du = wsc + WH_U0 + (wv * 2) * 2048 + lane * 32;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          halfx8 x0, x1;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x0[e] = static_cast<_Float16>(u0[8 * s2 + e]);
+            x1[e] = static_cast<_Float16>(u1[8 * s2 + e]);
+          }
+          *reinterpret_cast<halfx8*>(du + 16 * s2) = x0;
+          *reinterpret_cast<halfx8*>(du + 2048 + 16 * s2) = x1;
+        }
       }
     }
-    __syncthreads();  // sA, sT, sV are rewritten for the next value head
+    if (!kOneGroup && j0 + L::kNH < a.G) __syncthreads();  // the next group rewrites the matrices
   }
 }
+
 
 // =========================================================================
 // chain kernel: one workgroup (3 waves) per (32-column strip, value head, batch)
@@ -1024,7 +1065,7 @@ size_t chunk_ws_carry_bytes(const RecArgs& a) {
 int chunk_count(const RecArgs& a) { return (a.T + CH - 1) / CH + (a.cu_seqlens ? a.nseq : 0); }
 
 // Prep workgroups resident at once on the 256 CUs: their LDS lets two share a CU
-// up to 24 value heads per key head, one beyond.
+// up to 19 value heads per key head, one beyond.
 int prep_slots(int G) { return 256 * max(1, min(2, (160 * 1024) / PrepLds::bytes(G))); }
 
 // Chunks per window.  The chain kernel reads a window's operands back from the
@@ -1055,8 +1096,11 @@ int chunk_window_chunks(const RecArgs& a) {
 hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
   static PerDeviceOnce attrs;
   hipError_t ea = attrs.run([] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_prep_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_prep_kernel<true>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_prep_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<2>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<2>::kBytes);
@@ -1105,7 +1149,12 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
   float* carry = need_carry ? reinterpret_cast<float*>(wsb + static_cast<size_t>(nwin) * per_chunk) : a.state_out;
   for (int c0 = 0; c0 < nchunks; c0 += nwin) {
     const int nw = min(nwin, nchunks - c0);
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3(nw, a.Hk, a.B), dim3(256), PrepLds::bytes(a.G), s, r, c0, wsb, nwin);
+    if (a.G <= PrepLds::kNH)
+      hipLaunchKernelGGL(chunk_prep_kernel<true>, dim3(nw, a.Hk, a.B), dim3(256), PrepLds::bytes(a.G), s, r, c0, wsb,
+                         nwin);
+    else
+      hipLaunchKernelGGL(chunk_prep_kernel<false>, dim3(nw, a.Hk, a.B), dim3(256), PrepLds::bytes(a.G), s, r, c0, wsb,
+                         nwin);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // chain workgroups per (sequence, value head, strip); for a packed batch per
