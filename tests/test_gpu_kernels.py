@@ -51,6 +51,11 @@ CHUNK_CASES = [
     (2, 130, 2, 6, "tiny", True, False, 0.5),
     (1, 200, 1, 1, "qwen", False, True, 1.0),
     (1, 257, 2, 6, "qwen", True, False, 1.0),
+    # value heads per key head across the prep's groups of three: 4 (3 + 1), 5 (3 + 2), and 64,
+    # the most the chunked path takes (21 groups of 3 + 1)
+    (1, 100, 1, 4, "qwen", True, False, 1.0),
+    (2, 90, 1, 5, "qwen", False, False, 1.0),
+    (1, 70, 1, 64, "tiny", True, True, 1.0),
 ]
 
 
