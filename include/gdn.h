@@ -131,7 +131,7 @@ gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const
  * not depend on the state (55 KiB: the -W, K^T, U0 and P operands and the
  * row scalings, plus 16 KiB per key head for the scaled Q).  A window is a
  * whole number of rounds of resident prep workgroups (512 (chunk, key head)
- * pairs at up to 24 value heads per key head): as many rounds as keep it
+ * pairs at up to 19 value heads per key head, 256 beyond): as many rounds as keep it
  * within about 96 MiB, so that the chain kernel finds its operands in the
  * GPU's last-level cache, or, when one round alone is larger, as many as fit
  * in 2 GiB; windows are then balanced.  The state is carried between windows
