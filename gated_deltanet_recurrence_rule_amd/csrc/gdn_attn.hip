@@ -174,24 +174,23 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f7
 
 __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // Workgroup -> (sequence, query head, query block).  The 8 XCDs take linear
-  // indices round-robin; indices are re-ordered so that each XCD runs a
-  // contiguous range of (key/value group, query block, head) work, i.e. the
-  // query heads of one group, whose keys and values then stay in that XCD's
-  // L2.  Inside a group the query blocks go long, short, long, short ...
-  // (31, 0, 30, 1, ... for 32 blocks), so that any contiguous range of them,
-  // and thus each XCD's share, holds about the same causal work.
+  // Workgroup -> (sequence, query head, query block).  Workgroups start in
+  // index order, so the longest work goes first: index L is rank L / NG of
+  // key/value group L % NG, and a rank is a query block counted from the last
+  // (the most keys) with the group's query heads inside it.  The 8 XCDs take
+  // indices round-robin; with NG dividing 8, or a multiple of it, each XCD then
+  // sees one group only (its keys and values stay in that XCD's L2), and the
+  // XCDs sharing a group take alternate ranks, i.e. equal causal work.  Inside
+  // an XCD, a CU that finishes takes the longest item left, which balances
+  // the CUs far better than any fixed long/short interleave.
   const int nqb = (a.T + QB - 1) / QB;
   const int G = a.Hq / a.Hkv;
-  const int N = static_cast<int>(gridDim.x), L = static_cast<int>(blockIdx.x);
-  const int N8 = N / 8 * 8;
-  const int idx = L < N8 ? (L % 8) * (N8 / 8) + L / 8 : L;
-  const int per_group = nqb * G;
-  const int grp = idx / per_group, rr = idx - grp * per_group;
-  const int pos = rr / G;
-  const int qb = (pos & 1) ? pos >> 1 : nqb - 1 - (pos >> 1);
+  const int NG = a.B * a.Hkv;
+  const int L = static_cast<int>(blockIdx.x);
+  const int grp = L % NG, rank = L / NG;
+  const int qb = nqb - 1 - rank / G;
   const int b = grp / a.Hkv, j = grp - b * a.Hkv;
-  const int h = j * G + rr % G;
+  const int h = j * G + rank % G;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int q0 = qb * QB + 32 * w;  // the wave's first query
   const int qi = q0 + l32;          // the lane's query
