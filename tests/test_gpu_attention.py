@@ -51,7 +51,7 @@ def cache_views(kc, vc, n):
 
 
 @pytest.mark.parametrize("B,T,Hq,Hkv", [(1, 1, 6, 1), (2, 64, 6, 1), (1, 129, 12, 2), (2, 200, 12, 2),
-                                        (1, 300, 24, 4)])
+                                        (1, 300, 24, 4), (2, 300, 9, 3)])
 def test_prefill_parity_and_caches(B, T, Hq, Hkv):
     p = W.attn_problem(700 + T, B, T, Hq, Hkv)
     S_max = ((T + 63) // 64) * 64 + 64
