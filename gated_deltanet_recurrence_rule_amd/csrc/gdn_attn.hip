@@ -151,23 +151,28 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(AttnArgs a, RopeTable rt
 // 16-byte bank groups of a 256-byte bank line (5 % faster than swizzling with
 // r & 7).  A block is 32 + 32 pieces of 1 KiB copied straight from the caches
 // into LDS (lane i of a piece fills bytes 16i..16i+15 of it), 16 per wave.
-__device__ __forceinline__ void copy_block(const AttnArgs& a, int b, int j, int kb, int w, int lane,
-                                           unsigned char* kbuf, unsigned char* vbuf) {
+__device__ __forceinline__ void copy_pieces(const AttnArgs& a, int b, int j, int kb, int w, int lane,
+                                            unsigned char* kbuf, unsigned char* vbuf, int i0, int n) {
   const unsigned char* ks = reinterpret_cast<const unsigned char*>(a.kc + kc_index(a, b, j, kb * KB));
   const unsigned char* vs = reinterpret_cast<const unsigned char*>(a.vc + vc_block(a, b, j, kb * KB));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int pc = 8 * w + i;
-    const int r = 2 * pc + (lane >> 5), c = (lane & 31) ^ (r & 15);
-    const int key = 32 * (r >> 5) + key_of_row(r & 31);
-    __builtin_amdgcn_global_load_lds(ks + key * (AD * 2) + 16 * c, kbuf + 1024 * pc, 16, 0, 0);
+  for (int i = i0; i < i0 + n; ++i) {
+    if (i < 8) {
+      const int pc = 8 * w + i;
+      const int r = 2 * pc + (lane >> 5), c = (lane & 31) ^ (r & 15);
+      const int key = 32 * (r >> 5) + key_of_row(r & 31);
+      __builtin_amdgcn_global_load_lds(ks + key * (AD * 2) + 16 * c, kbuf + 1024 * pc, 16, 0, 0);
+    } else {
+      const int pc = 8 * w + i - 8;
+      const int r = 8 * pc + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+      __builtin_amdgcn_global_load_lds(vs + r * (KB * 2) + 16 * c, vbuf + 1024 * pc, 16, 0, 0);
+    }
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int pc = 8 * w + i;
-    const int r = 8 * pc + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
-    __builtin_amdgcn_global_load_lds(vs + r * (KB * 2) + 16 * c, vbuf + 1024 * pc, 16, 0, 0);
-  }
+}
+
+__device__ __forceinline__ void copy_block(const AttnArgs& a, int b, int j, int kb, int w, int lane,
+                                           unsigned char* kbuf, unsigned char* vbuf) {
+  copy_pieces(a, b, j, kb, w, lane, kbuf, vbuf, 0, 16);
 }
 
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
@@ -235,7 +240,14 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
     const int cur = kb & 1;
     const unsigned char* sk = smem + cur * KBUF;
     const unsigned char* sv = smem + 2 * KBUF + cur * VBUF;
-    if (kb + 1 < nkb) copy_block(a, b, j, kb + 1, w, lane, smem + (cur ^ 1) * KBUF, smem + 2 * KBUF + (cur ^ 1) * VBUF);
+    // the next block's copy goes out two pieces per group of products, so that
+    // the memory path works under the matrix cores instead of stalling the
+    // wave; after the last block the current one is copied again (harmless,
+    // nothing reads that buffer any more)
+    const int kn = min(kb + 1, nkb - 1);
+    auto cp = [&](int i0) {
+      copy_pieces(a, b, j, kn, w, lane, smem + (cur ^ 1) * KBUF, smem + 2 * KBUF + (cur ^ 1) * VBUF, i0, 2);
+    };
 
     // S^T tiles u = keys 32u.. of the block; key fragments are read from LDS eight
     // at a time, one group ahead of the products
@@ -258,6 +270,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         if (g < 3) kload(g + 1, kf[(g + 1) & 1]);
+        cp(2 * g);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -311,6 +324,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         if (ks < 3) vload(ks + 1, vf[(ks + 1) & 1]);
+        cp(8 + 2 * ks);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 8; ++t) O[t] = mfma32(__builtin_bit_cast(bf16x8, vf[ks & 1][t]), P[ks], O[t]);
