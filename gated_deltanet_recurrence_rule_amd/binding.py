@@ -43,7 +43,7 @@ class GdnDecodeLayerArgs(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int32), ("Hk", ctypes.c_int32), ("Hv", ctypes.c_int32), ("D", ctypes.c_int32),
         ("flags", ctypes.c_uint32), ("q_scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
-        ("norm_eps", ctypes.c_float),
+        ("norm_eps", ctypes.c_float), ("n_slots", ctypes.c_int32),
         ("x", p), ("stride_x", ctypes.c_int64), ("conv_w", p), ("conv_state_in", p), ("conv_state_out", p),
         ("ba", p), ("stride_ba", ctypes.c_int64), ("A_log", p), ("dt_bias", p), ("state_pool", p),
         ("slots", p), ("z", p), ("stride_z", ctypes.c_int64), ("norm_w", p), ("out", p),
@@ -96,7 +96,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
         L.gdn_gates.argtypes = [i64, i32, i32, p, i64, p, p, p, p, p]
         L.gdn_gates.restype = ctypes.c_int
-        L.gdn_decode_token.argtypes = [ctypes.POINTER(GdnDims), p, p, p, i32, p, i64, p, p, p, p, p, p]
+        L.gdn_decode_token.argtypes = [ctypes.POINTER(GdnDims), p, p, p, i32, p, i64, p, p, p, i32, p, p, p]
         L.gdn_decode_token.restype = ctypes.c_int
         L.gdn_decode_layer.argtypes = [ctypes.POINTER(GdnDecodeLayerArgs), p]
         L.gdn_decode_layer.restype = ctypes.c_int
@@ -131,6 +131,20 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on_stream(stream, *tensors):
+    """Buffers this binding allocated come from the current stream's pool; when the
+    kernels run on another stream, mark them used there so that the caching
+    allocator does not hand their memory out before that stream's work is done."""
+    import torch
+    if stream is None:
+        return
+    if stream.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _io(t) -> int:
@@ -185,8 +199,10 @@ def gdn_prefill(q, k, v, log_alpha, beta, state_in=None, state_out=None, o=None,
     io = _io(q)
     if k.dtype != q.dtype or v.dtype != q.dtype or (o is not None and o.dtype != q.dtype):
         raise ValueError("q, k, v and o must share one dtype")
+    own = []
     if o is None:
         o = torch.empty((B, T, Hv * D), dtype=q.dtype, device=q.device)
+        own.append(o)
     flags = (GDN_FLAG_QK_L2NORM if l2norm else 0) | (GDN_FLAG_TOKEN_SERIAL if token_serial else 0)
     dims = make_dims(B, T, Hk, Hv, D, io, flags,
                      _token_stride(q, B, T, Hk * D, "q"), _token_stride(k, B, T, Hk * D, "k"),
@@ -202,10 +218,12 @@ def gdn_prefill(q, k, v, log_alpha, beta, state_in=None, state_out=None, o=None,
     ws_bytes = gdn_prefill_workspace_size(dims)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        own.append(workspace)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().gdn_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                              _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o), _ptr(workspace),
                              ws_len, _stream(stream)))
+    _on_stream(stream, *own)
     return o
 
 
@@ -232,8 +250,10 @@ def gdn_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, state_in=None, stat
         raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor")
     if cu_seqlens.device != q.device:
         raise ValueError("cu_seqlens must be on the device of q")
+    own = []
     if o is None:
         o = torch.empty((T, Hv * D), dtype=q.dtype, device=q.device)
+        own.append(o)
     for name, t, w in (("q", q, Hk * D), ("k", k, Hk * D), ("v", v, Hv * D), ("o", o, Hv * D)):
         if t.dim() != 2 or t.shape[0] != T or t.shape[1] < w or (T > 0 and t.stride(1) != 1):
             raise ValueError(f"{name}: expected [T, >={w}] with contiguous rows")
@@ -251,10 +271,12 @@ def gdn_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, state_in=None, stat
     ws_bytes = gdn_prefill_varlen_workspace_size(dims)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        own.append(workspace)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().gdn_prefill_varlen(ctypes.byref(dims), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(log_alpha), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o),
                                     _ptr(workspace), ws_len, _stream(stream)))
+    _on_stream(stream, *own)
     return o
 
 
@@ -266,8 +288,9 @@ def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None, *, Hk: int, Hv: int
     B = int(state.shape[0])
     D = int(state.shape[2])
     io = _io(q)
+    own = None
     if o is None:
-        o = torch.empty((B, Hv * D), dtype=q.dtype, device=q.device)
+        o = own = torch.empty((B, Hv * D), dtype=q.dtype, device=q.device)
     for name, t, w in (("q", q, Hk * D), ("k", k, Hk * D), ("v", v, Hv * D), ("o", o, Hv * D)):
         if t.dim() != 2 or t.shape[0] != B or t.shape[1] < w or t.stride(1) != 1:
             raise ValueError(f"{name}: expected [B, >={w}] with contiguous rows")
@@ -282,6 +305,7 @@ def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None, *, Hk: int, Hv: int
                      q_scale, l2_eps)
     _check(lib().gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                  _ptr(beta), _ptr(state), _ptr(o), _stream(stream)))
+    _on_stream(stream, own)
     return o
 
 
@@ -292,8 +316,9 @@ def gdn_conv1d_silu(x, w, conv_state_in=None, conv_state_out=None, y=None, *, st
     B, T = int(x.shape[0]), int(x.shape[1])
     C, K = int(w.shape[0]), int(w.shape[1])
     io = _io(x)
+    own = None
     if y is None:
-        y = torch.empty((B, T, C), dtype=x.dtype, device=x.device)
+        y = own = torch.empty((B, T, C), dtype=x.dtype, device=x.device)
     sx = _token_stride(x, B, T, C, "x") if T > 0 else C
     sy = _token_stride(y, B, T, C, "y") if T > 0 else C
     if w.dtype != x.dtype or not w.is_contiguous():
@@ -303,6 +328,7 @@ def gdn_conv1d_silu(x, w, conv_state_in=None, conv_state_out=None, y=None, *, st
             raise ValueError(f"{name} must be contiguous [B, C, K-1] with x's dtype")
     _check(lib().gdn_conv1d_silu(B, T, C, K, io, _ptr(x), sx, _ptr(w), _ptr(conv_state_in),
                                  _ptr(conv_state_out), _ptr(y), sy, _stream(stream)))
+    _on_stream(stream, own)
     return y
 
 
@@ -313,8 +339,9 @@ def gdn_gated_rmsnorm(x, z, w, eps: float = 1e-5, y=None, *, H: int, stream=None
     D = int(w.shape[0])
     n = int(x.shape[0])
     io = _io(x)
+    own = None
     if y is None:
-        y = torch.empty((n, H * D), dtype=x.dtype, device=x.device)
+        y = own = torch.empty((n, H * D), dtype=x.dtype, device=x.device)
     for name, t in (("x", x), ("z", z), ("y", y)):
         if t.dim() != 2 or t.shape[0] != n or t.shape[1] < H * D or t.stride(1) != 1 or t.dtype != x.dtype:
             raise ValueError(f"{name}: expected [n_tok, >={H * D}] with contiguous channels")
@@ -323,6 +350,7 @@ def gdn_gated_rmsnorm(x, z, w, eps: float = 1e-5, y=None, *, H: int, stream=None
     _check(lib().gdn_gated_rmsnorm(n, H, D, io, _ptr(x), x.stride(0) if n > 1 else H * D, _ptr(z),
                                    z.stride(0) if n > 1 else H * D, _ptr(w), float(eps), _ptr(y),
                                    y.stride(0) if n > 1 else H * D, _stream(stream)))
+    _on_stream(stream, own)
     return y
 
 
@@ -341,15 +369,19 @@ def gdn_gates(ba, A_log, dt_bias, log_alpha=None, beta=None, *, Hv: int, stream=
     if ba.dim() != 2 or ba.shape[1] < 2 * Hv or (n > 0 and ba.stride(1) != 1):
         raise ValueError(f"ba: expected [n_tok, >={2 * Hv}] with contiguous columns")
     _params(A_log, dt_bias, Hv)
+    own = []
     if log_alpha is None:
         log_alpha = torch.empty((n, Hv), dtype=torch.float32, device=ba.device)
+        own.append(log_alpha)
     if beta is None:
         beta = torch.empty((n, Hv), dtype=torch.float32, device=ba.device)
+        own.append(beta)
     for name, g in (("log_alpha", log_alpha), ("beta", beta)):
         if g.dtype != torch.float32 or not g.is_contiguous() or g.numel() != n * Hv:
             raise ValueError(f"{name} must be contiguous fp32 with n_tok * Hv elements")
     _check(lib().gdn_gates(n, Hv, _io(ba), _ptr(ba), ba.stride(0) if n > 1 else 2 * Hv, _ptr(A_log),
                            _ptr(dt_bias), _ptr(log_alpha), _ptr(beta), _stream(stream)))
+    _on_stream(stream, *own)
     return log_alpha, beta
 
 
@@ -364,8 +396,9 @@ def gdn_decode_token(q, k, v, ba, A_log, dt_bias, state_pool, slots=None, o=None
     B = int(q.shape[0])
     D = int(state_pool.shape[2])
     io = _io(q)
+    own = None
     if o is None:
-        o = torch.empty((B, Hv * D), dtype=q.dtype, device=q.device)
+        o = own = torch.empty((B, Hv * D), dtype=q.dtype, device=q.device)
     for name, t, w in (("q", q, Hk * D), ("k", k, Hk * D), ("v", v, Hv * D), ("o", o, Hv * D),
                        ("ba", ba, 2 * Hv)):
         if t.dim() != 2 or t.shape[0] != B or t.shape[1] < w or t.stride(1) != 1:
@@ -384,7 +417,9 @@ def gdn_decode_token(q, k, v, ba, A_log, dt_bias, state_pool, slots=None, o=None
                      q_scale, l2_eps)
     _check(lib().gdn_decode_token(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _io(ba), _ptr(ba),
                                   ba.stride(0) if B > 1 else 2 * Hv, _ptr(A_log), _ptr(dt_bias),
-                                  _ptr(state_pool), _ptr(slots), _ptr(o), _stream(stream)))
+                                  _ptr(state_pool), int(state_pool.shape[0]), _ptr(slots), _ptr(o),
+                                  _stream(stream)))
+    _on_stream(stream, own)
     return o
 
 
@@ -400,8 +435,9 @@ def gdn_decode_layer(x, conv_w, conv_state_in, conv_state_out, ba, A_log, dt_bia
     D = 128
     B = int(x.shape[0])
     C = (2 * Hk + Hv) * D
+    own = None
     if out is None:
-        out = torch.empty((B, Hv * D), dtype=torch.bfloat16, device=x.device)
+        out = own = torch.empty((B, Hv * D), dtype=torch.bfloat16, device=x.device)
     for name, t, wdt in (("x", x, C), ("ba", ba, 2 * Hv), ("z", z, Hv * D), ("out", out, Hv * D)) + \
             ((("o", o, Hv * D),) if o is not None else ()):
         if t.dtype != torch.bfloat16 or t.dim() != 2 or t.shape[0] != B or t.shape[1] < wdt or t.stride(1) != 1:
@@ -424,12 +460,13 @@ def gdn_decode_layer(x, conv_w, conv_state_in, conv_state_out, ba, A_log, dt_bia
     if slots is not None and (slots.dtype != torch.int32 or not slots.is_contiguous() or tuple(slots.shape) != (B,)):
         raise ValueError("slots must be a contiguous int32 [B] tensor")
     st = lambda t, wdt: t.stride(0) if B > 1 else wdt
-    a = GdnDecodeLayerArgs(B, Hk, Hv, D, GDN_FLAG_QK_L2NORM if l2norm else 0, q_scale, l2_eps, norm_eps,
+    a = GdnDecodeLayerArgs(B, Hk, Hv, D, GDN_FLAG_QK_L2NORM if l2norm else 0, q_scale, l2_eps, norm_eps, S,
                            _ptr(x), st(x, C), _ptr(conv_w), _ptr(conv_state_in), _ptr(conv_state_out),
                            _ptr(ba), st(ba, 2 * Hv), _ptr(A_log), _ptr(dt_bias), _ptr(state_pool), _ptr(slots),
                            _ptr(z), st(z, Hv * D), _ptr(norm_w), _ptr(out), st(out, Hv * D), _ptr(o),
                            st(o, Hv * D) if o is not None else 0)
     _check(lib().gdn_decode_layer(ctypes.byref(a), _stream(stream)))
+    _on_stream(stream, own)
     return out
 
 
@@ -491,17 +528,21 @@ def gdn_attn_prefill(qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, o=None, *, 
     if two != 2 or tuple(k.shape) != (B, T, Hkv, D) or tuple(v.shape) != (B, T, Hkv, D):
         raise ValueError("qg must be [B, T, Hq, 2, D] and k, v [B, T, Hkv, D]")
     S_max = int(k_cache.shape[2])
+    own = []
     if o is None:
         o = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device=qg.device)
+        own.append(o)
     dims = make_attn_dims(B, T, Hq, Hkv, D, S_max, rot_dim, rope_theta, norm_eps, scale,
                           _rows(qg, 2, 2 * Hq * D, "qg"), _rows(k, 2, Hkv * D, "k"), _rows(v, 2, Hkv * D, "v"),
                           _rows(o, 2, Hq * D, "o"))
     need = int(lib().gdn_attn_prefill_workspace_size(ctypes.byref(dims)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=qg.device)
+        own.append(workspace)
     ws_len = 0 if workspace is None else workspace.numel()
     _check(lib().gdn_attn_prefill(ctypes.byref(dims), _ptr(qg), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w),
                                   _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(workspace), ws_len, _stream(stream)))
+    _on_stream(stream, *own)
     return o
 
 
@@ -518,16 +559,20 @@ def gdn_attn_decode(qg, k, v, q_norm_w, k_norm_w, cache_len, k_cache, v_cache, o
     if cache_len.dtype != torch.int32 or tuple(cache_len.shape) != (B,) or cache_len.device != qg.device:
         raise ValueError("cache_len must be an int32 [B] tensor on the device of qg")
     S_max = int(k_cache.shape[2])
+    own = []
     if o is None:
         o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=qg.device)
+        own.append(o)
     dims = make_attn_dims(B, 1, Hq, Hkv, D, S_max, rot_dim, rope_theta, norm_eps, scale,
                           _rows(qg, 1, 2 * Hq * D, "qg"), _rows(k, 1, Hkv * D, "k"), _rows(v, 1, Hkv * D, "v"),
                           _rows(o, 1, Hq * D, "o"))
     need = int(lib().gdn_attn_decode_workspace_size(ctypes.byref(dims)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=qg.device)
+        own.append(workspace)
     ws_len = 0 if workspace is None else workspace.numel()
     _check(lib().gdn_attn_decode(ctypes.byref(dims), _ptr(qg), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w),
                                  _ptr(cache_len), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(workspace), ws_len,
                                  _stream(stream)))
+    _on_stream(stream, *own)
     return o

@@ -7,12 +7,31 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 
 #include "gdn_internal.h"
+
+namespace gdn {
+
+int device_cu_count() {
+  static std::atomic<int> count[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+  if (dev < 64) count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace gdn
 
 namespace {
 
@@ -375,12 +394,14 @@ gdn_status gdn_gates(int64_t n_tok, int32_t Hv, int32_t dtype, const void* ba, i
 
 gdn_status gdn_decode_token(const gdn_dims* d, const void* q, const void* k, const void* v, int32_t ba_dtype,
                             const void* ba, int64_t stride_ba, const float* A_log, const float* dt_bias,
-                            float* state_pool, const int32_t* slots, void* o, void* stream) {
+                            float* state_pool, int32_t n_slots, const int32_t* slots, void* o, void* stream) {
   gdn_status st = check_dims(d, true);
   if (st != GDN_OK) return st;
   if (ba_dtype != GDN_F32 && ba_dtype != GDN_BF16) return fail(GDN_ERR_SHAPE, "ba dtype %d unknown", ba_dtype);
   if (stride_ba < 2 * static_cast<int64_t>(d->Hv))
     return fail(GDN_ERR_SHAPE, "stride_ba=%lld below 2*Hv=%d", (long long)stride_ba, 2 * d->Hv);
+  if (n_slots < 0 || (!slots && n_slots < d->B))
+    return fail(GDN_ERR_SHAPE, "n_slots=%d: the pool needs >= 0 entries, and >= B=%d without slots", n_slots, d->B);
   if (d->B == 0) return ok();
   if (!q || !k || !v || !ba || !A_log || !dt_bias || !state_pool || !o)
     return fail(GDN_ERR_NULL, "q, k, v, ba, A_log, dt_bias, state_pool and o are required");
@@ -397,6 +418,7 @@ gdn_status gdn_decode_token(const gdn_dims* d, const void* q, const void* k, con
   a.A_log = A_log;
   a.dt_bias = dt_bias;
   a.slots = slots;
+  a.nslots = n_slots;
   return from_hip(gdn::launch_recurrent(a, d->io, static_cast<hipStream_t>(stream)), "gdn_decode_token");
 }
 
@@ -408,6 +430,9 @@ gdn_status gdn_decode_layer(const gdn_decode_layer_args* p, void* stream) {
   if (p->flags & ~static_cast<uint32_t>(GDN_FLAG_QK_L2NORM))
     return fail(GDN_ERR_SHAPE, "flags 0x%x: only GDN_FLAG_QK_L2NORM applies", p->flags);
   if (!(p->l2_eps >= 0.0f) || !(p->norm_eps >= 0.0f)) return fail(GDN_ERR_SHAPE, "eps values must be >= 0");
+  if (p->n_slots < 0 || (!p->slots && p->n_slots < p->B))
+    return fail(GDN_ERR_SHAPE, "n_slots=%d: the pools need >= 0 entries, and >= B=%d without slots", p->n_slots,
+                p->B);
   const int64_t C = static_cast<int64_t>(2 * p->Hk + p->Hv) * p->D, W = static_cast<int64_t>(p->Hv) * p->D;
   if (p->stride_x < C || p->stride_ba < 2 * static_cast<int64_t>(p->Hv) || p->stride_z < W || p->stride_out < W ||
       (p->o && p->stride_o < W))
@@ -444,6 +469,7 @@ gdn_status gdn_decode_layer(const gdn_decode_layer_args* p, void* stream) {
   a.dt_bias = p->dt_bias;
   a.pool = p->state_pool;
   a.slots = p->slots;
+  a.nslots = p->n_slots;
   a.z = static_cast<const uint16_t*>(p->z);
   a.sz = p->stride_z;
   a.norm_w = static_cast<const uint16_t*>(p->norm_w);

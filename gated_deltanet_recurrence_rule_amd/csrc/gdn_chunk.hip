@@ -53,14 +53,19 @@
 // bound; its range (|x| < 65504) bounds the values of v, the state and the
 // intra-chunk matrices this path accepts.
 //
-// MFMA layout (v_mfma_f32_32x32x16_bf16 and _f16, wave64): A row = B column =
-// lane & 31; the accumulator holds column lane & 31, rows 8j + 4h + i
-// (h = lane >> 5, value index 4j + i).  The contraction index is permuted the
-// same way on A and B: inside each 16-wide k step, lane half h carries
-// k = 4h..4h+3 and 8+4h..8+4h+3.  With that permutation accumulator values
-// [8s, 8s+8) of a tile are directly the B operand for k step s of that tile,
-// so M and U feed the next product from registers, and a product computed in
-// transposed form (C^T = B^T A^T) leaves its result as an A fragment.
+// MFMA layouts (wave64).  The chunk operands that leave the prep kernel are
+// fragments of v_mfma_f32_16x16x32_f16: A row = B column = lane & 15, and the
+// lane group g = lane >> 4 carries 8 of a k step's 32 contraction indices; the
+// accumulator holds column lane & 15, rows 4g + v (v < 4).  The contraction
+// index is permuted the same way on A and B: slot e of group g is
+// kperm(g, e) = 4g + e for e < 4 and 16 + 4g + (e - 4) otherwise.  With that
+// permutation the values of two accumulator tiles stacked in rows (rows 0-15
+// and 16-31 of a 32-row block) are, lane by lane, the B operand of the k step
+// over that block, so M and U feed the next product straight from registers,
+// and a product computed in transposed form (C^T = B^T A^T) leaves its result
+// as an A fragment.  The key Gram K K^T that feeds the inverse is taken on
+// 32x32x16 tiles (A row = B column = lane & 31), whose layout stays inside the
+// prep kernel.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -75,23 +80,27 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 constexpr int CH = 64;    // chunk length
 constexpr int DK = 128;   // head width
 constexpr int KP = 136;   // LDS row pitch (bf16) of 64 x 128 row tiles
-constexpr int FP = 68;    // LDS row pitch (floats) of fp32 64 x 64 matrices (16-byte rows)
-constexpr int FT = 6;     // 32x16 fragment tiles covering a 64x64 lower triangle
-// workspace block per (batch, value head, chunk): fp16 MFMA fragments and fp32 scalings
-constexpr int WH_W = 0;        // -W = -T' diag(gamma rk) K: tile rt*8+ks (rows 32rt.., key step ks)
-constexpr int WH_KD = 16384;   // Kd = K^T diag(rk e^{g_63-g}): tile dt*4+ks (keys 32dt.., chunk step ks)
-constexpr int WH_U0 = 32768;   // U0 = T' V in accumulator layout: [value tile 4][row tile 2][lane 64][16]
-constexpr int WH_P = 49152;    // P: 6 tiles of the lower triangle
+// Workspace block per (batch, value head, chunk): 16x16x32 fp16 fragments (1 KiB each:
+// 64 lanes x 8 halves) and fp32 scalings.
+constexpr int WH_W = 0;        // -W = -T' diag(gamma rk) K, A operand: fragment rt*4+ks (rows 16rt.., keys 32ks..)
+constexpr int WH_KD = 16384;   // Kd = K^T diag(rk e^{g_63-g}), A operand: fragment dt*2+ks (keys 16dt.., rows 32ks..)
+constexpr int WH_U0 = 32768;   // U0 = T' V as accumulators of U: [value tile 8][lane 64][row tile 4][4 halves]
+constexpr int WH_P = 49152;    // P^T, B operand: 6 fragments (token tile ct, rows 32ks..), see pfrag()
 constexpr int WH_SC = 55296;   // gamma_r (64 floats), gamma_63
 constexpr int WH_BYTES = 56320;
-// workspace block per (batch, key head, chunk): Q^ = diag(rq) Q fragments, tile rt*8+ks
+// workspace block per (batch, key head, chunk): Q^T = (diag(rq) Q)^T, B operand: fragment ks*4+ct
+// (keys 32ks.., tokens 16ct..)
 constexpr int WK_BYTES = 16384;
 
-// fragment tile f covers rows 32*kFtRt[f].., k step kFtKs[f] (16 columns)
-__device__ __forceinline__ int ft_rt(int f) { return f < 2 ? 0 : 1; }
-__device__ __forceinline__ int ft_ks(int f) { return f < 2 ? f : f - 2; }
-// k offset (inside a 16-wide step) of element e for lane half h
-__device__ __forceinline__ int kperm(int h, int e) { return (e < 4) ? 4 * h + e : 8 + 4 * h + (e - 4); }
+// contraction index of slot e for lane group g, inside a 32-wide k step (16x16x32)
+__device__ __forceinline__ int kperm(int g, int e) { return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4); }
+// the same for a 16-wide k step of 32x32x16 and lane half h (the inverse's 32-block merge)
+__device__ __forceinline__ int kperm32(int h, int e) { return (e < 4) ? 4 * h + e : 8 + 4 * h + (e - 4); }
+// P^T fragments: (token tile ct, chunk-row step ks) pairs with ks == 0 or ct >= 2 (the others are zero)
+__device__ __forceinline__ int pfrag(int ct, int ks) { return ks == 0 ? ct : 2 + ct; }
+// (row tile rt, k step ki) pairs of the lower-triangular T' that are not all zero: ki == 0 or rt >= 2
+constexpr int kTriRt[6] = {0, 1, 2, 3, 2, 3};
+constexpr int kTriKi[6] = {0, 0, 0, 0, 1, 1};
 
 __device__ __forceinline__ bf16x8 lds_frag32(const uint16_t* row_k0, int h) {
   const u16x4 lo = *reinterpret_cast<const u16x4*>(row_k0 + 4 * h);
@@ -106,6 +115,34 @@ __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, con
 
 __device__ __forceinline__ floatx16 mfma32h(const halfx8& a, const halfx8& b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma16h(const halfx8& a, const halfx8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma16b(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// two stacked 16x16 accumulator tiles (rows 0-15, 16-31) as the fp16 B operand of a 32-wide k step
+__device__ __forceinline__ halfx8 stack_h(const floatx4& lo, const floatx4& hi) {
+  halfx8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = static_cast<_Float16>(lo[e]);
+    r[4 + e] = static_cast<_Float16>(hi[e]);
+  }
+  return r;
+}
+
+// a bf16 row segment of 32 contraction indices as a 16x16x32 operand slot set: lane group g
+// takes [4g, 4g+4) and [16+4g, 20+4g) of the segment
+__device__ __forceinline__ bf16x8 lds_frag16(const uint16_t* row_k0, int g) {
+  const u16x4 lo = *reinterpret_cast<const u16x4*>(row_k0 + 4 * g);
+  const u16x4 hi = *reinterpret_cast<const u16x4*>(row_k0 + 16 + 4 * g);
+  const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 __device__ __forceinline__ halfx8 acc_frag_h(const floatx16& t, int s) {
@@ -230,7 +267,7 @@ __device__ __forceinline__ void invert_unit_lower(float* M, int lane) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float av = e < 4 ? a0[e] : a1[e - 4];
-        const float bv = T0[(16 * ks + kperm(h, e)) * L::kTP + l32];
+        const float bv = T0[(16 * ks + kperm32(h, e)) * L::kTP + l32];
         ahi[e] = static_cast<_Float16>(av);
         alo[e] = static_cast<_Float16>(av - static_cast<float>(ahi[e]));
         bhi[e] = static_cast<_Float16>(bv);
@@ -389,51 +426,66 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
     if (lane == 0) sc[64] = __expf(gl);
   }
 
-  // ---- Q^ = diag(rq) Q as the output product's A fragments (fp16) -----------
-  //      tile rt*8+ks holds rows 32rt + (lane&31), k = 16ks + kperm
+  // ---- Q^T = (diag(rq) Q)^T as the output product's B fragments (fp16) ------
+  //      fragment ks*4+ct: token 16ct + (lane & 15), keys 32ks + kperm(g, e)
   {
     unsigned char* wsk = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WH_BYTES +
                          (static_cast<int64_t>(b * a.Hk + hk) * nwin + cl) * WK_BYTES;
     for (int slot = tid; slot < 16 * 64; slot += 256) {
-      const int tile = slot >> 6, ln = slot & 63;
-      const int r = 32 * (tile >> 3) + (ln & 31), hh = ln >> 5;
-      const uint16_t* src = sQ + r * KP + 16 * (tile & 7);
-      const u16x4 lo = *reinterpret_cast<const u16x4*>(src + 4 * hh);
-      const u16x4 hi = *reinterpret_cast<const u16x4*>(src + 8 + 4 * hh);
+      const int f = slot >> 6, ln = slot & 63;
+      const int r = 16 * (f & 3) + (ln & 15), gg = ln >> 4;
+      const uint16_t* src = sQ + r * KP + 32 * (f >> 2);
+      const u16x4 lo = *reinterpret_cast<const u16x4*>(src + 4 * gg);
+      const u16x4 hi = *reinterpret_cast<const u16x4*>(src + 16 + 4 * gg);
       const float rq = vRq[r];
-      u16x8 f;
+      u16x8 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        f[e] = f32_to_f16_bits(bf16_bits_to_f32(lo[e]) * rq);
-        f[4 + e] = f32_to_f16_bits(bf16_bits_to_f32(hi[e]) * rq);
+        x[e] = f32_to_f16_bits(bf16_bits_to_f32(lo[e]) * rq);
+        x[4 + e] = f32_to_f16_bits(bf16_bits_to_f32(hi[e]) * rq);
       }
-      *reinterpret_cast<u16x8*>(wsk + tile * 1024 + ln * 16) = f;
+      *reinterpret_cast<u16x8*>(wsk + f * 1024 + ln * 16) = x;
     }
   }
-  // ---- this wave's columns of K^T (key rows 32 wv + (lane&31)) at the chunk rows
-  //      of each 16-row k step, in fragment order; scaled per value head below
-  u16x8 kt[4];
-  {
-    const int d = 32 * wv + l32;
+  // ---- this wave's K^T values in A-fragment order: key tiles dt = 2wv, 2wv+1 (keys
+  //      16dt + (lane & 15)) at chunk rows 32ks + kperm(g, e); scaled per value head below
+  const int g4 = lane >> 4, l16 = lane & 15;
+  u16x8 kt[4];   // [dt - 2wv][ks]
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+  for (int t = 0; t < 2; ++t) {
+    const int d = 16 * (2 * wv + t) + l16;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kt[ks][e] = sK[(16 * ks + kperm(h, e)) * KP + d];
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kt[2 * t + ks][e] = sK[(32 * ks + kperm(g4, e)) * KP + d];
   }
-  // ---- Gram tiles (32x32), kept in registers of waves 0-2 -------------------
-  //  K K^T tile (rtK, ctK) in {(0,0), (1,0), (1,1)} -- tile wv of the lower
-  //  triangle: element (row r, column i) = k_r . k_i
-  //  K Q^T tile (itP, rtP) in {(0,0), (0,1), (1,1)}: element (row i, column r) = k_i . q_r
+  // ---- Gram tiles, kept in registers ---------------------------------------
+  //  K K^T (waves 0-2, 32x32 tile wv of the lower triangle): element (row r, column i) = k_r . k_i
+  //  K Q^T (all waves, 16x16 tiles): element (row i, column r) = k_i . q_r, for the P^T fragments
+  //  this wave writes: wave 0 (ct 0, 1 at ks 0), wave 1 (ct 2, 3 at ks 0), wave 2 (ct 2 at ks 1),
+  //  wave 3 (ct 3 at ks 1); a fragment (ct, ks) needs the tiles of rows 32ks.. and 32ks+16..
   const int rtK = wv == 0 ? 0 : 1, ctK = wv == 2 ? 1 : 0;
-  const int itP = wv == 2 ? 1 : 0, rtP = wv == 0 ? 0 : 1;
-  floatx16 gKK = zero16(), gKQ = zero16();
+  floatx16 gKK = zero16();
   if (wv < 3) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 8; ++ks)
       gKK = mfma32(lds_frag32(sK + (32 * rtK + l32) * KP + 16 * ks, h),
                    lds_frag32(sK + (32 * ctK + l32) * KP + 16 * ks, h), gKK);
-      gKQ = mfma32(lds_frag32(sK + (32 * itP + l32) * KP + 16 * ks, h),
-                   lds_frag32(sQ + (32 * rtP + l32) * KP + 16 * ks, h), gKQ);
+  }
+  const int npf = wv < 2 ? 2 : 1;                         // P^T fragments of this wave
+  const int pct0 = wv < 2 ? 2 * wv : wv, pks = wv < 2 ? 0 : 1;
+  floatx4 gKQ[4];                                         // [fragment][row half]
+#pragma unroll
+  for (int t = 0; t < 4; ++t) gKQ[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if ((t >> 1) < npf) {
+        const int ct = pct0 + (t >> 1), it = 2 * pks + (t & 1);
+        gKQ[t] = mfma16b(lds_frag16(sK + (16 * it + l16) * KP + 32 * kk, g4),
+                         lds_frag16(sQ + (16 * ct + l16) * KP + 32 * kk, g4), gKQ[t]);
+      }
     }
   }
   __syncthreads();  // the K and Q rows are dead from here on: their bytes hold the matrices
@@ -442,49 +494,45 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   // then each head's inverse on its own wave, then the products of each head.
   for (int j0 = 0; j0 < (kOneGroup ? 1 : a.G); j0 += L::kNH) {
     const int ng = kOneGroup ? a.G : min(L::kNH, a.G - j0);
-    // ---- A (fp32, strictly lower; tile wv) and the P fragments --------------
-    if (wv < 3) {
-      for (int jj = 0; jj < ng; ++jj) {
-        const int j = j0 + jj;
-        const float* vG = vgate(j);
-        const float* vBe = vG + CH;
-        {
-          float* At = mat(jj) + wv * L::kTile;
-          const int i = 32 * ctK + l32;
-          const float gi = vG[i], rki = vRk[i];
+    for (int jj = 0; jj < ng; ++jj) {
+      const int j = j0 + jj;
+      const float* vG = vgate(j);
+      const float* vBe = vG + CH;
+      // ---- A (fp32, strictly lower; tile wv) -----------------------------------
+      if (wv < 3) {
+        float* At = mat(jj) + wv * L::kTile;
+        const int i = 32 * ctK + l32;
+        const float gi = vG[i], rki = vRk[i];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r0 = 32 * rtK + 8 * q + 4 * h;
-            const floatx4 g4 = *reinterpret_cast<const floatx4*>(vG + r0);
-            const floatx4 b4 = *reinterpret_cast<const floatx4*>(vBe + r0);
-            const floatx4 k4 = *reinterpret_cast<const floatx4*>(vRk + r0);
+        for (int q = 0; q < 4; ++q) {
+          const int r0 = 32 * rtK + 8 * q + 4 * h;
+          const floatx4 g4v = *reinterpret_cast<const floatx4*>(vG + r0);
+          const floatx4 b4 = *reinterpret_cast<const floatx4*>(vBe + r0);
+          const floatx4 k4 = *reinterpret_cast<const floatx4*>(vRk + r0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = r0 + e;
-              const float x = b4[e] * k4[e] * rki * __expf(fminf(g4[e] - gi, 0.f)) * gKK[4 * q + e];
-              At[(8 * q + 4 * h + e) * L::kTP + l32] = i < r ? x : 0.f;
-            }
+          for (int e = 0; e < 4; ++e) {
+            const int r = r0 + e;
+            const float x = b4[e] * k4[e] * rki * __expf(fminf(g4v[e] - gi, 0.f)) * gKK[4 * q + e];
+            At[(8 * q + 4 * h + e) * L::kTP + l32] = i < r ? x : 0.f;
           }
         }
-        {
-          unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hk * a.G + j) * nwin + cl) * WH_BYTES;
-          const int r = 32 * rtP + l32;
-          const float gr = vG[r], rq = vRq[r];
+      }
+      // ---- P^T fragments: P_ri = e^{g_r - g_i} rq_r rk_i (q_r . k_i), i <= r --------
+      {
+        unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hk * a.G + j) * nwin + cl) * WH_BYTES;
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const int f = rtP == 0 ? s2 : 2 + 2 * itP + s2;
-            const int ia = 32 * itP + 16 * s2 + 4 * h, ib = ia + 8;
-            const floatx4 ga = *reinterpret_cast<const floatx4*>(vG + ia), gb = *reinterpret_cast<const floatx4*>(vG + ib);
-            const floatx4 ka = *reinterpret_cast<const floatx4*>(vRk + ia), kb = *reinterpret_cast<const floatx4*>(vRk + ib);
-            u16x8 pf;
+        for (int u = 0; u < 2; ++u) {
+          if (u < npf) {
+            const int ct = pct0 + u, r = 16 * ct + l16;
+            const float gr = vG[r], rq = vRq[r];
+            halfx8 pf;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int i = e < 4 ? ia + e : ib + e - 4;
-              const float gi = e < 4 ? ga[e] : gb[e - 4], rki = e < 4 ? ka[e] : kb[e - 4];
-              const float x = __expf(fminf(gr - gi, 0.f)) * rq * rki * gKQ[8 * s2 + e];
-              pf[e] = f32_to_f16_bits(i <= r ? x : 0.f);
+              const int i = 32 * pks + kperm(g4, e);
+              const float x = __expf(fminf(gr - vG[i], 0.f)) * rq * vRk[i] * gKQ[2 * u + (e >> 2)][e & 3];
+              pf[e] = static_cast<_Float16>(i <= r ? x : 0.f);
             }
-            *reinterpret_cast<u16x8*>(wsc + WH_P + f * 1024 + lane * 16) = pf;
+            *reinterpret_cast<halfx8*>(wsc + WH_P + pfrag(ct, pks) * 1024 + lane * 16) = pf;
           }
         }
       }
@@ -493,15 +541,16 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
     // ---- T = (I + A)^-1, head j0 + wv on wave wv ----------------------------
     if (wv < ng) invert_unit_lower(mat(wv), lane);
     __syncthreads();
-    // ---- per head, all waves: T' = T diag(beta) fragments (all six), the K^T
-    //      columns of key tile wv scaled two ways, and the V columns of value tile wv
+    // ---- per head, all waves: the six nonzero T' = T diag(beta) fragments (A operand of
+    //      T' V; the same registers are the B operand of Ks^T T'^T), then
+    //      -W (key tiles 2wv, 2wv+1), Kd (the same key tiles) and U0 (value tiles 2wv, 2wv+1)
     for (int jj = 0; jj < ng; ++jj) {
       const int j = j0 + jj, hv = hk * a.G + j;
       unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hv) * nwin + cl) * WH_BYTES;
       const float* vBe = vgate(j) + CH;
       const float* vKs = vgate(j) + 2 * CH;
       const float* vKd = vgate(j) + 3 * CH;
-      // this head's V tile through the wave's LDS tile, then the next head's loads
+      // this head's V tile (value columns 32wv..) through the wave's LDS tile, then the next head's loads
       wave_lds_sync();   // the previous head's reads of the tile are done
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -510,83 +559,90 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       }
       if (j + 1 < a.G) load_v(hv + 1);
       wave_lds_sync();
-      halfx8 vf[4];
+      halfx8 vf[4];   // [ki][value tile half]: value column 16 hh + (lane & 15), rows 32ki + kperm
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ki = 0; ki < 2; ++ki)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vf[ks][e] = static_cast<_Float16>(bf16_bits_to_f32(sVw[(16 * ks + kperm(h, e)) * L::kVP + l32]));
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            vf[2 * ki + hh][e] =
+                static_cast<_Float16>(bf16_bits_to_f32(sVw[(32 * ki + kperm(g4, e)) * L::kVP + 16 * hh + l16]));
       const float* M = mat(jj);
-      halfx8 tf[FT];
+      halfx8 tf[6];
 #pragma unroll
-      for (int f = 0; f < FT; ++f) {
-        // tile (0,0) for the row tile 0 fragments, (1,0) and (1,1) for row tile 1
-        const int r = 32 * ft_rt(f) + l32;
-        const float* tr4 = M + (f < 2 ? 0 : (f < 4 ? 1 : 2)) * L::kTile + l32 * L::kTP + 16 * (ft_ks(f) & 1) + 4 * h;
-        const int ca = 16 * ft_ks(f) + 4 * h, cb = ca + 8;
+      for (int f = 0; f < 6; ++f) {
+        const int rt = kTriRt[f], ki = kTriKi[f];
+        const int r = 16 * rt + l16;
+        const int tile = rt < 2 ? 0 : (ki == 0 ? 1 : 2);
+        const float* tr4 = M + tile * L::kTile + (r & 31) * L::kTP + 4 * g4;
         const floatx4 ta = *reinterpret_cast<const floatx4*>(tr4);
-        const floatx4 tb = *reinterpret_cast<const floatx4*>(tr4 + 8);
-        const floatx4 ba = *reinterpret_cast<const floatx4*>(vBe + ca), bb = *reinterpret_cast<const floatx4*>(vBe + cb);
+        const floatx4 tb = *reinterpret_cast<const floatx4*>(tr4 + 16);
+        const floatx4 ba = *reinterpret_cast<const floatx4*>(vBe + 32 * ki + 4 * g4);
+        const floatx4 bb = *reinterpret_cast<const floatx4*>(vBe + 32 * ki + 16 + 4 * g4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = e < 4 ? ca + e : cb + e - 4;
-          const float x = e < 4 ? ta[e] * ba[e] : tb[e - 4] * bb[e - 4];
-          tf[f][e] = static_cast<_Float16>(i <= r ? x : 0.f);
+        for (int e = 0; e < 4; ++e) {
+          tf[f][e] = static_cast<_Float16>(ta[e] * ba[e]);
+          tf[f][4 + e] = static_cast<_Float16>(tb[e] * bb[e]);
         }
       }
       {
-        // W^T tiles (key tile wv, row tile 0 / 1) = Ks^T T'^T with Ks = diag(gamma rk) K;
-        // Kd = K^T diag(rk e^{g_63 - g}) fragments go out as they are
-        floatx16 w0 = zero16(), w1 = zero16();
+        // W^T tiles (key tile 2wv + t, row tile rt) = Ks^T T'^T with Ks = diag(gamma rk) K; the two
+        // key tiles of a row tile stack into the -W fragment (rt, wv).  Kd fragments go out as they are.
+        floatx4 w[2][4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const floatx4 sa = *reinterpret_cast<const floatx4*>(vKs + 16 * ks + 4 * h);
-          const floatx4 sb = *reinterpret_cast<const floatx4*>(vKs + 16 * ks + 8 + 4 * h);
-          const floatx4 da = *reinterpret_cast<const floatx4*>(vKd + 16 * ks + 4 * h);
-          const floatx4 db = *reinterpret_cast<const floatx4*>(vKd + 16 * ks + 8 + 4 * h);
-          halfx8 kf, df;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float kv = bf16_bits_to_f32(kt[ks][e]);
-            kf[e] = static_cast<_Float16>(kv * (e < 4 ? sa[e] : sb[e - 4]));
-            df[e] = static_cast<_Float16>(kv * (e < 4 ? da[e] : db[e - 4]));
+          for (int rt = 0; rt < 4; ++rt) w[t][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int ki = 0; ki < 2; ++ki) {
+            const floatx4 sa = *reinterpret_cast<const floatx4*>(vKs + 32 * ki + 4 * g4);
+            const floatx4 sb = *reinterpret_cast<const floatx4*>(vKs + 32 * ki + 16 + 4 * g4);
+            const floatx4 da = *reinterpret_cast<const floatx4*>(vKd + 32 * ki + 4 * g4);
+            const floatx4 db = *reinterpret_cast<const floatx4*>(vKd + 32 * ki + 16 + 4 * g4);
+            halfx8 kf, df;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float kv = bf16_bits_to_f32(kt[2 * t + ki][e]);
+              kf[e] = static_cast<_Float16>(kv * (e < 4 ? sa[e] : sb[e - 4]));
+              df[e] = static_cast<_Float16>(kv * (e < 4 ? da[e] : db[e - 4]));
+            }
+            *reinterpret_cast<halfx8*>(wsc + WH_KD + ((2 * wv + t) * 2 + ki) * 1024 + lane * 16) = df;
+#pragma unroll
+            for (int f = 0; f < 6; ++f)
+              if (kTriKi[f] == ki) w[t][kTriRt[f]] = mfma16h(kf, tf[f], w[t][kTriRt[f]]);
           }
-          *reinterpret_cast<halfx8*>(wsc + WH_KD + (wv * 4 + ks) * 1024 + lane * 16) = df;
-          if (ks < 2) w0 = mfma32h(kf, tf[ks], w0);
-          w1 = mfma32h(kf, tf[2 + ks], w1);
         }
-        // accumulator values [8s, 8s+8) of W^T tile (wv, rt) are the -W fragment (rt, 2 wv + s)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          halfx8 n0, n1;
+        for (int rt = 0; rt < 4; ++rt) {
+          halfx8 n;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            n0[e] = static_cast<_Float16>(-w0[8 * s2 + e]);
-            n1[e] = static_cast<_Float16>(-w1[8 * s2 + e]);
+          for (int e = 0; e < 4; ++e) {
+            n[e] = static_cast<_Float16>(-w[0][rt][e]);
+            n[4 + e] = static_cast<_Float16>(-w[1][rt][e]);
           }
-          *reinterpret_cast<halfx8*>(wsc + WH_W + (2 * wv + s2) * 1024 + lane * 16) = n0;
-          *reinterpret_cast<halfx8*>(wsc + WH_W + (8 + 2 * wv + s2) * 1024 + lane * 16) = n1;
+          *reinterpret_cast<halfx8*>(wsc + WH_W + (rt * 4 + wv) * 1024 + lane * 16) = n;
         }
       }
       {
-        // U0 tiles (row tile 0 / 1, value tile wv) = T' V, stored in accumulator layout
-        floatx16 u0 = zero16(), u1 = zero16();
+        // U0 tiles (row tile rt, value tile 2wv + hh) = T' V, stored as U's accumulators
+        floatx4 u[2][4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          if (ks < 2) u0 = mfma32h(tf[ks], vf[ks], u0);
-          u1 = mfma32h(tf[2 + ks], vf[ks], u1);
-        }
-        unsigned char* du = wsc + WH_U0 + (wv * 2) * 2048 + lane * 32;
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          halfx8 x0, x1;
+          for (int rt = 0; rt < 4; ++rt) u[hh][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            x0[e] = static_cast<_Float16>(u0[8 * s2 + e]);
-            x1[e] = static_cast<_Float16>(u1[8 * s2 + e]);
-          }
-          *reinterpret_cast<halfx8*>(du + 16 * s2) = x0;
-          *reinterpret_cast<halfx8*>(du + 2048 + 16 * s2) = x1;
+        for (int f = 0; f < 6; ++f)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            u[hh][kTriRt[f]] = mfma16h(tf[f], vf[2 * kTriKi[f] + hh], u[hh][kTriRt[f]]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          unsigned char* du = wsc + WH_U0 + (2 * wv + hh) * 2048 + lane * 32;
+          *reinterpret_cast<halfx8*>(du) = stack_h(u[hh][0], u[hh][1]);
+          *reinterpret_cast<halfx8*>(du + 16) = stack_h(u[hh][2], u[hh][3]);
         }
       }
     }
@@ -598,45 +654,39 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
 // =========================================================================
 // chain kernel: one workgroup (3 waves) per (32-column strip, value head, batch)
 // =========================================================================
-// LDS: NS input slots (a chunk's -W, Kd, U0 strip and scalings, copied from the
-// workspace by the copy wave, NS - 1 chunks ahead, or with one slot once the
-// chunk's operands have been read), two buffers each of the M and U fragments
-// that the state wave publishes for the output wave, and the output wave's
-// staging tile.  The output wave reads its own operands (Q^ and P fragments)
-// from the workspace straight into registers.  Two slots take 98 KiB, so one
-// workgroup per CU; one slot 61 KiB, so two share a CU and cover each other's
-// copies when the grid holds more workgroups than there are CUs.
+// LDS: NS input slots, each a chunk's -W, Kd, the U0 of the strip, the
+// scalings, Q^T and P^T, copied from the workspace by the copy wave NS - 1
+// chunks ahead (or, with one slot, once the chunk's slot has been read).  Two
+// slots take 118 KiB, so one workgroup per CU; one slot 59 KiB, so two share a
+// CU and cover each other's copies when the grid holds more workgroups than
+// there are CUs.
 template <int NS>
 struct ChainLds {
-  static constexpr int kW = 0, kKd = 16384, kU0 = 32768, kSc = 36864;
-  static constexpr int kSlot = 37888;               // 37 blocks of 1 KiB
+  static constexpr int kW = 0, kKd = 16384, kU0 = 32768, kSc = 36864, kQ = 37888, kP = 54272;
+  static constexpr int kSlot = 60416;               // 59 blocks of 1 KiB
   static constexpr int kNSlot = NS;
-  static constexpr int kMf = kNSlot * kSlot;        // 2 x M fragments (fp16) [k step 8][lane 64] x 16 B
-  static constexpr int kUf = kMf + 2 * 8192;        // 2 x U fragments (fp16) [k step 4][lane 64] x 16 B;
-                                                    // once read, a U buffer stages the output tile
-  static constexpr int kBytes = kUf + 2 * 4096;
+  static constexpr int kBytes = kNSlot * kSlot;
 };
-constexpr int kSlotBlocks = 37;
+constexpr int kSlotBlocks = 59;
+constexpr int kAhead = 6;    // operand fragments a state wave reads ahead of its products
+// A state wave's 54 operand fragments per chunk, as slot offsets, in the order its
+// products take them: [0, 32) pairs of -W (even: row tile (j/2) & 3, key step j/8)
+// and Q^T (odd: key step j/8, token tile (j/2) & 3); [32, 48) Kd (key tile
+// (j-32) & 7, chunk step (j-32) / 8); [48, 54) the P^T fragments.
+constexpr int kNFrag = 54;
+constexpr int kFragOff[kNFrag] = {0, 37888, 4096, 38912, 8192, 39936, 12288, 40960, 1024, 41984, 5120, 43008, 9216, 44032, 13312, 45056, 2048, 46080, 6144, 47104, 10240, 48128, 14336, 49152, 3072, 50176, 7168, 51200, 11264, 52224, 15360, 53248, 16384, 18432, 20480, 22528, 24576, 26624, 28672, 30720, 17408, 19456, 21504, 23552, 25600, 27648, 29696, 31744, 54272, 55296, 56320, 57344, 58368, 59392};
 
 // source of 1 KiB block m of a chunk's input slot (blocks follow the slot layout)
-__device__ __forceinline__ const unsigned char* slot_src(int m, const unsigned char* wsh, int strip) {
+__device__ __forceinline__ const unsigned char* slot_src(int m, const unsigned char* wsh, const unsigned char* wsk,
+                                                         int strip) {
   return m < 32 ? wsh + 1024 * m                                         // -W, Kd
-       : m < 36 ? wsh + WH_U0 + strip * 4096 + 1024 * (m - 32)           // U0 columns of this strip
-                : wsh + WH_SC;                                           // scalings
+       : m < 36 ? wsh + WH_U0 + strip * 4096 + 1024 * (m - 32)           // U0 of this strip's two value tiles
+       : m < 37 ? wsh + WH_SC                                            // scalings
+       : m < 53 ? wsk + 1024 * (m - 37)                                  // Q^T of the key head
+                : wsh + WH_P + 1024 * (m - 53);                          // P^T
 }
-
-// s_waitcnt immediate that waits until at most n vector memory operations are outstanding
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-
-// Workgroup barrier that orders LDS only: global stores and the LDS copies in
-// flight are not waited for (the copy wave waits for its own copies explicitly).
-__device__ __forceinline__ void lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float floatx2v __attribute__((ext_vector_type(2)));
@@ -645,15 +695,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
-// One barrier per chunk.  Between barrier c-1 and barrier c:
-//  * the state wave turns M_c into U_c and M_{c+1}, publishing U_c into U buffer
-//    c & 1 and M_{c+1} into M buffer (c+1) & 1;
-//  * the output wave forms diag(gamma) Q^ M_c from M buffer c & 1 and completes the
-//    previous chunk, O_{c-1} += P U_{c-1} from U buffer (c-1) & 1, and stores it;
-//  * the copy wave starts chunk c+2's copy into the slot chunk c-1 used and waits
-//    until chunk c+1's copy has landed.
-// Each buffer is rewritten two chunks after it was filled, by which time its
-// reader has passed the barrier in between.
 // Chunks [cs, ce) of sequence b in the window numbering, the token index of its
 // first token and its length.  Fixed-length batches: every sequence has chunks
 // [0, ceil(T/64)) and starts at token b*T.
@@ -670,23 +711,20 @@ __device__ __forceinline__ void seq_chunks(const RecArgs& a, int b, int& cs, int
   ce = cs + (len + CH - 1) / CH;
 }
 
+// Each state wave runs one chunk step per barrier; the copy wave fills the slot
+// of chunk c+1 (two slots) while the state waves read chunk c's, and waits for
+// its copies before the barrier.  With one slot the copy waits for a second
+// barrier per chunk, which each state wave reaches once it has read the slot.
 // The window holds chunks [c0, c0 + nw) (workspace stride nwin).  A sequence's
 // state comes from state_in at its first chunk and from `carry` otherwise, and
 // goes to state_out after its last chunk and to `carry` otherwise.
-// With one slot the copy of chunk c+1 waits for a second barrier per chunk, which
-// each wave reaches once it has read chunk c's slot.
-__device__ __forceinline__ void slot_read_done() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads have returned
-  __builtin_amdgcn_s_barrier();
-}
-
 template <int NS>
 __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, const unsigned char* ws, int nwin,
                                                              int nw, float* carry) {
   using L = ChainLds<NS>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, h = lane >> 5;
+  const int l16 = lane & 15, g4 = lane >> 4;
   // Workgroups are handed to the 8 XCDs round-robin by linear index; when the
   // (slot, head) count is a multiple of 8, the 4 strips of a head get indices
   // that are equal modulo 8, so they share one XCD's L2 for the head's inputs.
@@ -721,11 +759,6 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
   const int lofs = lo - c0;
   const float* state_in = lo == cs ? a.state_in : carry;
   float* state_out = hi == ce ? a.state_out : carry;
-  // roles (one wave per SIMD): wave 1 carries the state of the strip, wave 0 produces
-  // its outputs, wave 2 copies the next chunks' inputs into LDS
-  const int role = wv == 2 ? 2 : (wv == 1 ? 0 : 1);
-  const int col = 32 * strip + l32;  // this lane's value column
-  uint16_t* go = static_cast<uint16_t*>(a.o);
 
   const int nchunk = hi - lo;
   const unsigned char* regK = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WH_BYTES;
@@ -734,243 +767,132 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
   auto copy_chunk = [&](int cl) {
     unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
     const unsigned char* wsh = wsh_of(cl);
+    const unsigned char* wsk = wsk_of(cl);
 #pragma unroll
     for (int m = 0; m < kSlotBlocks; ++m)
-      __builtin_amdgcn_global_load_lds(slot_src(m, wsh, strip) + 16 * lane, slot + 1024 * m, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(slot_src(m, wsh, wsk, strip) + 16 * lane, slot + 1024 * m, 16, 0, 0);
   };
 
-  // Each role runs its own chunk loop (same trip count, one barrier per chunk),
-  // so that the registers one role carries across chunks are free in the others.
-  if (role == 0) {
-    floatx16 Ms[4];
-    halfx8 Mfr[8];
+  // Waves 0 and 1 each carry 16 value columns of the strip (32 strip + 16 wave ..)
+  // and form their outputs; wave 2 copies.  The three waves sit on three SIMDs.
+  if (wv < 2) {
+    const int sh = wv;
+    const int col = 32 * strip + 16 * sh + l16;   // this lane's value column
+    floatx4 Ms[8];     // M rows 16dt + 4g + v, column col
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < 8; ++dt) {
       if (state_in) {
         const float* sp = state_in + static_cast<int64_t>(bhv) * DK * DK;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) Ms[dt][v] = sp[(32 * dt + acc_row(v, h)) * DK + col];
+        for (int v = 0; v < 4; ++v) Ms[dt][v] = sp[(16 * dt + 4 * g4 + v) * DK + col];
       } else {
-        Ms[dt] = zero16();
+        Ms[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
     }
+    halfx8 Mfr[4];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      Mfr[ks] = acc_frag_h(Ms[ks >> 1], ks & 1);
-      *reinterpret_cast<halfx8*>(smem + L::kMf + ks * 1024 + lane * 16) = Mfr[ks];
-    }
+    for (int ks = 0; ks < 4; ++ks) Mfr[ks] = stack_h(Ms[2 * ks], Ms[2 * ks + 1]);
+    uint16_t* go = static_cast<uint16_t*>(a.o) + tok0 * a.so + hv * DK + 32 * strip + 16 * sh + 4 * g4;
     __syncthreads();
     for (int cl = 0; cl < nchunk; ++cl) {
       unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
       const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
-      unsigned char* sUf = smem + L::kUf + (cl & 1) * 4096;
-      unsigned char* sMf = smem + L::kMf + ((cl + 1) & 1) * 8192;
-      // ---- U = U0 - W M (U0 enters as the accumulator) ; publish U ----------
-      // all reads are issued before the first use: the gate, U0, then the -W
-      // fragments in the order the products take them
+      // The step's operand fragments are read kAhead ahead of their products
+      // (kFragOff), across the three phases below.
+      auto rd = [&](int jf) { return *reinterpret_cast<const halfx8*>(slot + kFragOff[jf] + lane * 16); };
       const float gC = sSc[64];
+      const halfx8 u0a = *reinterpret_cast<const halfx8*>(slot + L::kU0 + sh * 2048 + lane * 32);
+      const halfx8 u0b = *reinterpret_cast<const halfx8*>(slot + L::kU0 + sh * 2048 + lane * 32 + 16);
+      float gam[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) gam[ct] = sSc[16 * ct + l16];
+      halfx8 F[kNFrag];
+#pragma unroll
+      for (int jf = 0; jf < kAhead; ++jf) F[jf] = rd(jf);
       __builtin_amdgcn_sched_barrier(0);
-      halfx8 x[4];
+      floatx4 U[4], O[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const halfx8*>(slot + L::kU0 + (i >> 1) * 2048 + lane * 32 + (i & 1) * 16);
-      halfx8 Af[16];
+      for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
+        for (int v = 0; v < 4; ++v) U[rt][v] = static_cast<float>(rt < 2 ? u0a[4 * rt + v] : u0b[4 * (rt - 2) + v]);
+        O[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      // ---- U = U0 - W M and O^T = M^T Q^T, interleaved ---------------------------
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          Af[rt * 8 + ks] = *reinterpret_cast<const halfx8*>(slot + L::kW + (rt * 8 + ks) * 1024 + lane * 16);
-      __builtin_amdgcn_sched_barrier(0);
-      floatx16 U[2];
+      for (int jf = 0; jf < 32; ++jf) {
+        F[jf + kAhead] = rd(jf + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+        const int x = (jf >> 1) & 3, ks = jf >> 3;
+        if (jf & 1) O[x] = mfma16h(Mfr[ks], F[jf], O[x]);
+        else U[x] = mfma16h(F[jf], Mfr[ks], U[x]);
+        if (jf == 16) {
+          // the state's decay, on the vector unit while the products run
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          U[rt][e] = static_cast<float>(x[2 * rt][e]);
-          U[rt][8 + e] = static_cast<float>(x[2 * rt + 1][e]);
+          for (int dt = 0; dt < 8; ++dt) Ms[dt] *= gC;
         }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) U[rt] = mfma32h(Af[rt * 8 + ks], Mfr[ks], U[rt]);
-      // the state's decay runs on the vector unit while the products occupy the
-      // matrix unit
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) Ms[dt] *= gC;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // Kd fragments for the update, read while the last products drain
+      halfx8 Uf[2];
+      Uf[0] = stack_h(U[0], U[1]);
+      Uf[1] = stack_h(U[2], U[3]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Af[i] = *reinterpret_cast<const halfx8*>(slot + L::kKd + i * 1024 + lane * 16);
-      if constexpr (NS == 1) slot_read_done();
-      halfx8 Uf[4];
+      for (int ct = 0; ct < 4; ++ct) O[ct] *= gam[ct];
+      // ---- M <- gamma_63 M + Kd U -------------------------------------------------
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        Uf[ks] = acc_frag_h(U[ks >> 1], ks & 1);
-        *reinterpret_cast<halfx8*>(sUf + ks * 1024 + lane * 16) = Uf[ks];
-      }
-      // ---- M <- gamma_63 M + Kd U, two state tiles at a time so that the first
-      //      pair's fragments are formed while the second pair runs ; publish M ----
-#pragma unroll
-      for (int dp = 0; dp < 4; dp += 2) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int dt = dp; dt < dp + 2; ++dt) Ms[dt] = mfma32h(Af[dt * 4 + ks], Uf[ks], Ms[dt]);
-#pragma unroll
-        for (int ks = 2 * dp; ks < 2 * dp + 4; ++ks) {
-          Mfr[ks] = acc_frag_h(Ms[ks >> 1], ks & 1);
-          *reinterpret_cast<halfx8*>(sMf + ks * 1024 + lane * 16) = Mfr[ks];
+      for (int jf = 32; jf < 48; ++jf) {
+        if (jf + kAhead < kNFrag) F[jf + kAhead] = rd(jf + kAhead);
+        if constexpr (NS == 1) {
+          if (jf + kAhead == kNFrag - 1) {
+            // the slot's last fragment is in flight: once it is back and every wave is here,
+            // the slot is refilled with chunk cl+1
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        Ms[(jf - 32) & 7] = mfma16h(F[jf], Uf[(jf - 32) >> 3], Ms[(jf - 32) & 7]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      lds_sync();
+      // ---- O^T += U^T P^T: P^T fragment f covers token tile f (chunk step 0) or f - 2 (step 1)
+#pragma unroll
+      for (int f = 0; f < 6; ++f) {
+        const int ct = f < 4 ? f : f - 2;
+        O[ct] = mfma16h(Uf[f < 4 ? 0 : 1], F[48 + f], O[ct]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) Mfr[ks] = stack_h(Ms[2 * ks], Ms[2 * ks + 1]);
+      // outputs: lane holds token 16ct + (lane & 15), value columns 4g..4g+3 of the wave's 16
+      const int ci = lo - cs + cl;   // chunk index inside the sequence
+      const int nval = min(CH, len - ci * CH);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int r = 16 * ct + l16;
+        const uint2 w = {pack_bf16x2(O[ct][0], O[ct][1]), pack_bf16x2(O[ct][2], O[ct][3])};
+        if (r < nval) *reinterpret_cast<uint2*>(go + (static_cast<int64_t>(ci) * CH + r) * a.so) = w;
+      }
+      // slot cl may be refilled once both state waves have passed this barrier
+      __builtin_amdgcn_s_barrier();
     }
     if (state_out) {
       float* sp = state_out + static_cast<int64_t>(bhv) * DK * DK;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sp[(32 * dt + acc_row(v, h)) * DK + col] = Ms[dt][v];
+        for (int v = 0; v < 4; ++v) sp[(16 * dt + 4 * g4 + v) * DK + col] = Ms[dt][v];
     }
-  } else if (role == 1) {
-    halfx8 Bq[16], Bp[FT];  // Q^ fragments of the current chunk, P fragments of the previous one
-#pragma unroll
-    for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(wsk_of(0) + i * 1024 + lane * 16);
-#pragma unroll
-    for (int f = 0; f < FT; ++f) Bp[f] = *reinterpret_cast<const halfx8*>(wsh_of(0) + WH_P + f * 1024 + lane * 16);
-
-    // O_c += U_c^T P_c^T, then the 64 x 32 bf16 tile is staged in LDS over the U
-    // fragments just read (64-byte rows, 16-byte units swizzled by the row so that the
-    // 4-column writes spread over the banks) and stored as 16-byte runs of 8 columns.
-    // The state wave refills that U buffer only after the next barrier.
-    auto finish = [&](floatx16 (&O)[2], int cp) {
-      unsigned char* sO = smem + L::kUf + (cp & 1) * 4096;
-      {
-        const unsigned char* sUf = sO;
-        halfx8 Au[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) Au[ks] = *reinterpret_cast<const halfx8*>(sUf + ks * 1024 + lane * 16);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int f = 0; f < FT; ++f) O[ft_rt(f)] = mfma32h(Au[ft_ks(f)], Bp[f], O[ft_rt(f)]);
-      }
-      if (cp + 1 < nchunk) {
-        const unsigned char* wp = wsh_of(cp + 1) + WH_P;
-#pragma unroll
-        for (int f = 0; f < FT; ++f) Bp[f] = *reinterpret_cast<const halfx8*>(wp + f * 1024 + lane * 16);
-      }
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int r = 32 * rt + l32;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint2 w = {pack_bf16x2(O[rt][4 * j], O[rt][4 * j + 1]), pack_bf16x2(O[rt][4 * j + 2], O[rt][4 * j + 3])};
-          *reinterpret_cast<uint2*>(sO + r * 64 + ((j ^ (r & 3)) * 16) + 8 * h) = w;
-        }
-      }
-      const int ci = lo - cs + cp;   // chunk index inside the sequence
-      const int nval = min(CH, len - ci * CH);
-      uint16_t* obase = go + (tok0 + static_cast<int64_t>(ci) * CH) * a.so + hv * DK + 32 * strip;
-      u16x8 x[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int vi = lane + 64 * m, r = vi >> 2, u = vi & 3;
-        x[m] = *reinterpret_cast<const u16x8*>(sO + r * 64 + ((u ^ (r & 3)) * 16));
-      }
-      if (nval == CH) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int vi = lane + 64 * m, r = vi >> 2, u = vi & 3;
-          *reinterpret_cast<u16x8*>(obase + static_cast<int64_t>(r) * a.so + 8 * u) = x[m];
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int vi = lane + 64 * m, r = vi >> 2, u = vi & 3;
-          if (r < nval) *reinterpret_cast<u16x8*>(obase + static_cast<int64_t>(r) * a.so + 8 * u) = x[m];
-        }
-      }
-    };
-
-    floatx16 Op[2];  // the previous chunk's outputs, waiting for P U
-    __syncthreads();
-    for (int cl = 0; cl < nchunk; ++cl) {
-      unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
-      const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
-      const unsigned char* sMf = smem + L::kMf + (cl & 1) * 8192;
-      const float g0 = sSc[l32], g1 = sSc[32 + l32];
-      if constexpr (NS == 1) slot_read_done();
-      // ---- O^T = M^T Q^^T diag(gamma) + U^T P^T: the M and U fragments serve as A
-      //      operands and Q^, P as B operands, so each lane holds one token and
-      //      runs of four value columns ------------------------------------------
-      floatx16 O[2] = {zero16(), zero16()};
-      {
-        halfx8 Am[8];   // M fragments, all read before the first product
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) Am[ks] = *reinterpret_cast<const halfx8*>(sMf + ks * 1024 + lane * 16);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) O[rt] = mfma32h(Am[ks], Bq[rt * 8 + ks], O[rt]);
-      }
-      // the next chunk's Q^ fragments: a chunk ahead of their use (the last chunk
-      // reloads its own)
-      {
-        const unsigned char* wq = wsk_of(min(cl + 1, nchunk - 1));
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Bq[i] = *reinterpret_cast<const halfx8*>(wq + i * 1024 + lane * 16);
-      }
-      if (cl > 0) finish(Op, cl - 1);
-      Op[0] = O[0] * g0;
-      Op[1] = O[1] * g1;
-      // the first chunk issues no stores; draining its loads here keeps the counts
-      // the compiler waits for at the loop head those of the later chunks, whose
-      // stores need not complete before the next chunk's products
-      if (cl == 0) wait_vm_all();
-      lds_sync();
-    }
-    if (nchunk > 0) finish(Op, nchunk - 1);
-  } else if constexpr (NS == 1) {
-    // one slot: chunk cl+1 is copied once every wave has read chunk cl's
+  } else {
+    // copy wave: chunk cl+1 into the other slot (two slots; slot (cl + 1) % 2 was last
+    // read during chunk cl-1) or, with one slot, once both state waves have read
+    // chunk cl's
     copy_chunk(0);
     wait_vm_all();
     __syncthreads();
     for (int cl = 0; cl < nchunk; ++cl) {
-      __builtin_amdgcn_s_barrier();
-      if (cl + 1 < nchunk) {
-        copy_chunk(cl + 1);
-        wait_vm_all();
-      }
-      __builtin_amdgcn_s_barrier();
-    }
-  } else {
-    // copies run kAhead = slots - 1 chunks ahead
-    constexpr int kAhead = L::kNSlot - 1;
-    static_assert(kAhead == 1 || kAhead == 2, "one or two chunks ahead");
-    copy_chunk(0);
-    if (kAhead == 2 && nchunk > 1) {
-      copy_chunk(1);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSlotBlocks));
-    } else {
+      if constexpr (NS == 1) __builtin_amdgcn_s_barrier();
+      if (cl + 1 < nchunk) copy_chunk(cl + 1);
       wait_vm_all();
-    }
-    __syncthreads();
-    for (int cl = 0; cl < nchunk; ++cl) {
-      // slot (cl + kAhead) % slots was last read during chunk cl-1
-      if (cl + kAhead < nchunk) {
-        copy_chunk(cl + kAhead);
-        // chunk cl+1 has landed
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kAhead - 1) * kSlotBlocks));
-      } else {
-        wait_vm_all();
-      }
-      // barrier without a fence: this wave writes LDS only through its copies, and
-      // the vector memory count above already covers the ones the others read next
+      // this wave writes LDS only through its copies, and the vector memory count
+      // above covers the ones the others read next
       __builtin_amdgcn_s_barrier();
     }
   }
@@ -1064,9 +986,9 @@ size_t chunk_ws_carry_bytes(const RecArgs& a) {
 // most ceil(T/64) + nseq (each sequence ends in at most one partial chunk).
 int chunk_count(const RecArgs& a) { return (a.T + CH - 1) / CH + (a.cu_seqlens ? a.nseq : 0); }
 
-// Prep workgroups resident at once on the 256 CUs: their LDS lets two share a CU
-// up to 19 value heads per key head, one beyond.
-int prep_slots(int G) { return 256 * max(1, min(2, (160 * 1024) / PrepLds::bytes(G))); }
+// Prep workgroups resident at once: their LDS lets two share a CU up to 19 value
+// heads per key head, one beyond.
+int prep_slots(int G) { return device_cu_count() * max(1, min(2, (160 * 1024) / PrepLds::bytes(G))); }
 
 // Chunks per window.  The chain kernel reads a window's operands back from the
 // memory-side last-level cache (256 MB) when they are still there: with the whole
@@ -1166,7 +1088,7 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     // runs one slot per sequence with chunks in the window, which the host does
     // not know; the few it has per window run better with two slots.
     const dim3 grid(slots * a.Hv * (DK / 32));
-    if (!a.cu_seqlens && a.B * a.Hv * (DK / 32) > 256)
+    if (!a.cu_seqlens && a.B * a.Hv * (DK / 32) > device_cu_count())
       hipLaunchKernelGGL(chunk_chain_kernel<1>, grid, dim3(192), ChainLds<1>::kBytes, s, r, c0,
                          static_cast<const unsigned char*>(wsb), nwin, nw, carry);
     else

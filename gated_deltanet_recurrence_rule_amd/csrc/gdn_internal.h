@@ -29,6 +29,11 @@ struct PerDeviceOnce {
   }
 };
 
+// Compute units of the current device (hipDeviceProp_t::multiProcessorCount),
+// read once per device; 256 (MI355X) when no device is visible, so that size
+// queries answer on a host without a GPU.
+int device_cu_count();
+
 // Arguments of the recurrence kernels (prefill and decode share them).
 struct RecArgs {
   int32_t B, T, Hk, Hv, G, D;
@@ -54,6 +59,7 @@ struct RecArgs {
   const float* A_log = nullptr;
   const float* dt_bias = nullptr;
   const int32_t* slots = nullptr;
+  int32_t nslots = 0;      // pool entries: slots outside [0, nslots) skip the row
   // Variable-length batch: nseq sequences packed along the token axis, sequence s
   // holding tokens [cu_seqlens[s], cu_seqlens[s+1]).  The chunked kernels then see
   // B == 1 (one packed token stream); chunks never span two sequences.
@@ -89,6 +95,7 @@ struct LayerArgs {
   const float* dt_bias;
   float* pool;                // [S][Hv][128][128]
   const int32_t* slots;       // [B] or null
+  int32_t nslots;             // S: slots outside [0, S) skip the sequence
   const uint16_t* z;          // [B][sz]
   int64_t sz;
   const uint16_t* norm_w;     // [128]

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(RecShape<D>::NT) void recurrent_kernel(RecArgs a) {
   int64_t sidx = bh;
   if (a.slots) {
     const int slot = a.slots[b];
-    if (slot < 0) return;  // the whole workgroup skips the row
+    if (slot < 0 || slot >= a.nslots) return;  // the whole workgroup skips the row
     sidx = static_cast<int64_t>(slot) * a.Hv + h;
   }
 
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void decode_layer_kernel(LayerArgs a) {
   int slot = b;
   if (a.slots) {
     slot = a.slots[b];
-    if (slot < 0) return;  // the whole workgroup skips the sequence
+    if (slot < 0 || slot >= a.nslots) return;  // the whole workgroup skips the sequence
   }
   const int64_t C = static_cast<int64_t>(2 * a.Hk + a.Hv) * D;
   const int64_t crow = static_cast<int64_t>(slot) * C;   // window pool row of this sequence

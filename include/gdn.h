@@ -254,16 +254,17 @@ gdn_status gdn_gates(int64_t n_tok, int32_t Hv, int32_t dtype, const void* ba, i
  *   - the states live in a caller-owned pool state_pool [S, Hv, Dk, Dv] fp32
  *     (16-byte aligned): sequence b uses entry slots[b] (slots: [B] int32,
  *     device memory), or entry b when slots is NULL.  A negative slot skips
- *     the sequence: neither its state nor its output row is touched.  Two
+ *     the sequence: neither its state nor its output row is touched, and so
+ *     does a slot >= n_slots (n_slots = S, the pool's entry count; slot values
+ *     are device data, so the kernel checks them, not the host).  Two
  *     sequences of one call must not share a slot (their updates would race).
- *     Slot values are not checked against S on the host (they are device
- *     data): every non-negative slot must be < S.
+ *     Without slots the pool needs n_slots >= B (GDN_ERR_SHAPE otherwise).
  * dims->T must be 1; q, k, v, o and flags (GDN_FLAG_QK_L2NORM) as for
  * gdn_decode_step.
  */
 gdn_status gdn_decode_token(const gdn_dims* dims, const void* q, const void* k, const void* v, int32_t ba_dtype,
                             const void* ba, int64_t stride_ba, const float* A_log, const float* dt_bias,
-                            float* state_pool, const int32_t* slots, void* o, void* stream);
+                            float* state_pool, int32_t n_slots, const int32_t* slots, void* o, void* stream);
 
 /*
  * gdn_decode_layer -- one decode token of a whole Gated DeltaNet mixer layer,
@@ -283,10 +284,12 @@ gdn_status gdn_decode_token(const gdn_dims* dims, const void* q, const void* k, 
  *     read from _in and written to _out (distinct buffers; a serving loop
  *     swaps them each step); the key head's q and k windows are written once
  *   ba [B, >= 2*Hv] (stride_ba); A_log, dt_bias [Hv] fp32
- *   state_pool [S, Hv, D, D] fp32, updated in place
- *   slots [B] int32 device memory or NULL (entry b); a negative slot skips the
- *     sequence (nothing of it is read or written); slots must be distinct and
- *     < S (device data, not checked on the host)
+ *   state_pool [S, Hv, D, D] fp32, updated in place; n_slots = S, the entry
+ *     count of both pools
+ *   slots [B] int32 device memory or NULL (entry b; then n_slots >= B); a
+ *     negative slot, or one >= n_slots, skips the sequence (nothing of it is
+ *     read or written; the kernel checks, since slots are device data); slots
+ *     must be distinct
  *   z [B, >= Hv*D] (stride_z); norm_w [D]; out [B, >= Hv*D] (stride_out)
  *   o [B, >= Hv*D] (stride_o) receives the output before the norm, or NULL
  * Alignment: state_pool and conv_w 16 bytes; x, conv_state_in and
@@ -296,6 +299,7 @@ typedef struct {
   int32_t B, Hk, Hv, D;
   uint32_t flags;               /* GDN_FLAG_QK_L2NORM or 0 */
   float q_scale, l2_eps, norm_eps;
+  int32_t n_slots;              /* entries S of state_pool and of the window pools */
   const void* x;
   int64_t stride_x;
   const void* conv_w;

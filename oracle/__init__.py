@@ -61,23 +61,28 @@ def lib():
     if _lib is None:
         if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
             build()
-        L = ctypes.CDLL(_LIB_PATH)
-        p = ctypes.c_void_p
-        i64, i32 = ctypes.c_int64, ctypes.c_int32
-        L.gdn_oracle_recurrence.argtypes = [ctypes.POINTER(_Dims), p, p, p, p, p, p, i64, p, p, p, i32]
-        L.gdn_oracle_recurrence.restype = ctypes.c_int
-        L.gdn_oracle_conv1d_silu.argtypes = [i64, i64, i64, i64, i64, i32, p, i32, p, i32, p,
-                                             i64, i64, i64, i64, i64, p, p, i32]
-        L.gdn_oracle_conv1d_silu.restype = ctypes.c_int
-        L.gdn_oracle_gated_rmsnorm.argtypes = [i64, i64, i32, p, i32, p, i32, p, ctypes.c_double,
-                                               i64, p, p, i32]
-        L.gdn_oracle_gated_rmsnorm.restype = ctypes.c_int
-        L.gdn_oracle_gates.argtypes = [i64, i64, i64, i32, p, i32, p, p, p, p]
-        L.gdn_oracle_gates.restype = ctypes.c_int
-        L.gdn_oracle_round_bf16.argtypes = [p, p, i64]
-        L.gdn_oracle_round_bf16.restype = None
-        _lib = L
+        _lib = load_library(_LIB_PATH)
     return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Loads a build of gdn_oracle.c from ``path`` and declares its entry points."""
+    L = ctypes.CDLL(path)
+    p = ctypes.c_void_p
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+    L.gdn_oracle_recurrence.argtypes = [ctypes.POINTER(_Dims), p, p, p, p, p, p, i64, p, p, p, i32]
+    L.gdn_oracle_recurrence.restype = ctypes.c_int
+    L.gdn_oracle_conv1d_silu.argtypes = [i64, i64, i64, i64, i64, i32, p, i32, p, i32, p,
+                                         i64, i64, i64, i64, i64, p, p, i32]
+    L.gdn_oracle_conv1d_silu.restype = ctypes.c_int
+    L.gdn_oracle_gated_rmsnorm.argtypes = [i64, i64, i32, p, i32, p, i32, p, ctypes.c_double,
+                                           i64, p, p, i32]
+    L.gdn_oracle_gated_rmsnorm.restype = ctypes.c_int
+    L.gdn_oracle_gates.argtypes = [i64, i64, i64, i32, p, i32, p, p, p, p]
+    L.gdn_oracle_gates.restype = ctypes.c_int
+    L.gdn_oracle_round_bf16.argtypes = [p, p, i64]
+    L.gdn_oracle_round_bf16.restype = None
+    return L
 
 
 def _code(a: np.ndarray) -> int:

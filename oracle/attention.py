@@ -23,10 +23,12 @@ and "Le RoPE partiel"; RMSNorm as in "Les briques d'un reseau de neurones", 4:
   reads key/value head h // 6; causal softmax(q k^T * scale) v with scale
   1/sqrt(D) (reading A5);
 * the output of each query head is multiplied by sigmoid(gate) (reading A1);
-* q and k enter the attention products as bf16 values, rounded once to
-  nearest-even after norm and RoPE: the page's "Le float32 n'est pas un
-  detail" keeps only the recurrent state in float32 and the rest of the model
-  in BF16 (reading A6).  ``qk_bf16=False`` keeps them in fp64.
+* k enters the attention products as a bf16 value, rounded once to
+  nearest-even after norm and RoPE, because the key cache holds it that way:
+  the page's "GQA a 6:1" counts 4,096 bytes of cache per token and layer
+  (4 key/value heads x 256 x 2 x 2 bytes), i.e. two-byte keys (reading A6).
+  q is not cached and stays fp64 here (``q_bf16=True`` rounds it too, as a
+  kernel that multiplies bf16 operands does); ``k_bf16=False`` keeps k fp64.
 
 Inputs may be float64, float32, or uint16 holding bf16 bit patterns (widened
 exactly).
@@ -72,16 +74,18 @@ def to_bf16(x):
     return widen(round_bf16(x))
 
 
-def prepare(qg, k, v, q_norm_w, k_norm_w, pos, *, rot_dim=64, theta=1e7, eps=1e-6, qk_bf16=True):
+def prepare(qg, k, v, q_norm_w, k_norm_w, pos, *, rot_dim=64, theta=1e7, eps=1e-6, q_bf16=False, k_bf16=True):
     """Per-head norm and RoPE of q and k.  qg [B, T, Hq, 2, D]; k, v [B, T, Hkv, D];
-    pos [B, T] or [T].  Returns (q, gate, k, v) as float64 with q and k rotated (and
-    rounded to bf16 values when ``qk_bf16``)."""
+    pos [B, T] or [T].  Returns (q, gate, k, v) as float64 with q and k rotated (each
+    rounded to bf16 values when its flag is set)."""
     qg = widen(qg)
     q, gate = qg[..., 0, :], qg[..., 1, :]
     q = rope(rms_norm(q, q_norm_w, eps), pos, rot_dim, theta)
     kr = rope(rms_norm(k, k_norm_w, eps), pos, rot_dim, theta)
-    if qk_bf16:
-        q, kr = to_bf16(q), to_bf16(kr)
+    if q_bf16:
+        q = to_bf16(q)
+    if k_bf16:
+        kr = to_bf16(kr)
     return q, gate, kr, widen(v)
 
 
@@ -100,7 +104,7 @@ def attend(q, gate, k, v, n_keys, scale):
 
 
 def prefill(qg, k, v, q_norm_w, k_norm_w, *, rot_dim=64, theta=1e7, eps=1e-6, scale=None, rows=None,
-            qk_bf16=True):
+            q_bf16=False, k_bf16=True):
     """Causal prefill of B sequences of T tokens from position 0.  Returns
     (o [B, T, Hq, D] (only ``rows``, a list of (b, t), when given: [n, Hq, D]),
     k_cache [B, T, Hkv, D] rotated keys, v [B, T, Hkv, D])."""
@@ -108,7 +112,7 @@ def prefill(qg, k, v, q_norm_w, k_norm_w, *, rot_dim=64, theta=1e7, eps=1e-6, sc
     B, T, Hq, _, D = qg.shape
     scale = 1.0 / np.sqrt(D) if scale is None else scale
     q, gate, kr, vv = prepare(qg, k, v, q_norm_w, k_norm_w, np.arange(T), rot_dim=rot_dim, theta=theta, eps=eps,
-                              qk_bf16=qk_bf16)
+                              q_bf16=q_bf16, k_bf16=k_bf16)
     if rows is not None:
         return np.stack([attend(q[b, t], gate[b, t], kr[b], vv[b], t + 1, scale) for b, t in rows]), kr, vv
     o = np.empty((B, T, Hq, D))
@@ -118,8 +122,31 @@ def prefill(qg, k, v, q_norm_w, k_norm_w, *, rot_dim=64, theta=1e7, eps=1e-6, sc
     return o, kr, vv
 
 
+def prefill_dense(qg, k, v, q_norm_w, k_norm_w, *, rot_dim=64, theta=1e7, eps=1e-6, scale=None, q_bf16=False,
+                  k_bf16=True):
+    """The causal prefill of ``prefill`` for every row at once: per sequence and query head,
+    softmax(q k^T * scale) with the future masked, times v, times sigmoid(gate), written as
+    whole matrices.  Returns o [B, T, Hq, D]."""
+    qg = widen(qg)
+    B, T, Hq, _, D = qg.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    q, gate, kr, vv = prepare(qg, k, v, q_norm_w, k_norm_w, np.arange(T), rot_dim=rot_dim, theta=theta, eps=eps,
+                              q_bf16=q_bf16, k_bf16=k_bf16)
+    Hkv = kr.shape[2]
+    G = Hq // Hkv
+    future = np.triu(np.ones((T, T), dtype=bool), 1)
+    o = np.empty((B, T, Hq, D))
+    for b in range(B):
+        for h in range(Hq):
+            s = (q[b, :, h] @ kr[b, :, h // G].T) * scale
+            s[future] = -np.inf
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            o[b, :, h] = (p @ vv[b, :, h // G]) / p.sum(axis=1, keepdims=True)
+    return o / (1.0 + np.exp(-gate))
+
+
 def decode(qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, lens, *, rot_dim=64, theta=1e7, eps=1e-6, scale=None,
-           qk_bf16=True):
+           q_bf16=False, k_bf16=True):
     """One new token per sequence at position lens[b]: qg [B, Hq, 2, D]; k, v
     [B, Hkv, D]; k_cache, v_cache [B, S, Hkv, D] (rotated keys, values) holding
     lens[b] tokens.  Returns (o [B, Hq, D], new rotated key [B, Hkv, D])."""
@@ -133,7 +160,7 @@ def decode(qg, k, v, q_norm_w, k_norm_w, k_cache, v_cache, lens, *, rot_dim=64, 
         n = int(lens[b])
         q, gate, kr, vv = prepare(qg[b][None, None], widen(k)[b][None, None], widen(v)[b][None, None],
                                   q_norm_w, k_norm_w, np.array([n]), rot_dim=rot_dim, theta=theta, eps=eps,
-                                  qk_bf16=qk_bf16)
+                                  q_bf16=q_bf16, k_bf16=k_bf16)
         keys = np.concatenate([kc[b, :n], kr[0]], axis=0)
         vals = np.concatenate([vc[b, :n], vv[0]], axis=0)
         o[b] = attend(q[0, 0], gate[0, 0], keys, vals, n + 1, scale)

@@ -52,15 +52,12 @@ def round_bf16_f64(x: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def out_metrics(o_gpu: np.ndarray, o_ref: np.ndarray, bf16: bool, upstream_rel: float = 0.0) -> dict:
-    """upstream_rel: extra allowance |o_ref| * upstream_rel for a bf16 rounding
-    that an earlier API boundary forced on this output's input (one bf16 ulp of
-    an input that enters the output linearly moves it by at most 2^-7 |o|)."""
+def out_metrics(o_gpu: np.ndarray, o_ref: np.ndarray, bf16: bool) -> dict:
     rms = float(np.sqrt(np.mean(o_ref ** 2)))
     err = np.abs(o_gpu - o_ref)
     m = dict(rms=rms, max_err_rms=float(err.max() / rms), rms_err_rms=float(np.sqrt(np.mean(err ** 2)) / rms))
     if bf16:
-        allow = ulp_bf16(o_ref) + upstream_rel * np.abs(o_ref)
+        allow = ulp_bf16(o_ref)
         m["excess_rms"] = float(np.maximum(0.0, err - allow).max() / rms)
         m["floor_rms"] = float(np.abs(round_bf16_f64(o_ref) - o_ref).max() / rms)
         m["metric"] = m["excess_rms"]
@@ -69,16 +66,17 @@ def out_metrics(o_gpu: np.ndarray, o_ref: np.ndarray, bf16: bool, upstream_rel: 
     return m
 
 
-def assert_out(o_gpu, o_ref, bf16: bool, tol: float = OUT_TOL, what: str = "o", upstream_rel: float = 0.0):
-    m = out_metrics(np.asarray(o_gpu, np.float64), np.asarray(o_ref, np.float64), bf16, upstream_rel)
+def assert_out(o_gpu, o_ref, bf16: bool, tol: float = OUT_TOL, what: str = "o"):
+    m = out_metrics(np.asarray(o_gpu, np.float64), np.asarray(o_ref, np.float64), bf16)
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite values"
     assert m["metric"] <= tol, f"{what}: {m}"
     return m
 
 
-def assert_out_rows(o_gpu, o_ref, tol: float = OUT_TOL, what: str = "o"):
+def assert_out_rows(o_gpu, o_ref, tol: float = OUT_TOL, what: str = "o", allow=None):
     """Attention outputs, bf16: per row r (the last axis, one query head of one token)
-    max_i max(0, |o_gpu,ri - o_ref,ri| - ulp_bf16(o_ref,ri)) <= tol * RMS(o_ref,r).
+    max_i max(0, |o_gpu,ri - o_ref,ri| - ulp_bf16(o_ref,ri) - allow_ri) <= tol * RMS(o_ref,r),
+    where ``allow`` (default 0) is an extra per-element allowance the caller derives.
     A row is a convex combination of the visible values, so its scale ranges from |v|
     (a row that sees one key) to about |v| / sqrt(n) (n keys of random direction); the
     kernel's own rounding (softmax weights to bf16 for the product, fp32 sums) errs in
@@ -87,7 +85,8 @@ def assert_out_rows(o_gpu, o_ref, tol: float = OUT_TOL, what: str = "o"):
     o_ref = np.asarray(o_ref, np.float64)
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite values"
     rms = np.sqrt(np.mean(o_ref ** 2, axis=-1, keepdims=True))
-    excess = np.maximum(0.0, np.abs(o_gpu - o_ref) - ulp_bf16(o_ref)) / rms
+    extra = 0.0 if allow is None else np.asarray(allow, np.float64)
+    excess = np.maximum(0.0, np.abs(o_gpu - o_ref) - ulp_bf16(o_ref) - extra) / rms
     worst = np.unravel_index(np.argmax(excess), excess.shape)
     m = dict(max_excess_row_rms=float(excess.max()), worst=tuple(int(i) for i in worst),
              rms_err_row_rms=float(np.sqrt(np.mean((np.abs(o_gpu - o_ref) / rms) ** 2))))

@@ -202,7 +202,7 @@ def test_gates_and_decode_token_argument_errors():
     def tok(d, **kw):
         return L.gdn_decode_token(ctypes.byref(d), FAKE, FAKE, FAKE, kw.get("bdt", B.GDN_BF16), kw.get("ba", FAKE),
                                   kw.get("s", 12), kw.get("A", FAKE), kw.get("dtb", FAKE), kw.get("pool", FAKE),
-                                  kw.get("slots", None), FAKE, None)
+                                  kw.get("ns", 8), kw.get("slots", None), FAKE, None)
     assert tok(dims(T=2)) == B.GDN_ERR_SHAPE                  # one token per sequence
     assert tok(dims(T=1), s=11) == B.GDN_ERR_SHAPE            # stride_ba below 2*Hv (Hv = 6)
     assert tok(dims(T=1), bdt=5) == B.GDN_ERR_SHAPE
@@ -210,17 +210,20 @@ def test_gates_and_decode_token_argument_errors():
     assert tok(dims(T=1), dtb=None) == B.GDN_ERR_NULL
     assert tok(dims(T=1), pool=ctypes.c_void_p(0x10008)) == B.GDN_ERR_ALIGN
     assert tok(dims(T=1), slots=FAKE_ODD) == B.GDN_ERR_ALIGN
+    assert tok(dims(T=1), ns=-1) == B.GDN_ERR_SHAPE
+    assert tok(dims(T=1, B=4), ns=3) == B.GDN_ERR_SHAPE           # no slot table: one entry per sequence
     assert tok(dims(T=1, B=0)) == B.GDN_OK
 
 
 def test_decode_layer_arguments():
     L = B.lib()
-    # gdn_decode_layer_args: 4 x int32, uint32, 3 x float, then 18 pointer / int64 fields
-    assert ctypes.sizeof(B.GdnDecodeLayerArgs) == 176
-    assert B.GdnDecodeLayerArgs.x.offset == 32 and B.GdnDecodeLayerArgs.stride_o.offset == 168
+    # gdn_decode_layer_args: 4 x int32, uint32, 3 x float, int32 n_slots, then 18 pointer / int64 fields
+    assert ctypes.sizeof(B.GdnDecodeLayerArgs) == 184
+    assert B.GdnDecodeLayerArgs.n_slots.offset == 32
+    assert B.GdnDecodeLayerArgs.x.offset == 40 and B.GdnDecodeLayerArgs.stride_o.offset == 176
 
     def args(**kw):
-        a = B.GdnDecodeLayerArgs(2, 2, 6, 128, 1, 1.0, 1e-6, 1e-6, FAKE, 10 * 128, FAKE, FAKE,
+        a = B.GdnDecodeLayerArgs(2, 2, 6, 128, 1, 1.0, 1e-6, 1e-6, 4, FAKE, 10 * 128, FAKE, FAKE,
                                  ctypes.c_void_p(0x20000), FAKE, 12, FAKE, FAKE, FAKE, None, FAKE, 768, FAKE, FAKE,
                                  768, None, 0)
         for k_, v_ in kw.items():
@@ -238,6 +241,8 @@ def test_decode_layer_arguments():
     assert args(state_pool=0x10008) == B.GDN_ERR_ALIGN
     assert args(out=0x10001) == B.GDN_ERR_ALIGN                    # bf16 needs 2-byte alignment
     assert args(conv_w=0x10008) == B.GDN_ERR_ALIGN                 # conv weights: 16 bytes
+    assert args(n_slots=-1) == B.GDN_ERR_SHAPE
+    assert args(n_slots=1) == B.GDN_ERR_SHAPE                      # no slot table: one entry per sequence
     assert args(stride_x=10 * 128 + 1) == B.GDN_ERR_ALIGN          # word loads of channel pairs
     assert args(B=0) == B.GDN_OK
 

@@ -1,22 +1,25 @@
 """The five workload configurations at their full sizes, in the launch
 configuration bench.py times, checked against the fp64 oracle.
 
-Large configs are checked on sampled (sequence, value head) pairs that the
+The block config is checked on sampled (sequence, value head) pairs that the
 oracle recomputes over every token (heads are independent, so a sampled head
-is exact, not an approximation).  Inputs come from the seeded generators in
+is exact, not an approximation); every other config is checked on every head.
+Inputs come from the seeded generators in
 gated_deltanet_recurrence_rule_amd.workloads.
 
   tiny      batch 1, T=64, 1/1 heads, D=16, fp32 -- every output and the state
-  prefill4k batch 1, T=4096, 16/48 heads, D=128, bf16 -- 8 sampled heads
-  decode    64 sequences, 48 heads of 128x128 fp32 state, 256 steps --
-            8 sampled (sequence, head) pairs, outputs at every step, state
-            after steps 1, 16 and 256; both gate recipes
-  long      batch 1, T=262144 -- 2 sampled heads; also two halves of 131072
+  prefill4k batch 1, T=4096, 16/48 heads, D=128, bf16 -- all 48 heads
+  decode    64 sequences, 48 heads of 128x128 fp32 state, 256 steps -- all
+            3072 (sequence, head) pairs: outputs at every step, state after
+            steps 1, 16 and 256; both gate recipes
+  long      batch 1, T=262144 -- all 48 heads; also two halves of 131072
             tokens chained through the state equal one pass
   block     batch 4, T=32768, 16/128 heads: conv+SiLU -> prefill with the L2
-            flag -> gated RMSNorm x swish(z); sampled heads end to end, with
-            the oracle rounding to bf16 exactly where the API hands a bf16
-            tensor on (the conv output, the prefill output)
+            flag -> gated RMSNorm x swish(z) on sampled heads, each stage
+            checked against the oracle applied to the bf16 tensor the previous
+            stage handed on through the API (the conv output y, the prefill
+            output o), so that every comparison is held to the stated bound
+            with no allowance for upstream rounding
 """
 import os
 
@@ -26,7 +29,7 @@ import pytest
 import oracle
 from gated_deltanet_recurrence_rule_amd import binding as G
 from gated_deltanet_recurrence_rule_amd import workloads as W
-from helpers import assert_out, assert_state, conv_abs_sum, conv_tol, to_dev, to_host
+from helpers import assert_out, assert_state, conv_abs_sum, conv_tol, to_dev, to_host, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 NTHR = min(16, os.cpu_count() or 1)
@@ -57,17 +60,23 @@ def test_cfg_tiny_full():
     print(f"tiny: max err/RMS {m['max_err_rms']:.2e}, state {e:.2e}")
 
 
-def _sampled_prefill_check(p, sel, o_dev, so_dev, tag):
+def _prefill_check(p, sel, o_dev, so_dev, tag, ref=None):
+    """Checks heads ``sel`` (flat b*Hv + h) of a prefill against the oracle over every token;
+    returns the oracle's (o, state) so that a second check can reuse them."""
     Hv, D, T = p["Hv"], p["D"], p["T"]
-    orf, srf = oracle.recurrence(p["q"], p["k"], p["v"], p["log_alpha"], p["beta"], p["Hk"], Hv, None,
-                                 sel=sel, n_threads=NTHR)
+    if ref is None:
+        ref = oracle.recurrence(p["q"], p["k"], p["v"], p["log_alpha"], p["beta"], p["Hk"], Hv, None,
+                                sel=sel, n_threads=NTHR)
+    orf, srf = ref
     og = o_dev.view(p["B"], T, Hv, D)
+    worst_o, worst_s = 0.0, 0.0
     for i, bh in enumerate(sel):
         b, h = divmod(int(bh), Hv)
         m = assert_out(to_host(og[b, :, h, :]), orf[i], bf16=True, what=f"{tag} o head {bh}")
         e = assert_state(to_host(so_dev[b, h]), srf[i], what=f"{tag} state head {bh}")
-        print(f"{tag} head {bh}: excess/RMS {m['excess_rms']:.2e} (literal {m['max_err_rms']:.2e}, "
-              f"bf16 floor {m['floor_rms']:.2e}), state {e:.2e}")
+        worst_o, worst_s = max(worst_o, m["excess_rms"]), max(worst_s, e)
+    print(f"{tag}: {len(sel)} heads, worst output excess/RMS {worst_o:.2e}, worst state {worst_s:.2e}")
+    return ref
 
 
 def test_cfg_prefill4k_full():
@@ -78,41 +87,48 @@ def test_cfg_prefill4k_full():
     o = G.gdn_prefill(to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"]), to_dev(p["log_alpha"]),
                       to_dev(p["beta"]), None, so, Hk=Hk, Hv=Hv)
     torch.cuda.synchronize()
-    _sampled_prefill_check(p, [0, 7, 13, 20, 26, 33, 41, 47], o, so, "prefill4k")
+    _prefill_check(p, list(range(B * Hv)), o, so, "prefill4k")
 
 
 @pytest.mark.parametrize("recipe", ["qwen", "tiny"])
 def test_cfg_decode_full(recipe):
+    """All 64 x 48 (sequence, head) pairs: the oracle advances every state in fp64 step by step;
+    every output row is checked at every step, every state after steps 1, 16 and 256."""
     torch = _torch()
     B, Hk, Hv, D, steps = 64, 16, 48, 128, 256
     pool = W.decode_pool(B, Hv, D)
-    sel = np.array([0, 101, 777, 1500, 2047, 2300, 2999, 3071], np.int64)   # b*Hv + h
     state = to_dev(pool)
-    ref = pool.reshape(B * Hv, D, D)[sel].copy()
-    sb, sh = sel // Hv, sel % Hv
+    ref = pool.astype(np.float64)
     o = torch.empty((B, Hv * D), dtype=torch.bfloat16, device="cuda")
+    worst_o, worst_s = 0.0, 0.0
     for s in range(steps):
         d = W.decode_step_inputs(s, B=B, Hk=Hk, Hv=Hv, D=D, recipe=recipe)
         G.gdn_decode_step(to_dev(d["q"][:, 0]), to_dev(d["k"][:, 0]), to_dev(d["v"][:, 0]),
                           to_dev(np.ascontiguousarray(d["log_alpha"][:, 0])),
                           to_dev(np.ascontiguousarray(d["beta"][:, 0])), state, o, Hk=Hk, Hv=Hv)
-        # oracle replay of the sampled heads: one sequence-head at a time, from its own state
-        og = to_host(o).reshape(B, Hv, D)
-        for i, (b, h) in enumerate(zip(sb, sh)):
-            hk = h // (Hv // Hk)
-            orf, srf = oracle.recurrence(
-                np.ascontiguousarray(d["q"][b:b + 1, :, hk * D:(hk + 1) * D]),
-                np.ascontiguousarray(d["k"][b:b + 1, :, hk * D:(hk + 1) * D]),
-                np.ascontiguousarray(d["v"][b:b + 1, :, h * D:(h + 1) * D]),
-                np.ascontiguousarray(d["log_alpha"][b:b + 1, :, h:h + 1]),
-                np.ascontiguousarray(d["beta"][b:b + 1, :, h:h + 1]), 1, 1, ref[i][None, None])
-            ref[i] = srf[0]
-            assert_out(og[b, h], orf[0, 0], bf16=True, what=f"decode step {s} head {b},{h}")
+        orf, srf = oracle.recurrence(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], Hk, Hv, ref,
+                                     n_threads=NTHR)
+        ref = srf.reshape(B, Hv, D, D)
+        og = to_host(o).reshape(B * Hv, D)
+        orf = orf.reshape(B * Hv, D)
+        # the stated bound over the step's whole output (all 3072 rows): excess over one bf16 ulp
+        # <= 2e-2 of the oracle output's RMS
+        m = assert_out(og, orf, bf16=True, what=f"decode step {s}")
+        worst_o = max(worst_o, m["excess_rms"])
         if s + 1 in (1, 16, 256):
-            st = to_host(state.view(B * Hv, D, D)[torch.from_numpy(sel).cuda()])
-            for i in range(len(sel)):
-                e = assert_state(st[i], ref[i], what=f"decode state after step {s + 1}")
-            print(f"decode {recipe}: state after step {s + 1}: last rel err {e:.2e}")
+            # diagnostic only: the same excess against each row's own RMS
+            rms = np.sqrt(np.mean(orf ** 2, axis=1))
+            exc = np.maximum(0.0, np.abs(og - orf) - ulp_bf16(orf)).max(axis=1) / rms
+            print(f"decode {recipe} step {s + 1}: excess/RMS {m['excess_rms']:.2e}; per-row worst "
+                  f"{exc.max():.2e} (row RMS {rms[exc.argmax()]:.2e} against {m['rms']:.2e})")
+        if s + 1 in (1, 16, 256):
+            st = to_host(state).reshape(B * Hv, D * D)
+            rr = ref.reshape(B * Hv, D * D)
+            rel = np.linalg.norm(st - rr, axis=1) / np.linalg.norm(rr, axis=1)
+            assert rel.max() <= 1e-3, f"decode state after step {s + 1}: pair {int(rel.argmax())} {rel.max():.3e}"
+            worst_s = max(worst_s, float(rel.max()))
+            print(f"decode {recipe}: after step {s + 1}, all {B * Hv} states within {rel.max():.2e}")
+    print(f"decode {recipe}: worst output excess/RMS {worst_o:.2e}, worst state {worst_s:.2e}")
     del state
     _free()
 
@@ -126,8 +142,8 @@ def test_cfg_long_full_and_two_halves():
     so = torch.empty((B, Hv, D, D), dtype=torch.float32, device="cuda")
     o = G.gdn_prefill(q, k, v, la, be, None, so, Hk=Hk, Hv=Hv)
     torch.cuda.synchronize()
-    sel = [5, 38]
-    _sampled_prefill_check(p, sel, o, so, "long")
+    sel = list(range(B * Hv))
+    ref = _prefill_check(p, sel, o, so, "long")
     # two halves chained through the state equal one pass (and the oracle)
     h = T // 2
     so1 = torch.empty_like(so)
@@ -140,7 +156,7 @@ def test_cfg_long_full_and_two_halves():
     for bh in sel:
         assert_state(to_host(so2[0, bh]), to_host(so[0, bh]), what="two halves vs one pass")
     o12 = torch.cat([o1, o2], dim=1)
-    _sampled_prefill_check(p, sel, o12, so2, "long-halves")
+    _prefill_check(p, sel, o12, so2, "long-halves", ref=ref)
     del q, k, v, o, o1, o2, o12
     _free()
 
@@ -160,34 +176,36 @@ def test_cfg_block_full():
     out = G.gdn_gated_rmsnorm(o.view(B * T, Hv * D), z.view(B * T, Hv * D), to_dev(blk["norm_w"]), 1e-5, H=Hv)
     torch.cuda.synchronize()
     del x
-    for (b, h) in [(0, 0), (1, 37), (2, 71), (3, 127)]:
+    worst = [0.0, 0.0, 0.0]
+    for (b, h) in [(0, 0), (0, 64), (1, 37), (1, 101), (2, 71), (2, 8), (3, 127), (3, 90)]:
         hk = h // (Hv // Hk)
         chans = [(hk * D, "q"), (Hk * D + hk * D, "k"), (2 * Hk * D + h * D, "v")]
-        ybf = {}
+        ygpu = {}
         for c0, name in chans:
+            # the conv stage against the oracle's conv of the same bf16 inputs
             yr, _ = oracle.conv1d_silu(blk["x"], blk["conv_w"], b=b, c0=c0, c1=c0 + D, n_threads=NTHR)
             yg = to_host(y[b, :, c0:c0 + D])
             err = np.abs(yg - yr)
             tol = conv_tol(yr, conv_abs_sum(blk["x"], blk["conv_w"], None, b, c0, c0 + D))
             assert np.all(err <= tol), f"conv {name} head {h}: {(err - tol).max()}"
-            ybf[name] = oracle.round_bf16(yr)   # the API fixes y as bf16
-        orf, srf = oracle.recurrence(ybf["q"][None], ybf["k"][None], ybf["v"][None],
+            # the bf16 tensor the API hands to the prefill
+            ygpu[name] = y[b:b + 1, :, c0:c0 + D].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        # the prefill stage against the oracle's recurrence on the GPU's own conv output
+        orf, srf = oracle.recurrence(ygpu["q"], ygpu["k"], ygpu["v"],
                                      np.ascontiguousarray(blk["log_alpha"][b:b + 1, :, h:h + 1]),
                                      np.ascontiguousarray(blk["beta"][b:b + 1, :, h:h + 1]), 1, 1, None,
                                      l2norm=True, l2_eps=1e-6, n_threads=NTHR)
-        # q, k, v crossed a bf16 API boundary (the conv output): where a token's decay wipes
-        # the state, o_t is beta (k^.q^) v_t, so one ulp of v_t, q_t, k_t moves it by up to
-        # 2^-7 + 2^-8 + 2^-8 of |o_t|
-        m = assert_out(to_host(o[b, :, h * D:(h + 1) * D]), orf[0], bf16=True, what=f"block prefill {b},{h}",
-                       upstream_rel=2.0 ** -6)
+        m = assert_out(to_host(o[b, :, h * D:(h + 1) * D]), orf[0], bf16=True, what=f"block prefill {b},{h}")
         e = assert_state(to_host(so[b, h]), srf[0], what=f"block state {b},{h}")
-        obf = oracle.round_bf16(orf[0])          # the API fixes o as bf16
+        # the norm stage against the oracle's norm of the GPU's own bf16 prefill output
+        ogpu = o[b, :, h * D:(h + 1) * D].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         zr = np.ascontiguousarray(blk["z"][b, :, h * D:(h + 1) * D])
-        yn = oracle.gated_rmsnorm(obf, zr, blk["norm_w"], 1e-5, n_threads=NTHR)
-        # the norm's input o crossed a bf16 API boundary (2^-7) on top of the conv's (2^-6)
+        yn = oracle.gated_rmsnorm(ogpu, zr, blk["norm_w"], 1e-5, n_threads=NTHR)
         mn = assert_out(to_host(out.view(B, T, Hv * D)[b, :, h * D:(h + 1) * D]), yn, bf16=True,
-                        what=f"block out {b},{h}", upstream_rel=2.0 ** -7 + 2.0 ** -6)
+                        what=f"block out {b},{h}")
+        worst = [max(worst[0], m["excess_rms"]), max(worst[1], e), max(worst[2], mn["excess_rms"])]
         print(f"block head {b},{h}: prefill excess {m['excess_rms']:.2e}, state {e:.2e}, "
               f"out excess {mn['excess_rms']:.2e} (literal {mn['max_err_rms']:.2e})")
+    print(f"block: worst prefill excess {worst[0]:.2e}, state {worst[1]:.2e}, norm excess {worst[2]:.2e}")
     del y, o, z, out
     _free()

@@ -51,6 +51,9 @@ CHUNK_CASES = [
     (2, 130, 2, 6, "tiny", True, False, 0.5),
     (1, 200, 1, 1, "qwen", False, True, 1.0),
     (1, 257, 2, 6, "qwen", True, False, 1.0),
+    # one short of two chunks, and one short of the 64 chunks of the headline length
+    (1, 127, 1, 3, "qwen", True, False, 1.0),
+    (1, 4095, 2, 6, "qwen", True, False, 1.0),
     # value heads per key head across the prep's groups of three: 4 (3 + 1), 5 (3 + 2), and 64,
     # the most the chunked path takes (21 groups of 3 + 1)
     (1, 100, 1, 4, "qwen", True, False, 1.0),
@@ -172,6 +175,27 @@ def test_prefill_small_workspace_windows(with_state_out):
         assert_out(to_host(o).reshape(B, T, Hv, D), orf, bf16=True)
         if with_state_out:
             assert_state(to_host(so), srf)
+
+
+@pytest.mark.parametrize("nwin", [1, 2, None])
+def test_prefill_state_in_place(nwin):
+    """state_out may be the same pointer as state_in (gdn.h): the chunked path reads the entry
+    state before it writes the final one, also when the sequence runs over several windows (a
+    workspace of one or two chunks) and each window hands the state on through state_out."""
+    torch = _torch()
+    B, T, Hk, Hv, D = 2, 300, 1, 3, 128
+    p = W.problem(4007, B, T, Hk, Hv, D, io="bf16", recipe="qwen", state="normal")
+    orf, srf = oracle_prefill(p, state_in=p["state_in"])
+    q, k, v = to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"])
+    la, be = to_dev(p["log_alpha"]), to_dev(p["beta"])
+    st = to_dev(p["state_in"].astype(np.float32))
+    ws = None
+    if nwin is not None:
+        ws = torch.empty(nwin * B * (Hv * WS_VALUE_HEAD + Hk * WS_KEY_HEAD), dtype=torch.uint8, device="cuda")
+    o = G.gdn_prefill(q, k, v, la, be, st, st, Hk=Hk, Hv=Hv, workspace=ws)
+    torch.cuda.synchronize()
+    assert_out(to_host(o).reshape(B, T, Hv, D), orf, bf16=True)
+    assert_state(to_host(st), srf)
 
 
 def test_prefill_one_slot_chain():
@@ -368,12 +392,12 @@ def test_gates_parity(io):
 @pytest.mark.parametrize("ba_io", ["bf16", "f32"])
 def test_decode_token_gates_and_slots(l2, ba_io):
     """gdn_decode_token: gates formed in the kernel from raw in_proj_ba outputs, states in a
-    pool addressed by a slot table (a permutation with one skipped sequence), against the oracle's
-    activation followed by its recurrence on the gathered states; untouched pool entries and the
-    skipped output row must stay bit-identical."""
+    pool addressed by a slot table (a permutation with a negative slot and one past the pool's
+    end, both skipped), against the oracle's activation followed by its recurrence on the gathered
+    states; untouched pool entries and the skipped output rows must stay bit-identical."""
     torch = _torch()
-    B, Hk, Hv, D, S, steps = 5, 2, 6, 128, 8, 3
-    slots = np.array([6, -1, 2, 0, 7], np.int32)
+    B, Hk, Hv, D, S, steps = 6, 2, 6, 128, 8, 3
+    slots = np.array([6, -1, 2, 0, 7, 8], np.int32)
     rng = np.random.default_rng(53)
     A = np.log(rng.uniform(1.0, 16.0, Hv)).astype(np.float32)
     dt = (rng.standard_normal(Hv) * 0.5).astype(np.float32)
@@ -390,7 +414,7 @@ def test_decode_token_gates_and_slots(l2, ba_io):
                            to_dev(A), to_dev(dt), pool_dev, to_dev(slots), o, Hk=Hk, Hv=Hv, l2norm=l2)
         torch.cuda.synchronize()
         la, be = oracle.gates(ba_in, Hv, A, dt)
-        live = slots >= 0
+        live = (slots >= 0) & (slots < S)
         c = np.ascontiguousarray
         sl = slice(s, s + 1)
         orf, srf = oracle.recurrence(c(p["q"][live][:, sl]), c(p["k"][live][:, sl]), c(p["v"][live][:, sl]),
@@ -445,8 +469,8 @@ def test_decode_layer_fused_parity(l2):
     torch = _torch()
     B, Hk, Hv, D, S, steps = 5, 2, 6, 128, 8, 3
     C = (2 * Hk + Hv) * D
-    slots = np.array([3, 7, -1, 0, 5], np.int32)
-    live = slots >= 0
+    slots = np.array([3, 7, -1, 0, 9], np.int32)   # -1 and 9 (past the 8-entry pools) are skipped
+    live = (slots >= 0) & (slots < S)
     rng = np.random.default_rng(61)
     bf = lambda a: W.f32_to_bf16(np.asarray(a, np.float32))
     A = np.log(rng.uniform(1.0, 16.0, Hv)).astype(np.float32)
@@ -504,3 +528,29 @@ def test_decode_layer_fused_parity(l2):
             else:
                 np.testing.assert_array_equal(written[sl], before[sl])
         cs[(s + 1) % 2] = written.copy()
+
+
+# A seeded grid over the shapes the survey's property test names: batch <= 3, T <= 300, 1 or 2 key
+# heads, 1, 3 or 8 value heads per key head, head width 16 or 128, fp32 or bf16 I/O.  Each case draws
+# its own lengths, gate recipe, initial state, L2 flag and q scale.  bf16 with width 128 runs the
+# chunked kernels; the other cases run the token-serial kernel.
+PROPERTY_GRID = [(Hk, G_, D, io) for Hk in (1, 2) for G_ in (1, 3, 8) for D in (16, 128) for io in ("f32", "bf16")]
+
+
+@pytest.mark.parametrize("Hk,G_,D,io", PROPERTY_GRID)
+def test_property_grid(Hk, G_, D, io):
+    rng = np.random.default_rng(9000 + 100 * Hk + 10 * G_ + D + (io == "bf16"))
+    B = int(rng.integers(1, 4))
+    T = int(rng.integers(1, 301))
+    recipe = "qwen" if rng.random() < 0.5 else "tiny"
+    state = bool(rng.random() < 0.5)
+    l2 = bool(rng.random() < 0.5)
+    qs = float(rng.choice([1.0, 0.5, D ** -0.5]))
+    p = W.problem(int(rng.integers(1, 1 << 30)), B, T, Hk, Hk * G_, D, io=io, recipe=recipe,
+                  state="normal" if state else None, normalise=not l2)
+    og, sg = run_prefill(p, l2=l2, q_scale=qs, state_in=p["state_in"])
+    orf, srf = oracle_prefill(p, l2=l2, q_scale=qs, state_in=p["state_in"])
+    m = assert_out(og, orf, bf16=(io == "bf16"))
+    e = assert_state(sg, srf)
+    print(f"grid B={B} T={T} Hk={Hk} G={G_} D={D} {io} {recipe} state={state} l2={l2} qs={qs:.3f}: "
+          f"out {m['metric']:.2e} state {e:.2e}")

@@ -146,16 +146,28 @@ def test_kv_cache_size_the_pages_print():
 
 
 def test_bf16_operands():
-    # with qk_bf16 (the default) the rotated q and k are bf16 values within half an ulp of the fp64
-    # ones; the cache keys returned are those rounded keys
+    # with q_bf16 / k_bf16 the rotated q and k are bf16 values within half an ulp of the fp64 ones;
+    # by default only k is rounded (the cache holds two-byte keys) and q stays fp64; the cache keys
+    # returned are the rounded keys
     qg, k, v, wq, wk = problem(7, 1, 5, 6, 1, 256)
-    q64, _, k64, _ = A.prepare(qg, k, v, wq, wk, np.arange(5), qk_bf16=False)
-    q16, _, k16, _ = A.prepare(qg, k, v, wq, wk, np.arange(5))
+    q64, _, k64, _ = A.prepare(qg, k, v, wq, wk, np.arange(5), q_bf16=False, k_bf16=False)
+    q16, _, k16, _ = A.prepare(qg, k, v, wq, wk, np.arange(5), q_bf16=True, k_bf16=True)
     for x64, x16 in ((q64, q16), (k64, k16)):
         f32 = x16.astype(np.float32)
         assert np.array_equal(f32.astype(np.float64), x16)
         assert np.all((f32.view(np.uint32) & 0xFFFF) == 0)               # bf16-representable
         m, e = np.frexp(np.abs(x64))
         assert np.all(np.abs(x16 - x64) <= np.ldexp(1.0, e - 9))          # half an ulp (8 significant bits)
+    qd, _, kd, _ = A.prepare(qg, k, v, wq, wk, np.arange(5))
+    np.testing.assert_array_equal(qd, q64)
+    np.testing.assert_array_equal(kd, k16)
     _, kr, _ = A.prefill(qg, k, v, wq, wk)
     np.testing.assert_array_equal(kr, k16)
+
+
+def test_dense_prefill_is_the_row_by_row_definition():
+    # the whole-matrix form used for full-size checks equals the row-by-row softmax definition
+    qg, k, v, wq, wk = problem(8, 2, 37, 12, 2, 256)
+    o_rows, _, _ = A.prefill(qg, k, v, wq, wk, rot_dim=64)
+    o_dense = A.prefill_dense(qg, k, v, wq, wk, rot_dim=64)
+    np.testing.assert_allclose(o_dense, o_rows, rtol=1e-12, atol=1e-12)
