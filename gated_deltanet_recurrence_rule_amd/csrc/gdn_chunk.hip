@@ -39,20 +39,23 @@
 //    accumulator layout of the chain's U.
 //  * chain (one workgroup per sequence, value head and 32-column strip of M,
 //    looping over the window's chunks; columns of M evolve independently).
-//    One wave carries the fp32 strip of M in registers and runs the serial
-//    path: 16 MFMAs for U = U0 - W M, 16 for the update.  A second wave forms
-//    the outputs from the M and U fragments the first publishes in LDS; a
-//    third copies the next operands from the workspace into LDS two chunks
-//    ahead with direct global-to-LDS loads.
+//    Two waves each carry 16 columns of the fp32 strip in registers and run,
+//    per chunk, U = U0 - W M interleaved with O^T = M^T Q^T (32 MFMAs), the
+//    update M <- gamma_63 M + Kd U (16) and O^T += U^T P^T (6), then store
+//    their outputs; a third copies the next chunk's operands from the
+//    workspace into LDS with direct global-to-LDS loads while they work.
 //
 // Precision.  MFMA accumulation is fp32 throughout and the state stays fp32.
 // The Gram products take the bf16 inputs as they are; every other product
 // runs on fp16 operands, each rounded once (in prep: -W, Kd, U0, P, Q^; in
 // the chain: M and U).  fp16 keeps 11 significant bits, which holds the state
 // within a few 1e-4 of the exact result and the outputs well inside their
-// bound; its range (|x| < 65504) bounds the values of v, the state and the
-// intra-chunk matrices this path accepts.
-//
+// bound.  Its range does not bound the inputs: the value-side operands (V,
+// U0, U, M) enter fp16 scaled by powers of two chosen per chunk and 16-column
+// value tile (see kRangeTop), and the key-side ones (-W, Kd, P, Q^) are
+// bounded by the L2-normalised keys and queries and the gates (every decay
+// factor is at most 1).
+
 // MFMA layouts (wave64).  The chunk operands that leave the prep kernel are
 // fragments of v_mfma_f32_16x16x32_f16: A row = B column = lane & 15, and the
 // lane group g = lane >> 4 carries 8 of a k step's 32 contraction indices; the
@@ -86,7 +89,9 @@ constexpr int WH_W = 0;        // -W = -T' diag(gamma rk) K, A operand: fragment
 constexpr int WH_KD = 16384;   // Kd = K^T diag(rk e^{g_63-g}), A operand: fragment dt*2+ks (keys 16dt.., rows 32ks..)
 constexpr int WH_U0 = 32768;   // U0 = T' V as accumulators of U: [value tile 8][lane 64][row tile 4][4 halves]
 constexpr int WH_P = 49152;    // P^T, B operand: 6 fragments (token tile ct, rows 32ks..), see pfrag()
-constexpr int WH_SC = 55296;   // gamma_r (64 floats), gamma_63
+constexpr int WH_SC = 55296;   // gamma_r (64 floats), gamma_63; int32: V scale exponents of the 8 value
+                               // tiles at [65, 73), gamma_63's exponent at 73, the next chunk's V scale
+                               // exponents at [80, 88); [96, 112): the chain's scale hand-over between windows
 constexpr int WH_BYTES = 56320;
 // workspace block per (batch, key head, chunk): Q^T = (diag(rq) Q)^T, B operand: fragment ks*4+ct
 // (keys 32ks.., tokens 16ct..)
@@ -96,6 +101,68 @@ constexpr int WK_BYTES = 16384;
 __device__ __forceinline__ int kperm(int g, int e) { return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4); }
 // the same for a 16-wide k step of 32x32x16 and lane half h (the inverse's 32-block merge)
 __device__ __forceinline__ int kperm32(int h, int e) { return (e < 4) ? 4 * h + e : 8 + 4 * h + (e - 4); }
+// Range of the fp16 operands on the value side.  V, U0, U and the state M enter the
+// fp16 products scaled by powers of two: each 16-column V tile of a chunk by 2^r, r
+// chosen so that its largest magnitude lands in [2^(kRangeTop-3), 2^(kRangeTop+1)) and
+// stored with the chunk's scalings; the chain's M and U by 2^s, s <= r, chosen from
+// the state's measured range (see the chain kernel).  Exponents are multiples of 4, so
+// that values of about unit size keep r = s = 0 and no rescaling at all.  Scaling by a
+// power of two is exact, so the fp32 results are those of unscaled operands; only
+// values smaller than a tile's largest by more than fp16's normal range lose bits.
+constexpr int kRangeTop = 2;
+constexpr int kCheck = 6;   // chunks between two measurements of the chain state's range
+constexpr int kExpLo = -120, kExpHi = 124;   // exponents whose powers of two are normal fp32
+// the multiple of 4 at or below x
+__device__ __forceinline__ int floor4(int x) { return (x >> 2) * 4; }
+
+// Largest x over the wave, in every lane, for x >= 0 as fp32 bits (they compare as
+// integers): the maximum over each row of 16 lanes by DPP, then over the four rows.
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0xB1, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x4E, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x141, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x140, 0xF, 0xF, false)));
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// max(|a|, |b|, |c|) in one instruction (fmaxf would add a NaN-quieting step per operand)
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// 2^st in all eight halves, -14 <= st <= 15 (normal fp16 powers of two)
+__device__ __forceinline__ halfx8 scale_h(int st) {
+  const _Float16 h = __builtin_bit_cast(_Float16, static_cast<uint16_t>((st + 15) << 10));
+  return halfx8{h, h, h, h, h, h, h, h};
+}
+
+// largest |x| of a lane's 32 state values, as four chains of three-way maxima
+__device__ __forceinline__ float lane_max_abs32(const floatx4 (&m)[8]) {
+  float m4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const floatx4 x = m[2 * i], y = m[2 * i + 1];
+    m4[i] = max3_abs(x[0], x[1], x[2]);
+    m4[i] = max3_abs(m4[i], x[3], y[0]);
+    m4[i] = max3_abs(m4[i], y[1], y[2]);
+    m4[i] = max3_abs(m4[i], y[3], y[3]);
+  }
+  return max3_abs(max3_abs(m4[0], m4[1], m4[2]), m4[3], m4[3]);
+}
+
+// exponent e with 2^e <= m < 2^(e+1) for the fp32 bits of m > 0 (subnormals count as 2^-127)
+__device__ __forceinline__ int exp_of_bits(uint32_t m) { return static_cast<int>((m >> 23) & 0xFFu) - 127; }
+
+// the scale exponent (a multiple of 4) that brings a largest magnitude with fp32 bits m to
+// [2^(kRangeTop-3), 2^(kRangeTop+1))
+__device__ __forceinline__ int range_exp(uint32_t m) {
+  return m == 0u ? 0 : min(kExpHi, max(kExpLo, floor4(kRangeTop - exp_of_bits(m))));
+}
+
 // P^T fragments: (token tile ct, chunk-row step ks) pairs with ks == 0 or ct >= 2 (the others are zero)
 __device__ __forceinline__ int pfrag(int ct, int ks) { return ks == 0 ? ct : 2 + ct; }
 // (row tile rt, k step ki) pairs of the lower-triangular T' that are not all zero: ki == 0 or rt >= 2
@@ -423,7 +490,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
     vg[3 * CH + lane] = __expf(gl - g) * vRk[lane];
     float* sc = reinterpret_cast<float*>(ws + (static_cast<int64_t>(b * a.Hv + hk * a.G + j) * nwin + cl) * WH_BYTES + WH_SC);
     sc[lane] = eg;
-    if (lane == 0) sc[64] = __expf(gl);
+    if (lane == 0) {
+      const float g63 = __expf(gl);
+      sc[64] = g63;
+      reinterpret_cast<int32_t*>(sc)[73] = exp_of_bits(__float_as_uint(g63));   // gamma_63 < 2^(this + 1)
+    }
   }
 
   // ---- Q^T = (diag(rq) Q)^T as the output product's B fragments (fp16) ------
@@ -559,15 +630,31 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       }
       if (j + 1 < a.G) load_v(hv + 1);
       wave_lds_sync();
+      // value tile 2wv + hh goes into fp16 scaled by 2^r, r from its largest |v| in the chunk
+      // (bf16 bits without the sign, shifted, are the fp32 bits of |v|)
       halfx8 vf[4];   // [ki][value tile half]: value column 16 hh + (lane & 15), rows 32ki + kperm
 #pragma unroll
-      for (int ki = 0; ki < 2; ++ki)
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t mb = 0u;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int ki = 0; ki < 2; ++ki)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            vf[2 * ki + hh][e] =
-                static_cast<_Float16>(bf16_bits_to_f32(sVw[(32 * ki + kperm(g4, e)) * L::kVP + 16 * hh + l16]));
+            mb = max(mb, static_cast<uint32_t>(sVw[(32 * ki + kperm(g4, e)) * L::kVP + 16 * hh + l16] & 0x7FFFu));
+        const int rexp = range_exp(wave_max_bits(mb << 16));
+#pragma unroll
+        for (int ki = 0; ki < 2; ++ki)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            vf[2 * ki + hh][e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(
+                bf16_bits_to_f32(sVw[(32 * ki + kperm(g4, e)) * L::kVP + 16 * hh + l16]), rexp));
+        if (lane == 0) {
+          // this chunk's exponent, and the same as the previous chunk's "next" one, so that the chain
+          // can choose a chunk's scale before the chunk's operands are in LDS
+          reinterpret_cast<int32_t*>(wsc + WH_SC)[65 + 2 * wv + hh] = rexp;
+          if (cl > 0) reinterpret_cast<int32_t*>(wsc - WH_BYTES + WH_SC)[80 + 2 * wv + hh] = rexp;
+        }
+      }
       const float* M = mat(jj);
       halfx8 tf[6];
 #pragma unroll
@@ -719,7 +806,7 @@ __device__ __forceinline__ void seq_chunks(const RecArgs& a, int b, int& cs, int
 // state comes from state_in at its first chunk and from `carry` otherwise, and
 // goes to state_out after its last chunk and to `carry` otherwise.
 template <int NS>
-__global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, const unsigned char* ws, int nwin,
+__global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, unsigned char* ws, int nwin,
                                                              int nw, float* carry) {
   using L = ChainLds<NS>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -778,7 +865,8 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
   if (wv < 2) {
     const int sh = wv;
     const int col = 32 * strip + 16 * sh + l16;   // this lane's value column
-    floatx4 Ms[8];     // M rows 16dt + 4g + v, column col
+    const int vtile = 2 * strip + sh;             // value tile of the head (16 columns)
+    floatx4 Ms[8];     // 2^s_cur M, rows 16dt + 4g + v, column col
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       if (state_in) {
@@ -789,11 +877,86 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
         Ms[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
     }
-    halfx8 Mfr[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) Mfr[ks] = stack_h(Ms[2 * ks], Ms[2 * ks + 1]);
+    // Range of the fp16 products.  The state is held scaled by 2^s_cur (a multiple of 4)
+    // and s_cur never exceeds the chunk's V exponent, so the chunk's V, scaled, stays below
+    // 2^(kRangeTop+1) = 8.  Every kCheck chunks of the sequence the largest |M| over the
+    // wave is measured; outside [2^(kRangeTop-4), 2^(kRangeTop+4)) s_cur moves by a
+    // multiple of 4 that brings it into [2^(kRangeTop-3), 2^(kRangeTop+1)).  So at a check
+    // |M| < 64 and its spectral norm is below 128 * 64; each token changes the state by at
+    // most |v|_2 < 8 sqrt(128) (for beta <= 1, log alpha <= 0 and key norms <= 1), so six
+    // chunks later it is below 8192 + 6 * 64 * 90.6 < 43000, and the rows of U (at most
+    // |v|_2 + |S|) stay below fp16's 65504 as well.  A large state that decays under small
+    // values is measured as soon as its decayed bound (est) leaves the window.  A sequence
+    // that runs on from the previous window starts from the scale and bound that window left
+    // in the scalings block of its last chunk (words 96 + value tile, 104 + value tile), so
+    // the scales, and so the results, do not depend on the window size.
+    const int hand = 96 + vtile;
+    const int ci0 = lo - cs;   // chunk index inside the sequence of the window's first chunk
     uint16_t* go = static_cast<uint16_t*>(a.o) + tok0 * a.so + hv * DK + 32 * strip + 16 * sh + 4 * g4;
     __syncthreads();
+    int s_cur, est;   // est: 2^(est+1) bounds the decayed part of the state measured last (scaled)
+    halfx8 Mfr[4];
+    // The scale of chunk ci (V exponent rn), decided once the previous chunk is done: the
+    // state is measured every kCheck chunks and when its decayed bound has faded below the
+    // window while V leaves room to raise the scale; s_cur never exceeds rn.  A change by 2^d
+    // reaches the fp32 state through the next decay factor and M's fp16 fragments through
+    // exact multiplies by powers of two.
+    auto decide = [&](int ci, int rn) {
+      const bool faded = est < kRangeTop - 4 && s_cur < rn - 3;
+      int d = 0;
+      if (s_cur > rn || ci % kCheck == 0 || faded) {
+        int s_new = s_cur;
+        if (ci % kCheck == 0 || faded) {
+          const uint32_t mb = wave_max_bits(__float_as_uint(lane_max_abs32(Ms)));
+          const int e = exp_of_bits(mb);
+          est = mb == 0u ? kExpLo : e;
+          if (mb == 0u) s_new = rn;
+          else if (e < kRangeTop - 4 || e >= kRangeTop + 4) s_new = floor4(kRangeTop - e) + s_cur;
+        }
+        s_new = __builtin_amdgcn_readfirstlane(min(kExpHi, max(kExpLo, min(s_new, rn))));
+        d = s_new - s_cur;
+        s_cur = s_new;
+        est = __builtin_amdgcn_readfirstlane(max(kExpLo, est + d));
+      }
+      return d;
+    };
+    auto scale_frags = [&](int d) {
+      while (d != 0) {
+        const int st = max(-14, min(15, d));
+        const halfx8 f = scale_h(st);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) Mfr[ks] *= f;
+        d -= st;
+      }
+    };
+    int dpend = 0;   // a change of scale that the next decay factor still has to apply to Ms
+    if (ci0 > 0) {
+      const int32_t* hw = reinterpret_cast<const int32_t*>(ws + (static_cast<int64_t>(bh) * nwin + nwin - 1) * WH_BYTES + WH_SC);
+      s_cur = __builtin_amdgcn_readfirstlane(hw[hand]);
+      est = __builtin_amdgcn_readfirstlane(hw[hand + 8]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Ms[dt][v] = __builtin_amdgcn_ldexpf(Ms[dt][v], s_cur);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) Mfr[ks] = stack_h(Ms[2 * ks], Ms[2 * ks + 1]);
+      // the decision an unbroken run takes at the end of the previous chunk
+      dpend = decide(ci0, __builtin_amdgcn_readfirstlane(reinterpret_cast<const int32_t*>(smem + L::kSc)[65 + vtile]));
+      scale_frags(dpend);
+    } else {
+      // the sequence's first chunk: from the entry state's range and the chunk's V exponent
+      const int r0 = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int32_t*>(smem + L::kSc)[65 + vtile]);
+      const uint32_t mb = wave_max_bits(__float_as_uint(lane_max_abs32(Ms)));
+      s_cur = mb == 0u ? r0 : min(r0, range_exp(mb));
+      est = mb == 0u ? kExpLo : exp_of_bits(mb) + s_cur;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Ms[dt][v] = __builtin_amdgcn_ldexpf(Ms[dt][v], s_cur);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) Mfr[ks] = stack_h(Ms[2 * ks], Ms[2 * ks + 1]);
+    }
+#pragma clang loop unroll(disable)
     for (int cl = 0; cl < nchunk; ++cl) {
       unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
       const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
@@ -806,17 +969,33 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
       float gam[4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) gam[ct] = sSc[16 * ct + l16];
+      // U0 holds 2^rexp U0; gamma_63 < 2^(gexp+1); rnext: the next chunk's V exponent (the same
+      // words in every lane)
+      const int rexp = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int32_t*>(sSc)[65 + vtile]);
+      const int gexp = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int32_t*>(sSc)[73]);
+      const int rnext = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int32_t*>(sSc)[80 + vtile]);
+      const int ci = ci0 + cl;   // chunk index inside the sequence
       halfx8 F[kNFrag];
 #pragma unroll
       for (int jf = 0; jf < kAhead; ++jf) F[jf] = rd(jf);
+      const float gCs = dpend == 0 ? gC : __builtin_amdgcn_ldexpf(gC, dpend);
       __builtin_amdgcn_sched_barrier(0);
       floatx4 U[4], O[4];
+      if (s_cur == rexp) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) U[rt][v] = static_cast<float>(rt < 2 ? u0a[4 * rt + v] : u0b[4 * (rt - 2) + v]);
-        O[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int v = 0; v < 4; ++v) U[rt][v] = static_cast<float>(rt < 2 ? u0a[4 * rt + v] : u0b[4 * (rt - 2) + v]);
+      } else {
+        const float u0s = __builtin_amdgcn_ldexpf(1.f, s_cur - rexp);   // a power of two < 1 (0 far below)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            U[rt][v] = static_cast<float>(rt < 2 ? u0a[4 * rt + v] : u0b[4 * (rt - 2) + v]) * u0s;
       }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) O[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
       // ---- U = U0 - W M and O^T = M^T Q^T, interleaved ---------------------------
 #pragma unroll
       for (int jf = 0; jf < 32; ++jf) {
@@ -828,7 +1007,7 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
         if (jf == 16) {
           // the state's decay, on the vector unit while the products run
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) Ms[dt] *= gC;
+          for (int dt = 0; dt < 8; ++dt) Ms[dt] *= gCs;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -861,9 +1040,20 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
       }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) Mfr[ks] = stack_h(Ms[2 * ks], Ms[2 * ks + 1]);
-      // outputs: lane holds token 16ct + (lane & 15), value columns 4g..4g+3 of the wave's 16
-      const int ci = lo - cs + cl;   // chunk index inside the sequence
+      // outputs, unscaled: lane holds token 16ct + (lane & 15), value columns 4g..4g+3 of the wave's 16
       const int nval = min(CH, len - ci * CH);
+      const int s_out = s_cur;
+      est = __builtin_amdgcn_readfirstlane(max(kExpLo, est + gexp + 1));   // this chunk's decay
+      dpend = 0;
+      if (cl + 1 < nchunk) {
+        dpend = decide(ci + 1, rnext);
+        scale_frags(dpend);
+      }
+      if (s_out != 0) {
+        const float os = __builtin_amdgcn_ldexpf(1.f, -s_out);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) O[ct] *= os;
+      }
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int r = 16 * ct + l16;
@@ -873,12 +1063,18 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
       // slot cl may be refilled once both state waves have passed this barrier
       __builtin_amdgcn_s_barrier();
     }
+    if (hi < ce && lane == 0) {
+      // the scale handed to the next window (the block of this window's last chunk, nwin - 1)
+      int32_t* hw = reinterpret_cast<int32_t*>(ws + (static_cast<int64_t>(bh) * nwin + nwin - 1) * WH_BYTES + WH_SC);
+      hw[hand] = s_cur;
+      hw[hand + 8] = est;
+    }
     if (state_out) {
       float* sp = state_out + static_cast<int64_t>(bhv) * DK * DK;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sp[(16 * dt + 4 * g4 + v) * DK + col] = Ms[dt][v];
+        for (int v = 0; v < 4; ++v) sp[(16 * dt + 4 * g4 + v) * DK + col] = __builtin_amdgcn_ldexpf(Ms[dt][v], -s_cur);
     }
   } else {
     // copy wave: chunk cl+1 into the other slot (two slots; slot (cl + 1) % 2 was last
@@ -1090,10 +1286,10 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     const dim3 grid(slots * a.Hv * (DK / 32));
     if (!a.cu_seqlens && a.B * a.Hv * (DK / 32) > device_cu_count())
       hipLaunchKernelGGL(chunk_chain_kernel<1>, grid, dim3(192), ChainLds<1>::kBytes, s, r, c0,
-                         static_cast<const unsigned char*>(wsb), nwin, nw, carry);
+                         wsb, nwin, nw, carry);
     else
       hipLaunchKernelGGL(chunk_chain_kernel<2>, grid, dim3(192), ChainLds<2>::kBytes, s, r, c0,
-                         static_cast<const unsigned char*>(wsb), nwin, nw, carry);
+                         wsb, nwin, nw, carry);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -67,10 +67,12 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  * l2_eps) before use (per-head L2 normalisation). */
 #define GDN_FLAG_QK_L2NORM 1u
 /* Flag (gdn_prefill): run the token-by-token kernel, fp32 arithmetic
- * throughout, instead of the chunked one.  The chunked kernel multiplies fp16
- * operands (fp32 accumulation), which bounds the magnitudes it accepts: v, the
- * state and the per-chunk intermediates must stay below fp16's 65504.  This
- * flag lifts that bound at the cost of speed; it needs no workspace. */
+ * throughout, instead of the chunked one; it needs no workspace.  The chunked
+ * kernel multiplies fp16 operands with fp32 accumulation.  It scales v and the
+ * state into fp16's range by powers of two (per chunk and 16-column value
+ * tile), so their magnitudes are not bounded; the key-side products assume
+ * keys and queries of norm about 1 or less (GDN_FLAG_QK_L2NORM gives that).
+ * Use this flag for keys far from unit norm without the L2 flag. */
 #define GDN_FLAG_TOKEN_SERIAL 2u
 
 /*

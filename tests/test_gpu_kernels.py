@@ -111,6 +111,51 @@ def test_prefill_token_serial_flag(v_scale):
     assert e < 1e-5, e   # fp32 arithmetic throughout
 
 
+# v and S0 far from unit scale on the chunked path (no token-serial flag): exponents of the
+# power of two that scales v and that scales S0.  fp16 alone would overflow at 2^12 (values and
+# the state past 65504) and drop bits at 2^-12 (most values below its normal range).
+RANGE_CASES = [(12, 12), (-12, -12), (12, 0), (0, 12), (-12, 0), (0, -12), (12, -12), (-12, 12)]
+
+
+def _scale_range(p, ev, es):
+    p["v"] = W.f32_to_bf16(W.bf16_to_f32(p["v"]) * np.float32(2.0 ** ev))
+    p["state_in"] = (p["state_in"] * np.float32(2.0 ** es)).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("recipe", ["tiny", "qwen"])
+@pytest.mark.parametrize("ev,es", RANGE_CASES)
+def test_prefill_chunk_value_range(ev, es, recipe):
+    """The chunked kernels take V, U and the state into fp16 products scaled per chunk and
+    value tile by powers of two, so results hold the stated bounds at any scale of v and
+    S0.  The oracle runs on the same scaled inputs in fp64."""
+    p = _scale_range(W.problem(4100 + 7 * ev + es, 1, 150, 1, 3, 128, io="bf16", recipe=recipe,
+                               state="normal"), ev, es)
+    og, sg = run_prefill(p, state_in=p["state_in"])
+    orf, srf = oracle_prefill(p, state_in=p["state_in"])
+    m = assert_out(og, orf, bf16=True)
+    e = assert_state(sg, srf)
+    print(f"range v 2^{ev} S0 2^{es} {recipe}: out {m} state {e:.2e}")
+
+
+@pytest.mark.parametrize("ev,es", [(12, 12), (-12, -12)])
+def test_prefill_chunk_value_range_windows(ev, es):
+    """The same with a workspace of one chunk, so that the scaled state is handed from
+    window to window through state_out (in place)."""
+    torch = _torch()
+    B, T, Hk, Hv, D = 2, 200, 1, 3, 128
+    p = _scale_range(W.problem(4200 + ev, B, T, Hk, Hv, D, io="bf16", recipe="tiny", state="normal"), ev, es)
+    orf, srf = oracle_prefill(p, state_in=p["state_in"])
+    q, k, v = to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"])
+    la, be = to_dev(p["log_alpha"]), to_dev(p["beta"])
+    st = to_dev(p["state_in"].astype(np.float32))
+    ws = torch.empty(B * (Hv * WS_VALUE_HEAD + Hk * WS_KEY_HEAD), dtype=torch.uint8, device="cuda")
+    o = G.gdn_prefill(q, k, v, la, be, st, st, Hk=Hk, Hv=Hv, workspace=ws)
+    torch.cuda.synchronize()
+    assert_out(to_host(o).reshape(B, T, Hv, D), orf, bf16=True)
+    assert_state(to_host(st), srf)
+
+
 @pytest.mark.parametrize("D,io,l2", [(128, "bf16", False), (128, "bf16", True), (16, "f32", False), (64, "bf16", False)])
 def test_decode_steps_parity(D, io, l2):
     torch = _torch()
