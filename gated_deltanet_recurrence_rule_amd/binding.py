@@ -20,7 +20,7 @@ GDN_FLAG_QK_L2NORM = 1
 GDN_FLAG_TOKEN_SERIAL = 2
 
 # Every exported symbol, in the order include/gdn.h, then include/gdn_attn.h declare them.
-EXPORTS = ("gdn_prefill", "gdn_prefill_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_size",
+EXPORTS = ("gdn_prefill", "gdn_prefill_static", "gdn_prefill_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_size",
            "gdn_decode_step", "gdn_conv1d_silu",
            "gdn_gated_rmsnorm", "gdn_gates", "gdn_decode_token", "gdn_decode_layer", "gdn_last_error",
            "gdn_version",
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.gdn_prefill.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p, p, ctypes.c_size_t, p]
         L.gdn_prefill.restype = ctypes.c_int
+        L.gdn_prefill_static.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p, p]
+        L.gdn_prefill_static.restype = ctypes.c_int
         L.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnDims)]
         L.gdn_prefill_workspace_size.restype = ctypes.c_size_t
         L.gdn_prefill_varlen.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p, p, p, ctypes.c_size_t, p]
@@ -224,6 +226,37 @@ def gdn_prefill(q, k, v, log_alpha, beta, state_in=None, state_out=None, o=None,
                              _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o), _ptr(workspace),
                              ws_len, _stream(stream)))
     _on_stream(stream, *own)
+    return o
+
+
+def gdn_prefill_static(q, k, v, log_alpha, beta, state_in, state_out, o, *, Hk: int, Hv: int,
+                       l2norm: bool = False, l2_eps: float = 1e-6, q_scale: float = 1.0,
+                       token_serial: bool = False, stream=None):
+    """gdn_prefill_static: gdn_prefill on the library's fixed device scratch.  The
+    caller passes every buffer (o included); nothing is allocated here or below.
+    Shapes as gdn_prefill.  Returns o."""
+    import torch
+    B, T = int(q.shape[0]), int(q.shape[1])
+    if q.shape[2] % Hk or v.shape[2] % Hv or q.shape[2] // Hk != v.shape[2] // Hv:
+        raise ValueError("q must be [B, T, Hk*D] and v [B, T, Hv*D] (views of exactly that width)")
+    D = int(q.shape[2]) // Hk
+    io = _io(q)
+    if o is None or k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+        raise ValueError("q, k, v and o (required) must share one dtype")
+    flags = (GDN_FLAG_QK_L2NORM if l2norm else 0) | (GDN_FLAG_TOKEN_SERIAL if token_serial else 0)
+    dims = make_dims(B, T, Hk, Hv, D, io, flags,
+                     _token_stride(q, B, T, Hk * D, "q"), _token_stride(k, B, T, Hk * D, "k"),
+                     _token_stride(v, B, T, Hv * D, "v"), _token_stride(o, B, T, Hv * D, "o"),
+                     q_scale, l2_eps)
+    for name, g in (("log_alpha", log_alpha), ("beta", beta)):
+        if g.dtype != torch.float32 or not g.is_contiguous() or tuple(g.shape) != (B, T, Hv):
+            raise ValueError(f"{name} must be contiguous fp32 [B, T, Hv]")
+    for name, s in (("state_in", state_in), ("state_out", state_out)):
+        if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()
+                              or tuple(s.shape) != (B, Hv, D, D)):
+            raise ValueError(f"{name} must be contiguous fp32 [B, Hv, D, D]")
+    _check(lib().gdn_prefill_static(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                    _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o), _stream(stream)))
     return o
 
 

@@ -35,6 +35,29 @@ int device_cu_count() {
 
 namespace {
 
+// gdn_prefill_static's workspace: a fixed device array that each GPU the library runs on holds
+// until the process ends.  Host code reaches its device address only through
+// hipGetSymbolAddress (the array's name on the host is not a device pointer), once per device
+// with that device current.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** out) {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 thread_local char g_err[512] = "";
 
 gdn_status fail(gdn_status st, const char* fmt, ...) {
@@ -279,6 +302,32 @@ gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const vo
                        float* state_out, void* o, void* workspace, size_t workspace_bytes,
                        void* stream) {
   return prefill(d, nullptr, q, k, v, log_alpha, beta, state_in, state_out, o, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_static(const gdn_dims* d, const void* q, const void* k, const void* v,
+                              const float* log_alpha, const float* beta, const float* state_in, float* state_out,
+                              void* o, void* stream) {
+  gdn_status st = check_dims(d, false);
+  if (st != GDN_OK) return st;
+  if (d->B == 0) return ok();
+  size_t need = 0;
+  if (use_chunk_kernel(d)) {
+    // the same smallest workspace gdn_prefill takes: one chunk per window (the whole call when it
+    // has one chunk) and the state carry when there is no state_out
+    const gdn::RecArgs a = chunk_args(d, nullptr, q, k, v, log_alpha, beta, state_in, state_out, o);
+    const int64_t nchunks = gdn::chunk_count(a);
+    need = gdn::chunk_ws_bytes_per_chunk(a) + ((nchunks > 1 && !state_out) ? gdn::chunk_ws_carry_bytes(a) : 0);
+    if (need > kStaticScratchBytes)
+      return fail(GDN_ERR_SHAPE, "gdn_prefill_static: these dims need at least %zu bytes of scratch, above its %zu",
+                  need, kStaticScratchBytes);
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = static_scratch(&ws);
+    if (e != hipSuccess) return from_hip(e, "gdn_prefill_static (scratch address)");
+  }
+  return prefill(d, nullptr, q, k, v, log_alpha, beta, state_in, state_out, o, ws, need > 0 ? kStaticScratchBytes : 0,
+                 stream);
 }
 
 gdn_status gdn_prefill_varlen(const gdn_dims* d, const int32_t* cu_seqlens, const void* q, const void* k,

@@ -127,6 +127,25 @@ gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const
                        void* stream);
 
 /*
+ * gdn_prefill_static -- gdn_prefill with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * chunked kernels run in a fixed 64 MiB device array that the library holds
+ * on each GPU it runs on until the process ends; the call allocates nothing
+ * and frees nothing.  Arguments, layouts and results are gdn_prefill's (the
+ * results are the same bits as gdn_prefill's with any workspace).  Dims
+ * whose smallest workspace (one chunk of operands, see
+ * gdn_prefill_workspace_size, plus the state carry when state_out is NULL)
+ * exceeds 64 MiB fail with GDN_ERR_SHAPE before anything runs.  Nothing in
+ * the array has to start at any value.  All calls on one GPU share its
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and give wrong results; serialise them.
+ */
+gdn_status gdn_prefill_static(const gdn_dims* dims, const void* q, const void* k, const void* v,
+                              const float* log_alpha, const float* beta, const float* state_in,
+                              float* state_out, void* o, void* stream);
+
+/*
  * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill wants
  * for these dims (0 when the call needs none).  The chunked kernel keeps, per
  * (sequence, value head, chunk of a window), the per-chunk matrices that do

@@ -308,3 +308,14 @@ def test_attention_argument_errors():
     assert dec(adims(T=1), cl=ctypes.c_void_p(0x10002)) == B.GDN_ERR_ALIGN
     assert dec(adims(T=1), n=1000) == B.GDN_ERR_SHAPE
     assert dec(adims(T=1, B=0)) == B.GDN_OK
+
+
+def test_prefill_static_rejects_dims_beyond_its_scratch():
+    """gdn_prefill_static refuses dims whose smallest workspace exceeds its 64 MiB array
+    before it reads any pointer or touches a device: 8 sequences x 128 value heads give one
+    chunk of 57 MiB of operands plus, without state_out, a 64 MiB state carry."""
+    L = B.lib()
+    d = B.make_dims(8, 128, 16, 128, 128, B.GDN_BF16)
+    st = L.gdn_prefill_static(ctypes.byref(d), None, None, None, None, None, None, None, None, None)
+    assert st == B.GDN_ERR_SHAPE
+    assert "scratch" in B.gdn_last_error()
