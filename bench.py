@@ -60,10 +60,11 @@ def bf16_dev(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def timed_launches(fn, steps, warmup, stream):
+def timed_launches(fn, steps, warmup, stream, p90=False):
     """Runs fn() warmup times, then `steps` times with a HIP event pair around
     each launch on `stream`.  Returns (total ms of the timed region from the
-    first start event to the last end event, mean ms per launch, median ms)."""
+    first start event to the last end event, mean ms per launch, median ms),
+    and the 90th percentile when p90 is set."""
     import torch
     for _ in range(warmup):
         fn()
@@ -78,6 +79,8 @@ def timed_launches(fn, steps, warmup, stream):
     torch.cuda.synchronize()
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     total = starts[0].elapsed_time(ends[-1])
+    if p90:
+        return total, float(per.mean()), float(np.median(per)), float(np.percentile(per, 90))
     return total, float(per.mean()), float(np.median(per))
 
 
@@ -105,7 +108,79 @@ def bench_prefill4k(steps, warmup, dev):
                 flops=prefill_flops(B, T, Hk, Hv, D), bytes=prefill_bytes(B, T, Hk, Hv, D))
 
 
-def bench_decode(dev, n_steps=256, pools=1):
+def bench_prefill_cold(dev, steps=20):
+    """The headline prefill with the 256 MB last-level cache emptied before each call: a
+    512 MB buffer is written between calls, outside the timed events."""
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding as G
+    from gated_deltanet_recurrence_rule_amd import workloads as W
+    p = W.cfg_prefill4k()
+    B, T, Hk, Hv, D = p["B"], p["T"], p["Hk"], p["Hv"], p["D"]
+    q, k, v = bf16_dev(p["q"], dev), bf16_dev(p["k"], dev), bf16_dev(p["v"], dev)
+    la = torch.from_numpy(p["log_alpha"]).to(dev)
+    be = torch.from_numpy(p["beta"]).to(dev)
+    o = torch.empty((B, T, Hv * D), dtype=torch.bfloat16, device=dev)
+    so = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(G.gdn_prefill_workspace_size(G.make_dims(B, T, Hk, Hv, D, G.GDN_BF16)),
+                     dtype=torch.uint8, device=dev)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    call = lambda: G.gdn_prefill(q, k, v, la, be, None, so, o, Hk=Hk, Hv=Hv, workspace=ws, stream=stream)
+    for _ in range(20):
+        call()
+    times = []
+    for i in range(steps):
+        scrub.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    med = float(np.median(times))
+    return dict(median_us=med * 1e3, tokens_per_s=B * T / (med * 1e-3))
+
+
+def attainable_peaks(dev):
+    """What this machine reaches on plain library work: a 1 GiB device copy (bytes read plus
+    written per second) and a large bf16 GEMM through torch (hipBLASLt)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        reps.append(e0.elapsed_time(e1))
+    copy_gbs = 2 * n / (min(reps) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((m, m), device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b)
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        reps.append(e0.elapsed_time(e1))
+    gemm = 2 * m ** 3 / (min(reps) * 1e-3) / 1e12
+    return dict(copy_1GiB_GBs=copy_gbs, copy_frac=copy_gbs / HBM_PEAK_GBS,
+                bf16_gemm_8192_TFLOPs=gemm, bf16_gemm_frac=gemm / BF16_PEAK_TFLOPS)
+
+
+def bench_decode(dev, n_steps=256, pools=1, graph=False):
     """256 successive decode steps on a resident [64, 48, 128, 128] fp32 pool
     (`pools` independent pools rotated step by step to defeat the 256 MB
     last-level cache); per-step inputs are staged in HBM beforehand."""
@@ -131,10 +206,39 @@ def bench_decode(dev, n_steps=256, pools=1):
         i[0] += 1
 
     torch.cuda.synchronize()
-    total, mean_ms, med_ms = timed_launches(step, n_steps, 8, stream)
+    total, mean_ms, med_ms, p90_ms = timed_launches(step, n_steps, 8, stream, p90=True)
     per = decode_bytes(B, Hk, Hv, D)
-    return dict(steps=n_steps, pools=pools, total_ms=total, mean_ms=mean_ms, median_ms=med_ms,
-                bytes_per_step=per, GBs=per / (med_ms * 1e-3) / 1e9)
+    out = dict(steps=n_steps, pools=pools, total_ms=total, mean_ms=mean_ms, median_ms=med_ms, p90_ms=p90_ms,
+               bytes_per_step=per, GBs=per / (med_ms * 1e-3) / 1e9)
+    if graph:
+        # the same 256 steps captured once in a HIP graph and replayed: launch cost out of the way
+        i[0] = 0
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()          # one eager step on the capture stream before capturing
+            i[0] = 0
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(n_steps):
+                q, k, v, la, be = steps_in[i[0] % n_steps]
+                G.gdn_decode_step(q, k, v, la, be, pool_list[i[0] % pools], o, Hk=Hk, Hv=Hv, stream=side)
+                i[0] += 1
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) / n_steps)
+        gm = float(np.median(reps))
+        out.update(graph_us_per_step=gm * 1e3, graph_GBs=per / (gm * 1e-3) / 1e9)
+    return out
 
 
 def bench_decode_front(dev, n_steps=256, n_inputs=32):
@@ -420,8 +524,40 @@ def cpu_baseline(reps=2):
                           n_threads=threads)
         times.append(time.perf_counter() - t0)
     t = min(times)
+    # one thread on a sample of 8 of the 48 value heads (its rate scaled to the whole layer)
+    sel = list(range(0, p["Hv"], p["Hv"] // 8))
+    t0 = time.perf_counter()
+    oracle.recurrence(p["q"], p["k"], p["v"], p["log_alpha"], p["beta"], p["Hk"], p["Hv"], None,
+                      sel=sel, n_threads=1)
+    t1 = (time.perf_counter() - t0) * p["Hv"] / len(sel)
+    model, phys, logical = cpu_info()
     return {"value": p["B"] * p["T"] / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole headline workload (B=1, T=4096, 48 value heads, fp64), best of {reps}: {t:.3f} s"}
+            "sample": f"whole headline workload (B=1, T=4096, 48 value heads, fp64), best of {reps}: {t:.3f} s",
+            "cpu_model": model, "physical_cores": phys, "logical_cpus": logical,
+            "one_thread": {"value": p["B"] * p["T"] / t1, "unit": "tokens/s",
+                           "sample": f"{len(sel)} of 48 value heads on 1 thread, scaled to 48: {t1:.3f} s"}}
+
+
+def cpu_info():
+    """CPU model name, physical cores and logical CPUs of this host, from /proc/cpuinfo."""
+    model, cores, logical = "unknown", set(), 0
+    try:
+        phys = core = None
+        for line in open("/proc/cpuinfo"):
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k == "processor":
+                logical += 1
+            elif k == "model name":
+                model = v
+            elif k == "physical id":
+                phys = v
+            elif k == "core id":
+                core = v
+                cores.add((phys, core))
+    except OSError:
+        pass
+    return model, (len(cores) or None), (logical or os.cpu_count())
 
 
 def traffic_from_profile(kernel_src_hash):
@@ -455,7 +591,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu baseline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (counter calibration)")
+    ap.add_argument("--decode-only", type=int, choices=(1, 2), default=0,
+                    help="run only the 256 decode steps on 1 or 2 state pools (for counter runs)")
     args = ap.parse_args()
+    if args.decode_only:
+        import torch
+        r = bench_decode(torch.device("cuda:0"), pools=args.decode_only)
+        print(json.dumps({k: r[k] for k in ("pools", "median_ms", "GBs", "bytes_per_step")}))
+        return
     if args.calib_copy:
         import torch
         n = 256 << 20
@@ -514,15 +657,30 @@ def main():
         },
     }
     if not args.no_extras:
+        # decode's figure is the cold one: two pools alternate step by step, so that no step finds
+        # its 201 MB pool in the 256 MB last-level cache
+        dec2 = bench_decode(dev, pools=2, graph=True)
         dec = bench_decode(dev)
-        print(f"[bench] decode: {dec['median_ms'] * 1e3:.1f} us/step, {dec['GBs']:.0f} GB/s", file=sys.stderr, flush=True)
-        dec2 = bench_decode(dev, pools=2)
+        print(f"[bench] decode: {dec2['median_ms'] * 1e3:.1f} us/step, {dec2['GBs']:.0f} GB/s cold "
+              f"(one pool {dec['GBs']:.0f} GB/s; graph of 256 steps {dec2['graph_us_per_step']:.1f} us/step)",
+              file=sys.stderr, flush=True)
         line["decode"] = {"config": "64 sequences x 48 value heads x 128x128 fp32 state, 16 key heads, bf16 q/k/v, "
-                                    "256 steps",
-                          "median_us": dec["median_ms"] * 1e3, "mean_us": dec["mean_ms"] * 1e3,
-                          "GBs": dec["GBs"], "hbm_frac": dec["GBs"] / HBM_PEAK_GBS,
-                          "bytes_per_step": dec["bytes_per_step"],
-                          "two_pools_GBs": dec2["GBs"], "two_pools_median_us": dec2["median_ms"] * 1e3}
+                                    "256 steps, two state pools alternating (cold)",
+                          "median_us": dec2["median_ms"] * 1e3, "mean_us": dec2["mean_ms"] * 1e3,
+                          "p90_us": dec2["p90_ms"] * 1e3,
+                          "GBs": dec2["GBs"], "hbm_frac": dec2["GBs"] / HBM_PEAK_GBS,
+                          "bytes_per_step": dec2["bytes_per_step"],
+                          "graph_us_per_step": dec2["graph_us_per_step"], "graph_GBs": dec2["graph_GBs"],
+                          "one_pool_median_us": dec["median_ms"] * 1e3, "one_pool_p90_us": dec["p90_ms"] * 1e3,
+                          "one_pool_GBs": dec["GBs"]}
+        cold = bench_prefill_cold(dev)
+        print(f"[bench] prefill4k cold (cache emptied before each call): {cold['median_us']:.1f} us",
+              file=sys.stderr, flush=True)
+        line["prefill_cold"] = {"config": "headline prefill, 512 MB written between calls", **cold}
+        pk = attainable_peaks(dev)
+        print(f"[bench] attainable: copy {pk['copy_1GiB_GBs']:.0f} GB/s, bf16 GEMM {pk['bf16_gemm_8192_TFLOPs']:.0f} "
+              f"TFLOP/s", file=sys.stderr, flush=True)
+        line["attainable"] = pk
         fr = bench_decode_front(dev)
         print(f"[bench] decode front end: {fr['median_us']:.1f} us/step (token {fr['token_median_us']:.1f} us, "
               f"fused layer {fr['fused_median_us']:.1f} us)",
