@@ -561,7 +561,32 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   }
   __syncthreads();  // the K and Q rows are dead from here on: their bytes hold the matrices
 
-  // Value heads in groups of up to kNH: A and P of the group from the Gram tiles,
+  // ---- P^T fragments of value head j: P_ri = e^{g_r - g_i} rq_r rk_i (q_r . k_i), i <= r
+  auto write_p = [&](int j) {
+    const float* vG = vgate(j);
+    unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hk * a.G + j) * nwin + cl) * WH_BYTES;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u < npf) {
+        const int ct = pct0 + u, r = 16 * ct + l16;
+        const float gr = vG[r], rq = vRq[r];
+        halfx8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 32 * pks + kperm(g4, e);
+          const float x = __expf(fminf(gr - vG[i], 0.f)) * rq * vRk[i] * gKQ[2 * u + (e >> 2)][e & 3];
+          pf[e] = static_cast<_Float16>(i <= r ? x : 0.f);
+        }
+        *reinterpret_cast<halfx8*>(wsc + WH_P + pfrag(ct, pks) * 1024 + lane * 16) = pf;
+      }
+    }
+  };
+  // With more value heads than one group, every head's P goes out first, so that the
+  // K Q^T tiles do not stay live across the groups.
+  if (!kOneGroup)
+    for (int j = 0; j < a.G; ++j) write_p(j);
+
+  // Value heads in groups of up to kNH: A (and with one group P) from the Gram tiles,
   // then each head's inverse on its own wave, then the products of each head.
   for (int j0 = 0; j0 < (kOneGroup ? 1 : a.G); j0 += L::kNH) {
     const int ng = kOneGroup ? a.G : min(L::kNH, a.G - j0);
@@ -588,25 +613,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
           }
         }
       }
-      // ---- P^T fragments: P_ri = e^{g_r - g_i} rq_r rk_i (q_r . k_i), i <= r --------
-      {
-        unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hk * a.G + j) * nwin + cl) * WH_BYTES;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          if (u < npf) {
-            const int ct = pct0 + u, r = 16 * ct + l16;
-            const float gr = vG[r], rq = vRq[r];
-            halfx8 pf;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int i = 32 * pks + kperm(g4, e);
-              const float x = __expf(fminf(gr - vG[i], 0.f)) * rq * vRk[i] * gKQ[2 * u + (e >> 2)][e & 3];
-              pf[e] = static_cast<_Float16>(i <= r ? x : 0.f);
-            }
-            *reinterpret_cast<halfx8*>(wsc + WH_P + pfrag(ct, pks) * 1024 + lane * 16) = pf;
-          }
-        }
-      }
+      if (kOneGroup) write_p(j);
     }
     __syncthreads();
     // ---- T = (I + A)^-1, head j0 + wv on wave wv ----------------------------
