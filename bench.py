@@ -313,8 +313,11 @@ def bench_decode_front(dev, n_steps=256, n_inputs=32):
 def bench_block(dev, steps=5, warmup=2):
     """Block front end at batch 4, T = 32768, 16 key / 128 value heads: conv+SiLU over
     [q|k|v] (20480 channels), prefill on strided views with the L2 flag, gated
-    RMSNorm x swish(z).  Inputs are drawn on the GPU (seeded torch generator) with
-    the recipe's distributions; timing does not depend on the values."""
+    RMSNorm x swish(z).  The block runs conv then gdn_prefill_gated, which applies
+    the norm inside the chain kernel here (the 512 heads fill the GPU); the separate
+    launches (prefill, then norm) are timed beside it.  Inputs are drawn on the GPU
+    (seeded torch generator) with the recipe's distributions; timing does not depend
+    on the values."""
     import torch
     from gated_deltanet_recurrence_rule_amd import binding as G
     B, T, Hk, Hv, D = 4, 32768, 16, 128, 128
@@ -341,17 +344,26 @@ def bench_block(dev, steps=5, warmup=2):
     pre = lambda: G.gdn_prefill(qv, kv, vv, la, be, None, so, o, Hk=Hk, Hv=Hv, l2norm=True, workspace=ws,
                                 stream=stream)
     norm = lambda: G.gdn_gated_rmsnorm(o.view(B * T, Hv * D), z, nw, 1e-5, out, H=Hv, stream=stream)
+    zv = z.view(B, T, Hv * D)
+    gated = lambda: G.gdn_prefill_gated(qv, kv, vv, la, be, zv, nw, 1e-5, None, so, out.view(B, T, Hv * D), Hk=Hk,
+                                        Hv=Hv, l2norm=True, workspace=ws, stream=stream)
     res = {}
-    for name, fn in (("conv", conv), ("prefill", pre), ("norm", norm)):
+    for name, fn in (("conv", conv), ("prefill", pre), ("norm", norm), ("prefill_gated", gated)):
         _, mean_ms, med_ms = timed_launches(fn, steps, warmup, stream)
         res[name + "_ms"] = med_ms
 
     def block():
         conv()
+        gated()
+
+    def block_unfused():
+        conv()
         pre()
         norm()
 
     total, _, med = timed_launches(block, steps, 1, stream)
+    _, _, med_unfused = timed_launches(block_unfused, steps, 1, stream)
+    res["block_unfused_ms"] = med_unfused
     conv_bytes = B * T * Cc * 2 * 2 + Cc * 4 * 2
     norm_bytes = B * T * Hv * D * 2 * 3 + D * 2
     res.update(block_ms=med, tokens_per_s=B * T / (med * 1e-3),
@@ -693,8 +705,9 @@ def main():
             "fused_hbm_frac": fr["fused_GBs"] / HBM_PEAK_GBS}
         blk = bench_block(dev)
         print(f"[bench] block: {blk['block_ms']:.2f} ms", file=sys.stderr, flush=True)
-        line["block"] = {"config": "batch 4, T=32768, 16 key / 128 value heads: conv+SiLU, prefill (L2 flag), "
-                                   "gated RMSNorm", **blk}
+        line["block"] = {"config": "batch 4, T=32768, 16 key / 128 value heads: conv+SiLU, prefill (L2 flag) with "
+                                   "the gated RMSNorm in the chain (gdn_prefill_gated); block_unfused_ms: conv, "
+                                   "prefill, norm as three launches", **blk}
         lg = bench_long(dev)
         print(f"[bench] long: {lg['ms']:.2f} ms", file=sys.stderr, flush=True)
         line["long"] = {"config": "batch 1, T=262144, 16 key / 48 value heads", **lg}

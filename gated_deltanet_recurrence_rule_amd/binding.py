@@ -18,9 +18,10 @@ GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIGN, GDN_ERR
 GDN_F32, GDN_BF16 = 0, 1
 GDN_FLAG_QK_L2NORM = 1
 GDN_FLAG_TOKEN_SERIAL = 2
+GDN_FLAG_NORM_IN_CHAIN = 4
 
 # Every exported symbol, in the order include/gdn.h, then include/gdn_attn.h declare them.
-EXPORTS = ("gdn_prefill", "gdn_prefill_static", "gdn_prefill_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_size",
+EXPORTS = ("gdn_prefill", "gdn_prefill_gated", "gdn_prefill_static", "gdn_prefill_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_size",
            "gdn_decode_step", "gdn_conv1d_silu",
            "gdn_gated_rmsnorm", "gdn_gates", "gdn_decode_token", "gdn_decode_layer", "gdn_last_error",
            "gdn_version",
@@ -82,6 +83,9 @@ def lib() -> ctypes.CDLL:
         p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.gdn_prefill.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p, p, ctypes.c_size_t, p]
         L.gdn_prefill.restype = ctypes.c_int
+        L.gdn_prefill_gated.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p, i64, p, ctypes.c_float, p, p,
+                                        ctypes.c_size_t, p]
+        L.gdn_prefill_gated.restype = ctypes.c_int
         L.gdn_prefill_static.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p, p]
         L.gdn_prefill_static.restype = ctypes.c_int
         L.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnDims)]
@@ -227,6 +231,54 @@ def gdn_prefill(q, k, v, log_alpha, beta, state_in=None, state_out=None, o=None,
                              ws_len, _stream(stream)))
     _on_stream(stream, *own)
     return o
+
+
+def gdn_prefill_gated(q, k, v, log_alpha, beta, z, norm_w, norm_eps: float = 1e-6, state_in=None, state_out=None,
+                      y=None, *, Hk: int, Hv: int, l2norm: bool = False, l2_eps: float = 1e-6,
+                      q_scale: float = 1.0, token_serial: bool = False, in_chain: bool = False,
+                      workspace=None, stream=None):
+    """gdn_prefill_gated: the prefill, then the gated RMSNorm of every output row.
+    Shapes as gdn_prefill; z: [B, T, >=Hv*D] view; norm_w: [D]; y: [B, T, >=Hv*D]
+    or None (allocated); in_chain: GDN_FLAG_NORM_IN_CHAIN.  Returns y."""
+    import torch
+    B, T = int(q.shape[0]), int(q.shape[1])
+    if q.shape[2] % Hk or v.shape[2] % Hv or q.shape[2] // Hk != v.shape[2] // Hv:
+        raise ValueError("q must be [B, T, Hk*D] and v [B, T, Hv*D] (views of exactly that width)")
+    D = int(q.shape[2]) // Hk
+    io = _io(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or z.dtype != q.dtype or norm_w.dtype != q.dtype or (
+            y is not None and y.dtype != q.dtype):
+        raise ValueError("q, k, v, z, norm_w and y must share one dtype")
+    if tuple(norm_w.shape) != (D,) or not norm_w.is_contiguous():
+        raise ValueError(f"norm_w must be contiguous [{D}]")
+    own = []
+    if y is None:
+        y = torch.empty((B, T, Hv * D), dtype=q.dtype, device=q.device)
+        own.append(y)
+    flags = ((GDN_FLAG_QK_L2NORM if l2norm else 0) | (GDN_FLAG_TOKEN_SERIAL if token_serial else 0) |
+             (GDN_FLAG_NORM_IN_CHAIN if in_chain else 0))
+    dims = make_dims(B, T, Hk, Hv, D, io, flags,
+                     _token_stride(q, B, T, Hk * D, "q"), _token_stride(k, B, T, Hk * D, "k"),
+                     _token_stride(v, B, T, Hv * D, "v"), _token_stride(y, B, T, Hv * D, "y"),
+                     q_scale, l2_eps)
+    sz = _token_stride(z, B, T, Hv * D, "z")
+    for name, g in (("log_alpha", log_alpha), ("beta", beta)):
+        if g.dtype != torch.float32 or not g.is_contiguous() or tuple(g.shape) != (B, T, Hv):
+            raise ValueError(f"{name} must be contiguous fp32 [B, T, Hv]")
+    for name, s in (("state_in", state_in), ("state_out", state_out)):
+        if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()
+                              or tuple(s.shape) != (B, Hv, D, D)):
+            raise ValueError(f"{name} must be contiguous fp32 [B, Hv, D, D]")
+    ws_bytes = gdn_prefill_workspace_size(dims)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        own.append(workspace)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gdn_prefill_gated(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                   _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(z), sz, _ptr(norm_w),
+                                   float(norm_eps), _ptr(y), _ptr(workspace), ws_len, _stream(stream)))
+    _on_stream(stream, *own)
+    return y
 
 
 def gdn_prefill_static(q, k, v, log_alpha, beta, state_in, state_out, o, *, Hk: int, Hv: int,

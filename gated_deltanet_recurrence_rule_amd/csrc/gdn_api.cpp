@@ -160,7 +160,11 @@ gdn::RecArgs chunk_args(const gdn_dims* d, const int32_t* cu, const void* q, con
   return a;
 }
 
-size_t workspace_size(const gdn_dims* d, const int32_t* cu) {
+size_t workspace_size(const gdn_dims* dims, const int32_t* cu) {
+  if (!dims) return 0;
+  gdn_dims dd = *dims;   // gdn_prefill_gated's dims ask for the same workspace
+  dd.flags &= ~GDN_FLAG_NORM_IN_CHAIN;
+  const gdn_dims* d = &dd;
   if (check_dims(d, false) != GDN_OK || d->B == 0 || !use_chunk_kernel(d)) return 0;
   const gdn::RecArgs a = chunk_args(d, cu, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
   const size_t per_chunk = gdn::chunk_ws_bytes_per_chunk(a);
@@ -171,9 +175,17 @@ size_t workspace_size(const gdn_dims* d, const int32_t* cu) {
   return maps + static_cast<size_t>(nwin) * per_chunk + gdn::chunk_ws_carry_bytes(a);
 }
 
+// The gated RMSNorm the chain applies to each output row (gdn_prefill_gated).
+struct NormIn {
+  const void* z;
+  int64_t stride_z;
+  const void* w;
+  float eps;
+};
+
 gdn_status prefill(const gdn_dims* d, const int32_t* cu, const void* q, const void* k, const void* v,
                    const float* log_alpha, const float* beta, const float* state_in, float* state_out, void* o,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+                   void* workspace, size_t workspace_bytes, void* stream, const NormIn* norm = nullptr) {
   gdn_status st = check_dims(d, false);
   if (st != GDN_OK) return st;
   if (d->B == 0) return ok();
@@ -187,7 +199,13 @@ gdn_status prefill(const gdn_dims* d, const int32_t* cu, const void* q, const vo
       return fail(GDN_ERR_ALIGN, "bf16 q, k, v, o must be 16-byte aligned");
     if ((d->stride_q % 8) || (d->stride_k % 8) || (d->stride_v % 8) || (d->stride_o % 8))
       return fail(GDN_ERR_ALIGN, "bf16 strides of q, k, v, o must be multiples of 8 elements");
-    const gdn::RecArgs a = chunk_args(d, cu, q, k, v, log_alpha, beta, state_in, state_out, o);
+    gdn::RecArgs a = chunk_args(d, cu, q, k, v, log_alpha, beta, state_in, state_out, o);
+    if (norm) {
+      a.gz = norm->z;
+      a.sz = norm->stride_z;
+      a.gw = norm->w;
+      a.geps = norm->eps;
+    }
     const size_t per_chunk = gdn::chunk_ws_bytes_per_chunk(a);
     const int64_t nchunks = gdn::chunk_count(a);
     const size_t maps = gdn::chunk_map_bytes(a);
@@ -328,6 +346,41 @@ gdn_status gdn_prefill_static(const gdn_dims* d, const void* q, const void* k, c
   }
   return prefill(d, nullptr, q, k, v, log_alpha, beta, state_in, state_out, o, ws, need > 0 ? kStaticScratchBytes : 0,
                  stream);
+}
+
+gdn_status gdn_prefill_gated(const gdn_dims* d, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, const float* state_in, float* state_out,
+                             const void* z, int64_t stride_z, const void* norm_w, float norm_eps, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!d) return fail(GDN_ERR_NULL, "dims is NULL");
+  gdn_dims dd = *d;
+  const bool force = (dd.flags & GDN_FLAG_NORM_IN_CHAIN) != 0;
+  dd.flags &= ~GDN_FLAG_NORM_IN_CHAIN;
+  gdn_status st = check_dims(&dd, false);
+  if (st != GDN_OK) return st;
+  if (dd.Dv != 64 && dd.Dv != 128) return fail(GDN_ERR_UNSUPPORTED, "the gated norm takes Dv in {64, 128}");
+  const int64_t wv = static_cast<int64_t>(dd.Hv) * dd.Dv;
+  if (stride_z < wv) return fail(GDN_ERR_SHAPE, "stride_z=%lld below Hv*Dv=%lld", (long long)stride_z, (long long)wv);
+  if (!(norm_eps >= 0.0f)) return fail(GDN_ERR_SHAPE, "norm_eps must be >= 0");
+  if (dd.B == 0) return ok();
+  if (dd.T > 0) {
+    if (!z || !norm_w || !y) return fail(GDN_ERR_NULL, "z, norm_w and y are required");
+    if (!aligned(z, 16) || !aligned(norm_w, 16) || !aligned(y, 16))
+      return fail(GDN_ERR_ALIGN, "z, norm_w and y must be 16-byte aligned");
+    if ((stride_z % 8) || (dd.stride_o % 8)) return fail(GDN_ERR_ALIGN, "stride_z and stride_o must be multiples of 8");
+  }
+  // In the chain when the per-head grid fills the GPU (or when asked): otherwise the
+  // prefill writes its outputs into y and the norm runs over y in place.
+  const bool fused = use_chunk_kernel(&dd) && (force || static_cast<int64_t>(dd.B) * dd.Hv >= gdn::device_cu_count());
+  if (fused) {
+    const NormIn n{z, stride_z, norm_w, norm_eps};
+    return prefill(&dd, nullptr, q, k, v, log_alpha, beta, state_in, state_out, y, workspace, workspace_bytes, stream,
+                   &n);
+  }
+  st = prefill(&dd, nullptr, q, k, v, log_alpha, beta, state_in, state_out, y, workspace, workspace_bytes, stream);
+  if (st != GDN_OK || dd.T == 0) return st;
+  return gdn_gated_rmsnorm(static_cast<int64_t>(dd.B) * dd.T, dd.Hv, dd.Dv, dd.io, y, dd.stride_o, z, stride_z, norm_w,
+                           norm_eps, y, dd.stride_o, stream);
 }
 
 gdn_status gdn_prefill_varlen(const gdn_dims* d, const int32_t* cu_seqlens, const void* q, const void* k,

@@ -746,38 +746,53 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
 
 
 // =========================================================================
-// chain kernel: one workgroup (3 waves) per (32-column strip, value head, batch)
+// chain kernel: one workgroup per (value head, batch) and column range of M
 // =========================================================================
-// LDS: NS input slots, each a chunk's -W, Kd, the U0 of the strip, the
-// scalings, Q^T and P^T, copied from the workspace by the copy wave NS - 1
-// chunks ahead (or, with one slot, once the chunk's slot has been read).  Two
-// slots take 118 KiB, so one workgroup per CU; one slot 59 KiB, so two share a
-// CU and cover each other's copies when the grid holds more workgroups than
-// there are CUs.
-template <int NS>
+// A workgroup covers SPW 32-column strips of a value head's M (SPW = 1: a strip,
+// three waves; SPW = 4: the whole head, nine waves): two state waves per strip,
+// each carrying 16 columns, and one copy wave.  LDS: NS input slots, each a
+// chunk's -W, Kd, the U0 of the workgroup's columns, the scalings, Q^T and P^T,
+// copied from the workspace by the copy wave NS - 1 chunks ahead (or, with one
+// slot, once the chunk's slot has been read).  A strip's two slots take 118 KiB,
+// so one workgroup per CU; one slot 59 KiB, so two share a CU and cover each
+// other's copies when the grid holds more workgroups than there are CUs.  A
+// whole head takes 142 KiB with two slots, and with GATED 4 KiB more for the
+// per-token sums of squares of the gated norm (see the kernel).
+template <int NS, int SPW, bool GATED>
 struct ChainLds {
-  static constexpr int kW = 0, kKd = 16384, kU0 = 32768, kSc = 36864, kQ = 37888, kP = 54272;
-  static constexpr int kSlot = 60416;               // 59 blocks of 1 KiB
+  static constexpr int kW = 0, kKd = 16384, kU0 = 32768;
+  static constexpr int kSc = kU0 + 4096 * SPW, kQ = kSc + 1024, kP = kQ + 16384;
+  static constexpr int kSlot = kP + 6144;           // 59 (a strip) or 71 (a head) blocks of 1 KiB
+  static constexpr int kBlocks = kSlot / 1024;
   static constexpr int kNSlot = NS;
-  static constexpr int kBytes = kNSlot * kSlot;
+  static constexpr int kNorm = NS * kSlot;          // GATED: [2 chunks][8 waves][64 tokens] fp32
+  static constexpr int kBytes = kNorm + (GATED ? 2 * 8 * CH * 4 : 0);
 };
-constexpr int kSlotBlocks = 59;
 constexpr int kAhead = 6;    // operand fragments a state wave reads ahead of its products
-// A state wave's 54 operand fragments per chunk, as slot offsets, in the order its
-// products take them: [0, 32) pairs of -W (even: row tile (j/2) & 3, key step j/8)
-// and Q^T (odd: key step j/8, token tile (j/2) & 3); [32, 48) Kd (key tile
-// (j-32) & 7, chunk step (j-32) / 8); [48, 54) the P^T fragments.
+// A state wave's 54 operand fragments per chunk, as slot offsets of a one-strip slot,
+// in the order its products take them: [0, 32) pairs of -W (even: row tile (j/2) & 3,
+// key step j/8) and Q^T (odd: key step j/8, token tile (j/2) & 3); [32, 48) Kd (key
+// tile (j-32) & 7, chunk step (j-32) / 8); [48, 54) the P^T fragments.
 constexpr int kNFrag = 54;
 constexpr int kFragOff[kNFrag] = {0, 37888, 4096, 38912, 8192, 39936, 12288, 40960, 1024, 41984, 5120, 43008, 9216, 44032, 13312, 45056, 2048, 46080, 6144, 47104, 10240, 48128, 14336, 49152, 3072, 50176, 7168, 51200, 11264, 52224, 15360, 53248, 16384, 18432, 20480, 22528, 24576, 26624, 28672, 30720, 17408, 19456, 21504, 23552, 25600, 27648, 29696, 31744, 54272, 55296, 56320, 57344, 58368, 59392};
+// the same offsets in a slot of spw strips (Q^T and P^T follow the longer U0).  spw
+// and the slot helpers below take the strip count as an argument, not a template
+// parameter: the kernel calls them from lambdas, where a call of a function template
+// keeps the host side from instantiating the kernel template's launch stub.
+__device__ __forceinline__ constexpr int frag_off(int jf, int spw) {
+  return (jf < 32 && (jf & 1)) || jf >= 48 ? kFragOff[jf] + 4096 * (spw - 1) : kFragOff[jf];
+}
 
-// source of 1 KiB block m of a chunk's input slot (blocks follow the slot layout)
+// source of 1 KiB block m of a chunk's input slot of spw strips (blocks follow the
+// slot layout); strip: the first of the workgroup's strips
 __device__ __forceinline__ const unsigned char* slot_src(int m, const unsigned char* wsh, const unsigned char* wsk,
-                                                         int strip) {
-  return m < 32 ? wsh + 1024 * m                                         // -W, Kd
-       : m < 36 ? wsh + WH_U0 + strip * 4096 + 1024 * (m - 32)           // U0 of this strip's two value tiles
-       : m < 37 ? wsh + WH_SC                                            // scalings
-       : m < 53 ? wsk + 1024 * (m - 37)                                  // Q^T of the key head
-                : wsh + WH_P + 1024 * (m - 53);                          // P^T
+                                                         int strip, int spw) {
+  const int kU = 32 + 4 * spw;
+  return m < 32 ? wsh + 1024 * m                                           // -W, Kd
+       : m < kU ? wsh + WH_U0 + strip * 4096 + 1024 * (m - 32)             // U0 of the strips' value tiles
+       : m < kU + 1 ? wsh + WH_SC                                          // scalings
+       : m < kU + 17 ? wsk + 1024 * (m - kU - 1)                           // Q^T of the key head
+                     : wsh + WH_P + 1024 * (m - kU - 17);                  // P^T
 }
 
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
@@ -812,25 +827,37 @@ __device__ __forceinline__ void seq_chunks(const RecArgs& a, int b, int& cs, int
 // The window holds chunks [c0, c0 + nw) (workspace stride nwin).  A sequence's
 // state comes from state_in at its first chunk and from `carry` otherwise, and
 // goes to state_out after its last chunk and to `carry` otherwise.
-template <int NS>
-__global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, unsigned char* ws, int nwin,
-                                                             int nw, float* carry) {
-  using L = ChainLds<NS>;
+// GATED (whole heads only): the gated RMSNorm of each output row needs the sum of
+// squares over the head's 128 columns, which eight waves hold.  Each state wave
+// leaves its 16 columns' sums of chunk c in LDS before the chunk's barrier and
+// finishes chunk c's rows (norm, gate, store) during chunk c+1, after the barrier;
+// the last chunk's rows after one more barrier.
+template <int NS, int SPW, bool GATED>
+__global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_chain_kernel(
+    RecArgs a, int c0, unsigned char* ws, int nwin, int nw, float* carry) {
+  static_assert(SPW == 1 || SPW == 4, "a strip or a whole head");
+  static_assert(!GATED || SPW == 4, "the gated norm needs whole rows");
+  using L = ChainLds<NS, SPW, GATED>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
-  // Workgroups are handed to the 8 XCDs round-robin by linear index; when the
-  // (slot, head) count is a multiple of 8, the 4 strips of a head get indices
-  // that are equal modulo 8, so they share one XCD's L2 for the head's inputs.
   const int L0 = blockIdx.x;
-  const int nheads = static_cast<int>(gridDim.x) >> 2;
   int jh, strip;
-  if ((nheads & 7) == 0) {
-    jh = (L0 >> 5) * 8 + (L0 & 7);
-    strip = (L0 >> 3) & 3;
+  if constexpr (SPW == 4) {
+    jh = L0;
+    strip = wv < 8 ? wv >> 1 : 0;   // a state wave's strip; the copy wave copies all four
   } else {
-    jh = L0 >> 2;
-    strip = L0 & 3;
+    // Workgroups are handed to the 8 XCDs round-robin by linear index; when the
+    // (slot, head) count is a multiple of 8, the 4 strips of a head get indices
+    // that are equal modulo 8, so they share one XCD's L2 for the head's inputs.
+    const int nheads = static_cast<int>(gridDim.x) >> 2;
+    if ((nheads & 7) == 0) {
+      jh = (L0 >> 5) * 8 + (L0 & 7);
+      strip = (L0 >> 3) & 3;
+    } else {
+      jh = L0 >> 2;
+      strip = L0 & 3;
+    }
   }
   const int j = jh / a.Hv, hv = jh - j * a.Hv;   // slot, value head
   int b = j;                                      // sequence
@@ -863,14 +890,16 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
     const unsigned char* wsh = wsh_of(cl);
     const unsigned char* wsk = wsk_of(cl);
 #pragma unroll
-    for (int m = 0; m < kSlotBlocks; ++m)
-      __builtin_amdgcn_global_load_lds(slot_src(m, wsh, wsk, strip) + 16 * lane, slot + 1024 * m, 16, 0, 0);
+    for (int m = 0; m < L::kBlocks; ++m)
+      __builtin_amdgcn_global_load_lds(slot_src(m, wsh, wsk, SPW == 1 ? strip : 0, SPW) + 16 * lane,
+                                       slot + 1024 * m, 16, 0, 0);
   };
 
-  // Waves 0 and 1 each carry 16 value columns of the strip (32 strip + 16 wave ..)
-  // and form their outputs; wave 2 copies.  The three waves sit on three SIMDs.
-  if (wv < 2) {
-    const int sh = wv;
+  // Waves 2s and 2s+1 each carry 16 value columns of strip s (32 strip + 16 wave ..)
+  // and form their outputs; the last wave copies.  With one strip the three waves
+  // sit on three SIMDs.
+  if (wv < 2 * SPW) {
+    const int sh = wv & 1;
     const int col = 32 * strip + 16 * sh + l16;   // this lane's value column
     const int vtile = 2 * strip + sh;             // value tile of the head (16 columns)
     floatx4 Ms[8];     // 2^s_cur M, rows 16dt + 4g + v, column col
@@ -900,6 +929,51 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
     const int hand = 96 + vtile;
     const int ci0 = lo - cs;   // chunk index inside the sequence of the window's first chunk
     uint16_t* go = static_cast<uint16_t*>(a.o) + tok0 * a.so + hv * DK + 32 * strip + 16 * sh + 4 * g4;
+    // GATED: the rows of the previous chunk (unscaled outputs, z) until they are normed
+    float* nrm = reinterpret_cast<float*>(smem + L::kNorm);
+    const uint16_t* gz = static_cast<const uint16_t*>(a.gz) + tok0 * a.sz + hv * DK + 32 * strip + 16 * sh + 4 * g4;
+    float nw4[4];     // norm weights of this lane's four columns
+    floatx4 Op[4];    // the previous chunk's outputs
+    uint2 zp[4];      // its gate inputs, four bf16 per token tile
+    if constexpr (GATED) {
+      const uint2 wb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.gw) + 16 * vtile + 4 * g4);
+      nw4[0] = bf16_bits_to_f32(static_cast<uint16_t>(wb.x));
+      nw4[1] = bf16_bits_to_f32(static_cast<uint16_t>(wb.x >> 16));
+      nw4[2] = bf16_bits_to_f32(static_cast<uint16_t>(wb.y));
+      nw4[3] = bf16_bits_to_f32(static_cast<uint16_t>(wb.y >> 16));
+    }
+    // z of chunk ci (rows past the sequence's end are not read)
+    auto load_z = [&](int ci, int nval) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int r = 16 * ct + l16;
+        zp[ct] = r < nval ? *reinterpret_cast<const uint2*>(gz + (static_cast<int64_t>(ci) * CH + r) * a.sz)
+                          : uint2{0u, 0u};
+      }
+    };
+    // the gated norm of chunk ci's rows (window chunk pcl), once every wave's sums are in LDS
+    auto finish_rows = [&](int pcl, int ci, int nval) {
+      const float* nb = nrm + (pcl & 1) * 8 * CH;
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) tot += nb[w * CH + lane];   // token `lane`
+      const float inv = rsqrtf(tot * (1.0f / DK) + a.geps);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int r = 16 * ct + l16;
+        const float iv = __shfl(inv, r, 64);
+        const uint32_t zw[2] = {zp[ct].x, zp[ct].y};
+        float y[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float z = bf16_bits_to_f32(static_cast<uint16_t>(zw[v >> 1] >> (16 * (v & 1))));
+          y[v] = Op[ct][v] * iv * nw4[v] * z * sigmoidf_(z);
+        }
+        const uint2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        if (r < nval) *reinterpret_cast<uint2*>(go + (static_cast<int64_t>(ci) * CH + r) * a.so) = w;
+      }
+    };
+    int pnval = 0;    // GATED: rows of the previous chunk
     __syncthreads();
     int s_cur, est;   // est: 2^(est+1) bounds the decayed part of the state measured last (scaled)
     halfx8 Mfr[4];
@@ -963,16 +1037,18 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) Mfr[ks] = stack_h(Ms[2 * ks], Ms[2 * ks + 1]);
     }
+    if constexpr (GATED) load_z(ci0, min(CH, len - ci0 * CH));
 #pragma clang loop unroll(disable)
     for (int cl = 0; cl < nchunk; ++cl) {
       unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
       const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
       // The step's operand fragments are read kAhead ahead of their products
       // (kFragOff), across the three phases below.
-      auto rd = [&](int jf) { return *reinterpret_cast<const halfx8*>(slot + kFragOff[jf] + lane * 16); };
+      auto rd = [&](int jf) { return *reinterpret_cast<const halfx8*>(slot + frag_off(jf, SPW) + lane * 16); };
       const float gC = sSc[64];
-      const halfx8 u0a = *reinterpret_cast<const halfx8*>(slot + L::kU0 + sh * 2048 + lane * 32);
-      const halfx8 u0b = *reinterpret_cast<const halfx8*>(slot + L::kU0 + sh * 2048 + lane * 32 + 16);
+      const int u0t = SPW == 1 ? sh : vtile;   // the value tile's place in the slot's U0
+      const halfx8 u0a = *reinterpret_cast<const halfx8*>(slot + L::kU0 + u0t * 2048 + lane * 32);
+      const halfx8 u0b = *reinterpret_cast<const halfx8*>(slot + L::kU0 + u0t * 2048 + lane * 32 + 16);
       float gam[4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) gam[ct] = sSc[16 * ct + l16];
@@ -1039,6 +1115,12 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
         Ms[(jf - 32) & 7] = mfma16h(F[jf], Uf[(jf - 32) >> 3], Ms[(jf - 32) & 7]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (GATED) {
+        if (cl > 0) {
+          finish_rows(cl - 1, ci - 1, pnval);
+          load_z(ci, min(CH, len - ci * CH));
+        }
+      }
       // ---- O^T += U^T P^T: P^T fragment f covers token tile f (chunk step 0) or f - 2 (step 1)
 #pragma unroll
       for (int f = 0; f < 6; ++f) {
@@ -1061,14 +1143,39 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) O[ct] *= os;
       }
+      if constexpr (GATED) {
+        // this chunk's sums of squares over the wave's 16 columns: token tile ct's in every
+        // lane of the row, token `lane`'s to LDS
+        float p[4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int r = 16 * ct + l16;
-        const uint2 w = {pack_bf16x2(O[ct][0], O[ct][1]), pack_bf16x2(O[ct][2], O[ct][3])};
-        if (r < nval) *reinterpret_cast<uint2*>(go + (static_cast<int64_t>(ci) * CH + r) * a.so) = w;
+        for (int ct = 0; ct < 4; ++ct) {
+          p[ct] = O[ct][0] * O[ct][0];
+#pragma unroll
+          for (int v = 1; v < 4; ++v) p[ct] = fmaf(O[ct][v], O[ct][v], p[ct]);
+          p[ct] += __shfl_xor(p[ct], 16, 64);
+          p[ct] += __shfl_xor(p[ct], 32, 64);
+          Op[ct] = O[ct];
+        }
+        nrm[((cl & 1) * 8 + wv) * CH + lane] = g4 == 0 ? p[0] : g4 == 1 ? p[1] : g4 == 2 ? p[2] : p[3];
+        pnval = nval;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int r = 16 * ct + l16;
+          const uint2 w = {pack_bf16x2(O[ct][0], O[ct][1]), pack_bf16x2(O[ct][2], O[ct][3])};
+          if (r < nval) *reinterpret_cast<uint2*>(go + (static_cast<int64_t>(ci) * CH + r) * a.so) = w;
+        }
       }
       // slot cl may be refilled once both state waves have passed this barrier
       __builtin_amdgcn_s_barrier();
+      if constexpr (GATED) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
+    if constexpr (GATED) {
+      // the last chunk's rows, once every wave's sums are in LDS
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      finish_rows(nchunk - 1, ci0 + nchunk - 1, pnval);
     }
     if (hi < ce && lane == 0) {
       // the scale handed to the next window (the block of this window's last chunk, nwin - 1)
@@ -1098,6 +1205,7 @@ __global__ __launch_bounds__(192, 2) void chunk_chain_kernel(RecArgs a, int c0, 
       // above covers the ones the others read next
       __builtin_amdgcn_s_barrier();
     }
+    if constexpr (GATED) __builtin_amdgcn_s_barrier();   // the state waves' last rows
   }
 }
 
@@ -1227,11 +1335,17 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_prep_kernel<false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<2>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<2>::kBytes);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<2, 1, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<2, 1, false>::kBytes);
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<1>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<1>::kBytes);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<1, 1, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<1, 1, false>::kBytes);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<2, 4, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<2, 4, false>::kBytes);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<2, 4, true>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<2, 4, true>::kBytes);
   });
   if (ea != hipSuccess) return ea;
   const int nchunks = chunk_count(a);
@@ -1290,13 +1404,24 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     // 4, 128 value heads: 9.9 ms of prefill against 10.7 ms).  A packed batch
     // runs one slot per sequence with chunks in the window, which the host does
     // not know; the few it has per window run better with two slots.
+    // When the heads alone fill the GPU, one workgroup per head copies each chunk's
+    // operands into LDS once instead of once per strip (batch 4, T=32768, 128 value
+    // heads: 8.37 ms of prefill against 10.34 ms with the one-slot strips, the same
+    // bits); the gated norm needs whole rows and always runs so.
     const dim3 grid(slots * a.Hv * (DK / 32));
-    if (!a.cu_seqlens && a.B * a.Hv * (DK / 32) > device_cu_count())
-      hipLaunchKernelGGL(chunk_chain_kernel<1>, grid, dim3(192), ChainLds<1>::kBytes, s, r, c0,
-                         wsb, nwin, nw, carry);
+    const bool heads_fill = !a.cu_seqlens && a.B * a.Hv >= device_cu_count();
+    if (a.gz)
+      hipLaunchKernelGGL((chunk_chain_kernel<2, 4, true>), dim3(slots * a.Hv), dim3(576),
+                         (ChainLds<2, 4, true>::kBytes), s, r, c0, wsb, nwin, nw, carry);
+    else if (heads_fill)
+      hipLaunchKernelGGL((chunk_chain_kernel<2, 4, false>), dim3(slots * a.Hv), dim3(576),
+                         (ChainLds<2, 4, false>::kBytes), s, r, c0, wsb, nwin, nw, carry);
+    else if (!a.cu_seqlens && a.B * a.Hv * (DK / 32) > device_cu_count())
+      hipLaunchKernelGGL((chunk_chain_kernel<1, 1, false>), grid, dim3(192), (ChainLds<1, 1, false>::kBytes), s, r,
+                         c0, wsb, nwin, nw, carry);
     else
-      hipLaunchKernelGGL(chunk_chain_kernel<2>, grid, dim3(192), ChainLds<2>::kBytes, s, r, c0,
-                         wsb, nwin, nw, carry);
+      hipLaunchKernelGGL((chunk_chain_kernel<2, 1, false>), grid, dim3(192), (ChainLds<2, 1, false>::kBytes), s, r,
+                         c0, wsb, nwin, nw, carry);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

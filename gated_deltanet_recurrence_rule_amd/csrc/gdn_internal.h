@@ -71,6 +71,13 @@ struct RecArgs {
   // by the launcher's map kernel.
   const int32_t* chunk_start = nullptr;
   const int32_t* chunk_seq = nullptr;
+  // Chunked prefill with the gated RMSNorm applied in the chain (bf16 I/O): o then
+  // receives y = o_row / sqrt(mean(o_row^2) + geps) * w * z * sigmoid(z) per (token,
+  // value head) row instead of o; z is [token][sz] bf16 (head h at h*D), w [D] bf16.
+  const void* gz = nullptr;
+  int64_t sz = 0;
+  const void* gw = nullptr;
+  float geps = 0.f;
 };
 
 // io: 0 = fp32, 1 = bf16 (same codes as gdn_dtype).
@@ -117,6 +124,8 @@ size_t chunk_map_bytes(const RecArgs& a);
 // chunks the windows run over, and the preferred number per window (balanced)
 int chunk_count(const RecArgs& a);
 int chunk_window_chunks(const RecArgs& a);
+// With a.gz set the chain applies the gated RMSNorm to every output row (one
+// workgroup per head); fixed-length batches only.
 hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 
 struct ConvArgs {

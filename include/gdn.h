@@ -74,6 +74,9 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  * keys and queries of norm about 1 or less (GDN_FLAG_QK_L2NORM gives that).
  * Use this flag for keys far from unit norm without the L2 flag. */
 #define GDN_FLAG_TOKEN_SERIAL 2u
+/* gdn_prefill_gated only: apply the norm inside the chunked kernels whatever the
+ * batch (without it they do when B * Hv is at least the GPU's CU count). */
+#define GDN_FLAG_NORM_IN_CHAIN 4u
 
 /*
  * Shapes of one recurrence call.
@@ -125,6 +128,33 @@ gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const
                        const float* log_alpha, const float* beta, const float* state_in,
                        float* state_out, void* o, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * gdn_prefill_gated -- gdn_prefill followed by the layer's gated RMSNorm of
+ * every output row ("L'attention hybride", config block: swish output gate;
+ * table "Le decompte": one 128-weight norm per layer; the prefill as for
+ * gdn_prefill):
+ *     y[b,t,h,:] = o / sqrt(mean(o^2) + norm_eps) * norm_w * z * sigmoid(z)
+ * with o[b,t,h,:] the row gdn_prefill would write; o itself is not written.
+ *   dims, q, k, v, log_alpha, beta, state_in, state_out, workspace: as for
+ *               gdn_prefill (same workspace size query); dims->Dv in {64, 128}
+ *   z           [B, T, Hv, Dv] io dtype, token stride stride_z >= Hv*Dv (the
+ *               gate half of the projection output, a view is fine)
+ *   norm_w      [Dv] io dtype, shared by all heads
+ *   y           [B, T, Hv, Dv] io dtype, token stride dims->stride_o
+ * z, norm_w and y 16-byte aligned, stride_z and stride_o multiples of 8.
+ * Where the chunked kernels run and B * Hv is at least the GPU's CU count (or
+ * with GDN_FLAG_NORM_IN_CHAIN), the norm is applied in the chain kernel's
+ * output epilogue (one workgroup per value head holds whole rows) and o never
+ * reaches memory; otherwise the prefill writes o into y and the norm runs over
+ * y in place (two launches, the same results up to o's bf16 rounding).
+ * Errors as for gdn_prefill and gdn_gated_rmsnorm.
+ */
+gdn_status gdn_prefill_gated(const gdn_dims* dims, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, const float* state_in,
+                             float* state_out, const void* z, int64_t stride_z, const void* norm_w,
+                             float norm_eps, void* y, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * gdn_prefill_static -- gdn_prefill with no workspace argument and no

@@ -319,3 +319,33 @@ def test_prefill_static_rejects_dims_beyond_its_scratch():
     st = L.gdn_prefill_static(ctypes.byref(d), None, None, None, None, None, None, None, None, None)
     assert st == B.GDN_ERR_SHAPE
     assert "scratch" in B.gdn_last_error()
+
+
+def call_gated(d, z=FAKE, sz=6 * 128, w=FAKE, eps=1e-6, y=FAKE, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, be=FAKE, si=None, so=None, ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 30)
+    a.update(kw)
+    return B.lib().gdn_prefill_gated(None if d is None else ctypes.byref(d), a["q"], a["k"], a["v"], a["la"], a["be"],
+                                     a["si"], a["so"], z, sz, w, ctypes.c_float(eps), y, a["ws"], a["ws_bytes"], None)
+
+
+def test_prefill_gated_argument_errors():
+    assert call_gated(None) == B.GDN_ERR_NULL
+    assert call_gated(dims(), z=None) == B.GDN_ERR_NULL
+    assert call_gated(dims(), w=None) == B.GDN_ERR_NULL
+    assert call_gated(dims(), y=None) == B.GDN_ERR_NULL
+    assert call_gated(dims(), sz=6 * 128 - 8) == B.GDN_ERR_SHAPE       # z rows narrower than Hv*Dv
+    assert call_gated(dims(), eps=-1.0) == B.GDN_ERR_SHAPE
+    assert call_gated(dims(io=B.GDN_F32, D=16)) == B.GDN_ERR_UNSUPPORTED   # the norm takes Dv 64 or 128
+    assert call_gated(dims(), z=ctypes.c_void_p(0x10008)) == B.GDN_ERR_ALIGN
+    assert call_gated(dims(), sz=6 * 128 + 4) == B.GDN_ERR_ALIGN
+    assert call_gated(dims(), q=None) == B.GDN_ERR_NULL                # the prefill's own checks
+    assert call_gated(dims(), ws=None) == B.GDN_ERR_NULL
+    d = dims()
+    d.flags = B.GDN_FLAG_NORM_IN_CHAIN | 0x8
+    assert call_gated(d) == B.GDN_ERR_SHAPE                             # unknown bit beside the chain flag
+    assert call_gated(dims(B=0)) == B.GDN_OK
+    # the chain flag is gdn_prefill_gated's own: gdn_prefill rejects it, the size query ignores it
+    d = dims(T=64)
+    d.flags = B.GDN_FLAG_NORM_IN_CHAIN
+    assert call_prefill(d) == B.GDN_ERR_SHAPE
+    assert B.gdn_prefill_workspace_size(d) == B.gdn_prefill_workspace_size(dims(T=64))

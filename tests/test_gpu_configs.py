@@ -19,7 +19,9 @@ gated_deltanet_recurrence_rule_amd.workloads.
             checked against the oracle applied to the bf16 tensor the previous
             stage handed on through the API (the conv output y, the prefill
             output o), so that every comparison is held to the stated bound
-            with no allowance for upstream rounding
+            with no allowance for upstream rounding; and gdn_prefill_gated (the
+            norm inside the chain kernel) against the oracle's norm of the
+            oracle's unrounded outputs
 """
 import os
 
@@ -162,7 +164,9 @@ def test_cfg_long_full_and_two_halves():
 
 
 def test_cfg_block_full():
-    """conv+SiLU -> prefill (L2 flag) -> gated RMSNorm at batch 4, T=32768, 16/128 heads."""
+    """conv+SiLU -> prefill (L2 flag) -> gated RMSNorm at batch 4, T=32768, 16/128 heads, with the
+    norm as its own launch and inside the chain kernel (gdn_prefill_gated, which takes that path
+    here since the 512 heads fill the GPU)."""
     torch = _torch()
     blk = W.block_inputs()
     B, T, Hk, Hv, D, C = blk["B"], blk["T"], blk["Hk"], blk["Hv"], blk["D"], blk["C"]
@@ -174,9 +178,13 @@ def test_cfg_block_full():
                       l2norm=True, l2_eps=1e-6)
     z = to_dev(blk["z"])
     out = G.gdn_gated_rmsnorm(o.view(B * T, Hv * D), z.view(B * T, Hv * D), to_dev(blk["norm_w"]), 1e-5, H=Hv)
+    so_f = torch.empty_like(so)
+    yf = G.gdn_prefill_gated(qv, kv, vv, to_dev(blk["log_alpha"]), to_dev(blk["beta"]), z, to_dev(blk["norm_w"]),
+                             1e-5, None, so_f, Hk=Hk, Hv=Hv, l2norm=True, l2_eps=1e-6)
     torch.cuda.synchronize()
-    del x
-    worst = [0.0, 0.0, 0.0]
+    assert torch.equal(so_f, so), "the gated call's state differs from gdn_prefill's"
+    del x, so_f
+    worst = [0.0, 0.0, 0.0, 0.0]
     for (b, h) in [(0, 0), (0, 64), (1, 37), (1, 101), (2, 71), (2, 8), (3, 127), (3, 90)]:
         hk = h // (Hv // Hk)
         chans = [(hk * D, "q"), (Hk * D + hk * D, "k"), (2 * Hk * D + h * D, "v")]
@@ -203,9 +211,15 @@ def test_cfg_block_full():
         yn = oracle.gated_rmsnorm(ogpu, zr, blk["norm_w"], 1e-5, n_threads=NTHR)
         mn = assert_out(to_host(out.view(B, T, Hv * D)[b, :, h * D:(h + 1) * D]), yn, bf16=True,
                         what=f"block out {b},{h}")
-        worst = [max(worst[0], m["excess_rms"]), max(worst[1], e), max(worst[2], mn["excess_rms"])]
+        # the norm in the chain against the oracle's norm of the oracle's unrounded outputs
+        yfr = oracle.gated_rmsnorm(np.ascontiguousarray(orf[0]), zr, blk["norm_w"], 1e-5, n_threads=NTHR)
+        mf = assert_out(to_host(yf[b, :, h * D:(h + 1) * D]), yfr, bf16=True, what=f"block gated {b},{h}")
+        worst = [max(worst[0], m["excess_rms"]), max(worst[1], e), max(worst[2], mn["excess_rms"]),
+                 max(worst[3], mf["excess_rms"])]
         print(f"block head {b},{h}: prefill excess {m['excess_rms']:.2e}, state {e:.2e}, "
-              f"out excess {mn['excess_rms']:.2e} (literal {mn['max_err_rms']:.2e})")
-    print(f"block: worst prefill excess {worst[0]:.2e}, state {worst[1]:.2e}, norm excess {worst[2]:.2e}")
-    del y, o, z, out
+              f"out excess {mn['excess_rms']:.2e} (literal {mn['max_err_rms']:.2e}), "
+              f"norm in chain excess {mf['excess_rms']:.2e}")
+    print(f"block: worst prefill excess {worst[0]:.2e}, state {worst[1]:.2e}, norm excess {worst[2]:.2e}, "
+          f"norm in chain excess {worst[3]:.2e}")
+    del y, o, z, out, yf
     _free()
