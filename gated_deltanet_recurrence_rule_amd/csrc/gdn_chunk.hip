@@ -127,6 +127,16 @@ __device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
   return max(max(r0, r1), max(r2, r3));
 }
 
+// Sum of x over each row of 16 lanes, in every lane of the row: pairs within quads,
+// then quads (lane i with 7 - i of each half row), then half rows (i with 15 - i).
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
 // max(|a|, |b|, |c|) in one instruction (fmaxf would add a NaN-quieting step per operand)
 __device__ __forceinline__ float max3_abs(float a, float b, float c) {
   float r;
@@ -438,15 +448,23 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   }
 
   // ---- K, Q rows and their norms ------------------------------------------
+  // All eight 16-byte loads go out before any is used (rows past the sequence end
+  // read the last valid row and are replaced by zeros), so the rows cost one memory
+  // round trip; each row's sums of squares over its 16 lanes by DPP.
+  u16x8 kq[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int vi = tid + 256 * j;
+    const int r = vi >> 4, c8 = (vi & 15) * 8, rr = r < nval ? r : nval - 1;
+    kq[2 * j] = *reinterpret_cast<const u16x8*>(gk + (tokbase + rr) * a.sk + hk * DK + c8);
+    kq[2 * j + 1] = *reinterpret_cast<const u16x8*>(gq + (tokbase + rr) * a.sq + hk * DK + c8);
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int vi = tid + 256 * j;
     const int r = vi >> 4, c8 = (vi & 15) * 8;
-    u16x8 kv = {0, 0, 0, 0, 0, 0, 0, 0}, qv = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (r < nval) {
-      kv = *reinterpret_cast<const u16x8*>(gk + (tokbase + r) * a.sk + hk * DK + c8);
-      qv = *reinterpret_cast<const u16x8*>(gq + (tokbase + r) * a.sq + hk * DK + c8);
-    }
+    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    const u16x8 kv = r < nval ? kq[2 * j] : z8, qv = r < nval ? kq[2 * j + 1] : z8;
     *reinterpret_cast<u16x8*>(sK + r * KP + c8) = kv;
     *reinterpret_cast<u16x8*>(sQ + r * KP + c8) = qv;
     float ssk = 0.f, ssq = 0.f;
@@ -456,11 +474,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       ssk = fmaf(kf, kf, ssk);
       ssq = fmaf(qf, qf, ssq);
     }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) {
-      ssk += __shfl_xor(ssk, m, 64);
-      ssq += __shfl_xor(ssq, m, 64);
-    }
+    ssk = row16_sum(ssk);
+    ssq = row16_sum(ssq);
     if ((vi & 15) == 0) {
       vRk[r] = l2 ? rsqrtf(ssk + a.l2_eps) : 1.f;
       vRq[r] = (l2 ? rsqrtf(ssq + a.l2_eps) : 1.f) * a.q_scale;
@@ -929,6 +944,9 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
     const int hand = 96 + vtile;
     const int ci0 = lo - cs;   // chunk index inside the sequence of the window's first chunk
     uint16_t* go = static_cast<uint16_t*>(a.o) + tok0 * a.so + hv * DK + 32 * strip + 16 * sh + 4 * g4;
+    int64_t roff[4];   // element offsets of this lane's output rows inside a chunk
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) roff[ct] = static_cast<int64_t>(16 * ct + l16) * a.so;
     // GATED: the rows of the previous chunk (unscaled outputs, z) until they are normed
     float* nrm = reinterpret_cast<float*>(smem + L::kNorm);
     const uint16_t* gz = static_cast<const uint16_t*>(a.gz) + tok0 * a.sz + hv * DK + 32 * strip + 16 * sh + 4 * g4;
@@ -1063,22 +1081,10 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
       for (int jf = 0; jf < kAhead; ++jf) F[jf] = rd(jf);
       const float gCs = dpend == 0 ? gC : __builtin_amdgcn_ldexpf(gC, dpend);
       __builtin_amdgcn_sched_barrier(0);
+      // U = -W M first and U0 after: the first products wait for nothing but their fragments
       floatx4 U[4], O[4];
-      if (s_cur == rexp) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) U[rt][v] = static_cast<float>(rt < 2 ? u0a[4 * rt + v] : u0b[4 * (rt - 2) + v]);
-      } else {
-        const float u0s = __builtin_amdgcn_ldexpf(1.f, s_cur - rexp);   // a power of two < 1 (0 far below)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            U[rt][v] = static_cast<float>(rt < 2 ? u0a[4 * rt + v] : u0b[4 * (rt - 2) + v]) * u0s;
-      }
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) O[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < 4; ++rt) U[rt] = O[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
       // ---- U = U0 - W M and O^T = M^T Q^T, interleaved ---------------------------
 #pragma unroll
       for (int jf = 0; jf < 32; ++jf) {
@@ -1093,6 +1099,14 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
           for (int dt = 0; dt < 8; ++dt) Ms[dt] *= gCs;
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        const float u0s = __builtin_amdgcn_ldexpf(1.f, s_cur - rexp);   // 1, or a power of two < 1 (0 far below)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            U[rt][v] = fmaf(static_cast<float>(rt < 2 ? u0a[4 * rt + v] : u0b[4 * (rt - 2) + v]), u0s, U[rt][v]);
       }
       halfx8 Uf[2];
       Uf[0] = stack_h(U[0], U[1]);
@@ -1160,11 +1174,19 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
         pnval = nval;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
       } else {
+        uint16_t* gc = go + static_cast<int64_t>(ci) * CH * a.so;
+        if (nval == CH) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const int r = 16 * ct + l16;
-          const uint2 w = {pack_bf16x2(O[ct][0], O[ct][1]), pack_bf16x2(O[ct][2], O[ct][3])};
-          if (r < nval) *reinterpret_cast<uint2*>(go + (static_cast<int64_t>(ci) * CH + r) * a.so) = w;
+          for (int ct = 0; ct < 4; ++ct) {
+            const uint2 w = {pack_bf16x2(O[ct][0], O[ct][1]), pack_bf16x2(O[ct][2], O[ct][3])};
+            *reinterpret_cast<uint2*>(gc + roff[ct]) = w;
+          }
+        } else {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const uint2 w = {pack_bf16x2(O[ct][0], O[ct][1]), pack_bf16x2(O[ct][2], O[ct][3])};
+            if (16 * ct + l16 < nval) *reinterpret_cast<uint2*>(gc + roff[ct]) = w;
+          }
         }
       }
       // slot cl may be refilled once both state waves have passed this barrier
