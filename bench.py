@@ -605,7 +605,14 @@ def main():
                     help="run only a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--decode-only", type=int, choices=(1, 2), default=0,
                     help="run only the 256 decode steps on 1 or 2 state pools (for counter runs)")
+    ap.add_argument("--block-only", action="store_true",
+                    help="run only the block leg (batch 4, T=32768, 16/128 heads; for trace runs)")
     args = ap.parse_args()
+    if args.block_only:
+        import torch
+        r = bench_block(torch.device("cuda:0"))
+        print(json.dumps(r))
+        return
     if args.decode_only:
         import torch
         r = bench_decode(torch.device("cuda:0"), pools=args.decode_only)
