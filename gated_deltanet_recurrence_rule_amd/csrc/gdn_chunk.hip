@@ -91,7 +91,8 @@ constexpr int WH_U0 = 32768;   // U0 = T' V as accumulators of U: [value tile 8]
 constexpr int WH_P = 49152;    // P^T, B operand: 6 fragments (token tile ct, rows 32ks..), see pfrag()
 constexpr int WH_SC = 55296;   // gamma_r (64 floats), gamma_63; int32: V scale exponents of the 8 value
                                // tiles at [65, 73), gamma_63's exponent at 73, the next chunk's V scale
-                               // exponents at [80, 88); [96, 112): the chain's scale hand-over between windows
+                               // exponents at [80, 88); [96, 112): the chain's scale hand-over between windows;
+                               // with khat, e^{g_63 - g_r} (64 floats) at [128, 192)
 constexpr int WH_BYTES = 56320;
 // workspace block per (batch, key head, chunk): Q^T = (diag(rq) Q)^T, B operand: fragment ks*4+ct
 // (keys 32ks.., tokens 16ct..)
@@ -502,9 +503,10 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
     vg[lane] = g;
     vg[CH + lane] = be;
     vg[2 * CH + lane] = eg * vRk[lane];
-    vg[3 * CH + lane] = __expf(gl - g) * vRk[lane];
+    vg[3 * CH + lane] = a.khat ? vRk[lane] : __expf(gl - g) * vRk[lane];
     float* sc = reinterpret_cast<float*>(ws + (static_cast<int64_t>(b * a.Hv + hk * a.G + j) * nwin + cl) * WH_BYTES + WH_SC);
     sc[lane] = eg;
+    if (a.khat) sc[128 + lane] = __expf(gl - g);
     if (lane == 0) {
       const float g63 = __expf(gl);
       sc[64] = g63;
@@ -718,7 +720,9 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
               kf[e] = static_cast<_Float16>(kv * (e < 4 ? sa[e] : sb[e - 4]));
               df[e] = static_cast<_Float16>(kv * (e < 4 ? da[e] : db[e - 4]));
             }
-            *reinterpret_cast<halfx8*>(wsc + WH_KD + ((2 * wv + t) * 2 + ki) * 1024 + lane * 16) = df;
+            // with khat only the key head's first value head stores its (head-independent) K^ = diag(rk) K
+            if (!a.khat || j == 0)
+              *reinterpret_cast<halfx8*>(wsc + WH_KD + ((2 * wv + t) * 2 + ki) * 1024 + lane * 16) = df;
 #pragma unroll
             for (int f = 0; f < 6; ++f)
               if (kTriKi[f] == ki) w[t][kTriRt[f]] = mfma16h(kf, tf[f], w[t][kTriRt[f]]);
@@ -800,10 +804,11 @@ __device__ __forceinline__ constexpr int frag_off(int jf, int spw) {
 
 // source of 1 KiB block m of a chunk's input slot of spw strips (blocks follow the
 // slot layout); strip: the first of the workgroup's strips
-__device__ __forceinline__ const unsigned char* slot_src(int m, const unsigned char* wsh, const unsigned char* wsk,
-                                                         int strip, int spw) {
+__device__ __forceinline__ const unsigned char* slot_src(int m, const unsigned char* wsh, const unsigned char* wkd,
+                                                         const unsigned char* wsk, int strip, int spw) {
   const int kU = 32 + 4 * spw;
-  return m < 32 ? wsh + 1024 * m                                           // -W, Kd
+  return m < 16 ? wsh + 1024 * m                                           // -W
+       : m < 32 ? wkd + 1024 * m                                           // Kd (or K^, see khat)
        : m < kU ? wsh + WH_U0 + strip * 4096 + 1024 * (m - 32)             // U0 of the strips' value tiles
        : m < kU + 1 ? wsh + WH_SC                                          // scalings
        : m < kU + 17 ? wsk + 1024 * (m - kU - 1)                           // Q^T of the key head
@@ -900,13 +905,18 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
   const unsigned char* regK = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WH_BYTES;
   auto wsh_of = [&](int cl) { return ws + (static_cast<int64_t>(bh) * nwin + lofs + cl) * WH_BYTES; };
   auto wsk_of = [&](int cl) { return regK + (static_cast<int64_t>(bw * a.Hk + hk) * nwin + lofs + cl) * WK_BYTES; };
+  // whole heads: K^ comes from the key head's first value head (khat)
+  auto wkd_of = [&](int cl) {
+    return SPW == 4 ? ws + (static_cast<int64_t>(bw * a.Hv + hk * a.G) * nwin + lofs + cl) * WH_BYTES : wsh_of(cl);
+  };
   auto copy_chunk = [&](int cl) {
     unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
     const unsigned char* wsh = wsh_of(cl);
+    const unsigned char* wkd = wkd_of(cl);
     const unsigned char* wsk = wsk_of(cl);
 #pragma unroll
     for (int m = 0; m < L::kBlocks; ++m)
-      __builtin_amdgcn_global_load_lds(slot_src(m, wsh, wsk, SPW == 1 ? strip : 0, SPW) + 16 * lane,
+      __builtin_amdgcn_global_load_lds(slot_src(m, wsh, wkd, wsk, SPW == 1 ? strip : 0, SPW) + 16 * lane,
                                        slot + 1024 * m, 16, 0, 0);
   };
 
@@ -950,15 +960,13 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
     // GATED: the rows of the previous chunk (unscaled outputs, z) until they are normed
     float* nrm = reinterpret_cast<float*>(smem + L::kNorm);
     const uint16_t* gz = static_cast<const uint16_t*>(a.gz) + tok0 * a.sz + hv * DK + 32 * strip + 16 * sh + 4 * g4;
-    float nw4[4];     // norm weights of this lane's four columns
+    // the gated norm's registers leave fewer for fragments in flight
+    constexpr int kAh = GATED ? 4 : kAhead;
+    uint2 nwb;        // norm weights of this lane's four columns (bf16)
     floatx4 Op[4];    // the previous chunk's outputs
     uint2 zp[4];      // its gate inputs, four bf16 per token tile
     if constexpr (GATED) {
-      const uint2 wb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.gw) + 16 * vtile + 4 * g4);
-      nw4[0] = bf16_bits_to_f32(static_cast<uint16_t>(wb.x));
-      nw4[1] = bf16_bits_to_f32(static_cast<uint16_t>(wb.x >> 16));
-      nw4[2] = bf16_bits_to_f32(static_cast<uint16_t>(wb.y));
-      nw4[3] = bf16_bits_to_f32(static_cast<uint16_t>(wb.y >> 16));
+      nwb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.gw) + 16 * vtile + 4 * g4);
     }
     // z of chunk ci (rows past the sequence's end are not read)
     auto load_z = [&](int ci, int nval) {
@@ -985,7 +993,8 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float z = bf16_bits_to_f32(static_cast<uint16_t>(zw[v >> 1] >> (16 * (v & 1))));
-          y[v] = Op[ct][v] * iv * nw4[v] * z * sigmoidf_(z);
+          const float nw = bf16_bits_to_f32(static_cast<uint16_t>((v < 2 ? nwb.x : nwb.y) >> (16 * (v & 1))));
+          y[v] = Op[ct][v] * iv * nw * z * sigmoidf_(z);
         }
         const uint2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
         if (r < nval) *reinterpret_cast<uint2*>(go + (static_cast<int64_t>(ci) * CH + r) * a.so) = w;
@@ -1060,7 +1069,7 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
     for (int cl = 0; cl < nchunk; ++cl) {
       unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
       const float* sSc = reinterpret_cast<const float*>(slot + L::kSc);
-      // The step's operand fragments are read kAhead ahead of their products
+      // The step's operand fragments are read kAh ahead of their products
       // (kFragOff), across the three phases below.
       auto rd = [&](int jf) { return *reinterpret_cast<const halfx8*>(slot + frag_off(jf, SPW) + lane * 16); };
       const float gC = sSc[64];
@@ -1078,7 +1087,7 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
       const int ci = ci0 + cl;   // chunk index inside the sequence
       halfx8 F[kNFrag];
 #pragma unroll
-      for (int jf = 0; jf < kAhead; ++jf) F[jf] = rd(jf);
+      for (int jf = 0; jf < kAh; ++jf) F[jf] = rd(jf);
       const float gCs = dpend == 0 ? gC : __builtin_amdgcn_ldexpf(gC, dpend);
       __builtin_amdgcn_sched_barrier(0);
       // U = -W M first and U0 after: the first products wait for nothing but their fragments
@@ -1088,7 +1097,7 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
       // ---- U = U0 - W M and O^T = M^T Q^T, interleaved ---------------------------
 #pragma unroll
       for (int jf = 0; jf < 32; ++jf) {
-        F[jf + kAhead] = rd(jf + kAhead);
+        F[jf + kAh] = rd(jf + kAh);
         __builtin_amdgcn_sched_barrier(0);
         const int x = (jf >> 1) & 3, ks = jf >> 3;
         if (jf & 1) O[x] = mfma16h(Mfr[ks], F[jf], O[x]);
@@ -1108,17 +1117,28 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
           for (int v = 0; v < 4; ++v)
             U[rt][v] = fmaf(static_cast<float>(rt < 2 ? u0a[4 * rt + v] : u0b[4 * (rt - 2) + v]), u0s, U[rt][v]);
       }
-      halfx8 Uf[2];
+      halfx8 Uf[2], Ug[2];   // U for the output products; Ug for the update
       Uf[0] = stack_h(U[0], U[1]);
       Uf[1] = stack_h(U[2], U[3]);
+      if constexpr (SPW == 4) {
+        // K^ holds no row factors: the update takes diag(e^{g_63 - g}) U
+        floatx4 Us[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) Us[rt] = U[rt] * *reinterpret_cast<const floatx4*>(sSc + 128 + 16 * rt + 4 * g4);
+        Ug[0] = stack_h(Us[0], Us[1]);
+        Ug[1] = stack_h(Us[2], Us[3]);
+      } else {
+        Ug[0] = Uf[0];
+        Ug[1] = Uf[1];
+      }
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) O[ct] *= gam[ct];
       // ---- M <- gamma_63 M + Kd U -------------------------------------------------
 #pragma unroll
       for (int jf = 32; jf < 48; ++jf) {
-        if (jf + kAhead < kNFrag) F[jf + kAhead] = rd(jf + kAhead);
+        if (jf + kAh < kNFrag) F[jf + kAh] = rd(jf + kAh);
         if constexpr (NS == 1) {
-          if (jf + kAhead == kNFrag - 1) {
+          if (jf + kAh == kNFrag - 1) {
             // the slot's last fragment is in flight: once it is back and every wave is here,
             // the slot is refilled with chunk cl+1
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
@@ -1126,7 +1146,7 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        Ms[(jf - 32) & 7] = mfma16h(F[jf], Uf[(jf - 32) >> 3], Ms[(jf - 32) & 7]);
+        Ms[(jf - 32) & 7] = mfma16h(F[jf], Ug[(jf - 32) >> 3], Ms[(jf - 32) & 7]);
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (GATED) {
@@ -1135,6 +1155,9 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
           load_z(ci, min(CH, len - ci * CH));
         }
       }
+      // the last fragments, when fewer than six are read ahead
+#pragma unroll
+      for (int jf = 48 + kAh; jf < kNFrag; ++jf) F[jf] = rd(jf);
       // ---- O^T += U^T P^T: P^T fragment f covers token tile f (chunk step 0) or f - 2 (step 1)
 #pragma unroll
       for (int f = 0; f < 6; ++f) {
@@ -1408,6 +1431,13 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
   if (nwin < 1) return hipErrorInvalidValue;
   if (nwin > nchunks) nwin = nchunks;
   float* carry = need_carry ? reinterpret_cast<float*>(wsb + static_cast<size_t>(nwin) * per_chunk) : a.state_out;
+  // When the heads alone fill the GPU, one chain workgroup per head copies each chunk's
+  // operands into LDS once instead of once per strip, and the prep stores K^ once per key
+  // head (batch 4, T=32768, 128 value heads: 7.31 ms of prefill against 10.34 ms with the
+  // one-slot strips, 8.34 ms with whole heads and Kd per value head); the gated norm needs
+  // whole rows and always runs so.
+  const bool heads = a.gz || (!a.cu_seqlens && a.B * a.Hv >= device_cu_count());
+  r.khat = heads ? 1 : 0;
   for (int c0 = 0; c0 < nchunks; c0 += nwin) {
     const int nw = min(nwin, nchunks - c0);
     if (a.G <= PrepLds::kNH)
@@ -1426,16 +1456,11 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     // 4, 128 value heads: 9.9 ms of prefill against 10.7 ms).  A packed batch
     // runs one slot per sequence with chunks in the window, which the host does
     // not know; the few it has per window run better with two slots.
-    // When the heads alone fill the GPU, one workgroup per head copies each chunk's
-    // operands into LDS once instead of once per strip (batch 4, T=32768, 128 value
-    // heads: 8.37 ms of prefill against 10.34 ms with the one-slot strips, the same
-    // bits); the gated norm needs whole rows and always runs so.
     const dim3 grid(slots * a.Hv * (DK / 32));
-    const bool heads_fill = !a.cu_seqlens && a.B * a.Hv >= device_cu_count();
     if (a.gz)
       hipLaunchKernelGGL((chunk_chain_kernel<2, 4, true>), dim3(slots * a.Hv), dim3(576),
                          (ChainLds<2, 4, true>::kBytes), s, r, c0, wsb, nwin, nw, carry);
-    else if (heads_fill)
+    else if (heads)
       hipLaunchKernelGGL((chunk_chain_kernel<2, 4, false>), dim3(slots * a.Hv), dim3(576),
                          (ChainLds<2, 4, false>::kBytes), s, r, c0, wsb, nwin, nw, carry);
     else if (!a.cu_seqlens && a.B * a.Hv * (DK / 32) > device_cu_count())

@@ -89,8 +89,10 @@ def test_prefill_gated_parity(B, T, Hk, Hv, recipe, state, l2, in_chain, windows
 
 
 def test_prefill_gated_state_matches_prefill_and_paths_agree():
-    """The fused path's state is gdn_prefill's to the bit (the same chain arithmetic); its y
-    and the two-launch y differ only through o's bf16 rounding before the norm."""
+    """The two-launch path's state is gdn_prefill's to the bit; the fused path (whole heads,
+    the key rows stored once per key head and scaled in the chain) rounds its fp16 operands
+    differently and is held to the oracle's bound.  The two y differ through o's bf16 rounding
+    before the norm and through those operand roundings."""
     torch = _torch()
     B, T, Hk, Hv, D = 2, 200, 2, 6, 128
     p = W.problem(7301, B, T, Hk, Hv, D, recipe="qwen", state="normal")
@@ -102,13 +104,11 @@ def test_prefill_gated_state_matches_prefill_and_paths_agree():
     G.gdn_prefill(q, k, v, to_dev(p["log_alpha"]), to_dev(p["beta"]), to_dev(p["state_in"].astype(np.float32)),
                   so, Hk=Hk, Hv=Hv, l2norm=True)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(s_chain, to_host(so))
     np.testing.assert_array_equal(s_two, to_host(so))
-    yr, _ = _oracle_gated(p, zb, wb, l2=True)
+    yr, sr = _oracle_gated(p, zb, wb, l2=True)
+    assert_state(s_chain, sr, what="state (norm in the chain)")
     assert_out(y_two, yr, bf16=True, what="y (two launches)")
-    # one bf16 rounding of o moves y by at most about one ulp of y; allow two
-    d = np.abs(y_chain - y_two)
-    assert np.all(d <= 2 * np.maximum(np.abs(y_two), 1e-30) * 2.0 ** -7 + 1e-6), float(d.max())
+    assert_out(y_chain, yr, bf16=True, what="y (norm in the chain)")
 
 
 def test_prefill_gated_windows_in_place_bit_identical():
