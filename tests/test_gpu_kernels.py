@@ -243,6 +243,30 @@ def test_prefill_state_in_place(nwin):
     assert_state(to_host(st), srf)
 
 
+@pytest.mark.parametrize("T,nwin,G_", [(200, None, 8), (130, 1, 8), (65, 2, 3)])
+def test_prefill_whole_heads(T, nwin, G_):
+    """B * Hv at least the CU count (2 x 128 value heads, or 3 x 96): one chain workgroup per
+    value head, with diag(rk) K stored once per key head and the row factors applied in the
+    chain.  All heads against the oracle, with an initial state, the L2 flag and ragged tails;
+    also over one- or two-chunk windows with the state updated in place."""
+    torch = _torch()
+    B, Hk, D = (2, 16, 128) if G_ == 8 else (3, 32, 128)
+    Hv = Hk * G_
+    p = W.problem(4010 + T, B, T, Hk, Hv, D, io="bf16", recipe="qwen", state="normal", normalise=False)
+    orf, srf = oracle_prefill(p, l2=True, state_in=p["state_in"])
+    q, k, v = to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"])
+    la, be = to_dev(p["log_alpha"]), to_dev(p["beta"])
+    st = to_dev(p["state_in"].astype(np.float32))
+    ws = None
+    if nwin is not None:
+        ws = torch.empty(nwin * B * (Hv * WS_VALUE_HEAD + Hk * WS_KEY_HEAD), dtype=torch.uint8, device="cuda")
+    o = G.gdn_prefill(q, k, v, la, be, st, st, Hk=Hk, Hv=Hv, l2norm=True, workspace=ws)
+    torch.cuda.synchronize()
+    m = assert_out(to_host(o).reshape(B, T, Hv, D), orf, bf16=True)
+    e = assert_state(to_host(st), srf)
+    print(f"whole heads B={B} T={T} {Hk}/{Hv} windows={nwin}: out excess {m['metric']:.2e} state {e:.2e}")
+
+
 def test_prefill_one_slot_chain():
     # 3 x 24 value heads x 4 strips = 288 chain workgroups, more than the 256 CUs: the chain runs
     # with one input slot per workgroup and a second barrier per chunk.  Checked with the whole
