@@ -347,8 +347,12 @@ def bench_block(dev, steps=5, warmup=2):
     zv = z.view(B, T, Hv * D)
     gated = lambda: G.gdn_prefill_gated(qv, kv, vv, la, be, zv, nw, 1e-5, None, so, out.view(B, T, Hv * D), Hk=Hk,
                                         Hv=Hv, l2norm=True, workspace=ws, stream=stream)
+    # the L2 norm of q and k in the conv's epilogue instead of in the prefill's loads
+    conv_l2 = lambda: G.gdn_conv1d_silu(x, w, None, None, y, l2_channels=2 * Hk * D, l2_eps=1e-6, stream=stream)
+    gated_nol2 = lambda: G.gdn_prefill_gated(qv, kv, vv, la, be, zv, nw, 1e-5, None, so, out.view(B, T, Hv * D), Hk=Hk,
+                                             Hv=Hv, l2norm=False, workspace=ws, stream=stream)
     res = {}
-    for name, fn in (("conv", conv), ("prefill", pre), ("norm", norm), ("prefill_gated", gated)):
+    for name, fn in (("conv", conv), ("prefill", pre), ("norm", norm), ("prefill_gated", gated), ("conv_l2", conv_l2)):
         _, mean_ms, med_ms = timed_launches(fn, steps, warmup, stream)
         res[name + "_ms"] = med_ms
 
@@ -361,9 +365,15 @@ def bench_block(dev, steps=5, warmup=2):
         pre()
         norm()
 
+    def block_l2():
+        conv_l2()
+        gated_nol2()
+
     total, _, med = timed_launches(block, steps, 1, stream)
     _, _, med_unfused = timed_launches(block_unfused, steps, 1, stream)
+    _, _, med_l2 = timed_launches(block_l2, steps, 1, stream)
     res["block_unfused_ms"] = med_unfused
+    res["block_conv_l2_ms"] = med_l2
     conv_bytes = B * T * Cc * 2 * 2 + Cc * 4 * 2
     norm_bytes = B * T * Hv * D * 2 * 3 + D * 2
     res.update(block_ms=med, tokens_per_s=B * T / (med * 1e-3),
@@ -714,7 +724,8 @@ def main():
         print(f"[bench] block: {blk['block_ms']:.2f} ms", file=sys.stderr, flush=True)
         line["block"] = {"config": "batch 4, T=32768, 16 key / 128 value heads: conv+SiLU, prefill (L2 flag) with "
                                    "the gated RMSNorm in the chain (gdn_prefill_gated); block_unfused_ms: conv, "
-                                   "prefill, norm as three launches", **blk}
+                                   "prefill, norm as three launches; block_conv_l2_ms: the L2 norm of q and k in the "
+                                   "conv (gdn_conv1d_silu_l2), then gdn_prefill_gated without the L2 flag", **blk}
         lg = bench_long(dev)
         print(f"[bench] long: {lg['ms']:.2f} ms", file=sys.stderr, flush=True)
         line["long"] = {"config": "batch 1, T=262144, 16 key / 48 value heads", **lg}

@@ -22,7 +22,7 @@ GDN_FLAG_NORM_IN_CHAIN = 4
 
 # Every exported symbol, in the order include/gdn.h, then include/gdn_attn.h declare them.
 EXPORTS = ("gdn_prefill", "gdn_prefill_gated", "gdn_prefill_static", "gdn_prefill_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_workspace_size",
-           "gdn_decode_step", "gdn_conv1d_silu",
+           "gdn_decode_step", "gdn_conv1d_silu", "gdn_conv1d_silu_l2",
            "gdn_gated_rmsnorm", "gdn_gates", "gdn_decode_token", "gdn_decode_layer", "gdn_last_error",
            "gdn_version",
            "gdn_attn_prefill", "gdn_attn_prefill_workspace_size", "gdn_attn_decode", "gdn_attn_decode_workspace_size")
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDims), p, p, p, p, p, p, p, p]
         L.gdn_decode_step.restype = ctypes.c_int
         L.gdn_conv1d_silu.argtypes = [i32, i32, i32, i32, i32, p, i64, p, p, p, p, i64, p]
+        L.gdn_conv1d_silu_l2.argtypes = [i32, i32, i32, i32, i32, p, i64, p, p, p, p, i64, i32, ctypes.c_float, p]
+        L.gdn_conv1d_silu_l2.restype = ctypes.c_int
         L.gdn_conv1d_silu.restype = ctypes.c_int
         L.gdn_gated_rmsnorm.argtypes = [i64, i32, i32, i32, p, i64, p, i64, p, ctypes.c_float, p, i64, p]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
@@ -394,9 +396,11 @@ def gdn_decode_step(q, k, v, log_alpha, beta, state, o=None, *, Hk: int, Hv: int
     return o
 
 
-def gdn_conv1d_silu(x, w, conv_state_in=None, conv_state_out=None, y=None, *, stream=None):
+def gdn_conv1d_silu(x, w, conv_state_in=None, conv_state_out=None, y=None, *, l2_channels: int = 0,
+                    l2_eps: float = 1e-6, stream=None):
     """x: [B, T, >=C] view (contiguous channels); w: [C, 4]; conv states [B, C, 3] or None;
-    y: [B, T, >=C] or None (allocated [B, T, C]).  Returns y."""
+    y: [B, T, >=C] or None (allocated [B, T, C]); l2_channels > 0 calls gdn_conv1d_silu_l2
+    (channels [0, l2_channels) L2-normalised per 128-channel head).  Returns y."""
     import torch
     B, T = int(x.shape[0]), int(x.shape[1])
     C, K = int(w.shape[0]), int(w.shape[1])
@@ -411,8 +415,13 @@ def gdn_conv1d_silu(x, w, conv_state_in=None, conv_state_out=None, y=None, *, st
     for name, s in (("conv_state_in", conv_state_in), ("conv_state_out", conv_state_out)):
         if s is not None and (s.dtype != x.dtype or not s.is_contiguous() or tuple(s.shape) != (B, C, K - 1)):
             raise ValueError(f"{name} must be contiguous [B, C, K-1] with x's dtype")
-    _check(lib().gdn_conv1d_silu(B, T, C, K, io, _ptr(x), sx, _ptr(w), _ptr(conv_state_in),
-                                 _ptr(conv_state_out), _ptr(y), sy, _stream(stream)))
+    if l2_channels:
+        _check(lib().gdn_conv1d_silu_l2(B, T, C, K, io, _ptr(x), sx, _ptr(w), _ptr(conv_state_in),
+                                        _ptr(conv_state_out), _ptr(y), sy, int(l2_channels), float(l2_eps),
+                                        _stream(stream)))
+    else:
+        _check(lib().gdn_conv1d_silu(B, T, C, K, io, _ptr(x), sx, _ptr(w), _ptr(conv_state_in),
+                                     _ptr(conv_state_out), _ptr(y), sy, _stream(stream)))
     _on_stream(stream, own)
     return y
 

@@ -409,9 +409,10 @@ gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, cons
                   "gdn_decode_step");
 }
 
-gdn_status gdn_conv1d_silu(int32_t B, int32_t T, int32_t C, int32_t K, int32_t dtype, const void* x,
-                           int64_t stride_x, const void* w, const void* conv_state_in,
-                           void* conv_state_out, void* y, int64_t stride_y, void* stream) {
+namespace {
+gdn_status conv1d_silu(int32_t B, int32_t T, int32_t C, int32_t K, int32_t dtype, const void* x, int64_t stride_x,
+                       const void* w, const void* conv_state_in, void* conv_state_out, void* y, int64_t stride_y,
+                       int32_t l2_channels, float l2_eps, const char* what, void* stream) {
   if (B < 0 || T < 0 || C < 1) return fail(GDN_ERR_SHAPE, "B=%d T=%d C=%d", B, T, C);
   if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_SHAPE, "dtype %d unknown", dtype);
   if (K != 4) return fail(GDN_ERR_UNSUPPORTED, "conv kernel width K=%d: only K=4 is implemented", K);
@@ -437,7 +438,29 @@ gdn_status gdn_conv1d_silu(int32_t B, int32_t T, int32_t C, int32_t K, int32_t d
   a.cs_in = conv_state_in;
   a.cs_out = conv_state_out;
   a.y = y;
-  return from_hip(gdn::launch_conv1d_silu(a, dtype, static_cast<hipStream_t>(stream)), "gdn_conv1d_silu");
+  a.l2c = l2_channels;
+  a.l2_eps = l2_eps;
+  return from_hip(gdn::launch_conv1d_silu(a, dtype, static_cast<hipStream_t>(stream)), what);
+}
+}  // namespace
+
+gdn_status gdn_conv1d_silu(int32_t B, int32_t T, int32_t C, int32_t K, int32_t dtype, const void* x,
+                           int64_t stride_x, const void* w, const void* conv_state_in,
+                           void* conv_state_out, void* y, int64_t stride_y, void* stream) {
+  return conv1d_silu(B, T, C, K, dtype, x, stride_x, w, conv_state_in, conv_state_out, y, stride_y, 0, 0.f,
+                     "gdn_conv1d_silu", stream);
+}
+
+gdn_status gdn_conv1d_silu_l2(int32_t B, int32_t T, int32_t C, int32_t K, int32_t dtype, const void* x,
+                              int64_t stride_x, const void* w, const void* conv_state_in, void* conv_state_out,
+                              void* y, int64_t stride_y, int32_t l2_channels, float l2_eps, void* stream) {
+  if (l2_channels < 0 || l2_channels % 128 || l2_channels > C)
+    return fail(GDN_ERR_SHAPE, "l2_channels=%d must be a multiple of 128 in [0, C=%d]", l2_channels, C);
+  if (l2_channels > 0 && C % 128)
+    return fail(GDN_ERR_UNSUPPORTED, "C=%d must be a multiple of 128 with l2_channels", C);
+  if (!(l2_eps >= 0.0f)) return fail(GDN_ERR_SHAPE, "l2_eps must be >= 0");
+  return conv1d_silu(B, T, C, K, dtype, x, stride_x, w, conv_state_in, conv_state_out, y, stride_y, l2_channels,
+                     l2_eps, "gdn_conv1d_silu_l2", stream);
 }
 
 gdn_status gdn_gated_rmsnorm(int64_t n_tok, int32_t H, int32_t D, int32_t dtype, const void* x,

@@ -128,16 +128,6 @@ __device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
   return max(max(r0, r1), max(r2, r3));
 }
 
-// Sum of x over each row of 16 lanes, in every lane of the row: pairs within quads,
-// then quads (lane i with 7 - i of each half row), then half rows (i with 15 - i).
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
-  return x;
-}
-
 // max(|a|, |b|, |c|) in one instruction (fmaxf would add a NaN-quieting step per operand)
 __device__ __forceinline__ float max3_abs(float a, float b, float c) {
   float r;

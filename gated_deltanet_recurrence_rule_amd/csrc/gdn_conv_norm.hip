@@ -7,6 +7,9 @@
 // and a run of TT tokens, slides a 4-token window in registers, and reads x
 // and writes y once with 16-byte accesses (a wave covers 512 consecutive
 // channels of one token).  Only the 3 halo tokens before a run are re-read.
+// Optionally the q and k channels are L2-normalised per 128-channel head in the
+// same pass (the per-head normalisation the prefill otherwise applies as it
+// loads q and k), before the one rounding of y.
 //
 // gated_rmsnorm: y = x / sqrt(mean(x^2) + eps) * w * z * sigmoid(z) per
 // D-row ("Les briques", section 4; "L'attention hybride", swish output gate
@@ -104,6 +107,16 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(ConvArgs a) {
       for (int j = 1; j < K - 1; ++j) acc = fmaf(w[e][j], win[j][e], acc);
       acc = fmaf(w[e][K - 1], xt[e], acc);
       y[e] = acc * sigmoidf_(acc);
+    }
+    if (c8 < a.l2c) {
+      // the head's 128 channels are the 16 lanes of this lane's row (16-lane rows start at
+      // multiples of 128 channels, and so do l2c and C), all of them here
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+      const float inv = rsqrtf(row16_sum(ss) + a.l2_eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= inv;
     }
     Vec8<IO>::store(a.y, yb + static_cast<int64_t>(t) * a.sy + c8, y);
 #pragma unroll

@@ -140,6 +140,10 @@ struct ConvArgs {
   const void* cs_in;
   void* cs_out;
   void* y;
+  // channels [0, l2c) are L2-normalised per 128-channel head after the SiLU:
+  // y <- y / sqrt(sum(y^2) + l2_eps) (l2c and C multiples of 128 when l2c > 0)
+  int32_t l2c = 0;
+  float l2_eps = 0.f;
 };
 hipError_t launch_conv1d_silu(const ConvArgs& a, int io, hipStream_t s);
 

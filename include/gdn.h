@@ -259,6 +259,23 @@ gdn_status gdn_conv1d_silu(int32_t B, int32_t T, int32_t C, int32_t K, int32_t d
                            int64_t stride_y, void* stream);
 
 /*
+ * gdn_conv1d_silu_l2 -- gdn_conv1d_silu with the per-head L2 normalisation of
+ * q and k in the same pass (the L2 flag of gdn_prefill / gdn_decode_step,
+ * moved into the conv's epilogue; the layer's q and k lead the q|k|v channels,
+ * "L'attention hybride", table "Le decompte"):
+ *     y[b,t,c] as gdn_conv1d_silu, then for each head of 128 channels
+ *     h < l2_channels / 128:  y_h <- y_h / sqrt(sum(y_h^2) + l2_eps)
+ * in fp32 before y is rounded once.  The prefill then runs without the L2 flag.
+ *   l2_channels  multiple of 128 in [0, C] (2 * Hk * Dk for the layer); when it
+ *                is above 0, C must be a multiple of 128
+ *   l2_eps       >= 0
+ * Other arguments, layouts and errors as gdn_conv1d_silu.
+ */
+gdn_status gdn_conv1d_silu_l2(int32_t B, int32_t T, int32_t C, int32_t K, int32_t dtype, const void* x,
+                              int64_t stride_x, const void* w, const void* conv_state_in, void* conv_state_out,
+                              void* y, int64_t stride_y, int32_t l2_channels, float l2_eps, void* stream);
+
+/*
  * gdn_gated_rmsnorm -- per-head RMSNorm with one shared D-weight, times
  * swish(z) ("L'attention hybride", config block: swish output gate; table
  * "Le decompte": 128 norm weights per layer; "Les briques", section 4):

@@ -185,6 +185,17 @@ def conv1d_silu(x, w, conv_state_in=None, *, b=0, t0=0, t1=None, c0=0, c1=None,
     return y, cs
 
 
+def l2norm_heads(y, head_dim: int, eps: float):
+    """fp64 per-head L2 normalisation along the last axis, in groups of head_dim channels:
+    each group x becomes x / sqrt(sum x^2 + eps), what the recurrence's L2 flag does to q and
+    k before they enter the rule (gdn_oracle.c, l2_normalise)."""
+    y = np.asarray(y, np.float64)
+    if y.shape[-1] % head_dim:
+        raise ValueError("the last axis must be a whole number of heads")
+    g = y.reshape(y.shape[:-1] + (y.shape[-1] // head_dim, head_dim))
+    return (g / np.sqrt((g * g).sum(-1, keepdims=True) + eps)).reshape(y.shape)
+
+
 def gated_rmsnorm(x, z, w, eps: float, *, rows=None, n_threads=0):
     """fp64 y = x / sqrt(mean(x^2)+eps) * w * z * sigmoid(z) over rows of D.
     x, z: [R, D] contiguous; w: [D]; rows: selected row indices (None = all)."""

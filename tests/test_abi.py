@@ -349,3 +349,15 @@ def test_prefill_gated_argument_errors():
     d.flags = B.GDN_FLAG_NORM_IN_CHAIN
     assert call_prefill(d) == B.GDN_ERR_SHAPE
     assert B.gdn_prefill_workspace_size(d) == B.gdn_prefill_workspace_size(dims(T=64))
+
+
+def test_conv_l2_argument_errors():
+    L = B.lib()
+    call = lambda C=1280, l2=512, eps=1e-6, T=4: L.gdn_conv1d_silu_l2(2, T, C, 4, B.GDN_BF16, FAKE, C, FAKE, None, None,
+                                                                      FAKE, C, l2, ctypes.c_float(eps), None)
+    assert call(l2=500) == B.GDN_ERR_SHAPE            # not a whole number of 128-channel heads
+    assert call(l2=-128) == B.GDN_ERR_SHAPE
+    assert call(l2=1408) == B.GDN_ERR_SHAPE           # beyond C
+    assert call(C=1288, l2=512) == B.GDN_ERR_UNSUPPORTED   # C not a multiple of 128
+    assert call(eps=-1.0) == B.GDN_ERR_SHAPE
+    assert call(T=0) == B.GDN_OK                      # nothing to do

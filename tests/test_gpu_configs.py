@@ -223,3 +223,49 @@ def test_cfg_block_full():
           f"norm in chain excess {worst[3]:.2e}")
     del y, o, z, out, yf
     _free()
+
+
+def test_cfg_block_conv_l2():
+    """The block config with the L2 norm of q and k in the conv's epilogue (gdn_conv1d_silu_l2)
+    and gdn_prefill_gated without the L2 flag, on four sampled (sequence, value head) pairs: the
+    conv stage against the oracle's conv and per-head normalisation, the prefill-and-norm stage
+    against the oracle applied to the GPU's own bf16 conv output."""
+    from helpers import conv_abs_sum, ulp_bf16
+    torch = _torch()
+    blk = W.block_inputs()
+    B, T, Hk, Hv, D, C = blk["B"], blk["T"], blk["Hk"], blk["Hv"], blk["D"], blk["C"]
+    eps = 1e-6
+    x = to_dev(blk["x"])
+    y = G.gdn_conv1d_silu(x, to_dev(blk["conv_w"]), l2_channels=2 * Hk * D, l2_eps=eps)
+    del x
+    qv, kv, vv = y[:, :, :Hk * D], y[:, :, Hk * D:2 * Hk * D], y[:, :, 2 * Hk * D:]
+    z = to_dev(blk["z"])
+    so = torch.empty((B, Hv, D, D), dtype=torch.float32, device="cuda")
+    yf = G.gdn_prefill_gated(qv, kv, vv, to_dev(blk["log_alpha"]), to_dev(blk["beta"]), z, to_dev(blk["norm_w"]),
+                             1e-5, None, so, Hk=Hk, Hv=Hv, l2norm=False)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 5), (1, 66), (2, 127), (3, 40)]:
+        hk = h // (Hv // Hk)
+        ygpu = {}
+        for c0, name in [(hk * D, "q"), (Hk * D + hk * D, "k"), (2 * Hk * D + h * D, "v")]:
+            ygpu[name] = y[b:b + 1, :, c0:c0 + D].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            if name == "v":
+                continue
+            yr, _ = oracle.conv1d_silu(blk["x"], blk["conv_w"], b=b, c0=c0, c1=c0 + D, n_threads=NTHR)
+            yn = oracle.l2norm_heads(yr, D, eps)
+            norm = np.sqrt((yr ** 2).sum(-1, keepdims=True) + eps)
+            tol = (2.0 ** -21 * conv_abs_sum(blk["x"], blk["conv_w"], None, b, c0, c0 + D) / norm + 2.0 ** -20
+                   + ulp_bf16(yn))
+            err = np.abs(to_host(y[b, :, c0:c0 + D]) - yn)
+            assert np.all(err <= tol), f"conv+L2 {name} head {h}: {(err - tol).max()}"
+        orf, srf = oracle.recurrence(ygpu["q"], ygpu["k"], ygpu["v"],
+                                     np.ascontiguousarray(blk["log_alpha"][b:b + 1, :, h:h + 1]),
+                                     np.ascontiguousarray(blk["beta"][b:b + 1, :, h:h + 1]), 1, 1, None,
+                                     n_threads=NTHR)
+        e = assert_state(to_host(so[b, h]), srf[0], what=f"block (conv L2) state {b},{h}")
+        zr = np.ascontiguousarray(blk["z"][b, :, h * D:(h + 1) * D])
+        yfr = oracle.gated_rmsnorm(np.ascontiguousarray(orf[0]), zr, blk["norm_w"], 1e-5, n_threads=NTHR)
+        mf = assert_out(to_host(yf[b, :, h * D:(h + 1) * D]), yfr, bf16=True, what=f"block (conv L2) gated {b},{h}")
+        print(f"block conv L2 head {b},{h}: state {e:.2e}, norm in chain excess {mf['excess_rms']:.2e}")
+    del y, z, yf
+    _free()

@@ -394,6 +394,45 @@ def test_conv1d_silu_parity(io, T):
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 5, 130])
+def test_conv1d_silu_l2_parity(io, T):
+    """gdn_conv1d_silu_l2: conv + SiLU, then the q and k channels [0, 2 Hk D) L2-normalised per
+    128-channel head, against the oracle's conv followed by the oracle's per-head normalisation.
+    The v channels and the conv window handed on are gdn_conv1d_silu's, bit for bit."""
+    from helpers import conv_abs_sum, ulp_bf16
+    torch = _torch()
+    B, Hk, Hv, D = 2, 2, 6, 128
+    C, L = (2 * Hk + Hv) * D, 2 * Hk * D
+    eps = 1e-6
+    x_full = W.normal_tokens(5100 + T, "x", B * T, C + 16).reshape(B, T, C + 16)
+    w = W.normal_tokens(5100, "conv_w", C, 4, scale=0.5)
+    cs = W.normal_tokens(5100, "conv_state", B * C, 3).reshape(B, C, 3)
+    cv = W.f32_to_bf16 if io == "bf16" else (lambda a: np.ascontiguousarray(a, np.float32))
+    xh, wh, csh = cv(x_full), cv(w), cv(cs)
+    x_dev = to_dev(xh)[:, :, :C]
+    cso = torch.zeros((B, C, 3), dtype=x_dev.dtype, device="cuda")
+    y = G.gdn_conv1d_silu(x_dev, to_dev(wh), to_dev(csh), cso, l2_channels=L, l2_eps=eps)
+    cso_p = torch.zeros_like(cso)
+    y_plain = G.gdn_conv1d_silu(x_dev, to_dev(wh), to_dev(csh), cso_p)
+    torch.cuda.synchronize()
+    yg, yp = to_host(y), to_host(y_plain)
+    np.testing.assert_array_equal(yg[:, :, L:], yp[:, :, L:])
+    np.testing.assert_array_equal(to_host(cso), to_host(cso_p))
+    xv = xh[:, :, :C]
+    for b in range(B):
+        yr, _ = oracle.conv1d_silu(xv, wh, csh, b=b)
+        yn = oracle.l2norm_heads(yr[:, :L], D, eps)
+        norm = np.repeat(np.sqrt((yr[:, :L].reshape(T, -1, D) ** 2).sum(-1) + eps), D, axis=1)
+        # the conv's fp32 accumulation error (2^-21 of the sum of |terms|) carried through the
+        # normalisation, the normalisation's own fp32 rounding, and the final rounding to io
+        tol = 2.0 ** -21 * conv_abs_sum(xh, wh, csh, b, 0, L) / norm + 2.0 ** -20
+        if io == "bf16":
+            tol = tol + ulp_bf16(yn)
+        err = np.abs(yg[b, :, :L] - yn)
+        assert np.all(err <= tol), float((err - tol).max())
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("H,D", [(1, 128), (3, 128), (4, 64)])
 def test_gated_rmsnorm_parity(io, H, D):
     torch = _torch()

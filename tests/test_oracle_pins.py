@@ -249,6 +249,25 @@ def test_l2_flag_and_q_scale():
     np.testing.assert_array_equal(s3, s1)
 
 
+def test_l2norm_heads_closed_forms_and_the_recurrence_flag():
+    """oracle.l2norm_heads: closed forms, unit norms, each head on its own, and the same
+    normalisation the recurrence's L2 flag applies (the C oracle's own routine)."""
+    np.testing.assert_allclose(oracle.l2norm_heads(np.array([3.0, 4.0]), 2, 0.0), [0.6, 0.8], rtol=1e-15)
+    np.testing.assert_allclose(oracle.l2norm_heads(np.array([3.0, 4.0]), 2, 11.0), [0.5, 4.0 / 6.0], rtol=1e-15)
+    rng = np.random.default_rng(23)
+    y = rng.standard_normal((5, 3 * 8)) * np.array([1e-3] * 8 + [1.0] * 8 + [1e3] * 8)
+    n = oracle.l2norm_heads(y, 8, 0.0).reshape(5, 3, 8)
+    np.testing.assert_allclose((n ** 2).sum(-1), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(oracle.l2norm_heads(7.0 * y, 8, 0.0), oracle.l2norm_heads(y, 8, 0.0), rtol=1e-13)
+    B, T, Hk, Hv, Dk, Dv = 1, 10, 2, 4, 8, 8
+    q, k, v, la, be, M0 = _rand_problem(rng, B, T, Hk, Hv, Dk, Dv, unit_keys=False)
+    eps = 1e-6
+    o1, s1 = oracle.recurrence(q, k, v, la, be, Hk, Hv, M0, l2norm=True, l2_eps=eps)
+    o2, s2 = oracle.recurrence(oracle.l2norm_heads(q, Dk, eps), oracle.l2norm_heads(k, Dk, eps), v, la, be, Hk, Hv, M0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s1, s2, rtol=1e-12, atol=1e-13)
+
+
 @pytest.mark.parametrize("C", [1, 3, 16, 64])
 @pytest.mark.parametrize("T", [37, 64, 100, 130])
 @pytest.mark.parametrize("form", ["fused", "wy"])
