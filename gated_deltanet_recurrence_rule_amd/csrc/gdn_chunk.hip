@@ -44,6 +44,11 @@
 //    update M <- gamma_63 M + Kd U (16) and O^T += U^T P^T (6), then store
 //    their outputs; a third copies the next chunk's operands from the
 //    workspace into LDS with direct global-to-LDS loads while they work.
+//    When the heads alone fill the GPU, one workgroup takes a whole value
+//    head (eight such waves and one copy wave), the prep then stores
+//    K^ = diag(rk) K once per key head and the chain applies the row factors
+//    e^{g_63 - g} to U; with the gated norm, that workgroup also normalises
+//    and gates its output rows.
 //
 // Precision.  MFMA accumulation is fp32 throughout and the state stays fp32.
 // The Gram products take the bf16 inputs as they are; every other product
