@@ -5,7 +5,8 @@ first, so that it runs on whatever the first left in the array.  The static
 call runs more windows than gdn_prefill with its full workspace (the first
 call: 64 chunks of 2.97 MB each, 22 per window against 32), and the results
 are the same bits for any window size, so the check is bit equality; the
-first call is also checked against the fp64 oracle on two heads."""
+first call is also checked against the fp64 oracle on two heads.  A third
+call runs the whole-head chain (heads that fill the GPU) over two windows."""
 import numpy as np
 import pytest
 
@@ -50,3 +51,7 @@ def test_prefill_static_two_calls():
     _both(p2, False)
     p2["state_in"] = None
     _both(p2, True)
+    # 3: heads that fill the GPU (2 x 128): whole-head chains, K^ once per key head; 14.8 MB of
+    # operands a chunk, so the array holds windows of 4 of the 5 chunks
+    p3 = W.problem(9102, 2, 300, 16, 128, 128, io="bf16", recipe="qwen", state="normal")
+    _both(p3, True)
