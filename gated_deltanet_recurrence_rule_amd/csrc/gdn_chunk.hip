@@ -23,9 +23,12 @@
 // exponent is <= 0.  Everything that does not depend on the state is folded
 // before the serial loop:
 //
-//   W  = T' diag(gamma rk) K,   U0 = T' V,   Kd = K^T diag(rk e^{g_63 - g}),
-//   Q^ = diag(rq) Q,            so that per chunk
-//   U  = U0 - W M,   M <- gamma_63 M + Kd U,   O = diag(gamma) Q^ M + P U.
+//   W  = T' diag(gamma rk) K,   U0 = T' V,   K^ = diag(rk) K,   Q^ = diag(rq) Q,
+//   f_r = e^{g_63 - g_r},       so that per chunk
+//   U  = U0 - W M,   M <- gamma_63 M + K^T diag(f) U,   O = diag(gamma) Q^ M + P U.
+//
+// K^ and Q^ depend on the key head only and are stored once per key head; W,
+// U0, P and f once per value head.
 //
 // Two kernels per window of chunks:
 //  * prep (one workgroup per chunk and key head, fully parallel over chunks):
@@ -33,7 +36,7 @@
 //    registers), and per value head the gate prefix sums, A, the inverse
 //    (16x16 forward substitution, a 16-block merge on fp32 MFMA, and the
 //    32x32 merge on MFMA with split-fp16 operands), T', and the products -W
-//    and U0 (fp16 MFMA).  The value heads of a key head are inverted up to
+//    and U0 (fp16 MFMA), and once per key head K^ and Q^.  The value heads of a key head are inverted up to
 //    three at a time, each on its own wave and in place.  All of it is
 //    written to the workspace as MFMA-ready fp16 fragments; U0 in the
 //    accumulator layout of the chain's U.
@@ -41,23 +44,21 @@
 //    looping over the window's chunks; columns of M evolve independently).
 //    Two waves each carry 16 columns of the fp32 strip in registers and run,
 //    per chunk, U = U0 - W M interleaved with O^T = M^T Q^T (32 MFMAs), the
-//    update M <- gamma_63 M + Kd U (16) and O^T += U^T P^T (6), then store
-//    their outputs; a third copies the next chunk's operands from the
+//    update M <- gamma_63 M + K^T (diag(f) U) (16) and O^T += U^T P^T (6), then
+//    store their outputs; a third copies the next chunk's operands from the
 //    workspace into LDS with direct global-to-LDS loads while they work.
 //    When the heads alone fill the GPU, one workgroup takes a whole value
-//    head (eight such waves and one copy wave), the prep then stores
-//    K^ = diag(rk) K once per key head and the chain applies the row factors
-//    e^{g_63 - g} to U; with the gated norm, that workgroup also normalises
-//    and gates its output rows.
+//    head (eight such waves and one copy wave); with the gated norm, that
+//    workgroup also normalises and gates its output rows.
 //
 // Precision.  MFMA accumulation is fp32 throughout and the state stays fp32.
 // The Gram products take the bf16 inputs as they are; every other product
-// runs on fp16 operands, each rounded once (in prep: -W, Kd, U0, P, Q^; in
-// the chain: M and U).  fp16 keeps 11 significant bits, which holds the state
+// runs on fp16 operands, each rounded once (in prep: -W, K^, U0, P, Q^; in
+// the chain: M, U and diag(f) U).  fp16 keeps 11 significant bits, which holds the state
 // within a few 1e-4 of the exact result and the outputs well inside their
 // bound.  Its range does not bound the inputs: the value-side operands (V,
 // U0, U, M) enter fp16 scaled by powers of two chosen per chunk and 16-column
-// value tile (see kRangeTop), and the key-side ones (-W, Kd, P, Q^) are
+// value tile (see kRangeTop), and the key-side ones (-W, K^, P, Q^) are
 // bounded by the L2-normalised keys and queries and the gates (every decay
 // factor is at most 1).
 
@@ -91,13 +92,14 @@ constexpr int KP = 136;   // LDS row pitch (bf16) of 64 x 128 row tiles
 // Workspace block per (batch, value head, chunk): 16x16x32 fp16 fragments (1 KiB each:
 // 64 lanes x 8 halves) and fp32 scalings.
 constexpr int WH_W = 0;        // -W = -T' diag(gamma rk) K, A operand: fragment rt*4+ks (rows 16rt.., keys 32ks..)
-constexpr int WH_KD = 16384;   // Kd = K^T diag(rk e^{g_63-g}), A operand: fragment dt*2+ks (keys 16dt.., rows 32ks..)
+constexpr int WH_KD = 16384;   // K^T = (diag(rk) K)^T, A operand: fragment dt*2+ks (keys 16dt.., rows 32ks..);
+                               // written in the block of the key head's first value head only
 constexpr int WH_U0 = 32768;   // U0 = T' V as accumulators of U: [value tile 8][lane 64][row tile 4][4 halves]
 constexpr int WH_P = 49152;    // P^T, B operand: 6 fragments (token tile ct, rows 32ks..), see pfrag()
 constexpr int WH_SC = 55296;   // gamma_r (64 floats), gamma_63; int32: V scale exponents of the 8 value
                                // tiles at [65, 73), gamma_63's exponent at 73, the next chunk's V scale
                                // exponents at [80, 88); [96, 112): the chain's scale hand-over between windows;
-                               // with khat, e^{g_63 - g_r} (64 floats) at [128, 192)
+                               // f_r = e^{g_63 - g_r} (64 floats) at [128, 192)
 constexpr int WH_BYTES = 56320;
 // workspace block per (batch, key head, chunk): Q^T = (diag(rq) Q)^T, B operand: fragment ks*4+ct
 // (keys 32ks.., tokens 16ct..)
@@ -259,7 +261,7 @@ struct PrepLds {
   static constexpr int kVP = 40;                  // V tile row pitch (bf16): 80-byte rows
   static constexpr int kV = kNH * kMat > 2 * CH * KP * 2 ? kNH * kMat : 2 * CH * KP * 2;
   static constexpr int kVec = kV + 4 * CH * kVP * 2;
-  static constexpr int bytes(int G) { return kVec + (2 + 4 * G) * CH * 4; }
+  static constexpr int bytes(int G) { return kVec + (2 + 3 * G) * CH * 4; }
 };
 
 // Orders one wave's LDS accesses across its lanes: the wave's LDS instructions
@@ -388,8 +390,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
   uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + L::kQ);
   float* vRk = reinterpret_cast<float*>(smem + L::kVec);
   float* vRq = vRk + CH;
-  // gate vectors of value head j of this key head
-  auto vgate = [&](int j) { return vRk + (2 + 4 * j) * CH; };
+  // gate vectors of value head j of this key head: g, beta, gamma rk
+  auto vgate = [&](int j) { return vRk + (2 + 3 * j) * CH; };
   // matrix of head jj of the current group
   auto mat = [&](int jj) { return reinterpret_cast<float*>(smem + jj * L::kMat); };
 
@@ -498,10 +500,9 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
     vg[lane] = g;
     vg[CH + lane] = be;
     vg[2 * CH + lane] = eg * vRk[lane];
-    vg[3 * CH + lane] = a.khat ? vRk[lane] : __expf(gl - g) * vRk[lane];
     float* sc = reinterpret_cast<float*>(ws + (static_cast<int64_t>(b * a.Hv + hk * a.G + j) * nwin + cl) * WH_BYTES + WH_SC);
     sc[lane] = eg;
-    if (a.khat) sc[128 + lane] = __expf(gl - g);
+    sc[128 + lane] = __expf(gl - g);
     if (lane == 0) {
       const float g63 = __expf(gl);
       sc[64] = g63;
@@ -541,6 +542,21 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) kt[2 * t + ks][e] = sK[(32 * ks + kperm(g4, e)) * KP + d];
+  }
+  // K^T = (diag(rk) K)^T fragments of the same key tiles: they do not depend on the value
+  // head, so they go once into the block of the key head's first value head
+  {
+    unsigned char* wkd = ws + (static_cast<int64_t>(b * a.Hv + hk * a.G) * nwin + cl) * WH_BYTES + WH_KD;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        halfx8 df;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          df[e] = static_cast<_Float16>(bf16_bits_to_f32(kt[2 * t + ks][e]) * vRk[32 * ks + kperm(g4, e)]);
+        *reinterpret_cast<halfx8*>(wkd + ((2 * wv + t) * 2 + ks) * 1024 + lane * 16) = df;
+      }
   }
   // ---- Gram tiles, kept in registers ---------------------------------------
   //  K K^T (waves 0-2, 32x32 tile wv of the lower triangle): element (row r, column i) = k_r . k_i
@@ -633,13 +649,12 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
     __syncthreads();
     // ---- per head, all waves: the six nonzero T' = T diag(beta) fragments (A operand of
     //      T' V; the same registers are the B operand of Ks^T T'^T), then
-    //      -W (key tiles 2wv, 2wv+1), Kd (the same key tiles) and U0 (value tiles 2wv, 2wv+1)
+    //      -W (key tiles 2wv, 2wv+1) and U0 (value tiles 2wv, 2wv+1)
     for (int jj = 0; jj < ng; ++jj) {
       const int j = j0 + jj, hv = hk * a.G + j;
       unsigned char* wsc = ws + (static_cast<int64_t>(b * a.Hv + hv) * nwin + cl) * WH_BYTES;
       const float* vBe = vgate(j) + CH;
       const float* vKs = vgate(j) + 2 * CH;
-      const float* vKd = vgate(j) + 3 * CH;
       // this head's V tile (value columns 32wv..) through the wave's LDS tile, then the next head's loads
       wave_lds_sync();   // the previous head's reads of the tile are done
 #pragma unroll
@@ -694,7 +709,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
       }
       {
         // W^T tiles (key tile 2wv + t, row tile rt) = Ks^T T'^T with Ks = diag(gamma rk) K; the two
-        // key tiles of a row tile stack into the -W fragment (rt, wv).  Kd fragments go out as they are.
+        // key tiles of a row tile stack into the -W fragment (rt, wv).
         floatx4 w[2][4];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -706,18 +721,10 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
           for (int ki = 0; ki < 2; ++ki) {
             const floatx4 sa = *reinterpret_cast<const floatx4*>(vKs + 32 * ki + 4 * g4);
             const floatx4 sb = *reinterpret_cast<const floatx4*>(vKs + 32 * ki + 16 + 4 * g4);
-            const floatx4 da = *reinterpret_cast<const floatx4*>(vKd + 32 * ki + 4 * g4);
-            const floatx4 db = *reinterpret_cast<const floatx4*>(vKd + 32 * ki + 16 + 4 * g4);
-            halfx8 kf, df;
+            halfx8 kf;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float kv = bf16_bits_to_f32(kt[2 * t + ki][e]);
-              kf[e] = static_cast<_Float16>(kv * (e < 4 ? sa[e] : sb[e - 4]));
-              df[e] = static_cast<_Float16>(kv * (e < 4 ? da[e] : db[e - 4]));
-            }
-            // with khat only the key head's first value head stores its (head-independent) K^ = diag(rk) K
-            if (!a.khat || j == 0)
-              *reinterpret_cast<halfx8*>(wsc + WH_KD + ((2 * wv + t) * 2 + ki) * 1024 + lane * 16) = df;
+            for (int e = 0; e < 8; ++e)
+              kf[e] = static_cast<_Float16>(bf16_bits_to_f32(kt[2 * t + ki][e]) * (e < 4 ? sa[e] : sb[e - 4]));
 #pragma unroll
             for (int f = 0; f < 6; ++f)
               if (kTriKi[f] == ki) w[t][kTriRt[f]] = mfma16h(kf, tf[f], w[t][kTriRt[f]]);
@@ -765,7 +772,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(RecArgs a, int c0, u
 // A workgroup covers SPW 32-column strips of a value head's M (SPW = 1: a strip,
 // three waves; SPW = 4: the whole head, nine waves): two state waves per strip,
 // each carrying 16 columns, and one copy wave.  LDS: NS input slots, each a
-// chunk's -W, Kd, the U0 of the workgroup's columns, the scalings, Q^T and P^T,
+// chunk's -W, K^, the U0 of the workgroup's columns, the scalings, Q^T and P^T,
 // copied from the workspace by the copy wave NS - 1 chunks ahead (or, with one
 // slot, once the chunk's slot has been read).  A strip's two slots take 118 KiB,
 // so one workgroup per CU; one slot 59 KiB, so two share a CU and cover each
@@ -785,7 +792,7 @@ struct ChainLds {
 constexpr int kAhead = 6;    // operand fragments a state wave reads ahead of its products
 // A state wave's 54 operand fragments per chunk, as slot offsets of a one-strip slot,
 // in the order its products take them: [0, 32) pairs of -W (even: row tile (j/2) & 3,
-// key step j/8) and Q^T (odd: key step j/8, token tile (j/2) & 3); [32, 48) Kd (key
+// key step j/8) and Q^T (odd: key step j/8, token tile (j/2) & 3); [32, 48) K^T (key
 // tile (j-32) & 7, chunk step (j-32) / 8); [48, 54) the P^T fragments.
 constexpr int kNFrag = 54;
 constexpr int kFragOff[kNFrag] = {0, 37888, 4096, 38912, 8192, 39936, 12288, 40960, 1024, 41984, 5120, 43008, 9216, 44032, 13312, 45056, 2048, 46080, 6144, 47104, 10240, 48128, 14336, 49152, 3072, 50176, 7168, 51200, 11264, 52224, 15360, 53248, 16384, 18432, 20480, 22528, 24576, 26624, 28672, 30720, 17408, 19456, 21504, 23552, 25600, 27648, 29696, 31744, 54272, 55296, 56320, 57344, 58368, 59392};
@@ -803,7 +810,7 @@ __device__ __forceinline__ const unsigned char* slot_src(int m, const unsigned c
                                                          const unsigned char* wsk, int strip, int spw) {
   const int kU = 32 + 4 * spw;
   return m < 16 ? wsh + 1024 * m                                           // -W
-       : m < 32 ? wkd + 1024 * m                                           // Kd (or K^, see khat)
+       : m < 32 ? wkd + 1024 * m                                           // K^T of the key head
        : m < kU ? wsh + WH_U0 + strip * 4096 + 1024 * (m - 32)             // U0 of the strips' value tiles
        : m < kU + 1 ? wsh + WH_SC                                          // scalings
        : m < kU + 17 ? wsk + 1024 * (m - kU - 1)                           // Q^T of the key head
@@ -900,10 +907,8 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
   const unsigned char* regK = ws + static_cast<int64_t>(a.B) * a.Hv * nwin * WH_BYTES;
   auto wsh_of = [&](int cl) { return ws + (static_cast<int64_t>(bh) * nwin + lofs + cl) * WH_BYTES; };
   auto wsk_of = [&](int cl) { return regK + (static_cast<int64_t>(bw * a.Hk + hk) * nwin + lofs + cl) * WK_BYTES; };
-  // whole heads: K^ comes from the key head's first value head (khat)
-  auto wkd_of = [&](int cl) {
-    return SPW == 4 ? ws + (static_cast<int64_t>(bw * a.Hv + hk * a.G) * nwin + lofs + cl) * WH_BYTES : wsh_of(cl);
-  };
+  // K^ sits in the block of the key head's first value head
+  auto wkd_of = [&](int cl) { return ws + (static_cast<int64_t>(bw * a.Hv + hk * a.G) * nwin + lofs + cl) * WH_BYTES; };
   auto copy_chunk = [&](int cl) {
     unsigned char* slot = smem + (cl % L::kNSlot) * L::kSlot;
     const unsigned char* wsh = wsh_of(cl);
@@ -1112,23 +1117,19 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
           for (int v = 0; v < 4; ++v)
             U[rt][v] = fmaf(static_cast<float>(rt < 2 ? u0a[4 * rt + v] : u0b[4 * (rt - 2) + v]), u0s, U[rt][v]);
       }
-      halfx8 Uf[2], Ug[2];   // U for the output products; Ug for the update
+      halfx8 Uf[2], Ug[2];   // U for the output products; Ug = diag(f) U for the update
       Uf[0] = stack_h(U[0], U[1]);
       Uf[1] = stack_h(U[2], U[3]);
-      if constexpr (SPW == 4) {
-        // K^ holds no row factors: the update takes diag(e^{g_63 - g}) U
+      {
         floatx4 Us[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) Us[rt] = U[rt] * *reinterpret_cast<const floatx4*>(sSc + 128 + 16 * rt + 4 * g4);
         Ug[0] = stack_h(Us[0], Us[1]);
         Ug[1] = stack_h(Us[2], Us[3]);
-      } else {
-        Ug[0] = Uf[0];
-        Ug[1] = Uf[1];
       }
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) O[ct] *= gam[ct];
-      // ---- M <- gamma_63 M + Kd U -------------------------------------------------
+      // ---- M <- gamma_63 M + K^T diag(f) U -----------------------------------------
 #pragma unroll
       for (int jf = 32; jf < 48; ++jf) {
         if (jf + kAh < kNFrag) F[jf + kAh] = rd(jf + kAh);
@@ -1427,12 +1428,10 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
   if (nwin > nchunks) nwin = nchunks;
   float* carry = need_carry ? reinterpret_cast<float*>(wsb + static_cast<size_t>(nwin) * per_chunk) : a.state_out;
   // When the heads alone fill the GPU, one chain workgroup per head copies each chunk's
-  // operands into LDS once instead of once per strip, and the prep stores K^ once per key
-  // head (batch 4, T=32768, 128 value heads: 7.31 ms of prefill against 10.34 ms with the
-  // one-slot strips, 8.34 ms with whole heads and Kd per value head); the gated norm needs
+  // operands into LDS once instead of once per strip (batch 4, T=32768, 128 value heads:
+  // 7.31 ms of prefill against 10.34 ms with the one-slot strips); the gated norm needs
   // whole rows and always runs so.
   const bool heads = a.gz || (!a.cu_seqlens && a.B * a.Hv >= device_cu_count());
-  r.khat = heads ? 1 : 0;
   for (int c0 = 0; c0 < nchunks; c0 += nwin) {
     const int nw = min(nwin, nchunks - c0);
     if (a.G <= PrepLds::kNH)

@@ -78,10 +78,6 @@ struct RecArgs {
   int64_t sz = 0;
   const void* gw = nullptr;
   float geps = 0.f;
-  // Chunked kernels, set by the launcher: the chain runs whole heads, so the prep stores
-  // diag(rk) K once per key head (in the Kd slot of its first value head) and the row
-  // factors e^{g_63 - g} per value head, instead of Kd per value head.
-  int32_t khat = 0;
 };
 
 // io: 0 = fp32, 1 = bf16 (same codes as gdn_dtype).
