@@ -825,6 +825,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const floatx2v f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
+// four outputs of a row as bf16
+__device__ __forceinline__ uint64_t pack_bf16x4(const floatx4& o) {
+  return static_cast<uint64_t>(pack_bf16x2(o[0], o[1])) | (static_cast<uint64_t>(pack_bf16x2(o[2], o[3])) << 32);
+}
 
 // Chunks [cs, ce) of sequence b in the window numbering, the token index of its
 // first token and its length.  Fixed-length batches: every sequence has chunks
@@ -854,7 +858,7 @@ __device__ __forceinline__ void seq_chunks(const RecArgs& a, int b, int& cs, int
 // leaves its 16 columns' sums of chunk c in LDS before the chunk's barrier and
 // finishes chunk c's rows (norm, gate, store) during chunk c+1, after the barrier;
 // the last chunk's rows after one more barrier.
-template <int NS, int SPW, bool GATED>
+template <int NS, int SPW, bool GATED, bool NTO = false>
 __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_chain_kernel(
     RecArgs a, int c0, unsigned char* ws, int nwin, int nw, float* carry) {
   static_assert(SPW == 1 || SPW == 4, "a strip or a whole head");
@@ -1197,15 +1201,18 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
         if (nval == CH) {
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
-            const uint2 w = {pack_bf16x2(O[ct][0], O[ct][1]), pack_bf16x2(O[ct][2], O[ct][3])};
-            *reinterpret_cast<uint2*>(gc + roff[ct]) = w;
+            // NTO: without allocating in the caches (chosen at compile time: the compiler
+            // merges the two stores of a run-time choice into a plain one)
+            if constexpr (NTO) __builtin_nontemporal_store(pack_bf16x4(O[ct]), reinterpret_cast<uint64_t*>(gc + roff[ct]));
+            else *reinterpret_cast<uint64_t*>(gc + roff[ct]) = pack_bf16x4(O[ct]);
           }
         } else {
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            const uint2 w = {pack_bf16x2(O[ct][0], O[ct][1]), pack_bf16x2(O[ct][2], O[ct][3])};
-            if (16 * ct + l16 < nval) *reinterpret_cast<uint2*>(gc + roff[ct]) = w;
-          }
+          for (int ct = 0; ct < 4; ++ct)
+            if (16 * ct + l16 < nval) {
+              if constexpr (NTO) __builtin_nontemporal_store(pack_bf16x4(O[ct]), reinterpret_cast<uint64_t*>(gc + roff[ct]));
+              else *reinterpret_cast<uint64_t*>(gc + roff[ct]) = pack_bf16x4(O[ct]);
+            }
         }
       }
       // slot cl may be refilled once both state waves have passed this barrier
@@ -1353,11 +1360,20 @@ int prep_slots(int G) { return device_cu_count() * max(1, min(2, (160 * 1024) / 
 // launches (batch 4, T=32768, 16/128 heads: 13.7 ms with windows of 8 chunks,
 // 10.7 ms with 64), so windows then take as many rounds as fit in 2 GiB.
 // Windows are then balanced, which never adds a round.
-int chunk_window_chunks(const RecArgs& a) {
+//
+// A long sequence on the two-slot strip chain (more than two such windows) runs
+// windows of about 200 MiB instead, with the chain's outputs stored without allocating
+// in the caches, so that they do not push the window's operands out: batch 1, 16/48
+// heads, 64-chunk windows against 32, T=8192 250 against 267 us, T=65536 2.00 against
+// 2.14 ms, T=262144 8.01 against 8.55 ms (8.58 ms with 64 and plain stores).  At T=4096
+// one such window is slower than two of 32 (127.0 against 125.1 us), and whole-head
+// chains write their outputs in pieces that the caches should merge (batch 4, T=32768:
+// 8.69 against 7.30 ms), so neither takes it.
+namespace {
+int window_for(const RecArgs& a, size_t cache) {
   const int nchunks = chunk_count(a);
   const size_t per = chunk_ws_bytes_per_chunk(a);
   const int round = max(1, prep_slots(a.G) / (a.Hk * a.B));   // chunks one round of prep covers
-  const size_t cache = size_t(96) << 20;
   const size_t budget = static_cast<size_t>(round) * per <= cache ? cache : size_t(2) << 30;
   const int fit = static_cast<int>(min(budget / per, static_cast<size_t>(1) << 30));
   int w = max(1, fit / round) * round;
@@ -1365,6 +1381,18 @@ int chunk_window_chunks(const RecArgs& a) {
   if (w >= nchunks) return nchunks;
   const int nwins = (nchunks + w - 1) / w;
   return (nchunks + nwins - 1) / nwins;
+}
+// the chain runs one workgroup per value head (and the prep stores for it)
+bool whole_heads(const RecArgs& a) { return a.gz || (!a.cu_seqlens && a.B * a.Hv >= device_cu_count()); }
+// the two-slot strip chain runs the sequences (a workgroup per CU at most)
+bool long_strip_run(const RecArgs& a) {
+  if (a.cu_seqlens || whole_heads(a) || a.B * a.Hv * (DK / 32) > device_cu_count()) return false;
+  return chunk_count(a) > 2 * window_for(a, size_t(96) << 20);
+}
+}  // namespace
+
+int chunk_window_chunks(const RecArgs& a) {
+  return window_for(a, long_strip_run(a) ? size_t(200) << 20 : size_t(96) << 20);
 }
 
 hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -1377,6 +1405,9 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<2, 1, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<2, 1, false>::kBytes);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<2, 1, false, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, ChainLds<2, 1, false>::kBytes);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_chain_kernel<1, 1, false>),
@@ -1431,7 +1462,7 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
   // operands into LDS once instead of once per strip (batch 4, T=32768, 128 value heads:
   // 7.31 ms of prefill against 10.34 ms with the one-slot strips); the gated norm needs
   // whole rows and always runs so.
-  const bool heads = a.gz || (!a.cu_seqlens && a.B * a.Hv >= device_cu_count());
+  const bool heads = whole_heads(a), ntout = long_strip_run(a);
   for (int c0 = 0; c0 < nchunks; c0 += nwin) {
     const int nw = min(nwin, nchunks - c0);
     if (a.G <= PrepLds::kNH)
@@ -1457,6 +1488,9 @@ hipError_t launch_chunk_prefill(const RecArgs& a, void* ws, size_t ws_bytes, hip
     else if (heads)
       hipLaunchKernelGGL((chunk_chain_kernel<2, 4, false>), dim3(slots * a.Hv), dim3(576),
                          (ChainLds<2, 4, false>::kBytes), s, r, c0, wsb, nwin, nw, carry);
+    else if (ntout)
+      hipLaunchKernelGGL((chunk_chain_kernel<2, 1, false, true>), grid, dim3(192), (ChainLds<2, 1, false>::kBytes), s,
+                         r, c0, wsb, nwin, nw, carry);
     else if (!a.cu_seqlens && a.B * a.Hv * (DK / 32) > device_cu_count())
       hipLaunchKernelGGL((chunk_chain_kernel<1, 1, false>), grid, dim3(192), (ChainLds<1, 1, false>::kBytes), s, r,
                          c0, wsb, nwin, nw, carry);

@@ -49,9 +49,15 @@ def test_workspace_size():
     big = dims(B=4, T=32768, Hk=16, Hv=128)
     per = 4 * (128 * WS_VALUE_HEAD + 16 * WS_KEY_HEAD)
     assert ws(big) == 64 * per + 4 * 128 * 128 * 128 * 4
-    # long sequence: 4096 chunks in 128 windows of 32 (one round of 512 prep workgroups each)
+    # a sequence that needs more than two such windows on the strip chain takes windows of
+    # ~200 MiB: 64 chunks (two rounds of 512 prep workgroups), T=8192 in 2, T=262144 in 64
     per = 48 * WS_VALUE_HEAD + 16 * WS_KEY_HEAD
-    assert ws(dims(T=262144, Hk=16, Hv=48)) == 32 * per + 48 * 128 * 128 * 4
+    assert ws(dims(T=8192, Hk=16, Hv=48)) == 64 * per + 48 * 128 * 128 * 4
+    assert ws(dims(T=262144, Hk=16, Hv=48)) == 64 * per + 48 * 128 * 128 * 4
+    # ... but not at batch 8, where the chain runs whole heads: a round of prep is 4 chunks
+    # (95 MB), so windows keep to ~96 MiB: 4 chunks, plus a carry
+    per8 = 8 * per
+    assert ws(dims(B=8, T=8192, Hk=16, Hv=48)) == 4 * per8 + 8 * 48 * 128 * 128 * 4
     # 32 value heads per key head: one prep workgroup per CU, a round is 256 chunks (466 MB), so
     # windows fill 2 GiB: 1024 chunks, and all 300 chunks fit in one window
     per = 32 * WS_VALUE_HEAD + WS_KEY_HEAD

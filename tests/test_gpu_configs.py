@@ -13,7 +13,8 @@ gated_deltanet_recurrence_rule_amd.workloads.
             3072 (sequence, head) pairs: outputs at every step, state after
             steps 1, 16 and 256; both gate recipes
   long      batch 1, T=262144 -- all 48 heads; also two halves of 131072
-            tokens chained through the state equal one pass
+            tokens chained through the state equal one pass (and T=8229, the
+            same windows with a ragged last chunk, from a nonzero state)
   block     batch 4, T=32768, 16/128 heads: conv+SiLU -> prefill with the L2
             flag -> gated RMSNorm x swish(z) on sampled heads, each stage
             checked against the oracle applied to the bf16 tensor the previous
@@ -90,6 +91,26 @@ def test_cfg_prefill4k_full():
                       to_dev(p["beta"]), None, so, Hk=Hk, Hv=Hv)
     torch.cuda.synchronize()
     _prefill_check(p, list(range(B * Hv)), o, so, "prefill4k")
+
+
+def test_prefill_long_windows_ragged():
+    """A sequence long enough for the strip chain's long windows (more than two windows of
+    ~96 MiB at 16/48 heads): T = 8229 runs as three windows of 43 chunks whose outputs are
+    stored without allocating in the caches, the last chunk 37 tokens long, from a nonzero
+    state and with the L2 flag; every head against the oracle."""
+    torch = _torch()
+    B, T, Hk, Hv, D = 1, 8229, 16, 48, 128
+    p = W.problem(9101, B, T, Hk, Hv, D, recipe="qwen", state="normal", normalise=False)
+    si = p["state_in"].astype(np.float32)
+    so = torch.empty((B, Hv, D, D), dtype=torch.float32, device="cuda")
+    o = G.gdn_prefill(to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"]), to_dev(p["log_alpha"]),
+                      to_dev(p["beta"]), to_dev(si), so, Hk=Hk, Hv=Hv, l2norm=True)
+    torch.cuda.synchronize()
+    ref = oracle.recurrence(p["q"], p["k"], p["v"], p["log_alpha"], p["beta"], Hk, Hv, si, l2norm=True,
+                            l2_eps=1e-6, n_threads=NTHR)
+    _prefill_check(p, list(range(B * Hv)), o, so, "long windows, ragged", ref=ref)
+    del o, so
+    _free()
 
 
 @pytest.mark.parametrize("recipe", ["qwen", "tiny"])
