@@ -506,15 +506,16 @@ def bench_varlen(dev, steps=20, warmup=20):
     stream = torch.cuda.current_stream()
     fn = lambda: G.gdn_prefill_varlen(q, k, v, la, be, cu, None, so, o, Hk=Hk, Hv=Hv, workspace=ws, stream=stream)
     _, _, med = timed_launches(fn, steps, warmup, stream)
-    # the same requests, one call each (views into the packed tensors; per-call workspaces)
+    # the same requests, one call each (views into the packed tensors; one workspace that
+    # holds the largest request's, whose windows may be longer than the packed call's)
+    wszs = [G.gdn_prefill_workspace_size(G.make_dims(1, int(cu_h[s + 1] - cu_h[s]), Hk, Hv, D, G.GDN_BF16))
+            for s in range(n)]
+    ws1 = torch.empty(max(wszs), dtype=torch.uint8, device=dev)
     views = []
     for s in range(n):
         a, b = int(cu_h[s]), int(cu_h[s + 1])
-        L = b - a
-        wsz = G.gdn_prefill_workspace_size(G.make_dims(1, L, Hk, Hv, D, G.GDN_BF16))
-        assert wsz <= ws.numel()
         views.append((q[a:b].unsqueeze(0), k[a:b].unsqueeze(0), v[a:b].unsqueeze(0), la[a:b].unsqueeze(0),
-                      be[a:b].unsqueeze(0), so[s:s + 1], o[a:b].unsqueeze(0), ws[:wsz]))
+                      be[a:b].unsqueeze(0), so[s:s + 1], o[a:b].unsqueeze(0), ws1[:wszs[s]]))
 
     def each():
         for qq, kk, vv, ll, bb, ss, oo, ww in views:
@@ -523,7 +524,7 @@ def bench_varlen(dev, steps=20, warmup=20):
     _, _, med_each = timed_launches(each, max(steps // 4, 3), 3, stream)
     fl = prefill_flops(1, T, Hk, Hv, D)
     by = prefill_bytes(1, T, Hk, Hv, D) + (n - 1) * Hv * D * D * 4
-    del q, k, v, o, ws
+    del q, k, v, o, ws, ws1, views
     torch.cuda.empty_cache()
     return dict(n_seq=n, tokens=T, min_len=int(lens.min()), max_len=int(lens.max()), ms=med,
                 tokens_per_s=T / (med * 1e-3), hbm_frac=by / (med * 1e-3) / (HBM_PEAK_GBS * 1e9),

@@ -1365,7 +1365,8 @@ int prep_slots(int G) { return device_cu_count() * max(1, min(2, (160 * 1024) / 
 // windows of about 200 MiB instead, with the chain's outputs stored without allocating
 // in the caches, so that they do not push the window's operands out: batch 1, 16/48
 // heads, 64-chunk windows against 32, T=8192 250 against 267 us, T=65536 2.00 against
-// 2.14 ms, T=262144 8.01 against 8.55 ms (8.58 ms with 64 and plain stores).  At T=4096
+// 2.14 ms, T=262144 8.01 against 8.55 ms (8.58 ms with 64 and plain stores); 32 packed
+// requests of 16 to 7,574 tokens (38,693 in all) 1.27 against 1.38 ms.  At T=4096
 // one such window is slower than two of 32 (127.0 against 125.1 us), and whole-head
 // chains write their outputs in pieces that the caches should merge (batch 4, T=32768:
 // 8.69 against 7.30 ms), so neither takes it.
@@ -1384,9 +1385,10 @@ int window_for(const RecArgs& a, size_t cache) {
 }
 // the chain runs one workgroup per value head (and the prep stores for it)
 bool whole_heads(const RecArgs& a) { return a.gz || (!a.cu_seqlens && a.B * a.Hv >= device_cu_count()); }
-// the two-slot strip chain runs the sequences (a workgroup per CU at most)
+// the two-slot strip chain runs the sequences (a workgroup per CU at most for a fixed batch;
+// a packed batch always runs it)
 bool long_strip_run(const RecArgs& a) {
-  if (a.cu_seqlens || whole_heads(a) || a.B * a.Hv * (DK / 32) > device_cu_count()) return false;
+  if (whole_heads(a) || a.B * a.Hv * (DK / 32) > device_cu_count()) return false;
   return chunk_count(a) > 2 * window_for(a, size_t(96) << 20);
 }
 }  // namespace
