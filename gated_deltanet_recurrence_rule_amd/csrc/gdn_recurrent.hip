@@ -236,15 +236,18 @@ __device__ __forceinline__ void conv_finish(const LayerArgs& a, const ConvPair& 
   }
 }
 
-__global__ __launch_bounds__(256) void decode_layer_kernel(LayerArgs a) {
+constexpr int kLayerThreads = 1024;
+
+__global__ __launch_bounds__(kLayerThreads) void decode_layer_kernel(LayerArgs a) {
   constexpr int D = 128;
-  using S = RecShape<D>;
+  using S = RecShape<D, kLayerThreads>;
   constexpr int RG = S::RG, RPT = S::RPT, TPR = S::TPR;
 
   __shared__ float s_q[D];
   __shared__ float s_k[D];
   __shared__ float s_v[D];
   __shared__ float s_red[2][RG][D];
+  __shared__ float s_uw[2][D];
   __shared__ float s_scal[4];
 
   const int bh = blockIdx.x;
@@ -334,12 +337,16 @@ __global__ __launch_bounds__(256) void decode_layer_kernel(LayerArgs a) {
   *reinterpret_cast<floatx4*>(&s_red[1][rg][c0]) = pw;
   __syncthreads();
 
-  floatx4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
+  // row groups 0 and 1 sum u and w over all row groups once, the rest read them
+  if (rg < 2) {
+    floatx4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    u += *reinterpret_cast<const floatx4*>(&s_red[0][g][c0]);
-    w += *reinterpret_cast<const floatx4*>(&s_red[1][g][c0]);
+    for (int g = 0; g < RG; ++g) t += *reinterpret_cast<const floatx4*>(&s_red[rg][g][c0]);
+    *reinterpret_cast<floatx4*>(&s_uw[rg][c0]) = t;
   }
+  __syncthreads();
+  const floatx4 u = *reinterpret_cast<const floatx4*>(&s_uw[0][c0]);
+  const floatx4 w = *reinterpret_cast<const floatx4*>(&s_uw[1][c0]);
   const float kq = s_scal[0], alpha = s_scal[1], beta = s_scal[2];
   const floatx4 vv = *reinterpret_cast<const floatx4*>(&s_v[c0]);
   const floatx4 d = beta * (vv - alpha * u);
@@ -387,7 +394,7 @@ hipError_t launch_rec(const RecArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_layer(const LayerArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_layer_kernel, dim3(static_cast<unsigned>(a.B * a.Hv)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(decode_layer_kernel, dim3(static_cast<unsigned>(a.B * a.Hv)), dim3(kLayerThreads), 0, s, a);
   return hipGetLastError();
 }
 
