@@ -142,8 +142,9 @@ def bench_prefill_cold(dev, steps=20):
 
 
 def attainable_peaks(dev):
-    """What this machine reaches on plain library work: a 1 GiB device copy (bytes read plus
-    written per second) and a large bf16 GEMM through torch (hipBLASLt)."""
+    """What this machine reaches on plain work: a 1 GiB device copy (bytes read plus written per
+    second) and a large bf16 GEMM through torch (hipBLASLt), then the library's probes: its
+    own copy kernel over the same 1 GiB and bf16 MFMAs on register operands (gdn_probe.h)."""
     import torch
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -176,8 +177,24 @@ def attainable_peaks(dev):
         torch.cuda.synchronize()
         reps.append(e0.elapsed_time(e1))
     gemm = 2 * m ** 3 / (min(reps) * 1e-3) / 1e12
+    del a, b
+    # the library's probes: a plain copy kernel over the same 1 GiB, and MFMAs on registers
+    from gated_deltanet_recurrence_rule_amd import binding as G
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    _, _, med = timed_launches(lambda: G.gdn_probe_copy(src, dst, stream=stream), 5, 3, stream)
+    probe_copy = 2 * n / (med * 1e-3) / 1e9
+    del src, dst
+    nwg, iters = 2048, 4096
+    sink = torch.empty(nwg * 256, dtype=torch.float32, device=dev)
+    fl = nwg * 4 * iters * 4 * 32768
+    _, _, med = timed_launches(lambda: G.gdn_probe_mfma(nwg, iters, sink, stream=stream), 5, 2, stream)
+    probe_mfma = fl / (med * 1e-3) / 1e12
     return dict(copy_1GiB_GBs=copy_gbs, copy_frac=copy_gbs / HBM_PEAK_GBS,
-                bf16_gemm_8192_TFLOPs=gemm, bf16_gemm_frac=gemm / BF16_PEAK_TFLOPS)
+                bf16_gemm_8192_TFLOPs=gemm, bf16_gemm_frac=gemm / BF16_PEAK_TFLOPS,
+                probe_copy_1GiB_GBs=probe_copy, probe_copy_frac=probe_copy / HBM_PEAK_GBS,
+                probe_mfma_bf16_TFLOPs=probe_mfma, probe_mfma_frac=probe_mfma / BF16_PEAK_TFLOPS)
 
 
 def bench_decode(dev, n_steps=256, pools=1, graph=False):
@@ -709,8 +726,9 @@ def main():
               file=sys.stderr, flush=True)
         line["prefill_cold"] = {"config": "headline prefill, 512 MB written between calls", **cold}
         pk = attainable_peaks(dev)
-        print(f"[bench] attainable: copy {pk['copy_1GiB_GBs']:.0f} GB/s, bf16 GEMM {pk['bf16_gemm_8192_TFLOPs']:.0f} "
-              f"TFLOP/s", file=sys.stderr, flush=True)
+        print(f"[bench] attainable: copy {pk['copy_1GiB_GBs']:.0f} GB/s (probe {pk['probe_copy_1GiB_GBs']:.0f}), "
+              f"bf16 GEMM {pk['bf16_gemm_8192_TFLOPs']:.0f} TFLOP/s (MFMA probe {pk['probe_mfma_bf16_TFLOPs']:.0f})",
+              file=sys.stderr, flush=True)
         line["attainable"] = pk
         fr = bench_decode_front(dev)
         print(f"[bench] decode front end: {fr['median_us']:.1f} us/step (token {fr['token_median_us']:.1f} us, "

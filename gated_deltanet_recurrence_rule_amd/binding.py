@@ -25,7 +25,8 @@ EXPORTS = ("gdn_prefill", "gdn_prefill_gated", "gdn_prefill_static", "gdn_prefil
            "gdn_decode_step", "gdn_conv1d_silu", "gdn_conv1d_silu_l2",
            "gdn_gated_rmsnorm", "gdn_gates", "gdn_decode_token", "gdn_decode_layer", "gdn_last_error",
            "gdn_version",
-           "gdn_attn_prefill", "gdn_attn_prefill_workspace_size", "gdn_attn_decode", "gdn_attn_decode_workspace_size")
+           "gdn_attn_prefill", "gdn_attn_prefill_workspace_size", "gdn_attn_decode", "gdn_attn_decode_workspace_size",
+           "gdn_probe_mfma", "gdn_probe_copy")
 
 
 class GdnDims(ctypes.Structure):
@@ -102,6 +103,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_conv1d_silu.restype = ctypes.c_int
         L.gdn_gated_rmsnorm.argtypes = [i64, i32, i32, i32, p, i64, p, i64, p, ctypes.c_float, p, i64, p]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
+        L.gdn_probe_mfma.argtypes = [i32, i32, p, p]
+        L.gdn_probe_mfma.restype = ctypes.c_int
+        L.gdn_probe_copy.argtypes = [p, p, ctypes.c_size_t, p]
+        L.gdn_probe_copy.restype = ctypes.c_int
         L.gdn_gates.argtypes = [i64, i32, i32, p, i64, p, p, p, p, p]
         L.gdn_gates.restype = ctypes.c_int
         L.gdn_decode_token.argtypes = [ctypes.POINTER(GdnDims), p, p, p, i32, p, i64, p, p, p, i32, p, p, p]
@@ -446,6 +451,25 @@ def gdn_gated_rmsnorm(x, z, w, eps: float = 1e-5, y=None, *, H: int, stream=None
                                    y.stride(0) if n > 1 else H * D, _stream(stream)))
     _on_stream(stream, own)
     return y
+
+
+def gdn_probe_mfma(n_workgroups: int, iters: int, sink, stream=None):
+    """Matrix-core probe: n_workgroups x 4 waves of `iters` rounds of four 32x32x16 bf16
+    MFMAs; sink: fp32 [n_workgroups * 256], each entry 1024 * iters afterwards.  Returns
+    the flop count."""
+    import torch
+    if sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() < n_workgroups * 256:
+        raise ValueError("sink must be contiguous fp32 with n_workgroups * 256 entries")
+    _check(lib().gdn_probe_mfma(int(n_workgroups), int(iters), _ptr(sink), _stream(stream)))
+    return n_workgroups * 4 * iters * 4 * 32 * 32 * 16 * 2
+
+
+def gdn_probe_copy(src, dst, stream=None):
+    """Device-copy probe: dst <- src, both contiguous, the same byte size (a multiple of 32 KiB)."""
+    n = src.numel() * src.element_size()
+    if not src.is_contiguous() or not dst.is_contiguous() or dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst must be contiguous and of the same byte size")
+    _check(lib().gdn_probe_copy(_ptr(src), _ptr(dst), n, _stream(stream)))
 
 
 def _params(A_log, dt_bias, Hv: int):

@@ -4,6 +4,7 @@
 // HIP call, so argument errors are reported even on a machine without a GPU.
 #include "../../include/gdn.h"
 #include "../../include/gdn_attn.h"
+#include "../../include/gdn_probe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -648,6 +649,28 @@ gdn_status gdn_attn_decode(const gdn_attn_dims* d, const void* qg, const void* k
   a.qrot = static_cast<uint16_t*>(workspace);
   a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + attn_qrot_bytes(d));
   return from_hip(gdn::launch_attn_decode(a, static_cast<hipStream_t>(stream)), "gdn_attn_decode");
+}
+
+gdn_status gdn_probe_mfma(int32_t n_workgroups, int32_t iters, float* sink, void* stream) {
+  if (n_workgroups < 1 || n_workgroups > (1 << 20) || iters < 4 || iters > 65536 || iters % 4)
+    return fail(GDN_ERR_SHAPE, "n_workgroups=%d must be in [1, 2^20] and iters=%d a multiple of 4 in [4, 65536]",
+                n_workgroups, iters);
+  if (!sink) return fail(GDN_ERR_NULL, "sink is required");
+  if (!aligned(sink, 4)) return fail(GDN_ERR_ALIGN, "sink must be 4-byte aligned");
+  return from_hip(gdn::launch_probe_mfma(n_workgroups, iters, sink, static_cast<hipStream_t>(stream)),
+                  "gdn_probe_mfma");
+}
+
+gdn_status gdn_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes % gdn::kProbeCopyBlockBytes || bytes >= (static_cast<size_t>(1) << 46))
+    return fail(GDN_ERR_SHAPE, "bytes=%zu must be a multiple of %zu below 2^46", bytes, gdn::kProbeCopyBlockBytes);
+  if (bytes == 0) return ok();
+  if (!src || !dst) return fail(GDN_ERR_NULL, "src and dst are required");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(GDN_ERR_ALIGN, "src and dst must be 16-byte aligned");
+  const unsigned char* s0 = static_cast<const unsigned char*>(src);
+  const unsigned char* d0 = static_cast<const unsigned char*>(dst);
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(GDN_ERR_SHAPE, "src and dst overlap");
+  return from_hip(gdn::launch_probe_copy(src, dst, bytes, static_cast<hipStream_t>(stream)), "gdn_probe_copy");
 }
 
 const char* gdn_last_error(void) { return g_err; }

@@ -197,4 +197,10 @@ __host__ __device__ inline int attn_splits(int S_max) { return (S_max + kAttnSpl
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
 
+// Measurement probes (gdn_probe.hip): n_workgroups x 4 waves of MFMA rounds, and
+// a device copy in blocks of kProbeCopyBlockBytes.
+constexpr size_t kProbeCopyBlockBytes = 256 * 8 * 16;
+hipError_t launch_probe_mfma(int n_workgroups, int iters, float* sink, hipStream_t s);
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
 }  // namespace gdn

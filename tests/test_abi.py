@@ -368,3 +368,18 @@ def test_conv_l2_argument_errors():
     assert call(C=1288, l2=512) == B.GDN_ERR_UNSUPPORTED   # C not a multiple of 128
     assert call(eps=-1.0) == B.GDN_ERR_SHAPE
     assert call(T=0) == B.GDN_OK                      # nothing to do
+
+
+def test_probe_argument_errors():
+    L = B.lib()
+    assert L.gdn_probe_mfma(0, 4, FAKE, None) == B.GDN_ERR_SHAPE
+    assert L.gdn_probe_mfma((1 << 20) + 1, 4, FAKE, None) == B.GDN_ERR_SHAPE
+    assert L.gdn_probe_mfma(1, 6, FAKE, None) == B.GDN_ERR_SHAPE        # not a multiple of 4
+    assert L.gdn_probe_mfma(1, 65540, FAKE, None) == B.GDN_ERR_SHAPE
+    assert L.gdn_probe_mfma(1, 4, None, None) == B.GDN_ERR_NULL
+    assert L.gdn_probe_mfma(1, 4, FAKE_ODD, None) == B.GDN_ERR_ALIGN
+    assert L.gdn_probe_copy(FAKE, ctypes.c_void_p(0x100000), 1000, None) == B.GDN_ERR_SHAPE
+    assert L.gdn_probe_copy(None, FAKE, 32768, None) == B.GDN_ERR_NULL
+    assert L.gdn_probe_copy(FAKE_ODD, ctypes.c_void_p(0x100000), 32768, None) == B.GDN_ERR_ALIGN
+    assert L.gdn_probe_copy(FAKE, ctypes.c_void_p(0x10000 + 16384), 32768, None) == B.GDN_ERR_SHAPE   # overlap
+    assert L.gdn_probe_copy(None, None, 0, None) == B.GDN_OK
