@@ -964,8 +964,9 @@ __global__ __launch_bounds__(64 * (2 * SPW + 1), SPW == 1 ? 2 : 1) void chunk_ch
     // GATED: the rows of the previous chunk (unscaled outputs, z) until they are normed
     float* nrm = reinterpret_cast<float*>(smem + L::kNorm);
     const uint16_t* gz = static_cast<const uint16_t*>(a.gz) + tok0 * a.sz + hv * DK + 32 * strip + 16 * sh + 4 * g4;
-    // the gated norm's registers leave fewer for fragments in flight
-    constexpr int kAh = GATED ? 4 : kAhead;
+    // the gated norm's registers leave fewer for fragments in flight: with three the
+    // kernel fits the 168 registers that three waves per SIMD allow, without spills
+    constexpr int kAh = GATED ? 3 : kAhead;
     uint2 nwb;        // norm weights of this lane's four columns (bf16)
     floatx4 Op[4];    // the previous chunk's outputs
     uint2 zp[4];      // its gate inputs, four bf16 per token tile
