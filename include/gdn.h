@@ -231,6 +231,8 @@ size_t gdn_prefill_varlen_workspace_size(const gdn_dims* dims);
  *   state [B, Hv, Dk, Dv] fp32, read once and overwritten in place.
  * Computes u = M^T k, w = M^T q in one pass over M, then
  * d = beta (v - alpha u), M <- alpha M + k d^T, o = alpha w + (k . q) d.
+ * The state is loaded and stored with non-temporal hints: a step leaves
+ * none of it in the caches for the next kernel.
  */
 gdn_status gdn_decode_step(const gdn_dims* dims, const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta, float* state, void* o,
