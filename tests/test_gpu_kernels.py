@@ -638,7 +638,7 @@ def test_decode_layer_fused_parity(l2):
         cs[(s + 1) % 2] = written.copy()
 
 
-# A seeded grid over the shapes the survey's property test names: batch <= 3, T <= 300, 1 or 2 key
+# A seeded property grid over small shapes: batch <= 3, T <= 300, 1 or 2 key
 # heads, 1, 3 or 8 value heads per key head, head width 16 or 128, fp32 or bf16 I/O.  Each case draws
 # its own lengths, gate recipe, initial state, L2 flag and q scale.  bf16 with width 128 runs the
 # chunked kernels; the other cases run the token-serial kernel.
