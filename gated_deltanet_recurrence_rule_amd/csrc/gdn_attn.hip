@@ -22,7 +22,8 @@
 //    block's copies in flight during the products.
 //  * attn_decode_kernel: one wave per (256 cached positions, key/value head,
 //    sequence) runs the same products on 16x16x32 tiles with the group's query
-//    heads as the MFMA columns, streaming keys and values through its own LDS;
+//    heads as the MFMA columns, streaming keys and values through its own LDS
+//    (keys a 32-position block at a time, values two blocks at a time);
 //    attn_combine_kernel merges the partial maxima, sums and outputs of a head
 //    and applies the gate.
 #include <cmath>
@@ -432,7 +433,7 @@ __device__ __forceinline__ floatx4 mfma16(const bf16x8& a, const bf16x8& b, cons
 }
 
 constexpr int DB = 32;                       // positions per decode block
-constexpr int kDecLds = DB * AD * 2 * 2;     // keys 16 KiB + transposed values 16 KiB
+constexpr int kDecLds = DB * AD * 2 * 3;     // keys 16 KiB + transposed values of two blocks 32 KiB
 
 __global__ __launch_bounds__(64, 2) void attn_decode_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -467,7 +468,11 @@ __global__ __launch_bounds__(64, 2) void attn_decode_kernel(AttnArgs a) {
     const int valid = min(DB, n - kb0);
     // Copy.  Key row r = 16 kt + m of LDS holds position 8 (m / 4) + 4 kt + m % 4, its
     // 16-byte chunk c at chunk position c ^ (r & 15); value row d (64 B) holds
-    // positions kb0.. kb0+31 of dim d, chunk c at c ^ ((d / 4) & 3).  (Copying the
+    // positions kb0.. kb0+31 of dim d, chunk c at c ^ ((d / 4) & 3).  The values of a
+    // block and the next are copied together at the even block, both halves of each
+    // 128-byte cache row back to back: copied a block at a time, the second half was
+    // gone from L2 when the next block asked for it, and the values crossed from memory
+    // nearly twice (1,542 MB fetched per call against 1,074 MB of cache).  (Copying the
     // next block's keys and values while this one is worked on timed the same.)
     __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the previous block's LDS reads are done
 #pragma unroll
@@ -478,12 +483,17 @@ __global__ __launch_bounds__(64, 2) void attn_decode_kernel(AttnArgs a) {
       __builtin_amdgcn_global_load_lds(kcb + static_cast<int64_t>(pos) * (AD * 2) + 16 * (cp ^ (r & 15)),
                                        sk + 1024 * q, 16, 0, 0);
     }
-    const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(a.vc + vc_block(a, b, j, kb0)) +
-                                2 * (kb0 % KB);
+    if ((blk & 1) == 0) {
+      // values of this block and the next together: whole 128-byte rows of the value block
+      const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(a.vc + vc_block(a, b, j, kb0));
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int d = 16 * q + (lane >> 2), cp = lane & 3;
-      __builtin_amdgcn_global_load_lds(vsrc + d * (KB * 2) + 16 * (cp ^ ((d >> 2) & 3)), sv + 1024 * q, 16, 0, 0);
+      for (int q = 0; q < 16; ++q) {
+        const int d = 16 * q + (lane >> 2), cp = lane & 3;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          __builtin_amdgcn_global_load_lds(vsrc + 64 * hh + d * (KB * 2) + 16 * (cp ^ ((d >> 2) & 3)),
+                                           sv + 16384 * hh + 1024 * q, 16, 0, 0);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0): the block is in LDS
     floatx4 S[2];
@@ -526,7 +536,7 @@ __global__ __launch_bounds__(64, 2) void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
       const int d = 16 * dt + c16;
-      u16x8 vv = *reinterpret_cast<const u16x8*>(sv + d * (DB * 2) + 16 * (g4 ^ ((d >> 2) & 3)));
+      u16x8 vv = *reinterpret_cast<const u16x8*>(sv + 16384 * (blk & 1) + d * (DB * 2) + 16 * (g4 ^ ((d >> 2) & 3)));
       if (valid < DB) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
