@@ -185,12 +185,15 @@ struct AttnArgs {
   uint16_t* o;
   uint16_t* qrot;
   float* part;                // decode only
+  int32_t split = 256;        // decode only: cached positions per wave, 256 or 512
 };
 // RoPE inverse frequencies theta^(-2f/rot_dim), f < rot_dim/2, computed on the host in fp64
 struct RopeTable {
   double inv_freq[128];
 };
-// the decode splits: keys per workgroup, and floats per partial result
+// Decode splits: the workspace holds partial results for ceil(S_max / kAttnSplit) splits,
+// the most a call uses (a wave takes kAttnSplit or 2 kAttnSplit positions); floats per
+// partial result
 constexpr int kAttnSplit = 256;
 constexpr int kAttnPartFloats = 260;
 __host__ __device__ inline int attn_splits(int S_max) { return (S_max + kAttnSplit - 1) / kAttnSplit; }
