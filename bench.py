@@ -60,6 +60,20 @@ def bf16_dev(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+def back_to_back(fn, steps, stream):
+    """`steps` calls of fn() back to back between one event pair on `stream`, synchronised on
+    both sides; returns ms per call."""
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def timed_launches(fn, steps, warmup, stream, p90=False):
     """Runs fn() warmup times, then `steps` times with a HIP event pair around
     each launch on `stream`.  Returns (total ms of the timed region from the
@@ -493,7 +507,8 @@ def bench_attention(dev, steps=20, warmup=20):
     ws = torch.empty(G.lib().gdn_attn_prefill_workspace_size(ctypes.byref(dims)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     fn = lambda: G.gdn_attn_prefill(qg, k, v, qw, kw, kc, vc, o, workspace=ws, stream=stream)
-    _, _, med_p = timed_launches(fn, steps, warmup, stream)
+    _, _, med_p_pair = timed_launches(fn, steps, warmup, stream)
+    med_p = back_to_back(fn, steps, stream)
     fl = attn_prefill_flops(1, T, Hq, D)
     del qg, k, v, kc, vc, o, ws
     B, S = 64, 4096
@@ -505,11 +520,14 @@ def bench_attention(dev, steps=20, warmup=20):
     dims = G.make_attn_dims(B, 1, Hq, Hkv, D, S)
     ws = torch.empty(G.lib().gdn_attn_decode_workspace_size(ctypes.byref(dims)), dtype=torch.uint8, device=dev)
     fn = lambda: G.gdn_attn_decode(qg, k, v, qw, kw, lens, kc, vc, o, workspace=ws, stream=stream)
-    _, _, med_d = timed_launches(fn, steps * 5, warmup, stream)
+    _, _, med_d_pair = timed_launches(fn, steps * 5, warmup, stream)
+    med_d = back_to_back(fn, steps * 5, stream)
     by = B * Hkv * S * D * 2 * 2 + B * (Hq * 2 * D + 2 * Hkv * D + Hq * D) * 2
     del kc, vc
     torch.cuda.empty_cache()
-    return dict(prefill_T=T, prefill_us=med_p * 1e3, prefill_tflops=fl / (med_p * 1e-3) / 1e12,
+    # prefill_us / decode_us: calls back to back; *_pair_median_us: an event pair around each call
+    return dict(prefill_T=T, prefill_us=med_p * 1e3, prefill_pair_median_us=med_p_pair * 1e3,
+                decode_pair_median_us=med_d_pair * 1e3, prefill_tflops=fl / (med_p * 1e-3) / 1e12,
                 prefill_mfma_frac=fl / (med_p * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
                 decode_B=B, decode_cached=S, decode_us=med_d * 1e3, decode_bytes=by,
                 decode_GBs=by / (med_d * 1e-3) / 1e9, decode_hbm_frac=by / (med_d * 1e-3) / (HBM_PEAK_GBS * 1e9))
